@@ -1,0 +1,139 @@
+"""Seeded synthetic inputs shared by the GPU library's tests/bench and the oracle.
+
+This module only draws random numbers and shapes them; it holds none of the
+attention method's arithmetic.  The workloads stand in for the attention
+layers the pages measure on (LLaDA-1.5 / LLaDA-8B and Dream-7B-Instruct at 8K
+context with 256 denoising steps, and a 64K long-context case), whose weights
+and evaluation data are not available:
+
+* Q, K, V ~ N(0, 1) in fp32, rounded to bf16 (round-to-nearest-even) before
+  either side sees them.
+* Per-query-head concentration: Q[h] *= t_h with t_h log-uniform in [0.5, 4]
+  ("different heads concentrate their attention mass to very different
+  extents", Step-dLLM abstract).
+* Attention sinks: keys 0-3 of every key head scaled by 4.
+* Denoising-step drift: after every step Q, K, V += 0.02 * N(0, 1), a fresh draw
+  per element ("attention patterns are only locally consistent across steps",
+  Step-dLLM abstract), with an abrupt full redraw of Q and K at chosen steps
+  ("shift abruptly at certain transitions").
+"""
+from dataclasses import dataclass, field
+import math
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    H: int                 # query heads
+    Hkv: int               # key/value heads
+    L: int                 # tokens
+    d: int                 # head dim
+    B: int                 # block size (tokens)
+    sparsities: tuple      # fraction of blocks dropped by the global budget
+    steps: int             # denoising steps
+    dense_steps: int       # dense warm-up steps before the first mask
+    refresh_every: int     # anchor period in steps; 0 = mask built once
+    temperatures: bool     # per-head Q temperature
+    sinks: bool            # keys 0-3 scaled by 4
+    drift: float           # per-step drift std (0 = static)
+    resample_steps: tuple = field(default=())
+    seed: int = 0
+
+    @property
+    def nb(self):
+        return self.L // self.B
+
+    @property
+    def rows(self):
+        return self.H * self.nb
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", H=2, Hkv=2, L=256, d=64, B=64, sparsities=(0.5,), steps=1,
+                     dense_steps=0, refresh_every=0, temperatures=False, sinks=True,
+                     drift=0.0, seed=1001),
+    "llada_2k": Workload("llada_2k", H=32, Hkv=32, L=2048, d=128, B=64, sparsities=(0.9,),
+                         steps=8, dense_steps=0, refresh_every=0, temperatures=True,
+                         sinks=False, drift=0.02, seed=1002),
+    "stepdllm_8k": Workload("stepdllm_8k", H=32, Hkv=32, L=8192, d=128, B=64,
+                            sparsities=(0.9,), steps=256, dense_steps=0, refresh_every=32,
+                            temperatures=True, sinks=False, drift=0.02,
+                            resample_steps=(64, 160), seed=1003),
+    "dream_gqa_8k": Workload("dream_gqa_8k", H=28, Hkv=4, L=8192, d=128, B=64,
+                             sparsities=(0.7, 0.8, 0.9, 0.95), steps=64, dense_steps=0,
+                             refresh_every=16, temperatures=True, sinks=False, drift=0.02,
+                             seed=1004),
+    "long_64k": Workload("long_64k", H=32, Hkv=32, L=65536, d=128, B=128, sparsities=(0.95,),
+                         steps=128, dense_steps=26, refresh_every=0, temperatures=False,
+                         sinks=True, drift=0.0, seed=1005),
+}
+
+
+def head_temperatures(H, seed):
+    """t_h = exp(U(ln 0.5, ln 4)) per query head, from a CPU generator."""
+    g = torch.Generator().manual_seed(seed)
+    u = torch.rand(H, generator=g, dtype=torch.float64)
+    return torch.exp(math.log(0.5) + u * (math.log(4.0) - math.log(0.5))).to(torch.float32)
+
+
+class Trajectory:
+    """Q/K/V (bf16) for each denoising step of a workload, generated in order.
+
+    ``next()`` returns the inputs of step 0, 1, 2, ...  The fp32 state drifts
+    between steps; the returned tensors are its bf16 rounding.
+    """
+
+    def __init__(self, w: Workload, device="cpu"):
+        self.w = w
+        self.device = torch.device(device)
+        self.temps = (head_temperatures(w.H, w.seed) if w.temperatures
+                      else torch.ones(w.H, dtype=torch.float32)).to(self.device)
+        self.gen = torch.Generator(device=self.device).manual_seed(w.seed)
+        self.step = 0
+        self.q = self._draw_q()
+        self.k = self._draw_k()
+        self.v = self._randn(w.Hkv, w.L, w.d)
+
+    def _randn(self, *shape):
+        return torch.randn(*shape, generator=self.gen, device=self.device, dtype=torch.float32)
+
+    def _draw_q(self):
+        return self._randn(self.w.H, self.w.L, self.w.d) * self.temps.view(-1, 1, 1)
+
+    def _draw_k(self):
+        k = self._randn(self.w.Hkv, self.w.L, self.w.d)
+        if self.w.sinks:
+            k[:, 0:4, :] *= 4.0
+        return k
+
+    def next(self):
+        """bf16 (q, k, v) for the current step, then advance the state."""
+        w = self.w
+        if self.step in w.resample_steps:
+            self.q = self._draw_q()
+            self.k = self._draw_k()
+        out = (self.q.to(torch.bfloat16), self.k.to(torch.bfloat16), self.v.to(torch.bfloat16))
+        if w.drift:
+            self.q += w.drift * self._randn(*self.q.shape)
+            self.k += w.drift * self._randn(*self.k.shape)
+            self.v += w.drift * self._randn(*self.v.shape)
+        self.step += 1
+        return out
+
+
+def random_qkv(H, Hkv, L, d, seed, device="cpu", q_scale=1.0, sinks=False):
+    """Plain seeded bf16 N(0,1) Q/K/V for small parity cases."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    q = torch.randn(H, L, d, generator=g, device=device) * q_scale
+    k = torch.randn(Hkv, L, d, generator=g, device=device)
+    v = torch.randn(Hkv, L, d, generator=g, device=device)
+    if sinks:
+        k[:, 0:4, :] *= 4.0
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+def to_host_f32(x):
+    """bf16 device/host tensor -> fp32 numpy array holding the same values."""
+    return x.detach().to("cpu").to(torch.float32).contiguous().numpy()

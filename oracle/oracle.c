@@ -1,0 +1,324 @@
+/*
+ * CPU oracle for pooled block-sparse bidirectional attention (Step-dLLM style).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plainly written reference
+ * that the GPU library is checked against.  Only the test suite, the smoke
+ * check and the CPU-baseline leg of the benchmark may load it.  It shares no
+ * code, header, table or constant with the GPU library.
+ *
+ * Sources (cited by page title and place):
+ *  [SD]  "Step-dLLM: Adaptive Step-aware Sparse Attention for Efficient
+ *        Diffusion LLM Inference" (arXiv 2611.01320), abstract: a block-sparse
+ *        mask refreshed at anchor steps and reused within each interval, a
+ *        head-adaptive global budget, bidirectional attention.
+ *  [SP]  "SparseD: Sparse Attention for Diffusion Language Models"
+ *        (arXiv 2509.24014), abstract: full attention in early steps, then one
+ *        precomputed sparse pattern reused for all later steps.
+ *  [BA]  "Block Approximate Sparse Attention (BA-Att)" abstract: blocks are
+ *        scored in a block-wise pre-downsampled space.
+ *
+ * The pages do not say how blocks are scored; the reading taken here is:
+ * mean-pool Q and K over each block of B tokens, score pooled pairs with
+ * Qb.Kb^T / sqrt(d), softmax each (head, query-block) row over key blocks,
+ * and keep the K = ceil((1-s) * H * nb^2) largest normalised scores over
+ * all heads together (one global budget), ties going to the lowest flat
+ * index (h*nb + i)*nb + j.
+ *
+ * Precision: the mask path (pool, score, softmax, select) is fp32, the
+ * precision in which the GPU takes the same integer decision; inputs are
+ * fp32 arrays holding bf16-rounded values.  Attention outputs are computed
+ * in fp64 (nothing is decided there, so the reference is as exact as the
+ * inputs allow).
+ *
+ * Layout: Q, O are [H, L, d]; K, V are [Hkv, L, d]; row-major, batch 1.
+ * Query head h reads key/value head h / (H / Hkv).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- pool --- */
+/* Block mean of B consecutive tokens ([BA] pre-downsampling; mean, not sum).
+ * x: [heads, L, d] -> xb: [heads, L/B, d].  Sum in fp32 in ascending token
+ * order, then scale by 1/B (a power of two here, so the scale is exact). */
+void oracle_pool(const float *x, int heads, int L, int d, int B, float *xb)
+{
+    int nb = L / B;
+    float inv_b = 1.0f / (float)B;
+    for (int h = 0; h < heads; ++h)
+        for (int i = 0; i < nb; ++i)
+            for (int c = 0; c < d; ++c) {
+                float sum = 0.0f;
+                for (int t = i * B; t < (i + 1) * B; ++t)
+                    sum = sum + x[((int64_t)h * L + t) * d + c];
+                xb[((int64_t)h * nb + i) * d + c] = sum * inv_b;
+            }
+}
+
+/* ------------------------------------------------------ score + softmax --- */
+/* S[h,i,j] = (Qb[h,i,:] . Kb[g(h),j,:]) * (1/sqrt(d)), then a softmax over j
+ * for each (h, i): the "normalised pooled scores" that the global budget
+ * ranks.  Dot product in fp32, ascending c; softmax max-subtracted, sum in
+ * ascending j. */
+void oracle_scores(const float *qb, const float *kb, int H, int Hkv, int nb,
+                   int d, float *P)
+{
+    int G = H / Hkv;
+    float sigma = (float)(1.0 / sqrt((double)d));
+    float *srow = (float *)malloc(sizeof(float) * (size_t)nb);
+    for (int h = 0; h < H; ++h) {
+        int g = h / G;
+        for (int i = 0; i < nb; ++i) {
+            const float *a = qb + ((int64_t)h * nb + i) * d;
+            float m = -INFINITY;
+            for (int j = 0; j < nb; ++j) {
+                const float *b = kb + ((int64_t)g * nb + j) * d;
+                float dot = 0.0f;
+                for (int c = 0; c < d; ++c) {
+                    float prod = a[c] * b[c];
+                    dot = dot + prod;
+                }
+                srow[j] = dot * sigma;
+                if (srow[j] > m)
+                    m = srow[j];
+            }
+            float *prow = P + ((int64_t)h * nb + i) * nb;
+            float sum = 0.0f;
+            for (int j = 0; j < nb; ++j) {
+                prow[j] = expf(srow[j] - m);
+                sum = sum + prow[j];
+            }
+            for (int j = 0; j < nb; ++j)
+                prow[j] = prow[j] / sum;
+        }
+    }
+    free(srow);
+}
+
+/* ------------------------------------------------------------ keep count --- */
+/* K = ceil((1 - s) * N) with N = H * nb^2 (the head-adaptive global budget of
+ * [SD] counts all query heads together).  A guard of 1e-9*N is subtracted
+ * before the ceiling so that a product that is mathematically an integer is
+ * not pushed up by binary representation error. */
+int64_t oracle_keep_count(int64_t n, double s)
+{
+    double x = (1.0 - s) * (double)n - 1e-9 * (double)n;
+    if (x <= 0.0)
+        return 0;
+    int64_t k = (int64_t)ceil(x);
+    return k > n ? n : k;
+}
+
+/* ---------------------------------------------------------------- select --- */
+/* Keep the K largest of all n normalised scores under the total order
+ * (value descending, flat index ascending): a full sort, the brute force
+ * definition of a global top-K with lowest-index ties. */
+static const float *g_sort_vals;
+
+static int by_value_desc_index_asc(const void *pa, const void *pb)
+{
+    int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    float va = g_sort_vals[a], vb = g_sort_vals[b];
+    if (va > vb) return -1;
+    if (va < vb) return 1;
+    return (a < b) ? -1 : (a > b);
+}
+
+void oracle_select(const float *P, int64_t n, int64_t K, uint8_t *keep)
+{
+    int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+    for (int64_t f = 0; f < n; ++f)
+        order[f] = f;
+    g_sort_vals = P;
+    qsort(order, (size_t)n, sizeof(int64_t), by_value_desc_index_asc);
+    memset(keep, 0, (size_t)n);
+    for (int64_t r = 0; r < K && r < n; ++r)
+        keep[order[r]] = 1;
+    free(order);
+}
+
+/* Value of the K-th kept score (the cut) under the same order; 0 if K == 0. */
+float oracle_cut_value(const float *P, int64_t n, int64_t K)
+{
+    if (K <= 0 || n <= 0)
+        return 0.0f;
+    int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+    for (int64_t f = 0; f < n; ++f)
+        order[f] = f;
+    g_sort_vals = P;
+    qsort(order, (size_t)n, sizeof(int64_t), by_value_desc_index_asc);
+    float v = P[order[(K < n ? K : n) - 1]];
+    free(order);
+    return v;
+}
+
+/* ------------------------------------------------------------------ lists --- */
+/* Per (head, query-block) row, the kept key blocks in ascending order. */
+void oracle_csr(const uint8_t *keep, int rows, int nb, int32_t *row_ptr,
+                int32_t *col_idx)
+{
+    int32_t nnz = 0;
+    for (int r = 0; r < rows; ++r) {
+        row_ptr[r] = nnz;
+        for (int j = 0; j < nb; ++j)
+            if (keep[(int64_t)r * nb + j])
+                col_idx[nnz++] = j;
+    }
+    row_ptr[rows] = nnz;
+}
+
+/* Full anchor-step mask build: pool, score, softmax, global select, lists.
+ * qb_out / kb_out / p_out receive the intermediates (caller-sized). */
+int64_t oracle_build_mask(const float *q, const float *k, int H, int Hkv, int L,
+                          int d, int B, double s, float *qb_out, float *kb_out,
+                          float *p_out, int32_t *row_ptr, int32_t *col_idx)
+{
+    int nb = L / B;
+    int64_t n = (int64_t)H * nb * nb;
+    oracle_pool(q, H, L, d, B, qb_out);
+    oracle_pool(k, Hkv, L, d, B, kb_out);
+    oracle_scores(qb_out, kb_out, H, Hkv, nb, d, p_out);
+    int64_t K = oracle_keep_count(n, s);
+    uint8_t *keep = (uint8_t *)malloc((size_t)n);
+    oracle_select(p_out, n, K, keep);
+    oracle_csr(keep, H * nb, nb, row_ptr, col_idx);
+    free(keep);
+    return K;
+}
+
+/* ------------------------------------------------------------------- plan --- */
+/* Work order for the attention launch: rows with at least one kept block,
+ * longest list first (ties by row id), then the empty rows in ascending id. */
+static const int32_t *g_row_ptr;
+
+static int by_len_desc_row_asc(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    int32_t la = g_row_ptr[a + 1] - g_row_ptr[a];
+    int32_t lb = g_row_ptr[b + 1] - g_row_ptr[b];
+    if (la > lb) return -1;
+    if (la < lb) return 1;
+    return (a < b) ? -1 : (a > b);
+}
+
+int32_t oracle_plan(const int32_t *row_ptr, int rows, int32_t *work)
+{
+    int32_t n_nonempty = 0;
+    for (int r = 0; r < rows; ++r) {
+        work[r] = r;
+        if (row_ptr[r + 1] > row_ptr[r])
+            ++n_nonempty;
+    }
+    g_row_ptr = row_ptr;
+    qsort(work, (size_t)rows, sizeof(int32_t), by_len_desc_row_asc);
+    return n_nonempty;
+}
+
+/* -------------------------------------------------------------- attention --- */
+/* Bidirectional softmax attention of one query token over an explicit list of
+ * key tokens (ascending), fp64:  o = sum_u softmax_u(q . k_u / sqrt(d)) v_u.
+ * An empty list gives o = 0 (a row that kept no block attends to nothing). */
+static void attend_token(const float *qt, const float *kh, const float *vh,
+                         int d, const int32_t *toks, int ntok, double *z,
+                         double *o)
+{
+    double scale = 1.0 / sqrt((double)d);
+    for (int c = 0; c < d; ++c)
+        o[c] = 0.0;
+    if (ntok == 0)
+        return;
+    double m = -INFINITY;
+    for (int a = 0; a < ntok; ++a) {
+        const float *ku = kh + (int64_t)toks[a] * d;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c)
+            dot += (double)qt[c] * (double)ku[c];
+        z[a] = dot * scale;
+        if (z[a] > m)
+            m = z[a];
+    }
+    double l = 0.0;
+    for (int a = 0; a < ntok; ++a) {
+        z[a] = exp(z[a] - m);
+        l += z[a];
+    }
+    for (int a = 0; a < ntok; ++a) {
+        const float *vu = vh + (int64_t)toks[a] * d;
+        double p = z[a] / l;
+        for (int c = 0; c < d; ++c)
+            o[c] += p * (double)vu[c];
+    }
+}
+
+/* Block-sparse attention for the listed rows r = h*nb + i (all rows when
+ * rows == NULL).  Each query token of block i in head h attends to every
+ * token of the kept key blocks col_idx[row_ptr[r] .. row_ptr[r+1]) of key
+ * head h / (H/Hkv).  Output o: [H, L, d] fp64; only listed rows are written. */
+void oracle_sparse_attn(const float *q, const float *k, const float *v, int H,
+                        int Hkv, int L, int d, int B, const int32_t *row_ptr,
+                        const int32_t *col_idx, const int32_t *rows, int n_rows,
+                        double *o)
+{
+    int nb = L / B, G = H / Hkv;
+    int total = rows ? n_rows : H * nb;
+    int32_t *toks = (int32_t *)malloc(sizeof(int32_t) * (size_t)L);
+    double *z = (double *)malloc(sizeof(double) * (size_t)L);
+    for (int x = 0; x < total; ++x) {
+        int r = rows ? rows[x] : x;
+        int h = r / nb, i = r % nb, g = h / G;
+        int ntok = 0;
+        for (int e = row_ptr[r]; e < row_ptr[r + 1]; ++e)
+            for (int t = 0; t < B; ++t)
+                toks[ntok++] = col_idx[e] * B + t;
+        const float *kh = k + (int64_t)g * L * d;
+        const float *vh = v + (int64_t)g * L * d;
+        for (int t = i * B; t < (i + 1) * B; ++t)
+            attend_token(q + ((int64_t)h * L + t) * d, kh, vh, d, toks, ntok, z,
+                         o + ((int64_t)h * L + t) * d);
+    }
+    free(toks);
+    free(z);
+}
+
+/* Dense bidirectional attention (every block kept) for the listed rows. */
+void oracle_dense_attn(const float *q, const float *k, const float *v, int H,
+                       int Hkv, int L, int d, int B, const int32_t *rows,
+                       int n_rows, double *o)
+{
+    int nb = L / B, G = H / Hkv;
+    int total = rows ? n_rows : H * nb;
+    int32_t *toks = (int32_t *)malloc(sizeof(int32_t) * (size_t)L);
+    double *z = (double *)malloc(sizeof(double) * (size_t)L);
+    for (int u = 0; u < L; ++u)
+        toks[u] = u;
+    for (int x = 0; x < total; ++x) {
+        int r = rows ? rows[x] : x;
+        int h = r / nb, i = r % nb, g = h / G;
+        const float *kh = k + (int64_t)g * L * d;
+        const float *vh = v + (int64_t)g * L * d;
+        for (int t = i * B; t < (i + 1) * B; ++t)
+            attend_token(q + ((int64_t)h * L + t) * d, kh, vh, d, toks, L, z,
+                         o + ((int64_t)h * L + t) * d);
+    }
+    free(toks);
+    free(z);
+}
+
+/* ----------------------------------------------------------------- driver --- */
+/* What a denoising step runs ([SD] anchors + reuse; [SP] dense warm-up then
+ * one mask reused): 0 = dense attention, 1 = anchor (rebuild the mask from
+ * this step's Q/K, then sparse attention), 2 = sparse attention on the stored
+ * mask.  refresh_every == 0 means the mask is built once, at the first
+ * sparse step, and never refreshed. */
+int oracle_step_kind(int step, int dense_steps, int refresh_every)
+{
+    if (step < dense_steps)
+        return 0;
+    int since = step - dense_steps;
+    if (since == 0)
+        return 1;
+    if (refresh_every > 0 && since % refresh_every == 0)
+        return 1;
+    return 2;
+}

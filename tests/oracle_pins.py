@@ -1,0 +1,356 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each ``pin_*`` function takes a loaded oracle library and raises
+AssertionError when the oracle disagrees with what the mathematics fixes:
+closed forms, worked examples whose answer is derived by hand, invariants,
+and brute force written in a different formulation (whole-matrix numpy fp64
+instead of the oracle's per-row list loops).  The mutation tests run every
+pin against deliberately broken copies of the oracle to show that the pins
+can fail.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+
+import oracle as O
+
+RNG_SEEDS = (11, 12, 13)
+
+
+def _bf16_round(x):
+    """Round fp32 numpy values to bf16 (RNE), kept as fp32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def _rand(shape, rng, scale=1.0):
+    return _bf16_round(rng.standard_normal(shape).astype(np.float32) * scale)
+
+
+def _expand_block_mask(keep, B):
+    """[H, nb, nb] block mask -> [H, L, L] token mask."""
+    return np.repeat(np.repeat(keep.astype(bool), B, axis=1), B, axis=2)
+
+
+def brute_attention(q, k, v, token_mask):
+    """Whole-matrix fp64 masked softmax attention; fully masked rows give 0."""
+    H, L, d = q.shape
+    Hkv = k.shape[0]
+    G = H // Hkv
+    out = np.zeros((H, L, d))
+    for h in range(H):
+        g = h // G
+        s = q[h].astype(np.float64) @ k[g].astype(np.float64).T / math.sqrt(d)
+        m = token_mask[h]
+        s = np.where(m, s, -np.inf)
+        rowmax = s.max(axis=1, keepdims=True)
+        live = np.isfinite(rowmax[:, 0])
+        e = np.zeros_like(s)
+        e[live] = np.exp(s[live] - rowmax[live])
+        den = e.sum(axis=1, keepdims=True)
+        den[~live] = 1.0
+        out[h] = (e / den) @ v[g].astype(np.float64)
+    return out
+
+
+# ------------------------------------------------------------------ budget --
+def pin_keep_count(lib):
+    """K = ceil((1-s)*N) in exact rational arithmetic, for every workload size."""
+    cases = [(32, "0.5"), (32768, "0.9"), (524288, "0.9"), (458752, "0.7"), (458752, "0.8"),
+             (458752, "0.9"), (458752, "0.95"), (8388608, "0.95"), (64, "0.75"), (96, "0"),
+             (100, "0.99"), (7, "0.5"), (1, "0.5")]
+    for n, s in cases:
+        want = math.ceil((1 - Fraction(s)) * n)
+        got = O.keep_count(n, float(s), lib)
+        assert got == want, (n, s, got, want)
+    # Values the workloads rely on, written out.
+    assert O.keep_count(524288, 0.9, lib) == 52429
+    assert O.keep_count(8388608, 0.95, lib) == 419431
+    assert O.keep_count(32, 0.5, lib) == 16
+
+
+# -------------------------------------------------------------------- pool --
+def pin_pool(lib):
+    # Closed form: a ramp x[h,t,c] = t + c/4 has block means i*B + (B-1)/2 + c/4.
+    for B in (64, 128):
+        H, L, d = 3, 4 * B, 64
+        t = np.arange(L, dtype=np.float32)[None, :, None]
+        c = np.arange(d, dtype=np.float32)[None, None, :] / 4
+        x = np.broadcast_to(t + c + np.arange(H, dtype=np.float32)[:, None, None] * 1000,
+                            (H, L, d)).astype(np.float32)
+        got = O.pool(x, B, lib)
+        i = np.arange(L // B, dtype=np.float64)[None, :, None]
+        want = (i * B + (B - 1) / 2 + np.arange(d)[None, None, :] / 4
+                + np.arange(H)[:, None, None] * 1000)
+        assert np.array_equal(got.astype(np.float64), want), "ramp block mean"
+    # Random data: within fp32 summation error of the fp64 mean.
+    rng = np.random.default_rng(RNG_SEEDS[0])
+    x = _rand((2, 256, 128), rng)
+    got = O.pool(x, 64, lib).astype(np.float64)
+    want = x.astype(np.float64).reshape(2, 4, 64, 128).mean(axis=2)
+    assert np.max(np.abs(got - want)) <= 64 * 2 ** -24 * np.max(np.abs(x)), "random block mean"
+
+
+# ---------------------------------------------------------- score/softmax --
+def pin_scores(lib):
+    rng = np.random.default_rng(RNG_SEEDS[1])
+    # Q = 0: every pooled score is 0, so every softmax row is exactly 1/nb.
+    qb = np.zeros((3, 8, 64), np.float32)
+    kb = _rand((3, 8, 64), rng)
+    P = O.scores(qb, kb, lib)
+    assert np.all(P == np.float32(1 / 8)), "uniform rows"
+    # fp64 definition with the GQA map g(h) = h // (H/Hkv), H=6, Hkv=2.
+    for d in (64, 128):
+        qb = _rand((6, 16, d), rng, 0.3)
+        kb = _rand((2, 16, d), rng, 0.3)
+        P = O.scores(qb, kb, lib).astype(np.float64)
+        G = 3
+        for h in range(6):
+            s = qb[h].astype(np.float64) @ kb[h // G].astype(np.float64).T / math.sqrt(d)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            want = e / e.sum(axis=1, keepdims=True)
+            rel = np.max(np.abs(P[h] - want) / want)
+            assert rel < 2e-6, (d, h, rel)
+        assert np.allclose(P.sum(axis=2), 1.0, atol=2e-6)
+
+
+# ------------------------------------------------------------------ select --
+def _brute_select(P, K):
+    flat = P.reshape(-1).astype(np.float64)
+    order = np.lexsort((np.arange(flat.size), -flat))   # value desc, then index asc
+    keep = np.zeros(flat.size, np.uint8)
+    keep[order[:K]] = 1
+    return keep.reshape(P.shape)
+
+
+def pin_select(lib):
+    rng = np.random.default_rng(RNG_SEEDS[2])
+    # Many exact ties: values drawn from 5 levels.
+    for n_levels, shape in ((5, (2, 8, 8)), (3, (4, 4, 4)), (50, (3, 16, 16))):
+        levels = np.sort(rng.random(n_levels)).astype(np.float32)
+        P = levels[rng.integers(0, n_levels, size=shape)]
+        N = P.size
+        for K in (0, 1, N // 3, N // 2, N - 1, N):
+            got = O.select(P, K, lib)
+            assert np.array_equal(got, _brute_select(P, K)), (shape, K)
+            assert int(got.sum()) == K
+    # All equal: the first K flat indices.
+    P = np.full((2, 4, 4), 0.25, np.float32)
+    for K in (0, 5, 16, 31, 32):
+        got = O.select(P, K, lib).reshape(-1)
+        assert np.array_equal(got, (np.arange(32) < K).astype(np.uint8)), K
+    # The cut value is the K-th largest.
+    P = rng.random((2, 8, 8)).astype(np.float32)
+    assert O.cut_value(P, 10, lib) == np.sort(P.reshape(-1))[::-1][9]
+
+
+def pin_csr(lib):
+    rng = np.random.default_rng(RNG_SEEDS[0] + 7)
+    keep = (rng.random((3, 8, 8)) < 0.3).astype(np.uint8)
+    keep[1, 2, :] = 0            # one empty row
+    row_ptr, col_idx = O.csr(keep, lib)
+    flat = keep.reshape(24, 8)
+    assert row_ptr[0] == 0 and np.array_equal(np.diff(row_ptr), flat.sum(axis=1))
+    for r in range(24):
+        assert np.array_equal(col_idx[row_ptr[r]:row_ptr[r + 1]], np.nonzero(flat[r])[0])
+
+
+def pin_plan(lib):
+    rng = np.random.default_rng(RNG_SEEDS[1] + 7)
+    lens = rng.integers(0, 6, size=40)
+    lens[[3, 17, 29]] = 0
+    row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    work, n = O.plan(row_ptr, lib)
+    want = sorted(range(40), key=lambda r: (-lens[r], r))
+    assert list(work) == want and n == int((lens > 0).sum())
+
+
+# --------------------------------------------------------------- attention --
+def _random_mask(H, nb, rng, frac):
+    keep = (rng.random((H, nb, nb)) < frac).astype(np.uint8)
+    return keep
+
+
+def pin_attention_brute(lib):
+    rng = np.random.default_rng(RNG_SEEDS[2] + 7)
+    for (H, Hkv, nb, d, B) in ((2, 2, 4, 64, 64), (4, 2, 3, 128, 64), (3, 1, 2, 64, 128)):
+        L = nb * B
+        q, k, v = _rand((H, L, d), rng), _rand((Hkv, L, d), rng), _rand((Hkv, L, d), rng)
+        keep = _random_mask(H, nb, rng, 0.5)
+        keep[0, 0, :] = 0                      # an empty row
+        row_ptr, col_idx = O.csr(keep, lib)
+        got = O.sparse_attn(q, k, v, B, row_ptr, col_idx, lib=lib)
+        want = brute_attention(q, k, v, _expand_block_mask(keep, B))
+        assert np.max(np.abs(got - want)) < 1e-12, ("sparse", H, Hkv, nb, d, B)
+        assert np.all(got[0, :B] == 0.0), "empty row is zero"
+        gd = O.dense_attn(q, k, v, B, lib=lib)
+        wd = brute_attention(q, k, v, np.ones((H, L, L), bool))
+        assert np.max(np.abs(gd - wd)) < 1e-12, ("dense", H, Hkv, nb, d, B)
+        # A row subset writes exactly those rows.
+        rows = np.array([H * nb - 1, 1], np.int32)
+        part = O.sparse_attn(q, k, v, B, row_ptr, col_idx, rows=rows, lib=lib)
+        for r in rows:
+            h, i = divmod(int(r), nb)
+            assert np.array_equal(part[h, i * B:(i + 1) * B], got[h, i * B:(i + 1) * B])
+
+
+def pin_attention_closed_forms(lib):
+    rng = np.random.default_rng(RNG_SEEDS[0] + 17)
+    H, Hkv, nb, d, B = 4, 2, 4, 64, 64
+    L = nb * B
+    q, k = _rand((H, L, d), rng), _rand((Hkv, L, d), rng)
+    keep = _random_mask(H, nb, rng, 0.4)
+    keep[1, 3, :] = 0
+    keep[2, 0, :] = 1
+    row_ptr, col_idx = O.csr(keep, lib)
+    rows_nonempty = keep.reshape(H * nb, nb).any(axis=1)
+    # Constant V = c gives O = c on every non-empty row.
+    c = np.float32(-1.5)
+    v = np.full((Hkv, L, d), c, np.float32)
+    o = O.sparse_attn(q, k, v, B, row_ptr, col_idx, lib=lib).reshape(H * nb, B, d)
+    assert np.all(np.abs(o[rows_nonempty] - c) < 1e-12) and np.all(o[~rows_nonempty] == 0)
+    # Q = 0 gives the mean of V over the kept blocks' tokens.
+    v = _rand((Hkv, L, d), rng)
+    o = O.sparse_attn(np.zeros_like(q), k, v, B, row_ptr, col_idx, lib=lib)
+    for h in range(H):
+        for i in range(nb):
+            kept = np.nonzero(keep[h, i])[0]
+            want = (v[h // 2].astype(np.float64).reshape(nb, B, d)[kept].reshape(-1, d).mean(axis=0)
+                    if kept.size else np.zeros(d))
+            assert np.max(np.abs(o[h, i * B:(i + 1) * B] - want)) < 1e-12, (h, i)
+    # s = 0 keeps everything: sparse equals dense.
+    full = np.ones((H, nb, nb), np.uint8)
+    rp, ci = O.csr(full, lib)
+    a = O.sparse_attn(q, k, v, B, rp, ci, lib=lib)
+    b = O.dense_attn(q, k, v, B, lib=lib)
+    assert np.max(np.abs(a - b)) < 1e-12
+    # GQA: H=4 over Hkv=2 equals H=4 over Hkv=4 with each key head duplicated.
+    k4, v4 = np.repeat(k, 2, axis=0), np.repeat(v, 2, axis=0)
+    a = O.sparse_attn(q, k, v, B, row_ptr, col_idx, lib=lib)
+    b = O.sparse_attn(q, k4, v4, B, row_ptr, col_idx, lib=lib)
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------- worked examples --
+def worked_example_w1():
+    """H=Hkv=2, d=64, L=256, B=64 (nb=4), s=0.5 -> K=16.
+
+    Head 0: every query token of block i is 20*e_i and every key token of
+    block j is 20*e_j, so S_ij = 400/8 * [i == j] = 50 [i == j]; each row's
+    softmax is 1 on the diagonal and e^-50 / (1 + 3 e^-50) elsewhere.
+    Head 1: Q = 0, so every score is exactly 1/4.
+    The 16 largest: head 0's four diagonal ones (value 1), then twelve 0.25s
+    of head 1 in lowest flat order -- rows 0, 1, 2 of head 1 complete, row 3
+    of head 1 empty.  The concentrated head keeps one block per row.
+    """
+    rng = np.random.default_rng(5)
+    H, d, B, nb = 2, 64, 64, 4
+    L = nb * B
+    q = np.zeros((H, L, d), np.float32)
+    k = _rand((H, L, d), rng)
+    for i in range(nb):
+        q[0, i * B:(i + 1) * B, i] = 20.0
+        k[0, i * B:(i + 1) * B, :] = 0.0
+        k[0, i * B:(i + 1) * B, i] = 20.0
+    v = _rand((H, L, d), rng)
+    keep = np.zeros((H, nb, nb), np.uint8)
+    for i in range(nb):
+        keep[0, i, i] = 1
+    keep[1, 0:3, :] = 1
+    return q, k, v, keep
+
+
+def pin_worked_w1(lib):
+    q, k, v, keep_want = worked_example_w1()
+    B = 64
+    m = O.build_mask(q, k, B, 0.5, lib)
+    P = m["P"]
+    assert m["K"] == 16
+    for i in range(4):
+        assert P[0, i, i] == np.float32(1.0)
+        for j in range(4):
+            if j != i:
+                assert abs(P[0, i, j] / math.exp(-50) - 1) < 1e-6
+    assert np.all(P[1] == np.float32(0.25))
+    keep = np.zeros(P.shape, np.uint8)
+    for r in range(8):
+        keep.reshape(8, 4)[r, m["col_idx"][m["row_ptr"][r]:m["row_ptr"][r + 1]]] = 1
+    assert np.array_equal(keep, keep_want)
+    o = O.sparse_attn(q, k, v, B, m["row_ptr"], m["col_idx"], lib=lib)
+    for i in range(4):
+        want = v[0, i * B:(i + 1) * B].astype(np.float64).mean(axis=0)
+        assert np.max(np.abs(o[0, i * B:(i + 1) * B] - want)) < 1e-12
+    want1 = v[1].astype(np.float64).mean(axis=0)
+    assert np.max(np.abs(o[1, :3 * B] - want1)) < 1e-12
+    assert np.all(o[1, 3 * B:] == 0)
+
+
+def pin_worked_w2(lib):
+    """Q = 0 for every head: every score is 1/nb and the mask is the first K
+    flat indices, whatever the sparsity."""
+    rng = np.random.default_rng(6)
+    H, Hkv, nb, d, B = 4, 2, 8, 128, 64
+    L = nb * B
+    q = np.zeros((H, L, d), np.float32)
+    k = _rand((Hkv, L, d), rng)
+    for s in (0.0, 0.3, 0.5, 0.9, 0.97):
+        m = O.build_mask(q, k, B, s, lib)
+        K = math.ceil((1 - Fraction(str(s))) * H * nb * nb)
+        assert m["K"] == K
+        flat = np.zeros(H * nb * nb, np.uint8)
+        for r in range(H * nb):
+            flat[r * nb + m["col_idx"][m["row_ptr"][r]:m["row_ptr"][r + 1]]] = 1
+        assert np.array_equal(flat, (np.arange(H * nb * nb) < K).astype(np.uint8)), s
+
+
+def pin_build_mask_brute(lib):
+    """The mask of build_mask equals a brute-force sort of fp64-recomputed
+    scores wherever the fp64 value is not within 1e-5 of the cut."""
+    rng = np.random.default_rng(7)
+    H, Hkv, nb, d, B = 4, 2, 8, 64, 64
+    L = nb * B
+    q = _rand((H, L, d), rng) * np.array([0.5, 1, 2, 4], np.float32)[:, None, None]
+    q = _bf16_round(q)
+    k = _rand((Hkv, L, d), rng)
+    m = O.build_mask(q, k, B, 0.8, lib)
+    qb = q.astype(np.float64).reshape(H, nb, B, d).mean(axis=2)
+    kb = k.astype(np.float64).reshape(Hkv, nb, B, d).mean(axis=2)
+    P64 = np.empty((H, nb, nb))
+    for h in range(H):
+        s = qb[h] @ kb[h // 2].T / math.sqrt(d)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        P64[h] = e / e.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(m["P"] - P64) / P64) < 2e-6
+    K = m["K"]
+    want = _brute_select(P64, K).reshape(-1)
+    got = np.zeros(H * nb * nb, np.uint8)
+    for r in range(H * nb):
+        got[r * nb + m["col_idx"][m["row_ptr"][r]:m["row_ptr"][r + 1]]] = 1
+    cut = np.sort(P64.reshape(-1))[::-1][K - 1]
+    near = np.abs(P64.reshape(-1) - cut) <= 1e-5 * cut
+    assert np.array_equal(got[~near], want[~near])
+    assert int(got.sum()) == K
+
+
+# ------------------------------------------------------------------ driver --
+def pin_step_kind(lib):
+    # Anchor every 32 steps over 256 steps: anchors 0, 32, ..., 224.
+    kinds = [O.step_kind(t, 0, 32, lib) for t in range(256)]
+    assert [t for t, x in enumerate(kinds) if x == 1] == list(range(0, 256, 32))
+    assert all(x in (1, 2) for x in kinds)
+    # Built once at step 0, reused for 7.
+    assert [O.step_kind(t, 0, 0, lib) for t in range(8)] == [1] + [2] * 7
+    # Dense warm-up for 26 of 128 steps, then one mask reused to the end.
+    kinds = [O.step_kind(t, 26, 0, lib) for t in range(128)]
+    assert kinds == [0] * 26 + [1] + [2] * 101
+    # Dense warm-up followed by periodic refresh.
+    kinds = [O.step_kind(t, 3, 4, lib) for t in range(12)]
+    assert kinds == [0, 0, 0, 1, 2, 2, 2, 1, 2, 2, 2, 1]
+
+
+ALL_PINS = [pin_keep_count, pin_pool, pin_scores, pin_select, pin_csr, pin_plan,
+            pin_attention_brute, pin_attention_closed_forms, pin_worked_w1, pin_worked_w2,
+            pin_build_mask_brute, pin_step_kind]

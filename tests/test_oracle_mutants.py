@@ -1,0 +1,79 @@
+"""Plant a plausible mistake in a copy of the oracle (on the CPU) and check that
+at least one pin catches it: the pins are strong enough to trust the oracle."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle as O
+
+SRC = os.path.join(os.path.dirname(O.__file__), "oracle.c")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (name, original text, mutated text, which occurrence)
+MUTANTS = [
+    ("pool_drops_last_token", "t < (i + 1) * B", "t < (i + 1) * B - 1", 0),
+    ("pool_skips_first_token", "int t = i * B;", "int t = i * B + 1;", 0),
+    ("pool_sum_not_mean", "xb[((int64_t)h * nb + i) * d + c] = sum * inv_b;",
+     "xb[((int64_t)h * nb + i) * d + c] = sum;", 0),
+    ("score_gqa_modulo", "int g = h / G;\n        for (int i = 0; i < nb; ++i) {",
+     "int g = h % Hkv;\n        for (int i = 0; i < nb; ++i) {", 0),
+    ("score_scale_1_over_d", "float sigma = (float)(1.0 / sqrt((double)d));",
+     "float sigma = (float)(1.0 / (double)d);", 0),
+    ("softmax_unnormalised", "prow[j] = prow[j] / sum;", "prow[j] = prow[j];", 0),
+    ("score_transposed_kb", "const float *b = kb + ((int64_t)g * nb + j) * d;",
+     "const float *b = kb + ((int64_t)g * nb + j);", 0),
+    ("keep_count_floor", "int64_t k = (int64_t)ceil(x);", "int64_t k = (int64_t)floor(x);", 0),
+    ("select_ascending", "if (va > vb) return -1;", "if (va < vb) return -1;", 0),
+    ("select_ties_highest_index", "return (a < b) ? -1 : (a > b);",
+     "return (a > b) ? -1 : (a < b);", 0),
+    ("select_keeps_one_less", "for (int64_t r = 0; r < K && r < n; ++r)",
+     "for (int64_t r = 1; r < K && r < n; ++r)", 0),
+    ("csr_transposed", "if (keep[(int64_t)r * nb + j])", "if (keep[(int64_t)j * nb + r])", 0),
+    ("plan_ascending", "if (la > lb) return -1;", "if (la < lb) return -1;", 0),
+    ("attn_block_index_not_scaled", "toks[ntok++] = col_idx[e] * B + t;",
+     "toks[ntok++] = col_idx[e] + t;", 0),
+    ("attn_no_scale", "double scale = 1.0 / sqrt((double)d);", "double scale = 1.0;", 0),
+    ("attn_unnormalised", "double p = z[a] / l;", "double p = z[a];", 0),
+    ("attn_gqa_modulo", "int h = r / nb, i = r % nb, g = h / G;",
+     "int h = r / nb, i = r % nb, g = h % Hkv;", 0),
+    ("dense_gqa_modulo", "int h = r / nb, i = r % nb, g = h / G;",
+     "int h = r / nb, i = r % nb, g = h % Hkv;", 1),
+    ("attn_wrong_query_block", "for (int t = i * B; t < (i + 1) * B; ++t)\n            attend_token(q + ((int64_t)h * L + t) * d, kh, vh, d, toks, ntok",
+     "for (int t = i * B; t < (i + 1) * B; ++t)\n            attend_token(q + ((int64_t)h * L + (t + B) % L) * d, kh, vh, d, toks, ntok", 0),
+    ("driver_period_from_zero", "since % refresh_every == 0", "step % refresh_every == 0", 0),
+]
+
+
+def _replace_nth(text, old, new, n):
+    start = -1
+    for _ in range(n + 1):
+        start = text.index(old, start + 1)
+    return text[:start] + new + text[start + len(old):]
+
+
+@pytest.mark.parametrize("name,old,new,nth", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new, nth, tmp_path):
+    text = open(SRC).read()
+    assert text.count(old) > nth, f"mutation site for {name} not found"
+    src = tmp_path / "oracle_mut.c"
+    src.write_text(_replace_nth(text, old, new, nth))
+    so = str(tmp_path / "liboracle_mut.so")
+    subprocess.run(["gcc", *O.oracle._CFLAGS, str(src), "-o", so, "-lm"], check=True)
+    # Run the pins in a child process: a mutant may also crash (that counts as caught).
+    script = (
+        "import sys; sys.path[:0] = [%r, %r]\n"
+        "import oracle as O, oracle_pins as pins\n"
+        "lib = O.load(%r)\n"
+        "failed = []\n"
+        "for pin in pins.ALL_PINS:\n"
+        "    try:\n"
+        "        pin(lib)\n"
+        "    except Exception as e:\n"
+        "        failed.append(pin.__name__)\n"
+        "print('caught by:', failed)\n"
+        "sys.exit(1 if failed else 0)\n"
+    ) % (ROOT, os.path.join(ROOT, "tests"), so)
+    r = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} passed every pin: {r.stdout} {r.stderr}"
