@@ -1,0 +1,251 @@
+// C ABI entry points (include/stepdllm.h): validation, workspace carve-up,
+// launch sequencing and the denoising-step driver.  Host code only.
+//
+// Schedule: "Step-dLLM: Adaptive Step-aware Sparse Attention for Efficient
+// Diffusion LLM Inference", abstract (mask refreshed at anchor steps, reused
+// within each interval); "SparseD: Sparse Attention for Diffusion Language
+// Models", abstract (dense attention for the early steps, then one sparse
+// pattern reused for every later step).
+#include <math.h>
+#include <stdlib.h>
+
+#include "../../include/stepdllm.h"
+#include "common.h"
+
+using sd::Dims;
+using sd::WsLayout;
+
+namespace {
+
+int check_dims(const stepdllm_dims *d, Dims *out) {
+    if (!d) return STEPDLLM_EINVAL;
+    if (d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->seq_len <= 0 || d->head_dim <= 0 ||
+        d->block <= 0)
+        return STEPDLLM_EINVAL;
+    if (d->n_q_heads % d->n_kv_heads != 0) return STEPDLLM_EINVAL;
+    if (d->seq_len % d->block != 0) return STEPDLLM_EINVAL;
+    if (d->head_dim != 64 && d->head_dim != 128) return STEPDLLM_EUNSUPPORTED;
+    if (d->block != 64 && d->block != 128) return STEPDLLM_EUNSUPPORTED;
+    const int64_t nb = d->seq_len / d->block;
+    if (nb > sd::kMaxBlocks) return STEPDLLM_EUNSUPPORTED;
+    if ((int64_t)d->n_q_heads * nb * nb >= ((int64_t)1 << 31)) return STEPDLLM_EUNSUPPORTED;
+    if ((int64_t)d->n_q_heads * d->seq_len * d->head_dim >= ((int64_t)1 << 40))
+        return STEPDLLM_EUNSUPPORTED;
+    if (out) {
+        out->H = d->n_q_heads;
+        out->Hkv = d->n_kv_heads;
+        out->L = d->seq_len;
+        out->d = d->head_dim;
+        out->B = d->block;
+        out->nb = (int)nb;
+        out->G = d->n_q_heads / d->n_kv_heads;
+    }
+    return STEPDLLM_OK;
+}
+
+int64_t keep_count(const Dims &D, double s) {
+    const double n = (double)D.n_scores();
+    const double x = (1.0 - s) * n - 1e-9 * n;
+    if (x <= 0.0) return 0;
+    int64_t k = (int64_t)ceil(x);
+    return k > D.n_scores() ? D.n_scores() : k;
+}
+
+bool sparsity_ok(double s) { return s >= 0.0 && s < 1.0; }   // false for NaN
+
+int hip_status(hipError_t e) { return e == hipSuccess ? STEPDLLM_OK : STEPDLLM_EHIP; }
+
+int select_and_plan(const Dims &D, double sparsity, const float *p, char *ws, const WsLayout &w,
+                    int32_t *row_ptr, int32_t *col_idx, hipStream_t s) {
+    int st = hip_status(sd::launch_select(D, keep_count(D, sparsity), p, ws, w, row_ptr, col_idx, s));
+    if (st) return st;
+    return hip_status(sd::launch_plan(D, row_ptr, ws, w, s));
+}
+
+}  // namespace
+
+struct stepdllm_driver {
+    Dims D;
+    stepdllm_schedule sched;
+    char *ws;
+    size_t ws_bytes;
+    int32_t *row_ptr, *col_idx;
+    int64_t K;
+    bool have_mask;
+};
+
+extern "C" {
+
+int64_t stepdllm_keep_count(const stepdllm_dims *dims, double sparsity) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!sparsity_ok(sparsity)) return STEPDLLM_EINVAL;
+    return keep_count(D, sparsity);
+}
+
+int64_t stepdllm_workspace_bytes(const stepdllm_dims *dims) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    return sd::ws_layout(D).total;
+}
+
+int stepdllm_workspace_layout(const stepdllm_dims *dims, stepdllm_ws_layout *out) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!out) return STEPDLLM_EINVAL;
+    WsLayout w = sd::ws_layout(D);
+    out->pooled_q = w.qb;
+    out->pooled_k = w.kb;
+    out->scores = w.p;
+    out->select = w.sel;
+    out->work = w.work;
+    out->work_meta = w.work_meta;
+    out->total = w.total;
+    return STEPDLLM_OK;
+}
+
+int stepdllm_build_mask(const stepdllm_dims *dims, double sparsity, const uint16_t *q,
+                        const uint16_t *k, void *ws, size_t ws_bytes, int32_t *row_ptr,
+                        int32_t *col_idx, float *scores_out, void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!sparsity_ok(sparsity) || !q || !k || !ws || !row_ptr || !col_idx) return STEPDLLM_EINVAL;
+    WsLayout w = sd::ws_layout(D);
+    if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
+    char *base = static_cast<char *>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *qb = reinterpret_cast<float *>(base + w.qb);
+    float *kb = reinterpret_cast<float *>(base + w.kb);
+    float *p = reinterpret_cast<float *>(base + w.p);
+    if ((st = hip_status(sd::launch_pool(D, q, k, qb, kb, s)))) return st;
+    if ((st = hip_status(sd::launch_scores(D, qb, kb, p, scores_out, s)))) return st;
+    return select_and_plan(D, sparsity, p, base, w, row_ptr, col_idx, s);
+}
+
+int stepdllm_select_mask(const stepdllm_dims *dims, double sparsity, const float *scores,
+                         void *ws, size_t ws_bytes, int32_t *row_ptr, int32_t *col_idx,
+                         void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!sparsity_ok(sparsity) || !scores || !ws || !row_ptr || !col_idx) return STEPDLLM_EINVAL;
+    WsLayout w = sd::ws_layout(D);
+    if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
+    return select_and_plan(D, sparsity, scores, static_cast<char *>(ws), w, row_ptr, col_idx,
+                           static_cast<hipStream_t>(stream));
+}
+
+int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr, void *ws, size_t ws_bytes,
+                  void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!row_ptr || !ws) return STEPDLLM_EINVAL;
+    WsLayout w = sd::ws_layout(D);
+    if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
+    return hip_status(
+        sd::launch_plan(D, row_ptr, static_cast<char *>(ws), w, static_cast<hipStream_t>(stream)));
+}
+
+int stepdllm_sparse_attn(const stepdllm_dims *dims, const uint16_t *q, const uint16_t *k,
+                         const uint16_t *v, const int32_t *row_ptr, const int32_t *col_idx,
+                         int64_t nnz, const void *ws, size_t ws_bytes, uint16_t *o,
+                         void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!q || !k || !v || !row_ptr || !col_idx || !ws || !o) return STEPDLLM_EINVAL;
+    if (nnz < 0 || nnz > D.n_scores()) return STEPDLLM_EINVAL;
+    WsLayout w = sd::ws_layout(D);
+    if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
+    const int32_t *work = reinterpret_cast<const int32_t *>(static_cast<const char *>(ws) + w.work);
+    return hip_status(sd::launch_sparse_attn(D, q, k, v, row_ptr, col_idx, work, nnz, o,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int stepdllm_dense_attn(const stepdllm_dims *dims, const uint16_t *q, const uint16_t *k,
+                        const uint16_t *v, uint16_t *o, void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!q || !k || !v || !o) return STEPDLLM_EINVAL;
+    return hip_status(sd::launch_dense_attn(D, q, k, v, o, static_cast<hipStream_t>(stream)));
+}
+
+int stepdllm_driver_create(stepdllm_driver **out, const stepdllm_dims *dims,
+                           const stepdllm_schedule *schedule, void *ws, size_t ws_bytes,
+                           int32_t *row_ptr, int32_t *col_idx) {
+    if (!out) return STEPDLLM_EINVAL;
+    *out = nullptr;
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!schedule || !ws || !row_ptr || !col_idx) return STEPDLLM_EINVAL;
+    if (!sparsity_ok(schedule->sparsity) || schedule->dense_steps < 0 ||
+        schedule->refresh_every < 0)
+        return STEPDLLM_EINVAL;
+    if ((int64_t)ws_bytes < sd::ws_layout(D).total) return STEPDLLM_EWORKSPACE;
+    stepdllm_driver *drv = static_cast<stepdllm_driver *>(malloc(sizeof(stepdllm_driver)));
+    if (!drv) return STEPDLLM_EINVAL;
+    drv->D = D;
+    drv->sched = *schedule;
+    drv->ws = static_cast<char *>(ws);
+    drv->ws_bytes = ws_bytes;
+    drv->row_ptr = row_ptr;
+    drv->col_idx = col_idx;
+    drv->K = keep_count(D, schedule->sparsity);
+    drv->have_mask = false;
+    *out = drv;
+    return STEPDLLM_OK;
+}
+
+int stepdllm_driver_step_kind(const stepdllm_driver *drv, int32_t step) {
+    if (!drv || step < 0) return STEPDLLM_EINVAL;
+    const int32_t dense = drv->sched.dense_steps, every = drv->sched.refresh_every;
+    if (step < dense) return 0;
+    const int32_t since = step - dense;
+    if (since == 0 || (every > 0 && since % every == 0)) return 1;
+    return 2;
+}
+
+int stepdllm_step(stepdllm_driver *drv, int32_t step, const uint16_t *q, const uint16_t *k,
+                  const uint16_t *v, uint16_t *o, void *stream) {
+    const int kind = stepdllm_driver_step_kind(drv, step);
+    if (kind < 0) return kind;
+    if (!q || !k || !v || !o) return STEPDLLM_EINVAL;
+    stepdllm_dims dims = {drv->D.H, drv->D.Hkv, drv->D.L, drv->D.d, drv->D.B};
+    if (kind == 0) return stepdllm_dense_attn(&dims, q, k, v, o, stream);
+    if (kind == 1) {
+        int st = stepdllm_build_mask(&dims, drv->sched.sparsity, q, k, drv->ws, drv->ws_bytes,
+                                     drv->row_ptr, drv->col_idx, nullptr, stream);
+        if (st) return st;
+        drv->have_mask = true;
+    } else if (!drv->have_mask) {
+        return STEPDLLM_ESTATE;
+    }
+    return stepdllm_sparse_attn(&dims, q, k, v, drv->row_ptr, drv->col_idx, drv->K, drv->ws,
+                                drv->ws_bytes, o, stream);
+}
+
+int stepdllm_driver_destroy(stepdllm_driver *drv) {
+    free(drv);
+    return STEPDLLM_OK;
+}
+
+const char *stepdllm_status_string(int status) {
+    switch (status) {
+    case STEPDLLM_OK: return "ok";
+    case STEPDLLM_EINVAL: return "invalid argument";
+    case STEPDLLM_EUNSUPPORTED: return "unsupported shape (head_dim, block or block count)";
+    case STEPDLLM_EWORKSPACE: return "workspace too small";
+    case STEPDLLM_EHIP: return "HIP launch error";
+    case STEPDLLM_ESTATE: return "no mask built yet (reuse step before any anchor)";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Internal helpers shared by the library's HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sd {
+
+constexpr int kWave = 64;            // CDNA wavefront width
+constexpr int kMaxBlocks = 1024;     // largest nb = L / B supported
+constexpr int kRadixBins = 2048;     // 11-bit digits (11 + 11 + 10 = 32 bits)
+constexpr int kSelectWords = 16;     // select state words in the workspace
+
+// Select state words.
+enum SelectWord {
+    SEL_CUT = 0,      // orderable key of the K-th largest score
+    SEL_ABOVE = 1,    // number of scores strictly above the cut
+    SEL_TIES = 2,     // ties at the cut to keep (lowest flat indices first)
+    SEL_K = 3,        // K
+    SEL_PREFIX = 4,   // running prefix during the radix passes
+    SEL_REMAIN = 5,   // K minus the count already above the prefix bucket
+};
+
+// Shapes after validation, with derived sizes.
+struct Dims {
+    int H, Hkv, L, d, B, nb, G;
+    int64_t rows() const { return (int64_t)H * nb; }
+    int64_t n_scores() const { return (int64_t)H * nb * nb; }
+};
+
+// Workspace carve-up (byte offsets, 256-byte aligned).
+struct WsLayout {
+    int64_t qb, kb, p, hist, sel, gt, eq, tie_base, work, work_meta, total;
+};
+
+inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+inline WsLayout ws_layout(const Dims &D) {
+    WsLayout w;
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) { int64_t o = off; off = align256(off + bytes); return o; };
+    w.qb = take((int64_t)D.H * D.nb * D.d * 4);
+    w.kb = take((int64_t)D.Hkv * D.nb * D.d * 4);
+    w.p = take(D.n_scores() * 4);
+    w.hist = take(3 * kRadixBins * 4);
+    w.sel = take(kSelectWords * 4);
+    w.gt = take(D.rows() * 4);
+    w.eq = take(D.rows() * 4);
+    w.tie_base = take(D.rows() * 4);
+    w.work = take(D.rows() * 4);
+    w.work_meta = take(16 * 4);
+    w.total = off;
+    return w;
+}
+
+// Monotone map from fp32 to uint32: a < b (as floats, -0 < +0) iff key(a) < key(b).
+__device__ __forceinline__ uint32_t order_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Mask-building launches (mask_kernels.hip).
+hipError_t launch_pool(const Dims &D, const uint16_t *q, const uint16_t *k, float *qb, float *kb,
+                       hipStream_t s);
+hipError_t launch_scores(const Dims &D, const float *qb, const float *kb, float *p, float *copy,
+                         hipStream_t s);
+hipError_t launch_select(const Dims &D, int64_t K, const float *p, char *ws, const WsLayout &w,
+                         int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
+hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, char *ws, const WsLayout &w,
+                       hipStream_t s);
+
+// Attention launches (attn_kernels.hip).
+hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
+                              const uint16_t *v, const int32_t *row_ptr, const int32_t *col_idx,
+                              const int32_t *work, int64_t n_idx, uint16_t *o, hipStream_t s);
+hipError_t launch_dense_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
+                             const uint16_t *v, uint16_t *o, hipStream_t s);
+
+}  // namespace sd

@@ -1,0 +1,479 @@
+// Anchor-step mask construction on gfx950: block mean-pooling, pooled scores
+// with a per-row softmax, the global top-K (radix select over all heads), the
+// per-row kept-block lists, and the attention work order.
+//
+// Method: "Step-dLLM: Adaptive Step-aware Sparse Attention for Efficient
+// Diffusion LLM Inference", abstract (block-sparse mask refreshed at anchor
+// steps under one head-adaptive global budget); block scores in a pooled,
+// pre-downsampled space as in the BA-Att abstract.  The pooled statistic is
+// the block mean, the score is Qb.Kb^T/sqrt(d) softmaxed over key blocks, and
+// the budget keeps the K largest scores of all heads together, ties to the
+// lowest flat index.
+//
+// These kernels are HBM/latency bound (they run once per anchor and touch
+// each byte of Q, K and the score matrix a few times); none is a contraction
+// worth MFMA.  Every reduction whose order fixes a result bit is written in a
+// fixed order, and atomics are used only for integer histogram counts, so the
+// mask is deterministic.
+#include "common.h"
+
+namespace sd {
+
+namespace {
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    return (1ull << (threadIdx.x & 63)) - 1ull;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Exclusive scan of one int64 per thread across a 1024-thread block.
+__device__ int64_t block_exclusive_scan_1024(int64_t x, int64_t *total) {
+    __shared__ int64_t wsum[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int64_t inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int64_t y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int64_t before = 0, all = 0;
+    for (int w = 0; w < 16; ++w) {
+        if (w < wave) before += wsum[w];
+        all += wsum[w];
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - x;
+}
+
+// ------------------------------------------------------------------- pool --
+// One thread owns 8 consecutive columns of one (head, block) and adds the B
+// rows in ascending token order in fp32, then scales by 1/B (a power of two,
+// exact).  A wave covers 8 (d=64) or 4 (d=128) blocks with 128/256-byte
+// contiguous segments per load.
+template <int D>
+__global__ __launch_bounds__(256) void k_pool(const uint16_t *__restrict__ q,
+                                              const uint16_t *__restrict__ k,
+                                              float *__restrict__ qb, float *__restrict__ kb,
+                                              int L, int B, int64_t nq_items, int64_t nk_items) {
+    constexpr int CG = D / 8;
+    int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const uint16_t *src = q;
+    float *dst = qb;
+    if (it >= nq_items) {
+        it -= nq_items;
+        if (it >= nk_items) return;
+        src = k;
+        dst = kb;
+    }
+    const int cg = (int)(it % CG);
+    const int64_t hb = it / CG;              // head * nb + block
+    const int nb = L / B;
+    const int64_t head = hb / nb;
+    const int blk = (int)(hb % nb);
+    const uint4 *p = reinterpret_cast<const uint4 *>(src + (head * L + (int64_t)blk * B) * D) + cg;
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+#pragma unroll 8
+    for (int t = 0; t < B; ++t) {
+        const uint4 u = p[(int64_t)t * CG];
+        uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            acc[2 * c] = acc[2 * c] + bf16_bits_to_float(w[c] & 0xFFFFu);
+            acc[2 * c + 1] = acc[2 * c + 1] + bf16_bits_to_float(w[c] >> 16);
+        }
+    }
+    const float inv_b = 1.0f / (float)B;
+    float4 *out = reinterpret_cast<float4 *>(dst + hb * D + cg * 8);
+    out[0] = make_float4(acc[0] * inv_b, acc[1] * inv_b, acc[2] * inv_b, acc[3] * inv_b);
+    out[1] = make_float4(acc[4] * inv_b, acc[5] * inv_b, acc[6] * inv_b, acc[7] * inv_b);
+}
+
+// ---------------------------------------------------------- score + softmax --
+// A workgroup owns 8 query-block rows of one head.  Key-block means stream
+// through LDS 32 rows at a time (read once per 8 rows); each thread forms one
+// dot product in ascending c with separately rounded multiply and add, then
+// each row is softmaxed by 32 lanes.
+constexpr int kScoreRows = 8;
+constexpr int kScoreCols = 32;
+
+template <int D>
+__global__ __launch_bounds__(256) void k_scores(const float *__restrict__ qb,
+                                                const float *__restrict__ kb,
+                                                float *__restrict__ p, float *__restrict__ copy,
+                                                int nb, int G, float sigma) {
+#pragma clang fp contract(off)
+    __shared__ float sq[kScoreRows][D];
+    __shared__ float sk[kScoreCols][D + 1];
+    __shared__ float srow[kScoreRows][kMaxBlocks];
+    const int tid = threadIdx.x;
+    const int tiles = (nb + kScoreRows - 1) / kScoreRows;
+    const int h = blockIdx.x / tiles;
+    const int i0 = (blockIdx.x % tiles) * kScoreRows;
+    const int g = h / G;
+    for (int x = tid; x < kScoreRows * D; x += 256) {
+        int r = x / D, c = x % D;
+        sq[r][c] = (i0 + r < nb) ? qb[((int64_t)h * nb + i0 + r) * D + c] : 0.0f;
+    }
+    const int r = tid / kScoreCols, jj = tid % kScoreCols;
+    for (int j0 = 0; j0 < nb; j0 += kScoreCols) {
+        __syncthreads();
+        for (int x = tid; x < kScoreCols * D; x += 256) {
+            int rr = x / D, c = x % D;
+            sk[rr][c] = (j0 + rr < nb) ? kb[((int64_t)g * nb + j0 + rr) * D + c] : 0.0f;
+        }
+        __syncthreads();
+        if (j0 + jj < nb) {
+            float dot = 0.0f;
+            for (int c = 0; c < D; ++c) {
+                float prod = sq[r][c] * sk[jj][c];
+                dot = dot + prod;
+            }
+            srow[r][j0 + jj] = dot * sigma;
+        }
+    }
+    __syncthreads();
+    if (i0 + r >= nb) return;
+    float m = -INFINITY;
+    for (int j = jj; j < nb; j += kScoreCols) m = fmaxf(m, srow[r][j]);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+    float sum = 0.0f;
+    for (int j = jj; j < nb; j += kScoreCols) {
+        float e = expf(srow[r][j] - m);
+        srow[r][j] = e;
+        sum = sum + e;
+    }
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) sum = sum + __shfl_xor(sum, o, 32);
+    const int64_t base = ((int64_t)h * nb + i0 + r) * nb;
+    for (int j = jj; j < nb; j += kScoreCols) {
+        float v = srow[r][j] / sum;
+        p[base + j] = v;
+        if (copy) copy[base + j] = v;
+    }
+}
+
+// ------------------------------------------------------------ radix select --
+// The K-th largest order key among all H*nb*nb scores, in three digit passes
+// (bits 31..21, 20..10, 9..0).  The state words hold the running prefix and the
+// rank still wanted inside the prefix bucket; at the end the cut key, the
+// count strictly above it and the number of ties at the cut to keep.
+__global__ __launch_bounds__(1024) void k_select_init(uint32_t *__restrict__ hist,
+                                                      uint32_t *__restrict__ sel, int64_t K) {
+    for (int b = threadIdx.x; b < 3 * kRadixBins; b += 1024) hist[b] = 0;
+    if (threadIdx.x == 0) {
+        sel[SEL_PREFIX] = 0;
+        sel[SEL_ABOVE] = 0;
+        sel[SEL_REMAIN] = (uint32_t)K;
+        sel[SEL_K] = (uint32_t)K;
+        sel[SEL_CUT] = 0xFFFFFFFFu;   // K == 0: nothing is above the cut ...
+        sel[SEL_TIES] = 0;            // ... and no tie is kept
+    }
+}
+
+__device__ __forceinline__ void digit_of_pass(int pass, int &shift, uint32_t &hi_mask,
+                                              uint32_t &dmask) {
+    shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    hi_mask = pass == 0 ? 0u : (pass == 1 ? 0xFFE00000u : 0xFFFFFC00u);
+    dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+}
+
+__global__ __launch_bounds__(256) void k_radix_hist(const float *__restrict__ p, int64_t n,
+                                                    const uint32_t *__restrict__ sel,
+                                                    uint32_t *__restrict__ hist, int pass) {
+    __shared__ uint32_t h[kRadixBins];
+    for (int b = threadIdx.x; b < kRadixBins; b += 256) h[b] = 0;
+    __syncthreads();
+    int shift;
+    uint32_t hi_mask, dmask;
+    digit_of_pass(pass, shift, hi_mask, dmask);
+    const uint32_t prefix = sel[SEL_PREFIX];
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t n4 = n >> 2;
+    const float4 *p4 = reinterpret_cast<const float4 *>(p);
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n4; x += stride) {
+        float4 v = p4[x];
+        float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint32_t key = order_key(e[c]);
+            if ((key & hi_mask) == prefix) atomicAdd(&h[(key >> shift) & dmask], 1u);
+        }
+    }
+    for (int64_t x = (n4 << 2) + (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += stride) {
+        uint32_t key = order_key(p[x]);
+        if ((key & hi_mask) == prefix) atomicAdd(&h[(key >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < kRadixBins; b += 256)
+        if (h[b]) atomicAdd(&hist[pass * kRadixBins + b], h[b]);
+}
+
+// One block: bins in descending order, thread t owns ranks 2t and 2t+1.
+__global__ __launch_bounds__(1024) void k_radix_find(const uint32_t *__restrict__ hist,
+                                                     uint32_t *__restrict__ sel, int pass) {
+    int shift;
+    uint32_t hi_mask, dmask;
+    digit_of_pass(pass, shift, hi_mask, dmask);
+    const int nbins = (int)dmask + 1;
+    const int64_t remain = sel[SEL_REMAIN];
+    const uint32_t *hp = hist + pass * kRadixBins;
+    const int r0 = 2 * threadIdx.x, r1 = r0 + 1;
+    const int b0 = nbins - 1 - r0, b1 = nbins - 1 - r1;
+    const int64_t c0 = r0 < nbins ? hp[b0] : 0;
+    const int64_t c1 = r1 < nbins ? hp[b1] : 0;
+    int64_t total;
+    const int64_t before = block_exclusive_scan_1024(c0 + c1, &total);
+    int win_bin = -1;
+    int64_t above = 0;
+    if (r0 < nbins && before < remain && remain <= before + c0) {
+        win_bin = b0;
+        above = before;
+    } else if (r1 < nbins && before + c0 < remain && remain <= before + c0 + c1) {
+        win_bin = b1;
+        above = before + c0;
+    }
+    if (win_bin >= 0) {
+        const uint32_t prefix = sel[SEL_PREFIX] | ((uint32_t)win_bin << shift);
+        sel[SEL_PREFIX] = prefix;
+        sel[SEL_ABOVE] = sel[SEL_ABOVE] + (uint32_t)above;
+        sel[SEL_REMAIN] = (uint32_t)(remain - above);
+        if (pass == 2) {
+            sel[SEL_CUT] = prefix;
+            sel[SEL_TIES] = (uint32_t)(remain - above);
+        }
+    }
+}
+
+// --------------------------------------------------------------- compaction --
+// Per row: how many scores are above the cut and how many equal it.
+__global__ __launch_bounds__(256) void k_row_count(const float *__restrict__ p, int nb,
+                                                   int64_t rows, const uint32_t *__restrict__ sel,
+                                                   int32_t *__restrict__ gt,
+                                                   int32_t *__restrict__ eq) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const uint32_t cut = sel[SEL_CUT];
+    int cg = 0, ce = 0;
+    for (int j = lane; j < nb; j += 64) {
+        uint32_t key = order_key(p[r * nb + j]);
+        cg += key > cut;
+        ce += key == cut;
+    }
+    cg = wave_sum(cg);
+    ce = wave_sum(ce);
+    if (lane == 0) {
+        gt[r] = cg;
+        eq[r] = ce;
+    }
+}
+
+// One block: ties before each row in flat order, kept count per row
+// (all above the cut plus the row's share of the first `ties` cut values),
+// and row_ptr as the exclusive prefix of the kept counts.
+__global__ __launch_bounds__(1024) void k_row_scan(const int32_t *__restrict__ gt,
+                                                   const int32_t *__restrict__ eq, int64_t rows,
+                                                   const uint32_t *__restrict__ sel,
+                                                   int32_t *__restrict__ tie_base,
+                                                   int32_t *__restrict__ row_ptr) {
+    const int64_t ties = sel[SEL_TIES];
+    const int64_t per = (rows + 1023) / 1024;
+    const int64_t lo = min(rows, (int64_t)threadIdx.x * per);
+    const int64_t hi = min(rows, lo + per);
+    int64_t local = 0;
+    for (int64_t r = lo; r < hi; ++r) local += eq[r];
+    int64_t total;
+    int64_t run = block_exclusive_scan_1024(local, &total);
+    int64_t kept_local = 0;
+    for (int64_t r = lo; r < hi; ++r) {
+        tie_base[r] = (int32_t)run;
+        int64_t take = ties - run;
+        take = take < 0 ? 0 : (take > eq[r] ? eq[r] : take);
+        kept_local += gt[r] + take;
+        run += eq[r];
+    }
+    int64_t kept_total;
+    int64_t out = block_exclusive_scan_1024(kept_local, &kept_total);
+    for (int64_t r = lo; r < hi; ++r) {
+        row_ptr[r] = (int32_t)out;
+        int64_t take = ties - tie_base[r];
+        take = take < 0 ? 0 : (take > eq[r] ? eq[r] : take);
+        out += gt[r] + take;
+    }
+    if (threadIdx.x == 0) row_ptr[rows] = (int32_t)kept_total;
+}
+
+// Per row (one wave): write the kept key blocks in ascending order.
+__global__ __launch_bounds__(256) void k_row_scatter(const float *__restrict__ p, int nb,
+                                                     int64_t rows,
+                                                     const uint32_t *__restrict__ sel,
+                                                     const int32_t *__restrict__ tie_base,
+                                                     const int32_t *__restrict__ row_ptr,
+                                                     int32_t *__restrict__ col_idx) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const uint32_t cut = sel[SEL_CUT];
+    const int64_t ties = sel[SEL_TIES];
+    const int64_t K = sel[SEL_K];
+    int64_t tie = tie_base[r];
+    int64_t out = row_ptr[r];
+    const uint64_t lt = lanemask_lt();
+    for (int j0 = 0; j0 < nb; j0 += 64) {
+        const int j = j0 + lane;
+        const bool valid = j < nb;
+        const uint32_t key = valid ? order_key(p[r * nb + j]) : 0u;
+        const bool is_eq = valid && key == cut;
+        const uint64_t eqm = __ballot(is_eq);
+        const int64_t my_tie = tie + __popcll(eqm & lt);
+        const bool keep = valid && (key > cut || (is_eq && my_tie < ties));
+        const uint64_t km = __ballot(keep);
+        const int64_t slot = out + __popcll(km & lt);
+        if (keep && slot < K) col_idx[slot] = j;   // K bounds the list; never exceeded
+        out += __popcll(km);
+        tie += __popcll(eqm);
+    }
+}
+
+// --------------------------------------------------------------------- plan --
+// Work order: rows with kept blocks by descending list length, ties by row id,
+// then the empty rows by id.  A stable counting sort in one workgroup: length
+// histogram, bucket starts, then tiles of 512 rows where each row's rank among
+// equal lengths comes from wave ballots over the length bits plus per-wave
+// counts of the earlier waves.
+constexpr int kPlanThreads = 512;
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+__global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict__ row_ptr,
+                                                       int64_t rows, int nb,
+                                                       int32_t *__restrict__ work,
+                                                       int32_t *__restrict__ meta) {
+    __shared__ int32_t next[kMaxBlocks + 1];
+    __shared__ int32_t whist[kPlanWaves][kMaxBlocks + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int l = tid; l <= nb; l += kPlanThreads) next[l] = 0;
+    __syncthreads();
+    for (int64_t r = tid; r < rows; r += kPlanThreads)
+        atomicAdd(&next[row_ptr[r + 1] - row_ptr[r]], 1);
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int l = nb; l >= 1; --l) {
+            int c = next[l];
+            next[l] = acc;
+            acc += c;
+        }
+        meta[0] = acc;          // non-empty rows
+        meta[1] = next[0];      // empty rows
+        next[0] = acc;
+    }
+    __syncthreads();
+    const uint64_t lt = lanemask_lt();
+    for (int64_t base = 0; base < rows; base += kPlanThreads) {
+        for (int x = tid; x < kPlanWaves * (nb + 1); x += kPlanThreads)
+            whist[x / (nb + 1)][x % (nb + 1)] = 0;
+        __syncthreads();
+        const int64_t r = base + tid;
+        const bool valid = r < rows;
+        const int len = valid ? row_ptr[r + 1] - row_ptr[r] : 0;
+        uint64_t same = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 11; ++bit) {
+            const bool mine = (len >> bit) & 1;
+            const uint64_t b = __ballot(valid && mine);
+            same &= mine ? b : ~b;
+        }
+        const int rank = __popcll(same & lt);
+        if (valid && rank == 0) whist[wave][len] = __popcll(same);
+        __syncthreads();
+        if (valid) {
+            int pos = next[len] + rank;
+            for (int w = 0; w < wave; ++w) pos += whist[w][len];
+            if (pos < rows) work[pos] = (int32_t)r;
+        }
+        __syncthreads();
+        for (int l = tid; l <= nb; l += kPlanThreads) {
+            int s = 0;
+            for (int w = 0; w < kPlanWaves; ++w) s += whist[w][l];
+            next[l] += s;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launches --
+hipError_t launch_pool(const Dims &D, const uint16_t *q, const uint16_t *k, float *qb, float *kb,
+                       hipStream_t s) {
+    const int64_t cg = D.d / 8;
+    const int64_t nq = (int64_t)D.H * D.nb * cg, nk = (int64_t)D.Hkv * D.nb * cg;
+    const int64_t grid = (nq + nk + 255) / 256;
+    if (D.d == 128)
+        hipLaunchKernelGGL(k_pool<128>, dim3((unsigned)grid), dim3(256), 0, s, q, k, qb, kb, D.L,
+                           D.B, nq, nk);
+    else
+        hipLaunchKernelGGL(k_pool<64>, dim3((unsigned)grid), dim3(256), 0, s, q, k, qb, kb, D.L,
+                           D.B, nq, nk);
+    return hipGetLastError();
+}
+
+hipError_t launch_scores(const Dims &D, const float *qb, const float *kb, float *p, float *copy,
+                         hipStream_t s) {
+    const int tiles = (D.nb + kScoreRows - 1) / kScoreRows;
+    const float sigma = (float)(1.0 / sqrt((double)D.d));
+    dim3 grid((unsigned)(D.H * tiles));
+    if (D.d == 128)
+        hipLaunchKernelGGL(k_scores<128>, grid, dim3(256), 0, s, qb, kb, p, copy, D.nb, D.G, sigma);
+    else
+        hipLaunchKernelGGL(k_scores<64>, grid, dim3(256), 0, s, qb, kb, p, copy, D.nb, D.G, sigma);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const Dims &D, int64_t K, const float *p, char *ws, const WsLayout &w,
+                         int32_t *row_ptr, int32_t *col_idx, hipStream_t s) {
+    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + w.hist);
+    uint32_t *sel = reinterpret_cast<uint32_t *>(ws + w.sel);
+    int32_t *gt = reinterpret_cast<int32_t *>(ws + w.gt);
+    int32_t *eq = reinterpret_cast<int32_t *>(ws + w.eq);
+    int32_t *tie_base = reinterpret_cast<int32_t *>(ws + w.tie_base);
+    const int64_t n = D.n_scores(), rows = D.rows();
+    hipLaunchKernelGGL(k_select_init, dim3(1), dim3(1024), 0, s, hist, sel, K);
+    if (K > 0) {
+        int64_t g = (n / 4 + 255) / 256;
+        g = g < 1 ? 1 : (g > 2048 ? 2048 : g);
+        for (int pass = 0; pass < 3; ++pass) {
+            hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)g), dim3(256), 0, s, p, n, sel, hist,
+                               pass);
+            hipLaunchKernelGGL(k_radix_find, dim3(1), dim3(1024), 0, s, hist, sel, pass);
+        }
+    }
+    const unsigned row_grid = (unsigned)((rows + 3) / 4);
+    hipLaunchKernelGGL(k_row_count, dim3(row_grid), dim3(256), 0, s, p, D.nb, rows, sel, gt, eq);
+    hipLaunchKernelGGL(k_row_scan, dim3(1), dim3(1024), 0, s, gt, eq, rows, sel, tie_base, row_ptr);
+    hipLaunchKernelGGL(k_row_scatter, dim3(row_grid), dim3(256), 0, s, p, D.nb, rows, sel, tie_base,
+                       row_ptr, col_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, char *ws, const WsLayout &w,
+                       hipStream_t s) {
+    int32_t *work = reinterpret_cast<int32_t *>(ws + w.work);
+    int32_t *meta = reinterpret_cast<int32_t *>(ws + w.work_meta);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.rows(), D.nb, work,
+                       meta);
+    return hipGetLastError();
+}
+
+}  // namespace sd

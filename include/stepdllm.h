@@ -1,0 +1,181 @@
+/*
+ * stepdllm.h -- C ABI of the MI355X (gfx950) pooled block-sparse attention
+ * library for diffusion-LLM denoising.
+ *
+ * What it computes (sources cited by page title and place):
+ *  - "Step-dLLM: Adaptive Step-aware Sparse Attention for Efficient Diffusion
+ *    LLM Inference" (arXiv 2611.01320), abstract: a diffusion LLM recomputes
+ *    full bidirectional attention at every denoising step; Step-dLLM refreshes
+ *    a block-sparse mask at anchor steps, reuses it within each interval,
+ *    allocates the kept blocks under one head-adaptive global budget, and runs
+ *    a fused block-sparse attention kernel, measured against dense
+ *    FlashAttention.
+ *  - "SparseD: Sparse Attention for Diffusion Language Models"
+ *    (arXiv 2509.24014), abstract: full attention in the early steps, then one
+ *    sparse pattern computed once and reused for all later steps.
+ *  - "Block Approximate Sparse Attention (BA-Att)" abstract: blocks are
+ *    selected in a block-wise pre-downsampled (pooled) space.
+ * The pages leave the block score open; this library scores a (query block,
+ * key block) pair by the mean-pooled queries and keys, Qb . Kb^T / sqrt(d),
+ * softmaxed over key blocks per (head, query block), and keeps the
+ * K = ceil((1 - s) * H * nb^2) largest over all heads at once, ties going to
+ * the lowest flat index (h * nb + i) * nb + j.
+ *
+ * Conventions for every entry point:
+ *  - bf16 tensors are passed as uint16_t (raw bf16 bits).
+ *  - Q and O are [H, L, d] row-major; K and V are [Hkv, L, d]; batch 1.
+ *    Query head h reads key/value head h / (H / Hkv).
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates or frees device memory; the caller provides a
+ *    workspace of stepdllm_workspace_bytes() bytes (256-byte aligned).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued asynchronously on it; no call synchronises the host.  Device
+ *    faults surface at the caller's next synchronisation.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is launched and a negative stepdllm_status is returned.
+ *  - The library holds no global mutable state: calls on different streams
+ *    with different workspaces may run concurrently.  Calls that share a
+ *    workspace must be ordered by the caller (same stream, or events).
+ *  - Supported shapes: head_dim in {64, 128}; block in {64, 128};
+ *    seq_len % block == 0; n_q_heads % n_kv_heads == 0; nb = seq_len / block
+ *    at most 1024; H * nb * nb < 2^31.
+ */
+#ifndef STEPDLLM_H
+#define STEPDLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    STEPDLLM_OK = 0,
+    STEPDLLM_EINVAL = -1,       /* bad argument: null pointer, bad size or ratio, sparsity not in [0,1) */
+    STEPDLLM_EUNSUPPORTED = -2, /* valid shape the kernels do not implement (head_dim, block, nb) */
+    STEPDLLM_EWORKSPACE = -3,   /* workspace smaller than stepdllm_workspace_bytes() */
+    STEPDLLM_EHIP = -4,         /* the HIP runtime rejected a launch */
+    STEPDLLM_ESTATE = -5        /* driver: a reuse step came before any mask was built */
+} stepdllm_status;
+
+typedef struct {
+    int32_t n_q_heads;  /* H   */
+    int32_t n_kv_heads; /* Hkv */
+    int32_t seq_len;    /* L   */
+    int32_t head_dim;   /* d   */
+    int32_t block;      /* B: tokens per block, for pooling and for the mask */
+} stepdllm_dims;
+
+/* Denoising schedule ([SparseD] dense warm-up, [Step-dLLM] anchors + reuse).
+ * Step t < dense_steps runs dense attention.  Step dense_steps is an anchor;
+ * after it, every refresh_every-th step is an anchor (refresh_every == 0:
+ * the first mask is reused to the end).  An anchor builds the mask from its
+ * own Q/K and then runs sparse attention with it. */
+typedef struct {
+    int32_t dense_steps;
+    int32_t refresh_every;
+    double sparsity;    /* s in [0, 1): fraction of the H*nb*nb blocks dropped */
+} stepdllm_schedule;
+
+/* Byte offsets of the intermediates inside a workspace (read-only views for
+ * inspection; contents are valid after the call that writes them). */
+typedef struct {
+    int64_t pooled_q;   /* fp32 [H, nb, d]: block means of Q                      */
+    int64_t pooled_k;   /* fp32 [Hkv, nb, d]: block means of K                    */
+    int64_t scores;     /* fp32 [H, nb, nb]: row-softmaxed pooled scores          */
+    int64_t select;     /* uint32 [16]: [0] cut key, [1] count above the cut,
+                           [2] ties kept at the cut, [3] K                        */
+    int64_t work;       /* int32 [H*nb]: attention work order (row ids)           */
+    int64_t work_meta;  /* int32 [16]: [0] number of non-empty rows               */
+    int64_t total;      /* == stepdllm_workspace_bytes()                          */
+} stepdllm_ws_layout;
+
+/* Number of kept blocks K = ceil((1 - s) * H * nb^2) (a guard of 1e-9 * N is
+ * subtracted first so an exact integer is not rounded up by representation
+ * error).  Host only.  Returns K >= 0, or a negative stepdllm_status. */
+int64_t stepdllm_keep_count(const stepdllm_dims *dims, double sparsity);
+
+/* Workspace size in bytes for these dims, or a negative stepdllm_status. */
+int64_t stepdllm_workspace_bytes(const stepdllm_dims *dims);
+
+/* Fill *out with the workspace layout for these dims. */
+int stepdllm_workspace_layout(const stepdllm_dims *dims, stepdllm_ws_layout *out);
+
+/* Anchor-step mask build (Step-dLLM abstract: mask refreshed at an anchor
+ * step under a head-adaptive global budget):
+ *   pool Q and K over blocks -> pooled scores + row softmax -> global top-K
+ *   -> per-row kept-block lists -> attention work order.
+ * q: [H, L, d] bf16, k: [Hkv, L, d] bf16.
+ * row_ptr: int32 [H*nb + 1] (out), col_idx: int32 [K] (out), K from
+ * stepdllm_keep_count: row r = h*nb + i keeps key blocks
+ * col_idx[row_ptr[r] .. row_ptr[r+1]) in ascending order; a row may be empty.
+ * scores_out (nullable): fp32 [H, nb, nb] copy of the softmaxed scores.
+ * The work order is left in the workspace for stepdllm_sparse_attn. */
+int stepdllm_build_mask(const stepdllm_dims *dims, double sparsity,
+                        const uint16_t *q, const uint16_t *k,
+                        void *ws, size_t ws_bytes,
+                        int32_t *row_ptr, int32_t *col_idx, float *scores_out,
+                        void *stream);
+
+/* The selection half of the mask build on caller-given scores: global top-K
+ * of scores [H, nb, nb] fp32 (finite; order is by value, ties by lowest flat
+ * index), per-row lists and work order.  Same outputs as stepdllm_build_mask. */
+int stepdllm_select_mask(const stepdllm_dims *dims, double sparsity,
+                         const float *scores, void *ws, size_t ws_bytes,
+                         int32_t *row_ptr, int32_t *col_idx, void *stream);
+
+/* Work order for a caller-built mask (row_ptr as above): rows with kept
+ * blocks, longest list first (ties by row id), then the empty rows. */
+int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* Block-sparse bidirectional attention (the fused kernel of the Step-dLLM
+ * abstract): for each token t of query block i in head h,
+ *   o_t = sum_u softmax_u(q_t . k_u / sqrt(d)) v_u
+ * over the tokens u of the key blocks listed for row h*nb + i, from key head
+ * h / (H/Hkv).  A row with no kept block outputs zeros.  Reads the work order
+ * that stepdllm_build_mask / select_mask / plan left in ws.
+ * nnz is the length of col_idx (row_ptr[H*nb] for a well-formed mask, K for a
+ * built one); list positions at or past nnz and block ids outside [0, nb) are
+ * ignored rather than read.
+ * q [H,L,d], k/v [Hkv,L,d], o [H,L,d] bf16; bf16 MFMA with fp32 accumulation
+ * and softmax; o rounded to nearest-even bf16. */
+int stepdllm_sparse_attn(const stepdllm_dims *dims, const uint16_t *q,
+                         const uint16_t *k, const uint16_t *v,
+                         const int32_t *row_ptr, const int32_t *col_idx,
+                         int64_t nnz, const void *ws, size_t ws_bytes,
+                         uint16_t *o, void *stream);
+
+/* Dense bidirectional attention, every block kept: the same-GPU baseline that
+ * stands for "dense FlashAttention" in the Step-dLLM and SparseD abstracts. */
+int stepdllm_dense_attn(const stepdllm_dims *dims, const uint16_t *q,
+                        const uint16_t *k, const uint16_t *v, uint16_t *o,
+                        void *stream);
+
+/* Step driver: a small host object owned by the library; device buffers
+ * (workspace, row_ptr [H*nb+1], col_idx [K]) stay owned by the caller and
+ * must outlive the driver.  stepdllm_step runs what the schedule asks for at
+ * step `step` (dense / anchor: build mask + sparse / reuse: sparse) and
+ * returns STEPDLLM_ESTATE for a reuse step before any anchor.  A driver is
+ * not thread-safe; use one driver per stream. */
+typedef struct stepdllm_driver stepdllm_driver;
+
+int stepdllm_driver_create(stepdllm_driver **out, const stepdllm_dims *dims,
+                           const stepdllm_schedule *schedule, void *ws,
+                           size_t ws_bytes, int32_t *row_ptr, int32_t *col_idx);
+/* Kind of step `step`: 0 dense, 1 anchor, 2 reuse (negative on error). */
+int stepdllm_driver_step_kind(const stepdllm_driver *drv, int32_t step);
+int stepdllm_step(stepdllm_driver *drv, int32_t step, const uint16_t *q,
+                  const uint16_t *k, const uint16_t *v, uint16_t *o,
+                  void *stream);
+int stepdllm_driver_destroy(stepdllm_driver *drv);
+
+/* Static description of a status code. */
+const char *stepdllm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STEPDLLM_H */

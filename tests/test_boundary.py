@@ -1,0 +1,156 @@
+"""The C ABI on the host: the library loads, exports every declared entry point,
+and validates arguments before anything reaches the GPU (no compute calls)."""
+import ctypes
+import math
+import os
+import re
+from fractions import Fraction
+
+import pytest
+
+from block_sparse_attention_pooled_amd import binding as B
+from block_sparse_attention_pooled_amd.inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "stepdllm.h")
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(stepdllm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load()
+    names = declared_functions()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTS) == names
+
+
+def dims(H=32, Hkv=32, L=8192, d=128, blk=64):
+    return B.make_dims(H, Hkv, L, d, blk)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_keep_count_matches_exact_rationals(name):
+    w = WORKLOADS[name]
+    for s in w.sparsities:
+        want = math.ceil((1 - Fraction(str(s))) * w.H * w.nb * w.nb)
+        assert B.keep_count(dims(w.H, w.Hkv, w.L, w.d, w.B), s) == want
+
+
+def test_keep_count_edges():
+    d = dims(2, 2, 256, 64, 64)                  # N = 32
+    assert B.keep_count(d, 0.0) == 32
+    assert B.keep_count(d, 0.5) == 16
+    assert B.keep_count(d, 0.999999) == 1
+    assert B.keep_count(d, 1 - 1e-12) == 0       # (1-s)*N below the guard
+    for bad in (-0.1, 1.0, 1.5, float("nan")):
+        with pytest.raises(B.StepDLLMError) as e:
+            B.keep_count(d, bad)
+        assert e.value.status == B.EINVAL
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 256, 64, 64), B.EINVAL),
+    ((4, 3, 256, 64, 64), B.EINVAL),         # H % Hkv != 0
+    ((2, 2, 200, 64, 64), B.EINVAL),         # L % B != 0
+    ((2, 2, 256, 96, 64), B.EUNSUPPORTED),   # head_dim
+    ((2, 2, 256, 64, 32), B.EUNSUPPORTED),   # block
+    ((2, 2, 64 * 1025, 64, 64), B.EUNSUPPORTED),   # nb > 1024
+    ((2, 2, -64, 64, 64), B.EINVAL),
+])
+def test_dims_validation(args, status):
+    with pytest.raises(B.StepDLLMError) as e:
+        B.workspace_bytes(B.make_dims(*args))
+    assert e.value.status == status
+
+
+def test_workspace_layout():
+    for w in WORKLOADS.values():
+        d = dims(w.H, w.Hkv, w.L, w.d, w.B)
+        lay = B.workspace_layout(d)
+        offs = [lay.pooled_q, lay.pooled_k, lay.scores, lay.select, lay.work, lay.work_meta]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+        assert lay.total == B.workspace_bytes(d)
+        assert lay.scores - lay.pooled_k >= w.Hkv * w.nb * w.d * 4
+        assert lay.select - lay.scores >= w.H * w.nb * w.nb * 4
+
+
+def test_entry_points_reject_bad_arguments_before_launch():
+    lib = B.load()
+    d = dims(2, 2, 256, 64, 64)
+    ws_need = B.workspace_bytes(d)
+    r = ctypes.byref
+    # null pointers
+    assert lib.stepdllm_build_mask(r(d), 0.5, None, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL
+    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, None, FAKE, FAKE, 16, FAKE, ws_need, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_dense_attn(r(d), FAKE, FAKE, FAKE, None, None) == B.EINVAL
+    assert lib.stepdllm_select_mask(r(d), 0.5, None, FAKE, ws_need, FAKE, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_plan(r(d), None, FAKE, ws_need, None) == B.EINVAL
+    # sparsity out of range
+    for s in (-0.5, 1.0, float("nan")):
+        assert lib.stepdllm_build_mask(r(d), s, FAKE, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL
+    # workspace too small
+    assert lib.stepdllm_build_mask(r(d), 0.5, FAKE, FAKE, FAKE, ws_need - 1, FAKE, FAKE, None, None) == B.EWORKSPACE
+    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 8, FAKE, None) == B.EWORKSPACE
+    assert lib.stepdllm_plan(r(d), FAKE, FAKE, 0, None) == B.EWORKSPACE
+    # nnz outside [0, H*nb*nb]
+    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, FAKE, FAKE, FAKE, 33, FAKE, ws_need, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, ws_need, FAKE, None) == B.EINVAL
+    # unsupported dims on a compute entry point
+    bad = dims(2, 2, 256, 80, 64)
+    assert lib.stepdllm_dense_attn(r(bad), FAKE, FAKE, FAKE, FAKE, None) == B.EUNSUPPORTED
+
+
+def _driver(d, dense, every, s, ws_bytes=None):
+    lib = B.load()
+    h = ctypes.c_void_p()
+    sched = B.Schedule(dense, every, s)
+    st = lib.stepdllm_driver_create(ctypes.byref(h), ctypes.byref(d), ctypes.byref(sched), FAKE,
+                                    B.workspace_bytes(d) if ws_bytes is None else ws_bytes,
+                                    FAKE, FAKE)
+    return st, h
+
+
+def test_driver_schedule_matches_oracle(olib):
+    import oracle as O
+    lib = B.load()
+    for name, w in WORKLOADS.items():
+        d = dims(w.H, w.Hkv, w.L, w.d, w.B)
+        st, h = _driver(d, w.dense_steps, w.refresh_every, w.sparsities[0])
+        assert st == B.OK
+        try:
+            got = [lib.stepdllm_driver_step_kind(h, t) for t in range(w.steps)]
+            want = [O.step_kind(t, w.dense_steps, w.refresh_every, olib) for t in range(w.steps)]
+            assert got == want, name
+        finally:
+            lib.stepdllm_driver_destroy(h)
+
+
+def test_driver_rejects_reuse_before_anchor_and_bad_schedules():
+    lib = B.load()
+    d = dims(2, 2, 256, 64, 64)
+    st, h = _driver(d, 0, 4, 0.5)
+    assert st == B.OK
+    try:
+        # Step 1 is a reuse step; no anchor ran, so nothing is launched.
+        assert lib.stepdllm_step(h, 1, FAKE, FAKE, FAKE, FAKE, None) == B.ESTATE
+        assert lib.stepdllm_step(h, -1, FAKE, FAKE, FAKE, FAKE, None) == B.EINVAL
+        assert lib.stepdllm_step(h, 0, FAKE, None, FAKE, FAKE, None) == B.EINVAL
+    finally:
+        lib.stepdllm_driver_destroy(h)
+    assert _driver(d, -1, 4, 0.5)[0] == B.EINVAL
+    assert _driver(d, 0, -4, 0.5)[0] == B.EINVAL
+    assert _driver(d, 0, 4, 1.0)[0] == B.EINVAL
+    assert _driver(d, 0, 4, 0.5, ws_bytes=16)[0] == B.EWORKSPACE
+
+
+def test_status_strings():
+    for st in (B.OK, B.EINVAL, B.EUNSUPPORTED, B.EWORKSPACE, B.EHIP, B.ESTATE):
+        assert B.status_string(st) and B.status_string(st) != "unknown status"
+    assert B.status_string(-99) == "unknown status"
