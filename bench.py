@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the pooled block-sparse attention path on one MI355X.
+
+Workload (default): the Step-dLLM headline attention layer shape -- H = 32
+query/key heads, L = 8192 tokens, d = 128, 64-token blocks, 90% of the blocks
+dropped under the global budget, 256 denoising steps with the mask rebuilt at
+every 32nd (anchor) step.  Inputs are seeded synthetic Q/K/V with per-head
+temperatures, per-step drift and abrupt redraws of Q/K at steps 64 and 160;
+the whole 256-step trajectory is generated into HBM before timing, so every
+timed step reads its own inputs.
+
+A timed step is one denoising step through the step driver (anchor: pool,
+score, select, lists, plan, then sparse attention; other steps: sparse
+attention on the stored mask).  `value` is the effective throughput
+4*B^2*d*K / (wall time per step), K = kept blocks.  The roofline object is for
+the sparse attention kernel, timed with HIP events on the launch stream.
+The CPU baseline runs the oracle (test infrastructure) on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn ms/step + effective TFLOP/s, L=8192 H=32 d=128 90% sparse"
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_pooled_amd", "csrc", "attn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_stepdllm_8k_traffic.json")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=256)
+    p.add_argument("--warmup", type=int, default=32)
+    p.add_argument("--workload", default="stepdllm_8k")
+    p.add_argument("--sparsity", type=float, default=None)
+    p.add_argument("--traj-steps", type=int, default=None,
+                   help="distinct input steps held in HBM (default: the workload's step count)")
+    p.add_argument("--dense-iters", type=int, default=5)
+    p.add_argument("--cpu-budget-s", type=float, default=15.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (for counter calibration)")
+    return p.parse_args()
+
+
+def src_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def traffic_record():
+    """HBM bytes per attention launch from committed counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != src_sha(ATTN_SRC):
+        return None
+    return rec
+
+
+def cpu_baseline(inputs0, w, sparsity, flops_per_step, budget_s):
+    """The oracle as it stands, on the host cores: one full mask build on step-0
+    Q/K plus sparse attention on a deterministic sample of rows, extrapolated
+    to one step by kept blocks (the anchor's mask build amortised over the
+    refresh period)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import oracle as O
+    from block_sparse_attention_pooled_amd.inputs import to_host_f32
+
+    q, k, v = (to_host_f32(x) for x in inputs0)
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    ref = O.build_mask(q, k, w.B, sparsity)
+    t_mask = time.perf_counter() - t0
+    rp, ci, K = ref["row_ptr"], ref["col_idx"], ref["K"]
+    lens = np.diff(rp)
+    nonempty = np.nonzero(lens)[0]
+    order = np.random.default_rng(w.seed).permutation(nonempty)
+    out = np.zeros(q.shape, np.float64)
+    done_rows, done_pairs = 0, 0
+    batch = threads * 2
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        while done_rows < order.size and time.perf_counter() - t0 < budget_s:
+            chunk = order[done_rows:done_rows + batch]
+            list(ex.map(lambda r: O.sparse_attn(q, k, v, w.B, rp, ci, rows=[int(r)], out=out),
+                        chunk))
+            done_rows += chunk.size
+            done_pairs += int(lens[chunk].sum())
+    t_attn = time.perf_counter() - t0
+    period = w.refresh_every if w.refresh_every > 0 else w.steps
+    t_step = t_attn * K / max(done_pairs, 1) + t_mask / period
+    return {
+        "value": round(flops_per_step / t_step / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"one full mask build on the step-0 Q/K ({t_mask:.2f} s, amortised over "
+                   f"{period} steps) + fp64 sparse attention on {done_rows} of {nonempty.size} "
+                   f"non-empty rows ({done_pairs} of {K} kept blocks, {t_attn:.2f} s), "
+                   f"extrapolated to one step by kept blocks"),
+        "ms_per_step": round(t_step * 1e3, 3),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard by query head, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_attention_pooled_amd import binding as B
+    from block_sparse_attention_pooled_amd.inputs import WORKLOADS, Trajectory
+
+    w = WORKLOADS[args.workload]
+    sparsity = args.sparsity if args.sparsity is not None else w.sparsities[-1]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T = args.traj_steps or w.steps
+
+    # Inputs for every step of the trajectory, resident in HBM before timing.
+    traj = Trajectory(w, dev)
+    inputs = [traj.next() for _ in range(T)]
+    del traj
+    torch.cuda.synchronize()
+    dims = B.make_dims(w.H, w.Hkv, w.L, w.d, w.B)
+    drv = B.Driver(dims, w.dense_steps, w.refresh_every, sparsity, device=dev)
+    o = torch.empty(w.H, w.L, w.d, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run_step(t):
+        p = t % T
+        q, k, v = inputs[p]
+        drv.step(p, q, k, v, o, stream)
+
+    for t in range(args.warmup):
+        run_step(t)
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K_steps)]
+    kinds = [drv.step_kind((args.warmup + i) % T) for i in range(K_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K_steps):
+        ev[i][0].record(stream)
+        run_step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / K_steps
+
+    def mean(xs):
+        return sum(xs) / len(xs) if xs else None
+
+    attn_ms = mean([m for m, kd in zip(step_ms, kinds) if kd == 2])
+    anchor_ms = mean([m for m, kd in zip(step_ms, kinds) if kd == 1])
+    dense_step_ms = mean([m for m, kd in zip(step_ms, kinds) if kd == 0])
+    n_anchor = sum(1 for kd in kinds if kd == 1)
+
+    Kkept = drv.K
+    flops_step = 4.0 * w.B * w.B * w.d * Kkept
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    # Same-GPU dense baseline on the step-0 inputs.
+    q0, k0, v0 = inputs[0]
+    od = torch.empty_like(o)
+    B.dense_attn(dims, q0, k0, v0, od, stream)
+    torch.cuda.synchronize()
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.dense_iters)]
+    for a, b in dev_ev:
+        a.record(stream)
+        B.dense_attn(dims, q0, k0, v0, od, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = mean([a.elapsed_time(b) for a, b in dev_ev])
+    dense_flops = 4.0 * w.H * w.L * w.L * w.d
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    attn_tflops = flops_step / (attn_ms * 1e-3) / 1e12 if attn_ms else None
+    trec = traffic_record()
+    roofline = {
+        "bound": "mfma",
+        "kernel": "k_attn<128,64,sparse>" if (w.d, w.B) == (128, 64) else "k_attn",
+        "achieved": round(attn_tflops, 3) if attn_tflops else None,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
+        "traffic": trec["hbm_bytes_per_launch"] if trec else None,
+        "algorithmic_flops_per_launch": flops_step,
+        "kernel_ms": round(attn_ms, 5) if attn_ms else None,
+    }
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "H": w.H, "Hkv": w.Hkv, "L": w.L, "d": w.d, "block": w.B,
+                   "sparsity": sparsity, "kept_blocks": Kkept,
+                   "refresh_every": w.refresh_every, "dense_steps": w.dense_steps,
+                   "distinct_input_steps": T, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "anchor_step_ms": round(anchor_ms, 5) if anchor_ms else None,
+        "mask_build_ms": round(anchor_ms - attn_ms, 5) if (anchor_ms and attn_ms) else None,
+        "anchors_timed": n_anchor,
+        "dense_step_ms": round(dense_step_ms, 5) if dense_step_ms else None,
+        "dense_kernel_ms": round(dense_ms, 5),
+        "dense_kernel_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 3),
+        "dense_kernel_frac": round(dense_flops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "speedup_vs_dense_kernel": round(dense_ms / attn_ms, 3) if attn_ms else None,
+        "speedup_vs_dense_per_step": round(dense_ms / ms_per_step, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inputs[0], w, sparsity, flops_step, args.cpu_budget_s)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

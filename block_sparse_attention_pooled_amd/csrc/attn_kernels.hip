@@ -10,22 +10,25 @@
 // bidirectional (no causal mask).
 //
 // Design (one workgroup per (head, query block) row):
-//  * A wave owns 64 query rows and half of every 64-token key chunk pair:
-//    waves (wq, wk) with wq the 64-row query slice and wk in {0, 1} taking
-//    alternate 32-token key chunks.  Each wave keeps its own online-softmax
-//    state; the two halves are merged once per row.
+//  * A wave owns 64 query rows and every other 32-key chunk of each kept
+//    block: waves (wq, wk), wq the 64-row query slice, wk in {0, 1}.  Each wave
+//    keeps its own online-softmax state; the two halves merge once per row.
 //  * Scores are computed transposed, S^T = K . Q^T, with
-//    v_mfma_f32_32x32x16_bf16: the key chunk is the A operand (straight 16-byte
-//    global loads of K rows), Q^T the B operand (held in registers for the whole
-//    row).  In the accumulator layout every lane then holds one query column,
-//    so the softmax rescale of O^T is a per-lane scalar and the fp32 scores
-//    convert in place into the B operand of O^T += V^T . P^T (the key order
-//    inside a 16-wide k step is permuted consistently on both operands).
-//  * V^T is the A operand of the second product; V rows are transposed into a
-//    per-wave LDS tile (4 keys x 1 column per 8-byte store) in that same
-//    permuted key order, then read back with 16-byte LDS loads.
-//  * fp32 accumulation and softmax (exp2 with log2(e)/sqrt(d) folded in), bf16
-//    round-to-nearest-even output.
+//    v_mfma_f32_32x32x16_bf16: K is the A operand, Q^T the B operand (held in
+//    registers for the whole row).  In the accumulator layout every lane holds
+//    one query column, so the softmax rescale of O^T is a per-lane scalar and
+//    the fp32 scores convert in place into the B operand of O^T += V^T . P^T.
+//    Inside a 16-wide k step the key order is permuted, consistently for P^T
+//    and V^T: slot 16*ks + 8*hh + e holds key 16*ks + 8*(e/4) + 4*hh + e%4.
+//  * K and V chunks stream through a per-wave two-stage LDS ring filled by
+//    direct global->LDS loads (global_load_lds_dwordx4), 16-byte segments
+//    XOR-swizzled per row against bank conflicts.  A chunk's operand
+//    fragments are read out of LDS (K with ds_read_b128, V^T with the gfx950
+//    transposing ds_read_b64_tr_b16) before the next chunk's loads are
+//    issued, so those loads fly during the whole MFMA/softmax body.
+//  * fp32 accumulation and softmax (exp2 with log2(e)/sqrt(d) folded in); the
+//    running max is raised only when a chunk exceeds it by more than 8 (log2
+//    units), so the O^T rescale is rare.  bf16 round-to-nearest-even output.
 #include "common.h"
 
 namespace sd {
@@ -33,10 +36,12 @@ namespace sd {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define SD_LDS __attribute__((address_space(3)))
+#define SD_GLOBAL __attribute__((address_space(1)))
 
 constexpr int kChunk = 32;          // keys per wave step
-constexpr int kVtStride = 40;       // bf16 per V^T row in LDS (32 keys + pad)
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
@@ -46,6 +51,24 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+// 16 bytes per lane from a buffer straight into LDS (64 lanes -> 1 KiB
+// contiguous at `lds`).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint16_t *lds,
+                                           uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (SD_LDS void *)lds, 16, voff, soff, 0, 0);
+}
+
+// Swizzles of the 16-byte segment index inside a row of a 32 x D tile.
+// K is read one row per lane (32 rows at a fixed segment): XOR with the row.
+// V is read by the transposing load, 4 consecutive rows x 4 segments per
+// 16 lanes: XOR with a multiple of 4 that differs between those rows.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) { return row & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
 template <int D, int BLK, bool DENSE>
 __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -53,16 +76,20 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
     const int32_t *__restrict__ col_idx, const int32_t *__restrict__ work,
     uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx, float scale_log2) {
     constexpr int WQ = BLK / 64;                // 64-row query slices per block
+    constexpr int WAVES = 2 * WQ;
     constexpr int KS = D / 16;                  // k steps of the score product
     constexpr int MT = D / 32;                  // 32-row tiles of O^T
-    constexpr int CHUNKS = BLK / kChunk;        // key chunks per key block
-    constexpr int VT_ELEMS = D * kVtStride;     // per wave
-    __shared__ __attribute__((aligned(16))) uint16_t vt_all[2 * WQ * VT_ELEMS];
-    __shared__ float xchg[WQ][32][64];          // O^T exchange, one tile at a time
+    constexpr int CPW = BLK / kChunk / 2;       // chunks per wave per key block
+    constexpr int TILE = kChunk * D;            // bf16 elements in a 32-key tile
+    constexpr int STAGE = 2 * TILE;             // K tile + V tile
+    constexpr int NSEG = D / 8;                 // 16-byte segments per row
+    constexpr int ROWS_PER_LOAD = 64 / NSEG;    // rows covered by one wave load
+    __shared__ __attribute__((aligned(16))) uint16_t ring[WAVES * 2 * STAGE];
     __shared__ float ml[WQ][4][64];             // m, l exchange
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int wq = wave >> 1, wk = wave & 1;
     const int col = lane & 31, hh = lane >> 5;
 
@@ -77,7 +104,7 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
             row = b;
         }
     } else {
-        row = work[blockIdx.x];
+        row = __builtin_amdgcn_readfirstlane(work[blockIdx.x]);   // uniform per workgroup
         if (row < 0 || row >= H * nb) return;   // malformed work order: nothing to do
     }
     const int h = row / nb, blk = row % nb, g = h / G;
@@ -87,8 +114,8 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
 
     int e_begin = 0, e_end = nb;
     if (!DENSE) {
-        e_begin = max(row_ptr[row], 0);
-        e_end = min(row_ptr[row + 1], n_idx);
+        e_begin = max(__builtin_amdgcn_readfirstlane(row_ptr[row]), 0);
+        e_end = min(__builtin_amdgcn_readfirstlane(row_ptr[row + 1]), n_idx);
     }
     if (e_end <= e_begin) {     // no kept block: the row attends to nothing
         if (wk == 0) {
@@ -117,105 +144,156 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
     float m_run[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.0f, 0.0f};
 
-    uint16_t *vt = vt_all + wave * VT_ELEMS;
+    // This wave's chunks: for every kept block e, chunks wk, wk + 2, ...
+    const int n_total = (e_end - e_begin) * CPW;
+    auto chunk_key0 = [&](int n) -> int {
+        const int e = e_begin + n / CPW;
+        int j = DENSE ? e : __builtin_amdgcn_readfirstlane(col_idx[e]);
+        j = min(max(j, 0), nb - 1);   // malformed ids are clamped into range
+        return j * BLK + (wk + 2 * (n % CPW)) * kChunk;
+    };
+    uint16_t *my_ring = ring + wave * 2 * STAGE;
 
-    for (int e = e_begin; e < e_end; ++e) {
-        const int j = DENSE ? e : col_idx[e];
-        if ((unsigned)j >= (unsigned)nb) continue;   // out-of-range block ids are skipped
+    // Direct global->LDS loads of chunk n's K and V rows into stage st.  Wave
+    // load t writes 64 x 16 contiguous bytes: rows t*ROWS_PER_LOAD + lane/NSEG,
+    // stored segment lane%NSEG, which holds source segment (stored ^ swizzle).
+    // Buffer loads over this key head: the chunk and row-group offsets are
+    // scalar, the per-lane swizzled offsets are fixed; reads past the head
+    // return zeros.
+    const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(k + kvbase), 0, L * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(v + kvbase), 0, L * D * 2, 0x00020000);
+    const int r_in = lane / NSEG, sp = lane % NSEG;
+    constexpr int LOADS = kChunk / ROWS_PER_LOAD;
+    constexpr int KPAT = (D / 8 > ROWS_PER_LOAD) ? (D / 8) / ROWS_PER_LOAD : 1;
+    uint32_t k_voff[KPAT];
 #pragma unroll
-        for (int c = wk; c < CHUNKS; c += 2) {
-            const int kv0 = j * BLK + c * kChunk;
-            // K chunk as the A operand: lane row = key (kv0 + col), dims 16*s + 8*hh.
-            bf16x8 kf[KS];
+    for (int x = 0; x < KPAT; ++x)
+        k_voff[x] = (uint32_t)(r_in * D * 2 + 16 * (sp ^ swz_k<D>(x * ROWS_PER_LOAD + r_in)));
+    const uint32_t v_voff = (uint32_t)(r_in * D * 2 + 16 * (sp ^ swz_v<D>(r_in)));
+    auto issue = [&](int n, int st) {
+        const uint32_t kv_off = (uint32_t)chunk_key0(n) * (D * 2);
+        uint16_t *kt = my_ring + st * STAGE;
+        uint16_t *vt = kt + TILE;
+#pragma unroll
+        for (int t = 0; t < LOADS; ++t) {
+            const uint32_t soff = kv_off + t * ROWS_PER_LOAD * D * 2;
+            load_lds16(k_rsrc, kt + t * 512, k_voff[t % KPAT], soff);
+            load_lds16(v_rsrc, vt + t * 512, v_voff, soff);
+        }
+    };
+
+    // Operand fragments of the chunk in stage st.
+    auto read_frags = [&](int st, bf16x8 (&kf)[KS], bf16x8 (&vf)[MT][2]) {
+        const uint16_t *kt = my_ring + st * STAGE;
+        const uint16_t *vt = kt + TILE;
+        // K as the A operand: lane row = key col, dims 16*s + 8*hh.
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            kf[s] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4 *>(
+                            kt + col * D + 8 * ((2 * s + hh) ^ swz_k<D>(col))));
+        // V^T as the A operand: lane row = dim 32*mt + col, 8 keys in slot order.
+        // Transposing load: lane i of a 16-lane group gets element i%4 of the
+        // 8-byte pieces addressed by lanes 4k + i/4, k = 0..3.  Addressing lane
+        // (group gq, index i) points at key row 16*ks + 8*r + 4*(gq/2) + i/4,
+        // dims 32*mt + 16*(gq%2) + 4*(i%4) .. +4.
+        const int gq = lane >> 4, i16 = lane & 15;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                i16x4 part[2];
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int vrow = 16 * ks + 8 * r + 4 * (gq >> 1) + (i16 >> 2);
+                    const int dim0 = 32 * mt + 16 * (gq & 1) + 4 * (i16 & 3);
+                    const int seg = dim0 >> 3;
+                    const uint16_t *pp =
+                        vt + vrow * D + 8 * (seg ^ swz_v<D>(vrow)) + (dim0 & 7);
+                    part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (SD_LDS i16x4 *)(pp));
+                }
+                vf[mt][ks] = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+    };
+
+    auto compute_chunk = [&](const bf16x8 (&kf)[KS], const bf16x8 (&vf)[MT][2]) {
+        // S^T = K . Q^T (32 keys x 64 queries).
+        f32x16 sacc[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[nt][i] = 0.0f;
 #pragma unroll
             for (int s = 0; s < KS; ++s)
-                kf[s] = load_bf16x8(k + kvbase + (int64_t)(kv0 + col) * D + 16 * s + 8 * hh);
-            // V chunk rows (4 consecutive keys x 8 dims per unit), to be transposed.
-            constexpr int UNITS = (8 * D / 8) / 64;    // units per lane
-            uint4 vrow[UNITS][4];
+                sacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nt][s], sacc[nt], 0,
+                                                                   0, 0);
+        }
+        // Online softmax per query column, log2 units, lazily rescaled.
+        float mx[2];
 #pragma unroll
-            for (int x = 0; x < UNITS; ++x) {
-                const int u = lane + 64 * x;
-                const int b = u % (D / 8), a = u / (D / 8);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    vrow[x][r] = *reinterpret_cast<const uint4 *>(
-                        v + kvbase + (int64_t)(kv0 + 4 * a + r) * D + 8 * b);
-            }
-            // S^T = K . Q^T (32 keys x 64 queries).
-            f32x16 sacc[2];
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[nt][i] = 0.0f;
-#pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    sacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nt][s], sacc[nt],
-                                                                       0, 0, 0);
-            }
-            // Transposed V tile into LDS: slot order within the chunk is
-            // 16*ks + 8*hh + e  <->  key 16*ks + 8*(e/4) + 4*hh + e%4.
-#pragma unroll
-            for (int x = 0; x < UNITS; ++x) {
-                const int u = lane + 64 * x;
-                const int b = u % (D / 8), a = u / (D / 8);
-                const int slot0 = 16 * (a >> 2) + 8 * (a & 1) + 4 * ((a & 3) >> 1);
-                const uint32_t w[4][4] = {
-                    {vrow[x][0].x, vrow[x][0].y, vrow[x][0].z, vrow[x][0].w},
-                    {vrow[x][1].x, vrow[x][1].y, vrow[x][1].z, vrow[x][1].w},
-                    {vrow[x][2].x, vrow[x][2].y, vrow[x][2].z, vrow[x][2].w},
-                    {vrow[x][3].x, vrow[x][3].y, vrow[x][3].z, vrow[x][3].w}};
-#pragma unroll
-                for (int dd = 0; dd < 8; ++dd) {
-                    const int sh = (dd & 1) * 16;
-                    const uint32_t e0 = (w[0][dd >> 1] >> sh) & 0xFFFFu;
-                    const uint32_t e1 = (w[1][dd >> 1] >> sh) & 0xFFFFu;
-                    const uint32_t e2 = (w[2][dd >> 1] >> sh) & 0xFFFFu;
-                    const uint32_t e3 = (w[3][dd >> 1] >> sh) & 0xFFFFu;
-                    *reinterpret_cast<uint2 *>(vt + (8 * b + dd) * kVtStride + slot0) =
-                        make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-                }
-            }
-            // Online softmax over this chunk, per query column.
-            bf16x8 pf[2][2];
+        for (int nt = 0; nt < 2; ++nt) {
+            float a0 = fmaxf(fmaxf(sacc[nt][0], sacc[nt][1]), sacc[nt][2]);
+            float a1 = fmaxf(fmaxf(sacc[nt][3], sacc[nt][4]), sacc[nt][5]);
+            float a2 = fmaxf(fmaxf(sacc[nt][6], sacc[nt][7]), sacc[nt][8]);
+            float a3 = fmaxf(fmaxf(sacc[nt][9], sacc[nt][10]), sacc[nt][11]);
+            float a4 = fmaxf(fmaxf(sacc[nt][12], sacc[nt][13]), sacc[nt][14]);
+            float m = fmaxf(fmaxf(a0, a1), fmaxf(fmaxf(a2, a3), fmaxf(a4, sacc[nt][15])));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            mx[nt] = m * scale_log2;
+        }
+        if (__any((mx[0] > m_run[0] + 8.0f) || (mx[1] > m_run[1] + 8.0f))) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                float mx = sacc[nt][0];
-#pragma unroll
-                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[nt][i]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run[nt], mx * scale_log2);
-                const float alpha = exp2f(m_run[nt] - m_new);
-                float psum = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float pv = exp2f(fmaf(sacc[nt][i], scale_log2, -m_new));
-                    psum += pv;
-                    pf[nt][i >> 3][i & 7] = (__bf16)pv;
-                }
-                l_run[nt] = l_run[nt] * alpha + psum;
+                const float m_new = fmaxf(m_run[nt], mx[nt]);
+                const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+                l_run[nt] *= alpha;
                 m_run[nt] = m_new;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) oacc[mt][nt][i] *= alpha;
             }
-            __builtin_amdgcn_wave_barrier();
-            // O^T += V^T . P^T.
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 vf = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const uint4 *>(
-                                    vt + (32 * mt + col) * kVtStride + 16 * ks + 8 * hh));
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-                        oacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            vf, pf[nt][ks], oacc[mt][nt], 0, 0, 0);
-                }
-            __builtin_amdgcn_wave_barrier();
         }
+        bf16x8 pf[2][2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const float neg_m = -m_run[nt];
+            float psum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[nt][i], scale_log2, neg_m));
+                psum += pv;
+                pf[nt][i >> 3][i & 7] = (__bf16)pv;
+            }
+            l_run[nt] += psum;
+        }
+        // O^T += V^T . P^T.
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    oacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        vf[mt][ks], pf[nt][ks], oacc[mt][nt], 0, 0, 0);
+    };
+
+    issue(0, 0);
+    for (int n = 0; n < n_total; ++n) {
+        const int st = n & 1;
+        bf16x8 kf[KS];
+        bf16x8 vf[MT][2];
+        // Chunk n's direct-to-LDS loads are the oldest vector-memory operations
+        // in flight: wait for all of them before any LDS read of the stage (the
+        // compiler does not order LDS reads after buffer->LDS loads by itself).
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        read_frags(st, kf, vf);
+        if (n + 1 < n_total) issue(n + 1, st ^ 1);
+        compute_chunk(kf, vf);
     }
 
     // Column sums: the two lane halves hold different keys of the same column.
@@ -223,6 +301,9 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
     for (int nt = 0; nt < 2; ++nt) l_run[nt] += __shfl_xor(l_run[nt], 32);
 
     // Merge the two key halves (wk = 1 hands its state to wk = 0), then write.
+    // The exchange tile reuses the ring once every wave has left the loop.
+    __syncthreads();
+    float(*xchg)[32][64] = reinterpret_cast<float(*)[32][64]>(ring);
     if (wk == 1) {
         ml[wq][0][lane] = m_run[0];
         ml[wq][1][lane] = m_run[1];
@@ -236,15 +317,15 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
         for (int nt = 0; nt < 2; ++nt) {
             const float m1 = ml[wq][nt][lane], l1 = ml[wq][2 + nt][lane];
             const float mm = fmaxf(m_run[nt], m1);
-            a_self[nt] = exp2f(m_run[nt] - mm);
-            a_other[nt] = exp2f(m1 - mm);
+            a_self[nt] = __builtin_amdgcn_exp2f(m_run[nt] - mm);
+            a_other[nt] = __builtin_amdgcn_exp2f(m1 - mm);
             inv_l[nt] = 1.0f / (l_run[nt] * a_self[nt] + l1 * a_other[nt]);
         }
     }
     uint16_t *orow = o + qbase;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        __syncthreads();
+        if (mt) __syncthreads();
         if (wk == 1) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)

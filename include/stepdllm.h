@@ -137,8 +137,9 @@ int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr,
  * h / (H/Hkv).  A row with no kept block outputs zeros.  Reads the work order
  * that stepdllm_build_mask / select_mask / plan left in ws.
  * nnz is the length of col_idx (row_ptr[H*nb] for a well-formed mask, K for a
- * built one); list positions at or past nnz and block ids outside [0, nb) are
- * ignored rather than read.
+ * built one).  Memory safety on malformed masks: list positions at or past nnz
+ * are not read, and block ids outside [0, nb) are clamped into range (the
+ * output of such a row is then unspecified).
  * q [H,L,d], k/v [Hkv,L,d], o [H,L,d] bf16; bf16 MFMA with fp32 accumulation
  * and softmax; o rounded to nearest-even bf16. */
 int stepdllm_sparse_attn(const stepdllm_dims *dims, const uint16_t *q,

@@ -116,3 +116,29 @@ def token_mask_for_rows(rows, H, nb, blk):
         h, i = divmod(int(r), nb)
         sel[h, i * blk:(i + 1) * blk] = True
     return sel
+
+
+def oracle_rows_parallel(fn, rows, threads=None, **kw):
+    """Run an oracle attention function over `rows` split across host threads
+    (ctypes releases the GIL); all calls write disjoint rows of one output."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    rows = np.asarray(rows, np.int32)
+    threads = threads or max(1, min(16, len(os.sched_getaffinity(0))))
+    out = kw.pop("out")
+    parts = [p for p in np.array_split(rows, threads * 4) if p.size]
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda p: fn(rows=p, out=out, **kw), parts))
+    return out
+
+
+def sample_rows(row_ptr, H, nb, heads=(0,), n_longest=64, n_random=64, seed=0):
+    """All rows of the given heads, the longest lists, and seeded random rows."""
+    lens = np.diff(np.asarray(row_ptr))
+    rows = set()
+    for h in heads:
+        rows.update(range(h * nb, (h + 1) * nb))
+    rows.update(np.argsort(-lens, kind="stable")[:n_longest].tolist())
+    rng = np.random.default_rng(seed)
+    rows.update(rng.choice(H * nb, size=min(n_random, H * nb), replace=False).tolist())
+    return np.array(sorted(rows), np.int32)

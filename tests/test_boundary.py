@@ -154,3 +154,12 @@ def test_status_strings():
     for st in (B.OK, B.EINVAL, B.EUNSUPPORTED, B.EWORKSPACE, B.EHIP, B.ESTATE):
         assert B.status_string(st) and B.status_string(st) != "unknown status"
     assert B.status_string(-99) == "unknown status"
+
+
+def test_library_has_no_undefined_kernel_stubs():
+    """Every kernel's host launch stub is defined (a host pass that drops a
+    kernel leaves an undefined stub and the library fails to load on a GPU)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    undefined = [l for l in out.splitlines() if " U " in l and "__device_stub__" in l]
+    assert not undefined, undefined
