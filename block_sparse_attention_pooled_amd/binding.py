@@ -250,8 +250,11 @@ class MaskBuffers:
     def select_state(self):
         return self.view(self.layout.select, 16, torch.int32)
 
+    def work_cap(self):
+        return -(-self.dims.n_q_heads // 8) * self.nb
+
     def work(self):
-        return self.view(self.layout.work, self.rows, torch.int32)
+        return self.view(self.layout.work, 8 * self.work_cap(), torch.int32)
 
     def work_meta(self):
         return self.view(self.layout.work_meta, 16, torch.int32)

@@ -23,6 +23,7 @@ int check_dims(const stepdllm_dims *d, Dims *out) {
         d->block <= 0)
         return STEPDLLM_EINVAL;
     if (d->n_q_heads % d->n_kv_heads != 0) return STEPDLLM_EINVAL;
+    if (d->n_q_heads > sd::kMaxHeads) return STEPDLLM_EUNSUPPORTED;
     if (d->seq_len % d->block != 0) return STEPDLLM_EINVAL;
     if (d->head_dim != 64 && d->head_dim != 128) return STEPDLLM_EUNSUPPORTED;
     if (d->block != 64 && d->block != 128) return STEPDLLM_EUNSUPPORTED;

@@ -104,8 +104,11 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
             row = b;
         }
     } else {
-        row = __builtin_amdgcn_readfirstlane(work[blockIdx.x]);   // uniform per workgroup
-        if (row < 0 || row >= H * nb) return;   // malformed work order: nothing to do
+        // Workgroup b runs on die b % kDies: take that die's list.
+        const int64_t cap = (int64_t)((H + kDies - 1) / kDies) * nb;
+        const int b = blockIdx.x;
+        row = __builtin_amdgcn_readfirstlane(work[(b % kDies) * cap + b / kDies]);
+        if (row < 0 || row >= H * nb) return;   // padding (or a malformed order): nothing to do
     }
     const int h = row / nb, blk = row % nb, g = h / G;
     const int q0 = blk * BLK + 64 * wq;
@@ -363,7 +366,8 @@ hipError_t launch_attn_t(const Dims &Dm, const uint16_t *q, const uint16_t *k, c
                          const int32_t *row_ptr, const int32_t *col_idx, const int32_t *work,
                          int n_idx, uint16_t *o, hipStream_t s) {
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    hipLaunchKernelGGL((k_attn<D, BLK, DENSE>), dim3((unsigned)Dm.rows()), dim3(128 * (BLK / 64)),
+    const unsigned grid = (unsigned)(DENSE ? Dm.rows() : kDies * Dm.die_cap());
+    hipLaunchKernelGGL((k_attn<D, BLK, DENSE>), dim3(grid), dim3(128 * (BLK / 64)),
                        0, s, q, k, v, row_ptr, col_idx, work, o, Dm.L, Dm.nb, Dm.G, Dm.H,
                        n_idx, scale_log2);
     return hipGetLastError();

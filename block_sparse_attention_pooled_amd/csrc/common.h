@@ -8,6 +8,8 @@ namespace sd {
 
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kMaxBlocks = 1024;     // largest nb = L / B supported
+constexpr int kMaxHeads = 1024;      // largest number of query heads supported
+constexpr int kDies = 8;             // XCDs: workgroup b of a launch runs on die b % 8
 constexpr int kRadixBins = 2048;     // 11-bit digits (11 + 11 + 10 = 32 bits)
 constexpr int kSelectWords = 16;     // select state words in the workspace
 
@@ -25,6 +27,8 @@ enum SelectWord {
 struct Dims {
     int H, Hkv, L, d, B, nb, G;
     int64_t rows() const { return (int64_t)H * nb; }
+    // Work-order positions per die (rows of ceil(H / kDies) heads).
+    int64_t die_cap() const { return (int64_t)((H + kDies - 1) / kDies) * nb; }
     int64_t n_scores() const { return (int64_t)H * nb * nb; }
 };
 
@@ -47,7 +51,7 @@ inline WsLayout ws_layout(const Dims &D) {
     w.gt = take(D.rows() * 4);
     w.eq = take(D.rows() * 4);
     w.tie_base = take(D.rows() * 4);
-    w.work = take(D.rows() * 4);
+    w.work = take(kDies * D.die_cap() * 4);
     w.work_meta = take(16 * 4);
     w.total = off;
     return w;

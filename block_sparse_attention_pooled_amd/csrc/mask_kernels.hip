@@ -347,68 +347,111 @@ __global__ __launch_bounds__(256) void k_row_scatter(const float *__restrict__ p
 }
 
 // --------------------------------------------------------------------- plan --
-// Work order: rows with kept blocks by descending list length, ties by row id,
-// then the empty rows by id.  A stable counting sort in one workgroup: length
-// histogram, bucket starts, then tiles of 512 rows where each row's rank among
-// equal lengths comes from wave ballots over the length bits plus per-wave
-// counts of the earlier waves.
+// Work order for the attention launch.  The GPU has kDies dies (XCDs), each
+// with its own L2, and workgroup b of a launch runs on die b % kDies.  All
+// rows of a head go to one die so that the head's K/V stay in that die's L2:
+//  * heads are ranked by kept blocks (descending, ties by head id) and, in
+//    that order, each goes to the die with the fewest kept blocks so far among
+//    those holding fewer than ceil(H / kDies) heads (ties: lowest die);
+//  * die x's list is its heads in assignment order, each head's rows by list
+//    length descending (ties by row id), at work[x*cap ...], cap =
+//    ceil(H / kDies) * nb; unused positions hold -1.
+// One workgroup: heads are ranked in parallel, assigned by one thread, then
+// each wave sorts whole heads with a stable counting sort (length histogram,
+// descending bucket starts, ranks among equal lengths from wave ballots).
 constexpr int kPlanThreads = 512;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict__ row_ptr,
-                                                       int64_t rows, int nb,
+                                                       int H, int nb,
                                                        int32_t *__restrict__ work,
                                                        int32_t *__restrict__ meta) {
-    __shared__ int32_t next[kMaxBlocks + 1];
-    __shared__ int32_t whist[kPlanWaves][kMaxBlocks + 1];
+    __shared__ int32_t kept[kMaxHeads];
+    __shared__ int32_t order[kMaxHeads];
+    __shared__ int32_t head_base[kMaxHeads];
+    __shared__ int32_t next[kPlanWaves][kMaxBlocks + 1];
+    __shared__ int32_t nonempty;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int l = tid; l <= nb; l += kPlanThreads) next[l] = 0;
+    const int cap_h = (H + kDies - 1) / kDies;
+    const int64_t cap = (int64_t)cap_h * nb;
+    if (tid == 0) nonempty = 0;
+    for (int h = tid; h < H; h += kPlanThreads)
+        kept[h] = row_ptr[(int64_t)(h + 1) * nb] - row_ptr[(int64_t)h * nb];
+    for (int64_t p = tid; p < kDies * cap; p += kPlanThreads) work[p] = -1;
     __syncthreads();
-    for (int64_t r = tid; r < rows; r += kPlanThreads)
-        atomicAdd(&next[row_ptr[r + 1] - row_ptr[r]], 1);
+    for (int h = tid; h < H; h += kPlanThreads) {
+        int rank = 0;
+        for (int o = 0; o < H; ++o)
+            rank += (kept[o] > kept[h]) || (kept[o] == kept[h] && o < h);
+        order[rank] = h;
+    }
     __syncthreads();
     if (tid == 0) {
-        int acc = 0;
-        for (int l = nb; l >= 1; --l) {
-            int c = next[l];
-            next[l] = acc;
-            acc += c;
+        int64_t load[kDies];
+        int count[kDies];
+        for (int x = 0; x < kDies; ++x) {
+            load[x] = 0;
+            count[x] = 0;
         }
-        meta[0] = acc;          // non-empty rows
-        meta[1] = next[0];      // empty rows
-        next[0] = acc;
+        for (int a = 0; a < H; ++a) {
+            const int h = order[a];
+            int best = -1;
+            for (int x = 0; x < kDies; ++x)
+                if (count[x] < cap_h && (best < 0 || load[x] < load[best])) best = x;
+            head_base[h] = (int32_t)(best * cap + (int64_t)count[best] * nb);
+            ++count[best];
+            load[best] += kept[h];
+        }
     }
     __syncthreads();
     const uint64_t lt = lanemask_lt();
-    for (int64_t base = 0; base < rows; base += kPlanThreads) {
-        for (int x = tid; x < kPlanWaves * (nb + 1); x += kPlanThreads)
-            whist[x / (nb + 1)][x % (nb + 1)] = 0;
-        __syncthreads();
-        const int64_t r = base + tid;
-        const bool valid = r < rows;
-        const int len = valid ? row_ptr[r + 1] - row_ptr[r] : 0;
-        uint64_t same = __ballot(valid);
+    int32_t *nx = next[wave];
+    int my_nonempty = 0;
+    for (int h = wave; h < H; h += kPlanWaves) {
+        const int64_t r0 = (int64_t)h * nb;
+        for (int l = lane; l <= nb; l += 64) nx[l] = 0;
+        for (int i = lane; i < nb; i += 64) {
+            const int len = row_ptr[r0 + i + 1] - row_ptr[r0 + i];
+            atomicAdd(&nx[len], 1);
+            my_nonempty += len > 0;
+        }
+        // Bucket starts, longest lists first: nx[l] = rows with length > l.
+        int carry = 0;
+        for (int c0 = nb; c0 >= 0; c0 -= 64) {
+            const int l = c0 - lane;
+            const int cnt = l >= 0 ? nx[l] : 0;
+            int inc = cnt;
 #pragma unroll
-        for (int bit = 0; bit < 11; ++bit) {
-            const bool mine = (len >> bit) & 1;
-            const uint64_t b = __ballot(valid && mine);
-            same &= mine ? b : ~b;
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(inc, o);
+                if (lane >= o) inc += y;
+            }
+            if (l >= 0) nx[l] = carry + inc - cnt;
+            carry += __shfl(inc, 63);
         }
-        const int rank = __popcll(same & lt);
-        if (valid && rank == 0) whist[wave][len] = __popcll(same);
-        __syncthreads();
-        if (valid) {
-            int pos = next[len] + rank;
-            for (int w = 0; w < wave; ++w) pos += whist[w][len];
-            if (pos < rows) work[pos] = (int32_t)r;
+        const int32_t base = head_base[h];
+        for (int i0 = 0; i0 < nb; i0 += 64) {
+            const int i = i0 + lane;
+            const bool valid = i < nb;
+            const int len = valid ? row_ptr[r0 + i + 1] - row_ptr[r0 + i] : 0;
+            uint64_t same = __ballot(valid);
+#pragma unroll
+            for (int bit = 0; bit < 11; ++bit) {
+                const bool mine = (len >> bit) & 1;
+                const uint64_t b = __ballot(valid && mine);
+                same &= mine ? b : ~b;
+            }
+            const int rank = __popcll(same & lt);
+            const int pos = valid ? nx[len] + rank : 0;
+            if (valid && pos < nb) work[(int64_t)base + pos] = (int32_t)(r0 + i);
+            if (valid && rank == 0) nx[len] += __popcll(same);
         }
-        __syncthreads();
-        for (int l = tid; l <= nb; l += kPlanThreads) {
-            int s = 0;
-            for (int w = 0; w < kPlanWaves; ++w) s += whist[w][l];
-            next[l] += s;
-        }
-        __syncthreads();
+    }
+    atomicAdd(&nonempty, my_nonempty);
+    __syncthreads();
+    if (tid == 0) {
+        meta[0] = (int32_t)cap;
+        meta[1] = nonempty;
     }
 }
 
@@ -471,7 +514,7 @@ hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, char *ws, const Ws
                        hipStream_t s) {
     int32_t *work = reinterpret_cast<int32_t *>(ws + w.work);
     int32_t *meta = reinterpret_cast<int32_t *>(ws + w.work_meta);
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.rows(), D.nb, work,
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.H, D.nb, work,
                        meta);
     return hipGetLastError();
 }

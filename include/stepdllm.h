@@ -38,7 +38,7 @@
  *    workspace must be ordered by the caller (same stream, or events).
  *  - Supported shapes: head_dim in {64, 128}; block in {64, 128};
  *    seq_len % block == 0; n_q_heads % n_kv_heads == 0; nb = seq_len / block
- *    at most 1024; H * nb * nb < 2^31.
+ *    at most 1024; H at most 1024; H * nb * nb < 2^31.
  */
 #ifndef STEPDLLM_H
 #define STEPDLLM_H
@@ -86,8 +86,9 @@ typedef struct {
     int64_t scores;     /* fp32 [H, nb, nb]: row-softmaxed pooled scores          */
     int64_t select;     /* uint32 [16]: [0] cut key, [1] count above the cut,
                            [2] ties kept at the cut, [3] K                        */
-    int64_t work;       /* int32 [H*nb]: attention work order (row ids)           */
-    int64_t work_meta;  /* int32 [16]: [0] number of non-empty rows               */
+    int64_t work;       /* int32 [8 * cap]: attention work order, cap =
+                           ceil(H/8) * nb positions per die; -1 = padding        */
+    int64_t work_meta;  /* int32 [16]: [0] cap, [1] number of non-empty rows      */
     int64_t total;      /* == stepdllm_workspace_bytes()                          */
 } stepdllm_ws_layout;
 
@@ -125,8 +126,12 @@ int stepdllm_select_mask(const stepdllm_dims *dims, double sparsity,
                          const float *scores, void *ws, size_t ws_bytes,
                          int32_t *row_ptr, int32_t *col_idx, void *stream);
 
-/* Work order for a caller-built mask (row_ptr as above): rows with kept
- * blocks, longest list first (ties by row id), then the empty rows. */
+/* Work order for a caller-built mask (row_ptr as above).  The GPU's 8 dies
+ * (XCDs) each have their own L2 and take workgroups round robin, so all rows
+ * of a head go to one die: heads are ranked by kept blocks (descending, ties
+ * by id) and each goes to the least-loaded die that holds fewer than
+ * ceil(H/8) heads (ties: lowest die); a die's list is its heads in that
+ * order, each head's rows by list length descending (ties by row id). */
 int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr,
                   void *ws, size_t ws_bytes, void *stream);
 

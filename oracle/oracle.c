@@ -188,9 +188,18 @@ int64_t oracle_build_mask(const float *q, const float *k, int H, int Hkv, int L,
 }
 
 /* ------------------------------------------------------------------- plan --- */
-/* Work order for the attention launch: rows with at least one kept block,
- * longest list first (ties by row id), then the empty rows in ascending id. */
+/* Work order for the attention launch on a GPU made of 8 dies (XCDs) that take
+ * workgroups round robin, so that all rows of a head share one die's L2:
+ *  - heads are taken in order of kept blocks (descending, ties by head id) and
+ *    each goes to the die with the fewest kept blocks so far among those that
+ *    hold fewer than ceil(H/8) heads (ties: lowest die);
+ *  - die x's list is its heads in that order, each head's rows by list
+ *    length descending (ties by row id);
+ *  - list x fills work[x*cap .. x*cap + cap), cap = ceil(H/8)*nb, and unused
+ *    positions hold -1.
+ * Returns the number of rows with at least one kept block. */
 static const int32_t *g_row_ptr;
+static const int64_t *g_head_kept;
 
 static int by_len_desc_row_asc(const void *pa, const void *pb)
 {
@@ -202,16 +211,59 @@ static int by_len_desc_row_asc(const void *pa, const void *pb)
     return (a < b) ? -1 : (a > b);
 }
 
-int32_t oracle_plan(const int32_t *row_ptr, int rows, int32_t *work)
+static int by_kept_desc_head_asc(const void *pa, const void *pb)
 {
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    if (g_head_kept[a] > g_head_kept[b]) return -1;
+    if (g_head_kept[a] < g_head_kept[b]) return 1;
+    return (a < b) ? -1 : (a > b);
+}
+
+enum { ORACLE_DIES = 8 };
+
+int32_t oracle_plan(const int32_t *row_ptr, int H, int nb, int32_t *work)
+{
+    int cap_heads = (H + ORACLE_DIES - 1) / ORACLE_DIES;
+    int64_t cap = (int64_t)cap_heads * nb;
+    int64_t *kept = (int64_t *)malloc(sizeof(int64_t) * (size_t)H);
+    int32_t *heads = (int32_t *)malloc(sizeof(int32_t) * (size_t)H);
+    int32_t *die_heads = (int32_t *)malloc(sizeof(int32_t) * (size_t)(ORACLE_DIES * cap_heads));
+    int64_t load[ORACLE_DIES] = {0};
+    int count[ORACLE_DIES] = {0};
     int32_t n_nonempty = 0;
-    for (int r = 0; r < rows; ++r) {
-        work[r] = r;
+    for (int h = 0; h < H; ++h) {
+        kept[h] = row_ptr[(h + 1) * nb] - row_ptr[h * nb];
+        heads[h] = h;
+    }
+    for (int r = 0; r < H * nb; ++r)
         if (row_ptr[r + 1] > row_ptr[r])
             ++n_nonempty;
+    g_head_kept = kept;
+    qsort(heads, (size_t)H, sizeof(int32_t), by_kept_desc_head_asc);
+    for (int a = 0; a < H; ++a) {
+        int best = -1;
+        for (int x = 0; x < ORACLE_DIES; ++x)
+            if (count[x] < cap_heads && (best < 0 || load[x] < load[best]))
+                best = x;
+        die_heads[best * cap_heads + count[best]++] = heads[a];
+        load[best] += kept[heads[a]];
     }
+    for (int64_t p = 0; p < ORACLE_DIES * cap; ++p)
+        work[p] = -1;
     g_row_ptr = row_ptr;
-    qsort(work, (size_t)rows, sizeof(int32_t), by_len_desc_row_asc);
+    for (int x = 0; x < ORACLE_DIES; ++x) {
+        int32_t *out = work + x * cap;
+        for (int c = 0; c < count[x]; ++c) {
+            int h = die_heads[x * cap_heads + c];
+            for (int i = 0; i < nb; ++i)
+                out[i] = h * nb + i;
+            qsort(out, (size_t)nb, sizeof(int32_t), by_len_desc_row_asc);
+            out += nb;
+        }
+    }
+    free(kept);
+    free(heads);
+    free(die_heads);
     return n_nonempty;
 }
 

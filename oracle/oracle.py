@@ -40,7 +40,7 @@ def _bind(lib):
         "oracle_cut_value": (ctypes.c_float, [f32p, ci64, ci64]),
         "oracle_csr": (None, [u8p, ci, ci, i32p, i32p]),
         "oracle_build_mask": (ci64, [f32p, f32p, ci, ci, ci, ci, ci, cd, f32p, f32p, f32p, i32p, i32p]),
-        "oracle_plan": (ctypes.c_int32, [i32p, ci, i32p]),
+        "oracle_plan": (ctypes.c_int32, [i32p, ci, ci, i32p]),
         "oracle_sparse_attn": (None, [f32p, f32p, f32p, ci, ci, ci, ci, ci, i32p, i32p, vp, ci, f64p]),
         "oracle_dense_attn": (None, [f32p, f32p, f32p, ci, ci, ci, ci, ci, vp, ci, f64p]),
         "oracle_step_kind": (ci, [ci, ci, ci]),
@@ -144,13 +144,16 @@ def build_mask(q, k, B, sparsity, lib=None):
     return dict(qb=qb, kb=kb, P=P, K=int(K), row_ptr=row_ptr, col_idx=col_idx[:K].copy())
 
 
-def plan(row_ptr, lib=None):
-    """-> (work [rows] int32, n_nonempty)."""
+DIES = 8
+
+
+def plan(row_ptr, H, nb, lib=None):
+    """-> (work [8 * ceil(H/8) * nb] int32 with -1 padding, n_nonempty)."""
     lib = lib or load()
     row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
-    rows = row_ptr.size - 1
-    work = np.empty(rows, np.int32)
-    n = lib.oracle_plan(row_ptr, rows, work)
+    cap = -(-H // DIES) * nb
+    work = np.empty(DIES * cap, np.int32)
+    n = lib.oracle_plan(row_ptr, int(H), int(nb), work)
     return work, int(n)
 
 

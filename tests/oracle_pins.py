@@ -158,14 +158,44 @@ def pin_csr(lib):
         assert np.array_equal(col_idx[row_ptr[r]:row_ptr[r + 1]], np.nonzero(flat[r])[0])
 
 
+def _plan_spec(lens, H, nb):
+    """The work-order spec written out in Python: heads by kept blocks
+    (descending, then id) to the least-loaded die with room for ceil(H/8)
+    heads; each die lists its heads in that order, rows by length desc."""
+    cap_h = -(-H // 8)
+    kept = [int(sum(lens[h * nb:(h + 1) * nb])) for h in range(H)]
+    dies = [[] for _ in range(8)]
+    load = [0] * 8
+    for h in sorted(range(H), key=lambda h: (-kept[h], h)):
+        x = min((x for x in range(8) if len(dies[x]) < cap_h), key=lambda x: (load[x], x))
+        dies[x].append(h)
+        load[x] += kept[h]
+    work = [-1] * (8 * cap_h * nb)
+    for x in range(8):
+        rows = [r for h in dies[x] for r in sorted(range(h * nb, (h + 1) * nb),
+                                                    key=lambda r: (-lens[r], r))]
+        work[x * cap_h * nb: x * cap_h * nb + len(rows)] = rows
+    return work
+
+
 def pin_plan(lib):
-    rng = np.random.default_rng(RNG_SEEDS[1] + 7)
-    lens = rng.integers(0, 6, size=40)
-    lens[[3, 17, 29]] = 0
+    # Hand-derived: H=3, nb=4, one head per die.  Kept per head: 5, 9, 5, so
+    # head 1 -> die 0, head 0 -> die 1, head 2 -> die 2; dies 3..7 stay empty.
+    lens = np.array([2, 0, 3, 0,   4, 1, 4, 0,   1, 1, 1, 2])
     row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    work, n = O.plan(row_ptr, lib)
-    want = sorted(range(40), key=lambda r: (-lens[r], r))
-    assert list(work) == want and n == int((lens > 0).sum())
+    work, n = O.plan(row_ptr, 3, 4, lib)
+    want = [4, 6, 5, 7,   2, 0, 1, 3,   11, 8, 9, 10] + [-1] * 20
+    assert list(work) == want and n == 9
+    # Spec in Python on random shapes (several heads per die, LPT balancing).
+    rng = np.random.default_rng(RNG_SEEDS[1] + 7)
+    for H, nb in ((20, 6), (28, 9), (8, 5), (33, 3)):
+        lens = rng.integers(0, nb + 1, size=H * nb) * (rng.random(H * nb) < 0.7)
+        lens[: nb] = 0                                  # one head keeps nothing
+        row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        work, n = O.plan(row_ptr, H, nb, lib)
+        assert list(work) == _plan_spec(lens, H, nb), (H, nb)
+        assert n == int((lens > 0).sum())
+        assert sorted(int(r) for r in work if r >= 0) == list(range(H * nb))
 
 
 # --------------------------------------------------------------- attention --

@@ -105,14 +105,15 @@ def test_plan_matches_oracle(shape):
     q, k, v = _qkv(shape, 303)
     m = PT.GpuMask(q, k, blk, 0.8)
     rp, _ = m.csr()
-    work_ref, n_ref = O.plan(rp)
+    work_ref, n_ref = O.plan(rp, H, L // blk)
     assert np.array_equal(m.buf.work().cpu().numpy(), work_ref)
-    assert int(m.buf.work_meta().cpu().numpy()[0]) == n_ref
+    meta = m.buf.work_meta().cpu().numpy()
+    assert int(meta[0]) == m.buf.work_cap() and int(meta[1]) == n_ref
 
 
-def test_plan_many_rows_and_lengths():
-    """Injected lists over 40 tiles of rows with every length 0..nb."""
-    H, nb = 64, 320
+@pytest.mark.parametrize("H,nb", [(64, 320), (28, 129), (3, 1024), (13, 7)])
+def test_plan_many_rows_and_lengths(H, nb):
+    """Injected lists with every length 0..nb, ragged head counts per die."""
     rng = np.random.default_rng(9)
     lens = rng.integers(0, nb + 1, size=H * nb)
     lens[rng.random(H * nb) < 0.3] = 0
@@ -121,9 +122,9 @@ def test_plan_many_rows_and_lengths():
     buf = B.MaskBuffers(dims, 0.5, device=DEV)
     B.plan(dims, torch.from_numpy(rp).to(DEV), buf.ws)
     torch.cuda.synchronize()
-    work_ref, n_ref = O.plan(rp)
+    work_ref, n_ref = O.plan(rp, H, nb)
     assert np.array_equal(buf.work().cpu().numpy(), work_ref)
-    assert int(buf.work_meta().cpu().numpy()[0]) == n_ref
+    assert int(buf.work_meta().cpu().numpy()[1]) == n_ref
 
 
 def _attn_case(shape, s, seed):

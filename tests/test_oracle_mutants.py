@@ -32,6 +32,10 @@ MUTANTS = [
      "for (int64_t r = 1; r < K && r < n; ++r)", 0),
     ("csr_transposed", "if (keep[(int64_t)r * nb + j])", "if (keep[(int64_t)j * nb + r])", 0),
     ("plan_ascending", "if (la > lb) return -1;", "if (la < lb) return -1;", 0),
+    ("plan_most_loaded_die", "load[x] < load[best]", "load[x] > load[best]", 0),
+    ("plan_heads_ascending",
+     "if (g_head_kept[a] > g_head_kept[b]) return -1;\n    if (g_head_kept[a] < g_head_kept[b]) return 1;",
+     "if (g_head_kept[a] > g_head_kept[b]) return 1;\n    if (g_head_kept[a] < g_head_kept[b]) return -1;", 0),
     ("attn_block_index_not_scaled", "toks[ntok++] = col_idx[e] * B + t;",
      "toks[ntok++] = col_idx[e] + t;", 0),
     ("attn_no_scale", "double scale = 1.0 / sqrt((double)d);", "double scale = 1.0;", 0),
