@@ -11,7 +11,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libstepdllm.so")
+# STEPDLLM_LIB selects another build of the same library (A/B comparisons).
+LIB_PATH = os.environ.get("STEPDLLM_LIB") or os.path.join(_PKG, "libstepdllm.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ESTATE = 0, -1, -2, -3, -4, -5
 

@@ -10,9 +10,11 @@
 // bidirectional (no causal mask).
 //
 // Design (one workgroup per (head, query block) row):
-//  * A wave owns 64 query rows and every other 32-key chunk of each kept
-//    block: waves (wq, wk), wq the 64-row query slice, wk in {0, 1}.  Each wave
-//    keeps its own online-softmax state; the two halves merge once per row.
+//  * A wave owns QW = 32 query rows and every other 32-key chunk of each kept
+//    block: waves (wq, wk), wq the query slice, wk in {0, 1} the key half.
+//    Each wave keeps its own online-softmax state; the key halves merge once
+//    per row.  About 200 VGPRs per wave, so two waves share each SIMD and one
+//    wave's softmax (VALU) overlaps the other's matrix work.
 //  * Scores are computed transposed, S^T = K . Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K is the A operand, Q^T the B operand (held in
 //    registers for the whole row).  In the accumulator layout every lane holds
@@ -20,12 +22,14 @@
 //    the fp32 scores convert in place into the B operand of O^T += V^T . P^T.
 //    Inside a 16-wide k step the key order is permuted, consistently for P^T
 //    and V^T: slot 16*ks + 8*hh + e holds key 16*ks + 8*(e/4) + 4*hh + e%4.
-//  * K and V chunks stream through a per-wave two-stage LDS ring filled by
-//    direct global->LDS loads (global_load_lds_dwordx4), 16-byte segments
-//    XOR-swizzled per row against bank conflicts.  A chunk's operand
-//    fragments are read out of LDS (K with ds_read_b128, V^T with the gfx950
-//    transposing ds_read_b64_tr_b16) before the next chunk's loads are
-//    issued, so those loads fly during the whole MFMA/softmax body.
+//  * K and V chunks stream through a two-stage LDS ring per key half, shared
+//    by the waves of that half and filled by direct buffer->LDS loads
+//    (buffer_load_dwordx4 ... lds), 16-byte segments XOR-swizzled per row so
+//    that operand reads are free of bank conflicts.  A chunk's fragments are
+//    read out of LDS (K with ds_read_b128, V^T with the gfx950 transposing
+//    ds_read_b64_tr_b16) before the next chunk's loads are issued, so those
+//    loads fly during the MFMA/softmax body; one barrier per chunk orders the
+//    shared stages.
 //  * fp32 accumulation and softmax (exp2 with log2(e)/sqrt(d) folded in); the
 //    running max is raised only when a chunk exceeds it by more than 8 (log2
 //    units), so the O^T rescale is rare.  bf16 round-to-nearest-even output.
@@ -42,6 +46,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define SD_GLOBAL __attribute__((address_space(1)))
 
 constexpr int kChunk = 32;          // keys per wave step
+constexpr int kQW = 32;             // query rows per wave
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
@@ -69,13 +74,14 @@ __device__ __forceinline__ int swz_v(int row) {
     return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
-template <int D, int BLK, bool DENSE>
-__global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
+template <int D, int BLK, int QW, bool DENSE>
+__global__ __launch_bounds__(2 * BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ row_ptr,
     const int32_t *__restrict__ col_idx, const int32_t *__restrict__ work,
     uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx, float scale_log2) {
-    constexpr int WQ = BLK / 64;                // 64-row query slices per block
+    constexpr int NT = QW / 32;                 // 32-query tiles per wave
+    constexpr int WQ = BLK / QW;                // query slices per block
     constexpr int WAVES = 2 * WQ;
     constexpr int KS = D / 16;                  // k steps of the score product
     constexpr int MT = D / 32;                  // 32-row tiles of O^T
@@ -84,8 +90,10 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
     constexpr int STAGE = 2 * TILE;             // K tile + V tile
     constexpr int NSEG = D / 8;                 // 16-byte segments per row
     constexpr int ROWS_PER_LOAD = 64 / NSEG;    // rows covered by one wave load
-    __shared__ __attribute__((aligned(16))) uint16_t ring[WAVES * 2 * STAGE];
-    __shared__ float ml[WQ][4][64];             // m, l exchange
+    constexpr int LOADS = kChunk / ROWS_PER_LOAD;   // wave loads per tile
+    // One two-stage ring per key half, shared by the WQ waves of that half.
+    __shared__ __attribute__((aligned(16))) uint16_t ring[2 * 2 * STAGE];
+    __shared__ float ml[WQ][2 * NT][64];        // m, l exchange
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -111,7 +119,7 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
         if (row < 0 || row >= H * nb) return;   // padding (or a malformed order): nothing to do
     }
     const int h = row / nb, blk = row % nb, g = h / G;
-    const int q0 = blk * BLK + 64 * wq;
+    const int q0 = blk * BLK + QW * wq;
     const int64_t qbase = ((int64_t)h * L + q0) * D;
     const int64_t kvbase = (int64_t)g * L * D;
 
@@ -123,29 +131,33 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
     if (e_end <= e_begin) {     // no kept block: the row attends to nothing
         if (wk == 0) {
             uint4 z = make_uint4(0, 0, 0, 0);
-            for (int x = lane; x < 64 * D / 8; x += 64)
+            for (int x = lane; x < QW * D / 8; x += 64)
                 *reinterpret_cast<uint4 *>(o + qbase + (int64_t)x * 8) = z;
         }
         return;
     }
 
     // Q^T operand fragments: lane holds query col (32*nt + col), dims 16*s + 8*hh .. +8.
-    bf16x8 qf[2][KS];
+    bf16x8 qf[NT][KS];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int s = 0; s < KS; ++s)
             qf[nt][s] = load_bf16x8(q + qbase + (int64_t)(32 * nt + col) * D + 16 * s + 8 * hh);
 
-    f32x16 oacc[MT][2];
+    f32x16 oacc[MT][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[mt][nt][i] = 0.0f;
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.0f, 0.0f};
+    float m_run[NT], l_run[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        m_run[nt] = -INFINITY;
+        l_run[nt] = 0.0f;
+    }
 
     // This wave's chunks: for every kept block e, chunks wk, wk + 2, ...
     const int n_total = (e_end - e_begin) * CPW;
@@ -155,7 +167,7 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
         j = min(max(j, 0), nb - 1);   // malformed ids are clamped into range
         return j * BLK + (wk + 2 * (n % CPW)) * kChunk;
     };
-    uint16_t *my_ring = ring + wave * 2 * STAGE;
+    uint16_t *my_ring = ring + wk * 2 * STAGE;
 
     // Direct global->LDS loads of chunk n's K and V rows into stage st.  Wave
     // load t writes 64 x 16 contiguous bytes: rows t*ROWS_PER_LOAD + lane/NSEG,
@@ -168,21 +180,27 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
     const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(v + kvbase), 0, L * D * 2, 0x00020000);
     const int r_in = lane / NSEG, sp = lane % NSEG;
-    constexpr int LOADS = kChunk / ROWS_PER_LOAD;
-    constexpr int KPAT = (D / 8 > ROWS_PER_LOAD) ? (D / 8) / ROWS_PER_LOAD : 1;
-    uint32_t k_voff[KPAT];
+    // The WQ waves sharing a key half split each tile's LOADS wave loads:
+    // this wave issues loads t = tt*WQ + wq.  Per-lane offsets (row within the
+    // load and swizzled segment) are fixed per tt; row groups and the chunk
+    // are scalar offsets.
+    constexpr int MY_LOADS = LOADS / WQ;
+    uint32_t k_voff[MY_LOADS];
 #pragma unroll
-    for (int x = 0; x < KPAT; ++x)
-        k_voff[x] = (uint32_t)(r_in * D * 2 + 16 * (sp ^ swz_k<D>(x * ROWS_PER_LOAD + r_in)));
+    for (int tt = 0; tt < MY_LOADS; ++tt) {
+        const int r = (tt * WQ + wq) * ROWS_PER_LOAD + r_in;
+        k_voff[tt] = (uint32_t)(r_in * D * 2 + 16 * (sp ^ swz_k<D>(r)));
+    }
     const uint32_t v_voff = (uint32_t)(r_in * D * 2 + 16 * (sp ^ swz_v<D>(r_in)));
     auto issue = [&](int n, int st) {
         const uint32_t kv_off = (uint32_t)chunk_key0(n) * (D * 2);
         uint16_t *kt = my_ring + st * STAGE;
         uint16_t *vt = kt + TILE;
 #pragma unroll
-        for (int t = 0; t < LOADS; ++t) {
+        for (int tt = 0; tt < MY_LOADS; ++tt) {
+            const int t = tt * WQ + wq;
             const uint32_t soff = kv_off + t * ROWS_PER_LOAD * D * 2;
-            load_lds16(k_rsrc, kt + t * 512, k_voff[t % KPAT], soff);
+            load_lds16(k_rsrc, kt + t * 512, k_voff[tt], soff);
             load_lds16(v_rsrc, vt + t * 512, v_voff, soff);
         }
     };
@@ -225,9 +243,9 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
 
     auto compute_chunk = [&](const bf16x8 (&kf)[KS], const bf16x8 (&vf)[MT][2]) {
         // S^T = K . Q^T (32 keys x 64 queries).
-        f32x16 sacc[2];
+        f32x16 sacc[NT];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) sacc[nt][i] = 0.0f;
 #pragma unroll
@@ -236,9 +254,10 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
                                                                    0, 0);
         }
         // Online softmax per query column, log2 units, lazily rescaled.
-        float mx[2];
+        float mx[NT];
+        bool raise = false;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
             float a0 = fmaxf(fmaxf(sacc[nt][0], sacc[nt][1]), sacc[nt][2]);
             float a1 = fmaxf(fmaxf(sacc[nt][3], sacc[nt][4]), sacc[nt][5]);
             float a2 = fmaxf(fmaxf(sacc[nt][6], sacc[nt][7]), sacc[nt][8]);
@@ -247,10 +266,11 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
             float m = fmaxf(fmaxf(a0, a1), fmaxf(fmaxf(a2, a3), fmaxf(a4, sacc[nt][15])));
             m = fmaxf(m, __shfl_xor(m, 32));
             mx[nt] = m * scale_log2;
+            raise = raise || (mx[nt] > m_run[nt] + 8.0f);
         }
-        if (__any((mx[0] > m_run[0] + 8.0f) || (mx[1] > m_run[1] + 8.0f))) {
+        if (__any(raise)) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NT; ++nt) {
                 const float m_new = fmaxf(m_run[nt], mx[nt]);
                 const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
                 l_run[nt] *= alpha;
@@ -261,9 +281,9 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
                     for (int i = 0; i < 16; ++i) oacc[mt][nt][i] *= alpha;
             }
         }
-        bf16x8 pf[2][2];
+        bf16x8 pf[NT][2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
             const float neg_m = -m_run[nt];
             float psum = 0.0f;
 #pragma unroll
@@ -280,7 +300,7 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
+                for (int nt = 0; nt < NT; ++nt)
                     oacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         vf[mt][ks], pf[nt][ks], oacc[mt][nt], 0, 0, 0);
     };
@@ -294,31 +314,37 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
         // in flight: wait for all of them before any LDS read of the stage (the
         // compiler does not order LDS reads after buffer->LDS loads by itself).
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // With a shared ring, the other waves' loads of this chunk must have
+        // landed too, and every wave must have finished reading the stage the
+        // next loads overwrite (read in the previous step, before its wait).
+        if (WQ > 1) __syncthreads();
         read_frags(st, kf, vf);
+        if (WQ > 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (n + 1 < n_total) issue(n + 1, st ^ 1);
         compute_chunk(kf, vf);
     }
 
     // Column sums: the two lane halves hold different keys of the same column.
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) l_run[nt] += __shfl_xor(l_run[nt], 32);
+    for (int nt = 0; nt < NT; ++nt) l_run[nt] += __shfl_xor(l_run[nt], 32);
 
     // Merge the two key halves (wk = 1 hands its state to wk = 0), then write.
     // The exchange tile reuses the ring once every wave has left the loop.
     __syncthreads();
-    float(*xchg)[32][64] = reinterpret_cast<float(*)[32][64]>(ring);
+    float(*xchg)[16 * NT][64] = reinterpret_cast<float(*)[16 * NT][64]>(ring);
     if (wk == 1) {
-        ml[wq][0][lane] = m_run[0];
-        ml[wq][1][lane] = m_run[1];
-        ml[wq][2][lane] = l_run[0];
-        ml[wq][3][lane] = l_run[1];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            ml[wq][nt][lane] = m_run[nt];
+            ml[wq][NT + nt][lane] = l_run[nt];
+        }
     }
     __syncthreads();
-    float a_self[2], a_other[2], inv_l[2];
+    float a_self[NT], a_other[NT], inv_l[NT];
     if (wk == 0) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const float m1 = ml[wq][nt][lane], l1 = ml[wq][2 + nt][lane];
+        for (int nt = 0; nt < NT; ++nt) {
+            const float m1 = ml[wq][nt][lane], l1 = ml[wq][NT + nt][lane];
             const float mm = fmaxf(m_run[nt], m1);
             a_self[nt] = __builtin_amdgcn_exp2f(m_run[nt] - mm);
             a_other[nt] = __builtin_amdgcn_exp2f(m1 - mm);
@@ -331,14 +357,14 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
         if (mt) __syncthreads();
         if (wk == 1) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) xchg[wq][16 * nt + i][lane] = oacc[mt][nt][i];
         }
         __syncthreads();
         if (wk == 0) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
                     uint32_t packed[2];
@@ -361,13 +387,13 @@ __global__ __launch_bounds__(128 * (BLK / 64)) void k_attn(
     }
 }
 
-template <int D, int BLK, bool DENSE>
+template <int D, int BLK, int QW, bool DENSE>
 hipError_t launch_attn_t(const Dims &Dm, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const int32_t *row_ptr, const int32_t *col_idx, const int32_t *work,
                          int n_idx, uint16_t *o, hipStream_t s) {
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const unsigned grid = (unsigned)(DENSE ? Dm.rows() : kDies * Dm.die_cap());
-    hipLaunchKernelGGL((k_attn<D, BLK, DENSE>), dim3(grid), dim3(128 * (BLK / 64)),
+    hipLaunchKernelGGL((k_attn<D, BLK, QW, DENSE>), dim3(grid), dim3(2 * BLK / QW * 64),
                        0, s, q, k, v, row_ptr, col_idx, work, o, Dm.L, Dm.nb, Dm.G, Dm.H,
                        n_idx, scale_log2);
     return hipGetLastError();
@@ -378,12 +404,12 @@ hipError_t launch_attn(const Dims &D, const uint16_t *q, const uint16_t *k, cons
                        const int32_t *row_ptr, const int32_t *col_idx, const int32_t *work,
                        int n_idx, uint16_t *o, hipStream_t s) {
     if (D.d == 128 && D.B == 64)
-        return launch_attn_t<128, 64, DENSE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
+        return launch_attn_t<128, 64, kQW, DENSE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
     if (D.d == 128 && D.B == 128)
-        return launch_attn_t<128, 128, DENSE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
+        return launch_attn_t<128, 128, kQW, DENSE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
     if (D.d == 64 && D.B == 64)
-        return launch_attn_t<64, 64, DENSE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
-    return launch_attn_t<64, 128, DENSE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
+        return launch_attn_t<64, 64, kQW, DENSE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
+    return launch_attn_t<64, 128, kQW, DENSE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
 }
 
 }  // namespace
