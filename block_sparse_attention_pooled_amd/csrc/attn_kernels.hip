@@ -10,11 +10,12 @@
 // bidirectional (no causal mask).
 //
 // Design (one workgroup per (head, query block) row):
-//  * A wave owns QW = 32 query rows and every other 32-key chunk of each kept
-//    block: waves (wq, wk), wq the query slice, wk in {0, 1} the key half.
-//    Each wave keeps its own online-softmax state; the key halves merge once
-//    per row.  About 200 VGPRs per wave, so two waves share each SIMD and one
-//    wave's softmax (VALU) overlaps the other's matrix work.
+//  * A wave owns QW = 32 query rows and walks every 32-key chunk of every
+//    kept block with one online-softmax state, so no partial results are
+//    merged; a workgroup is the BLK / 32 waves of one query block.  About 200
+//    VGPRs per wave, so two waves share each SIMD and one wave's softmax
+//    (VALU) overlaps the other's matrix work; with a 32 KiB ring per
+//    workgroup, four 64-row workgroups fit on a CU.
 //  * Scores are computed transposed, S^T = K . Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K is the A operand, Q^T the B operand (held in
 //    registers for the whole row).  In the accumulator layout every lane holds
@@ -22,8 +23,8 @@
 //    the fp32 scores convert in place into the B operand of O^T += V^T . P^T.
 //    Inside a 16-wide k step the key order is permuted, consistently for P^T
 //    and V^T: slot 16*ks + 8*hh + e holds key 16*ks + 8*(e/4) + 4*hh + e%4.
-//  * K and V chunks stream through a two-stage LDS ring per key half, shared
-//    by the waves of that half and filled by direct buffer->LDS loads
+//  * K and V chunks stream through a two-stage LDS ring shared by the waves
+//    of the workgroup and filled by direct buffer->LDS loads
 //    (buffer_load_dwordx4 ... lds), 16-byte segments XOR-swizzled per row so
 //    that operand reads are free of bank conflicts.  A chunk's fragments are
 //    read out of LDS (K with ds_read_b128, V^T with the gfx950 transposing
@@ -75,30 +76,28 @@ __device__ __forceinline__ int swz_v(int row) {
 }
 
 template <int D, int BLK, int QW, bool DENSE>
-__global__ __launch_bounds__(2 * BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
+__global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ row_ptr,
     const int32_t *__restrict__ col_idx, const int32_t *__restrict__ work,
     uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx, float scale_log2) {
     constexpr int NT = QW / 32;                 // 32-query tiles per wave
-    constexpr int WQ = BLK / QW;                // query slices per block
-    constexpr int WAVES = 2 * WQ;
+    constexpr int WQ = BLK / QW;                // query slices (= waves) per block
     constexpr int KS = D / 16;                  // k steps of the score product
     constexpr int MT = D / 32;                  // 32-row tiles of O^T
-    constexpr int CPW = BLK / kChunk / 2;       // chunks per wave per key block
+    constexpr int CPB = BLK / kChunk;           // chunks per key block
     constexpr int TILE = kChunk * D;            // bf16 elements in a 32-key tile
     constexpr int STAGE = 2 * TILE;             // K tile + V tile
     constexpr int NSEG = D / 8;                 // 16-byte segments per row
     constexpr int ROWS_PER_LOAD = 64 / NSEG;    // rows covered by one wave load
     constexpr int LOADS = kChunk / ROWS_PER_LOAD;   // wave loads per tile
-    // One two-stage ring per key half, shared by the WQ waves of that half.
-    __shared__ __attribute__((aligned(16))) uint16_t ring[2 * 2 * STAGE];
-    __shared__ float ml[WQ][2 * NT][64];        // m, l exchange
+    // One two-stage ring, shared by the WQ waves of the workgroup.
+    __shared__ __attribute__((aligned(16))) uint16_t ring[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-    const int wq = wave >> 1, wk = wave & 1;
+    const int wq = wave;
     const int col = lane & 31, hh = lane >> 5;
 
     // Row of this workgroup.
@@ -129,11 +128,9 @@ __global__ __launch_bounds__(2 * BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         e_end = min(__builtin_amdgcn_readfirstlane(row_ptr[row + 1]), n_idx);
     }
     if (e_end <= e_begin) {     // no kept block: the row attends to nothing
-        if (wk == 0) {
-            uint4 z = make_uint4(0, 0, 0, 0);
-            for (int x = lane; x < QW * D / 8; x += 64)
-                *reinterpret_cast<uint4 *>(o + qbase + (int64_t)x * 8) = z;
-        }
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        for (int x = lane; x < QW * D / 8; x += 64)
+            *reinterpret_cast<uint4 *>(o + qbase + (int64_t)x * 8) = z;
         return;
     }
 
@@ -159,15 +156,15 @@ __global__ __launch_bounds__(2 * BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         l_run[nt] = 0.0f;
     }
 
-    // This wave's chunks: for every kept block e, chunks wk, wk + 2, ...
-    const int n_total = (e_end - e_begin) * CPW;
+    // The row's chunks: every 32-key chunk of every kept block e, in order.
+    const int n_total = (e_end - e_begin) * CPB;
     auto chunk_key0 = [&](int n) -> int {
-        const int e = e_begin + n / CPW;
+        const int e = e_begin + n / CPB;
         int j = DENSE ? e : __builtin_amdgcn_readfirstlane(col_idx[e]);
         j = min(max(j, 0), nb - 1);   // malformed ids are clamped into range
-        return j * BLK + (wk + 2 * (n % CPW)) * kChunk;
+        return j * BLK + (n % CPB) * kChunk;
     };
-    uint16_t *my_ring = ring + wk * 2 * STAGE;
+    uint16_t *my_ring = ring;
 
     // Direct global->LDS loads of chunk n's K and V rows into stage st.  Wave
     // load t writes 64 x 16 contiguous bytes: rows t*ROWS_PER_LOAD + lane/NSEG,
@@ -180,7 +177,7 @@ __global__ __launch_bounds__(2 * BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(v + kvbase), 0, L * D * 2, 0x00020000);
     const int r_in = lane / NSEG, sp = lane % NSEG;
-    // The WQ waves sharing a key half split each tile's LOADS wave loads:
+    // The WQ waves of the workgroup split each tile's LOADS wave loads:
     // this wave issues loads t = tt*WQ + wq.  Per-lane offsets (row within the
     // load and swizzled segment) are fixed per tt; row groups and the chunk
     // are scalar offsets.
@@ -328,62 +325,25 @@ __global__ __launch_bounds__(2 * BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) l_run[nt] += __shfl_xor(l_run[nt], 32);
 
-    // Merge the two key halves (wk = 1 hands its state to wk = 0), then write.
-    // The exchange tile reuses the ring once every wave has left the loop.
-    __syncthreads();
-    float(*xchg)[16 * NT][64] = reinterpret_cast<float(*)[16 * NT][64]>(ring);
-    if (wk == 1) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            ml[wq][nt][lane] = m_run[nt];
-            ml[wq][NT + nt][lane] = l_run[nt];
-        }
-    }
-    __syncthreads();
-    float a_self[NT], a_other[NT], inv_l[NT];
-    if (wk == 0) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const float m1 = ml[wq][nt][lane], l1 = ml[wq][NT + nt][lane];
-            const float mm = fmaxf(m_run[nt], m1);
-            a_self[nt] = __builtin_amdgcn_exp2f(m_run[nt] - mm);
-            a_other[nt] = __builtin_amdgcn_exp2f(m1 - mm);
-            inv_l[nt] = 1.0f / (l_run[nt] * a_self[nt] + l1 * a_other[nt]);
-        }
-    }
+    // O = O^T / l, rounded to bf16: lane holds query col (32*nt + col) and 4
+    // consecutive dims per group of 4 accumulators.
     uint16_t *orow = o + qbase;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        if (mt) __syncthreads();
-        if (wk == 1) {
+    for (int nt = 0; nt < NT; ++nt) {
+        const float inv_l = 1.0f / l_run[nt];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) xchg[wq][16 * nt + i][lane] = oacc[mt][nt][i];
-        }
-        __syncthreads();
-        if (wk == 0) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    uint32_t packed[2];
-#pragma unroll
-                    for (int r = 0; r < 4; r += 2) {
-                        const int i = 4 * i4 + r;
-                        const float x0 = (oacc[mt][nt][i] * a_self[nt] +
-                                          xchg[wq][16 * nt + i][lane] * a_other[nt]) * inv_l[nt];
-                        const float x1 = (oacc[mt][nt][i + 1] * a_self[nt] +
-                                          xchg[wq][16 * nt + i + 1][lane] * a_other[nt]) * inv_l[nt];
-                        packed[r >> 1] = (uint32_t)bf16_rne(x0) | ((uint32_t)bf16_rne(x1) << 16);
-                    }
-                    const int qr = 32 * nt + col;
-                    const int dcol = 32 * mt + 8 * i4 + 4 * hh;
-                    *reinterpret_cast<uint2 *>(orow + (int64_t)qr * D + dcol) =
-                        make_uint2(packed[0], packed[1]);
-                }
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int i = 4 * i4;
+                const uint32_t lo = (uint32_t)bf16_rne(oacc[mt][nt][i] * inv_l) |
+                                    ((uint32_t)bf16_rne(oacc[mt][nt][i + 1] * inv_l) << 16);
+                const uint32_t hi = (uint32_t)bf16_rne(oacc[mt][nt][i + 2] * inv_l) |
+                                    ((uint32_t)bf16_rne(oacc[mt][nt][i + 3] * inv_l) << 16);
+                const int qr = 32 * nt + col;
+                const int dcol = 32 * mt + 8 * i4 + 4 * hh;
+                *reinterpret_cast<uint2 *>(orow + (int64_t)qr * D + dcol) = make_uint2(lo, hi);
             }
-        }
     }
 }
 
@@ -393,7 +353,7 @@ hipError_t launch_attn_t(const Dims &Dm, const uint16_t *q, const uint16_t *k, c
                          int n_idx, uint16_t *o, hipStream_t s) {
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const unsigned grid = (unsigned)(DENSE ? Dm.rows() : kDies * Dm.die_cap());
-    hipLaunchKernelGGL((k_attn<D, BLK, QW, DENSE>), dim3(grid), dim3(2 * BLK / QW * 64),
+    hipLaunchKernelGGL((k_attn<D, BLK, QW, DENSE>), dim3(grid), dim3(BLK / QW * 64),
                        0, s, q, k, v, row_ptr, col_idx, work, o, Dm.L, Dm.nb, Dm.G, Dm.H,
                        n_idx, scale_log2);
     return hipGetLastError();

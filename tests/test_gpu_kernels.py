@@ -226,8 +226,10 @@ def test_worked_example_w1_on_gpu():
 
 
 def test_constant_values_and_zero_queries():
-    """V = c gives O = c (exactly representable) on non-empty rows; Q = 0 gives
-    the mean of V over the kept blocks."""
+    """V = c gives O = c on non-empty rows (to one bf16 ulp: the weights enter
+    the value product rounded to bf16, unit roundoff 2^-8, while the softmax
+    normaliser sums them in fp32); Q = 0 gives the mean of V over the kept
+    blocks."""
     H, Hkv, L, d, blk = 4, 2, 8 * 64, 128, 64
     q, k, v = random_qkv(H, Hkv, L, d, 808, device=DEV, q_scale=2.0)
     vc = torch.full_like(v, -1.5)
@@ -237,7 +239,7 @@ def test_constant_values_and_zero_queries():
     torch.cuda.synchronize()
     nonempty = np.diff(m.csr()[0]) > 0
     on = o.cpu().to(torch.float32).numpy().reshape(H * (L // blk), blk, d)
-    assert np.all(on[nonempty] == -1.5) and np.all(on[~nonempty] == 0)
+    assert np.all(np.abs(on[nonempty] + 1.5) <= 1.5 * 2.0 ** -7) and np.all(on[~nonempty] == 0)
     z = torch.zeros_like(q)
     B.sparse_attn(m.dims, z, k, v, m.buf.row_ptr, m.buf.col_idx, m.buf.ws, o)
     torch.cuda.synchronize()
