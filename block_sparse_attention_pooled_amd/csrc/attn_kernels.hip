@@ -12,9 +12,8 @@
 // Design (one workgroup per (head, query block) row):
 //  * A wave owns QW = 32 query rows and walks every 32-key chunk of every
 //    kept block with one online-softmax state, so no partial results are
-//    merged; a workgroup is the BLK / 32 waves of one query block.  About 200
-//    VGPRs per wave, so two waves share each SIMD and one wave's softmax
-//    (VALU) overlaps the other's matrix work; with a 32 KiB ring per
+//    merged; a workgroup is the BLK / 32 waves of one query block.  Under 256
+//    VGPRs per wave, so two waves share each SIMD; with 40 KiB of LDS per
 //    workgroup, four 64-row workgroups fit on a CU.
 //  * Scores are computed transposed, S^T = K . Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K is the A operand, Q^T the B operand (held in
@@ -23,17 +22,19 @@
 //    the fp32 scores convert in place into the B operand of O^T += V^T . P^T.
 //    Inside a 16-wide k step the key order is permuted, consistently for P^T
 //    and V^T: slot 16*ks + 8*hh + e holds key 16*ks + 8*(e/4) + 4*hh + e%4.
-//  * K and V chunks stream through a two-stage LDS ring shared by the waves
-//    of the workgroup and filled by direct buffer->LDS loads
-//    (buffer_load_dwordx4 ... lds), 16-byte segments XOR-swizzled per row so
-//    that operand reads are free of bank conflicts.  A chunk's fragments are
-//    read out of LDS (K with ds_read_b128, V^T with the gfx950 transposing
-//    ds_read_b64_tr_b16) before the next chunk's loads are issued, so those
-//    loads fly during the MFMA/softmax body; one barrier per chunk orders the
-//    shared stages.
+//  * K and V chunks stream through LDS rings (three K stages, two V stages)
+//    shared by the waves of the workgroup and filled by direct buffer->LDS
+//    loads (buffer_load_dwordx4 ... lds), 16-byte segments XOR-swizzled per
+//    row so that operand reads are free of bank conflicts.  K fragments are
+//    read with ds_read_b128, V^T fragments with the gfx950 transposing
+//    ds_read_b64_tr_b16; one barrier per chunk orders the shared stages.
+//  * Software pipeline: the scores of chunk n+1 are formed on the matrix
+//    cores while the weights of chunk n are formed on the VALU, and the next
+//    chunks' loads fly during the whole step.
 //  * fp32 accumulation and softmax (exp2 with log2(e)/sqrt(d) folded in); the
 //    running max is raised only when a chunk exceeds it by more than 8 (log2
-//    units), so the O^T rescale is rare.  bf16 round-to-nearest-even output.
+//    units), so the O^T rescale is rare; the normaliser sums the bf16-rounded
+//    weights that enter the product.  bf16 round-to-nearest-even output.
 #include "common.h"
 
 namespace sd {
@@ -42,6 +43,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define SD_LDS __attribute__((address_space(3)))
 #define SD_GLOBAL __attribute__((address_space(1)))
@@ -87,12 +89,13 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     constexpr int MT = D / 32;                  // 32-row tiles of O^T
     constexpr int CPB = BLK / kChunk;           // chunks per key block
     constexpr int TILE = kChunk * D;            // bf16 elements in a 32-key tile
-    constexpr int STAGE = 2 * TILE;             // K tile + V tile
     constexpr int NSEG = D / 8;                 // 16-byte segments per row
     constexpr int ROWS_PER_LOAD = 64 / NSEG;    // rows covered by one wave load
     constexpr int LOADS = kChunk / ROWS_PER_LOAD;   // wave loads per tile
-    // One two-stage ring, shared by the WQ waves of the workgroup.
-    __shared__ __attribute__((aligned(16))) uint16_t ring[2 * STAGE];
+    // A three-stage K ring and a two-stage V ring, shared by the WQ waves of
+    // the workgroup.
+    __shared__ __attribute__((aligned(16))) uint16_t kring[3 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t vring[2 * TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -142,6 +145,17 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         for (int s = 0; s < KS; ++s)
             qf[nt][s] = load_bf16x8(q + qbase + (int64_t)(32 * nt + col) * D + 16 * s + 8 * hh);
 
+    // The row's key-block ids, 64 at a time in one register: lane i holds the
+    // id of kept block e_begin + 64*ids_grp + i.  Ids are then taken with
+    // readlane, so the chunk loop issues no scalar loads (a wait on one would
+    // also wait on every LDS read in flight).  Loaded after Q, so the first
+    // wait on them also retires the Q loads before the loop.
+    int ids = 0, ids_grp = 0;
+    if (!DENSE) {
+        const int e = e_begin + lane;
+        ids = e < e_end ? col_idx[e] : 0;
+    }
+
     f32x16 oacc[MT][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -159,14 +173,24 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     // The row's chunks: every 32-key chunk of every kept block e, in order.
     const int n_total = (e_end - e_begin) * CPB;
     auto chunk_key0 = [&](int n) -> int {
-        const int e = e_begin + n / CPB;
-        int j = DENSE ? e : __builtin_amdgcn_readfirstlane(col_idx[e]);
+        const int e_rel = n / CPB;
+        int j;
+        if (DENSE) {
+            j = e_begin + e_rel;
+        } else {
+            const int grp = e_rel >> 6;
+            if (grp != ids_grp) {
+                const int e = e_begin + 64 * grp + lane;
+                ids = e < e_end ? col_idx[e] : 0;
+                ids_grp = grp;
+            }
+            j = __builtin_amdgcn_readlane(ids, e_rel & 63);
+        }
         j = min(max(j, 0), nb - 1);   // malformed ids are clamped into range
         return j * BLK + (n % CPB) * kChunk;
     };
-    uint16_t *my_ring = ring;
 
-    // Direct global->LDS loads of chunk n's K and V rows into stage st.  Wave
+    // Direct global->LDS loads of chunk c's K (or V) rows into stage st.  Wave
     // load t writes 64 x 16 contiguous bytes: rows t*ROWS_PER_LOAD + lane/NSEG,
     // stored segment lane%NSEG, which holds source segment (stored ^ swizzle).
     // Buffer loads over this key head: the chunk and row-group offsets are
@@ -178,9 +202,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         (void *)(v + kvbase), 0, L * D * 2, 0x00020000);
     const int r_in = lane / NSEG, sp = lane % NSEG;
     // The WQ waves of the workgroup split each tile's LOADS wave loads:
-    // this wave issues loads t = tt*WQ + wq.  Per-lane offsets (row within the
-    // load and swizzled segment) are fixed per tt; row groups and the chunk
-    // are scalar offsets.
+    // this wave issues loads t = tt*WQ + wq.
     constexpr int MY_LOADS = LOADS / WQ;
     uint32_t k_voff[MY_LOADS];
 #pragma unroll
@@ -189,34 +211,42 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         k_voff[tt] = (uint32_t)(r_in * D * 2 + 16 * (sp ^ swz_k<D>(r)));
     }
     const uint32_t v_voff = (uint32_t)(r_in * D * 2 + 16 * (sp ^ swz_v<D>(r_in)));
-    auto issue = [&](int n, int st) {
-        const uint32_t kv_off = (uint32_t)chunk_key0(n) * (D * 2);
-        uint16_t *kt = my_ring + st * STAGE;
-        uint16_t *vt = kt + TILE;
+    auto issue_k = [&](int key0, int st) {
+        const uint32_t off = (uint32_t)key0 * (D * 2);
 #pragma unroll
         for (int tt = 0; tt < MY_LOADS; ++tt) {
             const int t = tt * WQ + wq;
-            const uint32_t soff = kv_off + t * ROWS_PER_LOAD * D * 2;
-            load_lds16(k_rsrc, kt + t * 512, k_voff[tt], soff);
-            load_lds16(v_rsrc, vt + t * 512, v_voff, soff);
+            load_lds16(k_rsrc, kring + st * TILE + t * 512, k_voff[tt],
+                       off + t * ROWS_PER_LOAD * D * 2);
+        }
+    };
+    auto issue_v = [&](int key0, int st) {
+        const uint32_t off = (uint32_t)key0 * (D * 2);
+#pragma unroll
+        for (int tt = 0; tt < MY_LOADS; ++tt) {
+            const int t = tt * WQ + wq;
+            load_lds16(v_rsrc, vring + st * TILE + t * 512, v_voff,
+                       off + t * ROWS_PER_LOAD * D * 2);
         }
     };
 
-    // Operand fragments of the chunk in stage st.
-    auto read_frags = [&](int st, bf16x8 (&kf)[KS], bf16x8 (&vf)[MT][2]) {
-        const uint16_t *kt = my_ring + st * STAGE;
-        const uint16_t *vt = kt + TILE;
-        // K as the A operand: lane row = key col, dims 16*s + 8*hh.
+    // K as the A operand of the score product: lane row = key col, dims
+    // 16*s + 8*hh.
+    auto read_k = [&](int st, bf16x8 (&kf)[KS]) {
+        const uint16_t *kt = kring + st * TILE;
 #pragma unroll
         for (int s = 0; s < KS; ++s)
             kf[s] = __builtin_bit_cast(
                 bf16x8, *reinterpret_cast<const uint4 *>(
                             kt + col * D + 8 * ((2 * s + hh) ^ swz_k<D>(col))));
-        // V^T as the A operand: lane row = dim 32*mt + col, 8 keys in slot order.
-        // Transposing load: lane i of a 16-lane group gets element i%4 of the
-        // 8-byte pieces addressed by lanes 4k + i/4, k = 0..3.  Addressing lane
-        // (group gq, index i) points at key row 16*ks + 8*r + 4*(gq/2) + i/4,
-        // dims 32*mt + 16*(gq%2) + 4*(i%4) .. +4.
+    };
+    // V^T as the A operand: lane row = dim 32*mt + col, 8 keys in slot order.
+    // Transposing load: lane i of a 16-lane group gets element i%4 of the
+    // 8-byte pieces addressed by lanes 4k + i/4, k = 0..3.  Addressing lane
+    // (group gq, index i) points at key row 16*ks + 8*r + 4*(gq/2) + i/4,
+    // dims 32*mt + 16*(gq%2) + 4*(i%4) .. +4.
+    auto read_v = [&](int st, bf16x8 (&vf)[MT][2]) {
+        const uint16_t *vt = vring + st * TILE;
         const int gq = lane >> 4, i16 = lane & 15;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -238,9 +268,8 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
             }
     };
 
-    auto compute_chunk = [&](const bf16x8 (&kf)[KS], const bf16x8 (&vf)[MT][2]) {
-        // S^T = K . Q^T (32 keys x 64 queries).
-        f32x16 sacc[NT];
+    // S^T = K . Q^T (32 keys x QW queries).
+    auto scores = [&](const bf16x8 (&kf)[KS], f32x16 (&sacc)[NT]) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -250,7 +279,12 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
                 sacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nt][s], sacc[nt], 0,
                                                                    0, 0);
         }
-        // Online softmax per query column, log2 units, lazily rescaled.
+    };
+    // Online softmax per query column, log2 units, lazily rescaled: each lane
+    // checks its 16 keys of the column (the other 16 are in lane ^ 32) against
+    // the running max; the max only moves here, from the max over all 32 keys,
+    // so both halves of a column always hold the same value.
+    auto update_max = [&](const f32x16 (&sacc)[NT]) {
         float mx[NT];
         bool raise = false;
 #pragma unroll
@@ -260,15 +294,14 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
             float a2 = fmaxf(fmaxf(sacc[nt][6], sacc[nt][7]), sacc[nt][8]);
             float a3 = fmaxf(fmaxf(sacc[nt][9], sacc[nt][10]), sacc[nt][11]);
             float a4 = fmaxf(fmaxf(sacc[nt][12], sacc[nt][13]), sacc[nt][14]);
-            float m = fmaxf(fmaxf(a0, a1), fmaxf(fmaxf(a2, a3), fmaxf(a4, sacc[nt][15])));
-            m = fmaxf(m, __shfl_xor(m, 32));
+            const float m = fmaxf(fmaxf(a0, a1), fmaxf(fmaxf(a2, a3), fmaxf(a4, sacc[nt][15])));
             mx[nt] = m * scale_log2;
             raise = raise || (mx[nt] > m_run[nt] + 8.0f);
         }
         if (__any(raise)) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const float m_new = fmaxf(m_run[nt], mx[nt]);
+                const float m_new = fmaxf(m_run[nt], fmaxf(mx[nt], __shfl_xor(mx[nt], 32)));
                 const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
                 l_run[nt] *= alpha;
                 m_run[nt] = m_new;
@@ -278,48 +311,111 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
                     for (int i = 0; i < 16; ++i) oacc[mt][nt][i] *= alpha;
             }
         }
-        bf16x8 pf[NT][2];
+    };
+    // Weights of chunk (scores sacc) as the bf16 B operand; the normaliser
+    // sums the weights as rounded for the product.
+    auto weights = [&](const f32x16 (&sacc)[NT], bf16x8 (&pf)[NT][2]) {
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const float neg_m = -m_run[nt];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                pf[nt][i >> 3][i & 7] =
+                    (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[nt][i], scale_log2, neg_m));
             float psum = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[nt][i], scale_log2, neg_m));
-                psum += pv;
-                pf[nt][i >> 3][i & 7] = (__bf16)pv;
-            }
+            for (int i = 0; i < 8; ++i)
+                psum = __builtin_amdgcn_fdot2_f32_bf16(
+                    bf16x2{pf[nt][i >> 2][2 * (i & 3)], pf[nt][i >> 2][2 * (i & 3) + 1]}, one,
+                    psum, false);
             l_run[nt] += psum;
         }
-        // O^T += V^T . P^T.
+    };
+    // O^T += V^T . P^T.
+    auto pv = [&](const bf16x8 (&vf)[MT][2], const bf16x8 (&pf)[NT][2]) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
                     oacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         vf[mt][ks], pf[nt][ks], oacc[mt][nt], 0, 0, 0);
     };
 
-    issue(0, 0);
-    for (int n = 0; n < n_total; ++n) {
-        const int st = n & 1;
-        bf16x8 kf[KS];
-        bf16x8 vf[MT][2];
-        // Chunk n's direct-to-LDS loads are the oldest vector-memory operations
-        // in flight: wait for all of them before any LDS read of the stage (the
-        // compiler does not order LDS reads after buffer->LDS loads by itself).
+    // Ring waits.  Only direct-to-LDS loads are in flight at the vmcnt wait,
+    // so vmcnt(0) means this wave's share of the stages has landed (the
+    // compiler does not order LDS reads after buffer->LDS loads by itself);
+    // lgkmcnt(0) means this wave has finished every read it issued.  After
+    // both, the barrier makes every wave's share visible and frees the stages
+    // read before it.
+    auto sync = [&] {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // With a shared ring, the other waves' loads of this chunk must have
-        // landed too, and every wave must have finished reading the stage the
-        // next loads overwrite (read in the previous step, before its wait).
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (WQ > 1) __syncthreads();
-        read_frags(st, kf, vf);
-        if (WQ > 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (n + 1 < n_total) issue(n + 1, st ^ 1);
-        compute_chunk(kf, vf);
+    };
+
+    // Software pipeline over the row's chunks; K(c) sits in K stage c%3, V(c)
+    // in V stage c%2.  Entering step n: the scores S(n) are formed and the
+    // running max covers them, K(n+1) is in registers, and V(n) and K(n+2)
+    // are being loaded.  Step n:
+    //   sync; read V(n); S(n+1) = K(n+1) . Q^T on the matrix cores while the
+    //   weights P(n) are formed on the VALU; read K(n+2) into registers once
+    //   S(n+1) has consumed K(n+1); load V(n+1) (its stage was read in step
+    //   n-1) and K(n+3) (stage of K(n), read in step n-2); O^T += V(n) . P(n)
+    //   on the matrix cores while the max of S(n+1) is taken; rare rescale.
+    // Every LDS read of a step precedes its loads: the compiler makes an LDS
+    // read wait for every buffer->LDS load in flight.  FULL steps have every
+    // chunk up to n+3; the last steps are guarded.
+    bf16x8 kf[KS];
+    auto step = [&](int n, bool full, f32x16 (&s_cur)[NT], f32x16 (&s_next)[NT]) {
+        const bool has1 = full || n + 1 < n_total;
+        const bool has2 = full || n + 2 < n_total;
+        const bool has3 = full || n + 3 < n_total;
+        sync();
+        // Keys of the next loads first: a reload of the ids waits on vector
+        // memory, which is idle right after the sync.
+        const int key1 = has1 ? chunk_key0(n + 1) : 0;
+        const int key3 = has3 ? chunk_key0(n + 3) : 0;
+        bf16x8 vf[MT][2];
+        bf16x8 pf[NT][2];
+        read_v(n & 1, vf);
+        if (has1) scores(kf, s_next);
+        weights(s_cur, pf);
+        if (has2) read_k((n + 2) % 3, kf);
+        if (has1) issue_v(key1, (n + 1) & 1);
+        if (has3) issue_k(key3, n % 3);
+        pv(vf, pf);
+        if (has1) update_max(s_next);
+    };
+
+    f32x16 sA[NT], sB[NT];
+    // Prologue: K(0..2) and V(0) in flight; S(0) and its max; K(1) into
+    // registers.
+    {
+        const int key0 = chunk_key0(0);
+        issue_k(key0, 0);
+        issue_v(key0, 0);
+        if (n_total > 1) issue_k(chunk_key0(1), 1);
+        if (n_total > 2) issue_k(chunk_key0(2), 2);
     }
+    sync();
+    read_k(0, kf);
+    scores(kf, sA);
+    if (n_total > 1) read_k(1, kf);
+    update_max(sA);
+
+    int n = 0;
+    for (; n + 4 < n_total; n += 2) {
+        step(n, true, sA, sB);
+        step(n + 1, true, sB, sA);
+    }
+    // 1 to 4 chunks remain, starting at an even n.
+    step(n, false, sA, sB);
+    if (n + 1 < n_total) step(n + 1, false, sB, sA);
+    if (n + 2 < n_total) step(n + 2, false, sA, sB);
+    if (n + 3 < n_total) step(n + 3, false, sB, sA);
 
     // Column sums: the two lane halves hold different keys of the same column.
 #pragma unroll
