@@ -153,6 +153,18 @@ float oracle_cut_value(const float *P, int64_t n, int64_t K)
     return v;
 }
 
+/* Uniform per-head budget, the baseline that the Step-dLLM abstract sets
+ * against its head-adaptive one (every head gets the same share): head h
+ * keeps the k_h = ceil((1-s) * nb^2) largest of its own nb^2 scores under the
+ * same order (value descending, index ascending), i.e. the global select run
+ * on each head's slice on its own. */
+void oracle_select_per_head(const float *P, int H, int nb, int64_t k_h, uint8_t *keep)
+{
+    int64_t per = (int64_t)nb * nb;
+    for (int h = 0; h < H; ++h)
+        oracle_select(P + h * per, per, k_h, keep + h * per);
+}
+
 /* ------------------------------------------------------------------ lists --- */
 /* Per (head, query-block) row, the kept key blocks in ascending order. */
 void oracle_csr(const uint8_t *keep, int rows, int nb, int32_t *row_ptr,
@@ -182,6 +194,26 @@ int64_t oracle_build_mask(const float *q, const float *k, int H, int Hkv, int L,
     int64_t K = oracle_keep_count(n, s);
     uint8_t *keep = (uint8_t *)malloc((size_t)n);
     oracle_select(p_out, n, K, keep);
+    oracle_csr(keep, H * nb, nb, row_ptr, col_idx);
+    free(keep);
+    return K;
+}
+
+/* The mask build with the uniform per-head budget; returns K = H * k_h. */
+int64_t oracle_build_mask_per_head(const float *q, const float *k, int H, int Hkv,
+                                   int L, int d, int B, double s, float *qb_out,
+                                   float *kb_out, float *p_out, int32_t *row_ptr,
+                                   int32_t *col_idx)
+{
+    int nb = L / B;
+    int64_t n = (int64_t)H * nb * nb;
+    oracle_pool(q, H, L, d, B, qb_out);
+    oracle_pool(k, Hkv, L, d, B, kb_out);
+    oracle_scores(qb_out, kb_out, H, Hkv, nb, d, p_out);
+    int64_t k_h = oracle_keep_count((int64_t)nb * nb, s);
+    int64_t K = k_h * H;
+    uint8_t *keep = (uint8_t *)malloc((size_t)n);
+    oracle_select_per_head(p_out, H, nb, k_h, keep);
     oracle_csr(keep, H * nb, nb, row_ptr, col_idx);
     free(keep);
     return K;

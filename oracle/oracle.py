@@ -37,9 +37,12 @@ def _bind(lib):
         "oracle_scores": (None, [f32p, f32p, ci, ci, ci, ci, f32p]),
         "oracle_keep_count": (ci64, [ci64, cd]),
         "oracle_select": (None, [f32p, ci64, ci64, u8p]),
+        "oracle_select_per_head": (None, [f32p, ci, ci, ci64, u8p]),
         "oracle_cut_value": (ctypes.c_float, [f32p, ci64, ci64]),
         "oracle_csr": (None, [u8p, ci, ci, i32p, i32p]),
         "oracle_build_mask": (ci64, [f32p, f32p, ci, ci, ci, ci, ci, cd, f32p, f32p, f32p, i32p, i32p]),
+        "oracle_build_mask_per_head": (ci64, [f32p, f32p, ci, ci, ci, ci, ci, cd, f32p, f32p, f32p,
+                                              i32p, i32p]),
         "oracle_plan": (ctypes.c_int32, [i32p, ci, ci, i32p]),
         "oracle_sparse_attn": (None, [f32p, f32p, f32p, ci, ci, ci, ci, ci, i32p, i32p, vp, ci, f64p]),
         "oracle_dense_attn": (None, [f32p, f32p, f32p, ci, ci, ci, ci, ci, vp, ci, f64p]),
@@ -110,6 +113,16 @@ def select(P, K, lib=None):
     return keep
 
 
+def select_per_head(P, k_h, lib=None):
+    """Uniform per-head budget: top-k_h of each head's slice P[h] -> uint8 keep mask."""
+    lib = lib or load()
+    P = _f32(P)
+    H, nb, _ = P.shape
+    keep = np.empty(P.shape, np.uint8)
+    lib.oracle_select_per_head(P.reshape(-1), H, nb, int(k_h), keep.reshape(-1))
+    return keep
+
+
 def cut_value(P, K, lib=None):
     lib = lib or load()
     P = _f32(P)
@@ -128,8 +141,9 @@ def csr(keep, lib=None):
     return row_ptr, col_idx[: row_ptr[-1]].copy()
 
 
-def build_mask(q, k, B, sparsity, lib=None):
-    """Anchor-step mask build. Returns dict(qb, kb, P, K, row_ptr, col_idx)."""
+def build_mask(q, k, B, sparsity, lib=None, per_head=False):
+    """Anchor-step mask build. Returns dict(qb, kb, P, K, row_ptr, col_idx).
+    per_head: the uniform per-head budget instead of the global one."""
     lib = lib or load()
     q, k = _f32(q), _f32(k)
     H, L, d = q.shape
@@ -140,7 +154,8 @@ def build_mask(q, k, B, sparsity, lib=None):
     P = np.empty((H, nb, nb), np.float32)
     row_ptr = np.empty(H * nb + 1, np.int32)
     col_idx = np.empty(H * nb * nb, np.int32)
-    K = lib.oracle_build_mask(q, k, H, Hkv, L, d, B, float(sparsity), qb, kb, P, row_ptr, col_idx)
+    fn = lib.oracle_build_mask_per_head if per_head else lib.oracle_build_mask
+    K = fn(q, k, H, Hkv, L, d, B, float(sparsity), qb, kb, P, row_ptr, col_idx)
     return dict(qb=qb, kb=kb, P=P, K=int(K), row_ptr=row_ptr, col_idx=col_idx[:K].copy())
 
 
@@ -191,5 +206,6 @@ def step_kind(step, dense_steps, refresh_every, lib=None):
     return int(lib.oracle_step_kind(int(step), int(dense_steps), int(refresh_every)))
 
 
-__all__ = ["build", "load", "pool", "scores", "keep_count", "select", "cut_value", "csr",
+__all__ = ["build", "load", "pool", "scores", "keep_count", "select", "select_per_head",
+           "cut_value", "csr",
            "build_mask", "plan", "sparse_attn", "dense_attn", "step_kind"]

@@ -147,6 +147,39 @@ def pin_select(lib):
     assert O.cut_value(P, 10, lib) == np.sort(P.reshape(-1))[::-1][9]
 
 
+def _check_top_k(vals, keep, k):
+    """keep (bool, flat order) holds exactly the k largest of vals, ties at the
+    cut going to the lowest indices: the properties that fix a top-k uniquely."""
+    kept, dropped = np.nonzero(keep)[0], np.nonzero(~keep)[0]
+    assert kept.size == k
+    if kept.size == 0 or dropped.size == 0:
+        return
+    lo, hi = vals[kept].min(), vals[dropped].max()
+    assert lo >= hi, (lo, hi)
+    if lo == hi:
+        assert kept[vals[kept] == lo].max() < dropped[vals[dropped] == hi].min()
+
+
+def pin_select_per_head(lib):
+    rng = np.random.default_rng(RNG_SEEDS[2] + 11)
+    for n_levels, shape in ((4, (3, 8, 8)), (40, (2, 16, 16)), (2, (5, 4, 4))):
+        levels = np.sort(rng.random(n_levels)).astype(np.float32)
+        P = levels[rng.integers(0, n_levels, size=shape)]
+        per = shape[1] * shape[2]
+        for k in (0, 1, per // 3, per // 2, per - 1, per):
+            keep = O.select_per_head(P, k, lib).astype(bool)
+            for h in range(shape[0]):
+                _check_top_k(P[h].reshape(-1), keep[h].reshape(-1), k)
+            # One head alone is the global select.
+            assert np.array_equal(O.select_per_head(P[:1], k, lib), O.select(P[:1], k, lib))
+        # A head's choice does not depend on the other heads' scores.
+        k = per // 2
+        base = O.select_per_head(P, k, lib)
+        P2 = P.copy()
+        P2[1:] = rng.random(P2[1:].shape).astype(np.float32)
+        assert np.array_equal(O.select_per_head(P2, k, lib)[0], base[0])
+
+
 def pin_csr(lib):
     rng = np.random.default_rng(RNG_SEEDS[0] + 7)
     keep = (rng.random((3, 8, 8)) < 0.3).astype(np.uint8)
@@ -318,6 +351,30 @@ def pin_worked_w1(lib):
     assert np.all(o[1, 3 * B:] == 0)
 
 
+def pin_worked_w1_per_head(lib):
+    """W1 under the uniform per-head budget: each head keeps k_h = 8 of 16.
+    Head 0 keeps its diagonal (value 1) and the four lowest-index blocks among
+    its equal off-diagonal scores, (0,1), (0,2), (0,3), (1,0); head 1 keeps its
+    first 8 flat positions, rows 0 and 1 whole, rows 2 and 3 empty."""
+    q, k, v, _ = worked_example_w1()
+    B = 64
+    m = O.build_mask(q, k, B, 0.5, lib, per_head=True)
+    assert m["K"] == 16
+    want = {0: [0, 1, 2, 3], 1: [0, 1], 2: [2], 3: [3], 4: [0, 1, 2, 3], 5: [0, 1, 2, 3],
+            6: [], 7: []}
+    rp, ci = m["row_ptr"], m["col_idx"]
+    for r, cols in want.items():
+        assert list(ci[rp[r]:rp[r + 1]]) == cols, (r, list(ci[rp[r]:rp[r + 1]]))
+    o = O.sparse_attn(q, k, v, B, rp, ci, lib=lib)
+    # Head 0: the own block outweighs the others by e^50.
+    for i in range(4):
+        want0 = v[0, i * B:(i + 1) * B].astype(np.float64).mean(axis=0)
+        assert np.max(np.abs(o[0, i * B:(i + 1) * B] - want0)) < 1e-12
+    want1 = v[1].astype(np.float64).mean(axis=0)
+    assert np.max(np.abs(o[1, :2 * B] - want1)) < 1e-12
+    assert np.all(o[1, 2 * B:] == 0)
+
+
 def pin_worked_w2(lib):
     """Q = 0 for every head: every score is 1/nb and the mask is the first K
     flat indices, whatever the sparsity."""
@@ -381,6 +438,7 @@ def pin_step_kind(lib):
     assert kinds == [0, 0, 0, 1, 2, 2, 2, 1, 2, 2, 2, 1]
 
 
-ALL_PINS = [pin_keep_count, pin_pool, pin_scores, pin_select, pin_csr, pin_plan,
+ALL_PINS = [pin_keep_count, pin_pool, pin_scores, pin_select, pin_select_per_head, pin_csr,
+            pin_plan, pin_worked_w1_per_head,
             pin_attention_brute, pin_attention_closed_forms, pin_worked_w1, pin_worked_w2,
             pin_build_mask_brute, pin_step_kind]

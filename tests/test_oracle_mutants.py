@@ -30,6 +30,12 @@ MUTANTS = [
      "return (a > b) ? -1 : (a < b);", 0),
     ("select_keeps_one_less", "for (int64_t r = 0; r < K && r < n; ++r)",
      "for (int64_t r = 1; r < K && r < n; ++r)", 0),
+    ("per_head_reads_head_0", "oracle_select(P + h * per, per, k_h, keep + h * per);",
+     "oracle_select(P, per, k_h, keep + h * per);", 0),
+    ("per_head_build_uses_global", "oracle_select_per_head(p_out, H, nb, k_h, keep);",
+     "oracle_select(p_out, n, K, keep);", 0),
+    ("per_head_budget_total", "oracle_select(P + h * per, per, k_h, keep + h * per);",
+     "oracle_select(P + h * per, per, k_h * H, keep + h * per);", 0),
     ("csr_transposed", "if (keep[(int64_t)r * nb + j])", "if (keep[(int64_t)j * nb + r])", 0),
     ("plan_ascending", "if (la > lb) return -1;", "if (la < lb) return -1;", 0),
     ("plan_most_loaded_die", "load[x] < load[best]", "load[x] > load[best]", 0),
