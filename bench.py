@@ -45,6 +45,9 @@ def parse_args():
     p.add_argument("--dense-iters", type=int, default=5)
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--per-head-budget", action="store_true",
+                   help="uniform per-head budget (the baseline the head-adaptive one is "
+                        "compared with) instead of the global budget")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (for counter calibration)")
     return p.parse_args()
@@ -66,7 +69,7 @@ def traffic_record():
     return rec
 
 
-def cpu_baseline(inputs0, w, sparsity, flops_per_step, budget_s):
+def cpu_baseline(inputs0, w, sparsity, flops_per_step, budget_s, per_head=False):
     """The oracle as it stands, on the host cores: one full mask build on step-0
     Q/K plus sparse attention on a deterministic sample of rows, extrapolated
     to one step by kept blocks (the anchor's mask build amortised over the
@@ -80,7 +83,7 @@ def cpu_baseline(inputs0, w, sparsity, flops_per_step, budget_s):
     q, k, v = (to_host_f32(x) for x in inputs0)
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     t0 = time.perf_counter()
-    ref = O.build_mask(q, k, w.B, sparsity)
+    ref = O.build_mask(q, k, w.B, sparsity, per_head=per_head)
     t_mask = time.perf_counter() - t0
     rp, ci, K = ref["row_ptr"], ref["col_idx"], ref["K"]
     lens = np.diff(rp)
@@ -136,7 +139,8 @@ def main():
     del traj
     torch.cuda.synchronize()
     dims = B.make_dims(w.H, w.Hkv, w.L, w.d, w.B)
-    drv = B.Driver(dims, w.dense_steps, w.refresh_every, sparsity, device=dev)
+    drv = B.Driver(dims, w.dense_steps, w.refresh_every, sparsity, device=dev,
+                   per_head_budget=args.per_head_budget)
     o = torch.empty(w.H, w.L, w.d, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -173,6 +177,11 @@ def main():
     n_anchor = sum(1 for kd in kinds if kd == 1)
 
     Kkept = drv.K
+    # Kept blocks per head in the mask left by the last anchor before timing ended.
+    rp = drv.row_ptr.cpu()
+    per_head = [int(rp[(h + 1) * w.nb] - rp[h * w.nb]) for h in range(w.H)]
+    ph_mean = sum(per_head) / len(per_head)
+    ph_cv = (sum((x - ph_mean) ** 2 for x in per_head) / len(per_head)) ** 0.5 / ph_mean
     flops_step = 4.0 * w.B * w.B * w.d * Kkept
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
@@ -228,9 +237,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "H": w.H, "Hkv": w.Hkv, "L": w.L, "d": w.d, "block": w.B,
                    "sparsity": sparsity, "kept_blocks": Kkept,
+                   "budget": "per_head" if args.per_head_budget else "global",
                    "refresh_every": w.refresh_every, "dense_steps": w.dense_steps,
                    "distinct_input_steps": T, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
+        "kept_per_head": {"min": min(per_head), "max": max(per_head),
+                          "cv": round(ph_cv, 4)},
         "anchor_step_ms": round(anchor_ms, 5) if anchor_ms else None,
         "mask_build_ms": round(anchor_ms - attn_ms, 5) if (anchor_ms and attn_ms) else None,
         "anchors_timed": n_anchor,
@@ -242,7 +254,8 @@ def main():
         "speedup_vs_dense_per_step": round(dense_ms / ms_per_step, 3),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inputs[0], w, sparsity, flops_step, args.cpu_budget_s)
+        result["cpu_baseline"] = cpu_baseline(inputs[0], w, sparsity, flops_step, args.cpu_budget_s,
+                                              per_head=args.per_head_budget)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

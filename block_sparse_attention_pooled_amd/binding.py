@@ -25,12 +25,13 @@ class Dims(ctypes.Structure):
 
 class Schedule(ctypes.Structure):
     _fields_ = [("dense_steps", ctypes.c_int32), ("refresh_every", ctypes.c_int32),
-                ("sparsity", ctypes.c_double)]
+                ("sparsity", ctypes.c_double), ("per_head_budget", ctypes.c_int32)]
 
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
-                ("pooled_q", "pooled_k", "scores", "select", "work", "work_meta", "total")]
+                ("pooled_q", "pooled_k", "scores", "select", "work", "work_meta",
+                 "head_select", "total")]
 
 
 class StepDLLMError(RuntimeError):
@@ -55,10 +56,13 @@ def load():
     i32, i64, dbl, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_size_t
     sig = {
         "stepdllm_keep_count": (i64, [D, dbl]),
+        "stepdllm_keep_count_per_head": (i64, [D, dbl]),
         "stepdllm_workspace_bytes": (i64, [D]),
         "stepdllm_workspace_layout": (i32, [D, ctypes.POINTER(WsLayout)]),
         "stepdllm_build_mask": (i32, [D, dbl, _vp, _vp, _vp, sz, _vp, _vp, _vp, _vp]),
         "stepdllm_select_mask": (i32, [D, dbl, _vp, _vp, sz, _vp, _vp, _vp]),
+        "stepdllm_build_mask_per_head": (i32, [D, dbl, _vp, _vp, _vp, sz, _vp, _vp, _vp, _vp]),
+        "stepdllm_select_mask_per_head": (i32, [D, dbl, _vp, _vp, sz, _vp, _vp, _vp]),
         "stepdllm_plan": (i32, [D, _vp, _vp, sz, _vp]),
         "stepdllm_sparse_attn": (i32, [D, _vp, _vp, _vp, _vp, _vp, i64, _vp, sz, _vp, _vp]),
         "stepdllm_dense_attn": (i32, [D, _vp, _vp, _vp, _vp, _vp]),
@@ -78,7 +82,8 @@ def load():
 
 
 EXPORTS = ["stepdllm_keep_count", "stepdllm_workspace_bytes", "stepdllm_workspace_layout",
-           "stepdllm_build_mask", "stepdllm_select_mask", "stepdllm_plan",
+           "stepdllm_build_mask", "stepdllm_select_mask", "stepdllm_keep_count_per_head",
+           "stepdllm_build_mask_per_head", "stepdllm_select_mask_per_head", "stepdllm_plan",
            "stepdllm_sparse_attn", "stepdllm_dense_attn", "stepdllm_driver_create",
            "stepdllm_driver_step_kind", "stepdllm_step", "stepdllm_driver_destroy",
            "stepdllm_status_string"]
@@ -120,10 +125,12 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def keep_count(dims, sparsity):
-    r = load().stepdllm_keep_count(ctypes.byref(dims), float(sparsity))
+def keep_count(dims, sparsity, per_head=False):
+    """K of the global budget, or H * k_h of the uniform per-head one."""
+    fn = "stepdllm_keep_count_per_head" if per_head else "stepdllm_keep_count"
+    r = getattr(load(), fn)(ctypes.byref(dims), float(sparsity))
     if r < 0:
-        raise StepDLLMError(int(r), "stepdllm_keep_count")
+        raise StepDLLMError(int(r), fn)
     return int(r)
 
 
@@ -141,20 +148,23 @@ def workspace_layout(dims):
     return out
 
 
-def build_mask(dims, sparsity, q, k, ws, row_ptr, col_idx, scores_out=None, stream=None):
+def build_mask(dims, sparsity, q, k, ws, row_ptr, col_idx, scores_out=None, stream=None,
+               per_head=False):
     bf = torch.bfloat16
-    _check(load().stepdllm_build_mask(
+    fn = "stepdllm_build_mask_per_head" if per_head else "stepdllm_build_mask"
+    _check(getattr(load(), fn)(
         ctypes.byref(dims), float(sparsity), _ptr(q, bf, "q"), _ptr(k, bf, "k"),
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _ptr(row_ptr, torch.int32, "row_ptr"),
         _ptr(col_idx, torch.int32, "col_idx"), _ptr(scores_out, torch.float32, "scores_out"),
-        _stream(stream)), "stepdllm_build_mask")
+        _stream(stream)), fn)
 
 
-def select_mask(dims, sparsity, scores, ws, row_ptr, col_idx, stream=None):
-    _check(load().stepdllm_select_mask(
+def select_mask(dims, sparsity, scores, ws, row_ptr, col_idx, stream=None, per_head=False):
+    fn = "stepdllm_select_mask_per_head" if per_head else "stepdllm_select_mask"
+    _check(getattr(load(), fn)(
         ctypes.byref(dims), float(sparsity), _ptr(scores, torch.float32, "scores"),
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _ptr(row_ptr, torch.int32, "row_ptr"),
-        _ptr(col_idx, torch.int32, "col_idx"), _stream(stream)), "stepdllm_select_mask")
+        _ptr(col_idx, torch.int32, "col_idx"), _stream(stream)), fn)
 
 
 def plan(dims, row_ptr, ws, stream=None):
@@ -184,15 +194,17 @@ def dense_attn(dims, q, k, v, o, stream=None):
 class Driver:
     """Owns the C driver handle; buffers are torch device tensors kept alive here."""
 
-    def __init__(self, dims, dense_steps, refresh_every, sparsity, device="cuda"):
+    def __init__(self, dims, dense_steps, refresh_every, sparsity, device="cuda",
+                 per_head_budget=False):
         self.dims = dims
-        self.K = keep_count(dims, sparsity)
+        self.K = keep_count(dims, sparsity, per_head_budget)
         rows = dims.n_q_heads * (dims.seq_len // dims.block)
         self.ws = torch.empty(workspace_bytes(dims), dtype=torch.uint8, device=device)
         self.row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=device)
         self.col_idx = torch.empty(max(self.K, 1), dtype=torch.int32, device=device)
         self._h = _vp()
-        sched = Schedule(int(dense_steps), int(refresh_every), float(sparsity))
+        sched = Schedule(int(dense_steps), int(refresh_every), float(sparsity),
+                         int(bool(per_head_budget)))
         _check(load().stepdllm_driver_create(
             ctypes.byref(self._h), ctypes.byref(dims), ctypes.byref(sched), self.ws.data_ptr(),
             self.ws.numel(), self.row_ptr.data_ptr(), self.col_idx.data_ptr()),
@@ -225,10 +237,10 @@ class Driver:
 class MaskBuffers:
     """Workspace + CSR buffers for one shape and sparsity (torch device memory)."""
 
-    def __init__(self, dims, sparsity, device="cuda"):
+    def __init__(self, dims, sparsity, device="cuda", per_head=False):
         self.dims = dims
         self.sparsity = float(sparsity)
-        self.K = keep_count(dims, sparsity)
+        self.K = keep_count(dims, sparsity, per_head)
         self.nb = dims.seq_len // dims.block
         self.rows = dims.n_q_heads * self.nb
         self.ws = torch.empty(workspace_bytes(dims), dtype=torch.uint8, device=device)
@@ -259,3 +271,6 @@ class MaskBuffers:
 
     def work_meta(self):
         return self.view(self.layout.work_meta, 16, torch.int32)
+
+    def head_select(self):
+        return self.view(self.layout.head_select, 8 * self.dims.n_q_heads, torch.int32)

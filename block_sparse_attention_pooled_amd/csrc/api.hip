@@ -52,15 +52,58 @@ int64_t keep_count(const Dims &D, double s) {
     return k > D.n_scores() ? D.n_scores() : k;
 }
 
+// Uniform per-head budget: k_h of each head's nb * nb scores.
+int64_t keep_count_per_head(const Dims &D, double s) {
+    const double n = (double)D.nb * D.nb;
+    const double x = (1.0 - s) * n - 1e-9 * n;
+    if (x <= 0.0) return 0;
+    int64_t k = (int64_t)ceil(x);
+    return k > (int64_t)D.nb * D.nb ? (int64_t)D.nb * D.nb : k;
+}
+
 bool sparsity_ok(double s) { return s >= 0.0 && s < 1.0; }   // false for NaN
 
 int hip_status(hipError_t e) { return e == hipSuccess ? STEPDLLM_OK : STEPDLLM_EHIP; }
 
-int select_and_plan(const Dims &D, double sparsity, const float *p, char *ws, const WsLayout &w,
-                    int32_t *row_ptr, int32_t *col_idx, hipStream_t s) {
-    int st = hip_status(sd::launch_select(D, keep_count(D, sparsity), p, ws, w, row_ptr, col_idx, s));
+int select_and_plan(const Dims &D, double sparsity, bool per_head, const float *p, char *ws,
+                    const WsLayout &w, int32_t *row_ptr, int32_t *col_idx, hipStream_t s) {
+    int st = hip_status(
+        per_head ? sd::launch_select_per_head(D, keep_count_per_head(D, sparsity), p, ws, w,
+                                              row_ptr, col_idx, s)
+                 : sd::launch_select(D, keep_count(D, sparsity), p, ws, w, row_ptr, col_idx, s));
     if (st) return st;
     return hip_status(sd::launch_plan(D, row_ptr, ws, w, s));
+}
+
+int build_mask(const stepdllm_dims *dims, double sparsity, bool per_head, const uint16_t *q,
+               const uint16_t *k, void *ws, size_t ws_bytes, int32_t *row_ptr, int32_t *col_idx,
+               float *scores_out, void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!sparsity_ok(sparsity) || !q || !k || !ws || !row_ptr || !col_idx) return STEPDLLM_EINVAL;
+    WsLayout w = sd::ws_layout(D);
+    if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
+    char *base = static_cast<char *>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *qb = reinterpret_cast<float *>(base + w.qb);
+    float *kb = reinterpret_cast<float *>(base + w.kb);
+    float *p = reinterpret_cast<float *>(base + w.p);
+    if ((st = hip_status(sd::launch_pool(D, q, k, qb, kb, s)))) return st;
+    if ((st = hip_status(sd::launch_scores(D, qb, kb, p, scores_out, s)))) return st;
+    return select_and_plan(D, sparsity, per_head, p, base, w, row_ptr, col_idx, s);
+}
+
+int select_mask(const stepdllm_dims *dims, double sparsity, bool per_head, const float *scores,
+                void *ws, size_t ws_bytes, int32_t *row_ptr, int32_t *col_idx, void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!sparsity_ok(sparsity) || !scores || !ws || !row_ptr || !col_idx) return STEPDLLM_EINVAL;
+    WsLayout w = sd::ws_layout(D);
+    if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
+    return select_and_plan(D, sparsity, per_head, scores, static_cast<char *>(ws), w, row_ptr,
+                           col_idx, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -85,6 +128,14 @@ int64_t stepdllm_keep_count(const stepdllm_dims *dims, double sparsity) {
     return keep_count(D, sparsity);
 }
 
+int64_t stepdllm_keep_count_per_head(const stepdllm_dims *dims, double sparsity) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!sparsity_ok(sparsity)) return STEPDLLM_EINVAL;
+    return keep_count_per_head(D, sparsity) * D.H;
+}
+
 int64_t stepdllm_workspace_bytes(const stepdllm_dims *dims) {
     Dims D;
     int st = check_dims(dims, &D);
@@ -104,6 +155,7 @@ int stepdllm_workspace_layout(const stepdllm_dims *dims, stepdllm_ws_layout *out
     out->select = w.sel;
     out->work = w.work;
     out->work_meta = w.work_meta;
+    out->head_select = w.hsel;
     out->total = w.total;
     return STEPDLLM_OK;
 }
@@ -111,33 +163,27 @@ int stepdllm_workspace_layout(const stepdllm_dims *dims, stepdllm_ws_layout *out
 int stepdllm_build_mask(const stepdllm_dims *dims, double sparsity, const uint16_t *q,
                         const uint16_t *k, void *ws, size_t ws_bytes, int32_t *row_ptr,
                         int32_t *col_idx, float *scores_out, void *stream) {
-    Dims D;
-    int st = check_dims(dims, &D);
-    if (st) return st;
-    if (!sparsity_ok(sparsity) || !q || !k || !ws || !row_ptr || !col_idx) return STEPDLLM_EINVAL;
-    WsLayout w = sd::ws_layout(D);
-    if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
-    char *base = static_cast<char *>(ws);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    float *qb = reinterpret_cast<float *>(base + w.qb);
-    float *kb = reinterpret_cast<float *>(base + w.kb);
-    float *p = reinterpret_cast<float *>(base + w.p);
-    if ((st = hip_status(sd::launch_pool(D, q, k, qb, kb, s)))) return st;
-    if ((st = hip_status(sd::launch_scores(D, qb, kb, p, scores_out, s)))) return st;
-    return select_and_plan(D, sparsity, p, base, w, row_ptr, col_idx, s);
+    return build_mask(dims, sparsity, false, q, k, ws, ws_bytes, row_ptr, col_idx, scores_out,
+                      stream);
+}
+
+int stepdllm_build_mask_per_head(const stepdllm_dims *dims, double sparsity, const uint16_t *q,
+                                 const uint16_t *k, void *ws, size_t ws_bytes, int32_t *row_ptr,
+                                 int32_t *col_idx, float *scores_out, void *stream) {
+    return build_mask(dims, sparsity, true, q, k, ws, ws_bytes, row_ptr, col_idx, scores_out,
+                      stream);
 }
 
 int stepdllm_select_mask(const stepdllm_dims *dims, double sparsity, const float *scores,
                          void *ws, size_t ws_bytes, int32_t *row_ptr, int32_t *col_idx,
                          void *stream) {
-    Dims D;
-    int st = check_dims(dims, &D);
-    if (st) return st;
-    if (!sparsity_ok(sparsity) || !scores || !ws || !row_ptr || !col_idx) return STEPDLLM_EINVAL;
-    WsLayout w = sd::ws_layout(D);
-    if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
-    return select_and_plan(D, sparsity, scores, static_cast<char *>(ws), w, row_ptr, col_idx,
-                           static_cast<hipStream_t>(stream));
+    return select_mask(dims, sparsity, false, scores, ws, ws_bytes, row_ptr, col_idx, stream);
+}
+
+int stepdllm_select_mask_per_head(const stepdllm_dims *dims, double sparsity,
+                                  const float *scores, void *ws, size_t ws_bytes,
+                                  int32_t *row_ptr, int32_t *col_idx, void *stream) {
+    return select_mask(dims, sparsity, true, scores, ws, ws_bytes, row_ptr, col_idx, stream);
 }
 
 int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr, void *ws, size_t ws_bytes,
@@ -187,7 +233,8 @@ int stepdllm_driver_create(stepdllm_driver **out, const stepdllm_dims *dims,
     if (st) return st;
     if (!schedule || !ws || !row_ptr || !col_idx) return STEPDLLM_EINVAL;
     if (!sparsity_ok(schedule->sparsity) || schedule->dense_steps < 0 ||
-        schedule->refresh_every < 0)
+        schedule->refresh_every < 0 ||
+        (schedule->per_head_budget != 0 && schedule->per_head_budget != 1))
         return STEPDLLM_EINVAL;
     if ((int64_t)ws_bytes < sd::ws_layout(D).total) return STEPDLLM_EWORKSPACE;
     stepdllm_driver *drv = static_cast<stepdllm_driver *>(malloc(sizeof(stepdllm_driver)));
@@ -198,7 +245,8 @@ int stepdllm_driver_create(stepdllm_driver **out, const stepdllm_dims *dims,
     drv->ws_bytes = ws_bytes;
     drv->row_ptr = row_ptr;
     drv->col_idx = col_idx;
-    drv->K = keep_count(D, schedule->sparsity);
+    drv->K = schedule->per_head_budget ? keep_count_per_head(D, schedule->sparsity) * D.H
+                                       : keep_count(D, schedule->sparsity);
     drv->have_mask = false;
     *out = drv;
     return STEPDLLM_OK;
@@ -221,8 +269,8 @@ int stepdllm_step(stepdllm_driver *drv, int32_t step, const uint16_t *q, const u
     stepdllm_dims dims = {drv->D.H, drv->D.Hkv, drv->D.L, drv->D.d, drv->D.B};
     if (kind == 0) return stepdllm_dense_attn(&dims, q, k, v, o, stream);
     if (kind == 1) {
-        int st = stepdllm_build_mask(&dims, drv->sched.sparsity, q, k, drv->ws, drv->ws_bytes,
-                                     drv->row_ptr, drv->col_idx, nullptr, stream);
+        int st = build_mask(&dims, drv->sched.sparsity, drv->sched.per_head_budget != 0, q, k,
+                            drv->ws, drv->ws_bytes, drv->row_ptr, drv->col_idx, nullptr, stream);
         if (st) return st;
         drv->have_mask = true;
     } else if (!drv->have_mask) {

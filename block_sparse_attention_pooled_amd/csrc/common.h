@@ -12,6 +12,7 @@ constexpr int kMaxHeads = 1024;      // largest number of query heads supported
 constexpr int kDies = 8;             // XCDs: workgroup b of a launch runs on die b % 8
 constexpr int kRadixBins = 2048;     // 11-bit digits (11 + 11 + 10 = 32 bits)
 constexpr int kSelectWords = 16;     // select state words in the workspace
+constexpr int kHeadSelWords = 8;     // per-head select state words (uniform budget)
 
 // Select state words.
 enum SelectWord {
@@ -34,7 +35,7 @@ struct Dims {
 
 // Workspace carve-up (byte offsets, 256-byte aligned).
 struct WsLayout {
-    int64_t qb, kb, p, hist, sel, gt, eq, tie_base, work, work_meta, total;
+    int64_t qb, kb, p, hist, sel, gt, eq, tie_base, work, work_meta, hsel, total;
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -53,6 +54,7 @@ inline WsLayout ws_layout(const Dims &D) {
     w.tie_base = take(D.rows() * 4);
     w.work = take(kDies * D.die_cap() * 4);
     w.work_meta = take(16 * 4);
+    w.hsel = take((int64_t)D.H * kHeadSelWords * 4);
     w.total = off;
     return w;
 }
@@ -74,6 +76,10 @@ hipError_t launch_scores(const Dims &D, const float *qb, const float *kb, float 
                          hipStream_t s);
 hipError_t launch_select(const Dims &D, int64_t K, const float *p, char *ws, const WsLayout &w,
                          int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
+// Uniform per-head budget: head h keeps its k_h largest scores.
+hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, char *ws,
+                                  const WsLayout &w, int32_t *row_ptr, int32_t *col_idx,
+                                  hipStream_t s);
 hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, char *ws, const WsLayout &w,
                        hipStream_t s);
 

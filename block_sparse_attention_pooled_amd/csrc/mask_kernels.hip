@@ -256,15 +256,18 @@ __global__ __launch_bounds__(1024) void k_radix_find(const uint32_t *__restrict_
 }
 
 // --------------------------------------------------------------- compaction --
-// Per row: how many scores are above the cut and how many equal it.
+// Per row: how many scores are above the cut and how many equal it.  Rows
+// come in groups of group_rows that share one select state (all rows for the
+// global budget, one head's rows for the per-head one), kHeadSelWords apart.
 __global__ __launch_bounds__(256) void k_row_count(const float *__restrict__ p, int nb,
-                                                   int64_t rows, const uint32_t *__restrict__ sel,
+                                                   int64_t rows, int64_t group_rows,
+                                                   const uint32_t *__restrict__ sel,
                                                    int32_t *__restrict__ gt,
                                                    int32_t *__restrict__ eq) {
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= rows) return;
     const int lane = threadIdx.x & 63;
-    const uint32_t cut = sel[SEL_CUT];
+    const uint32_t cut = sel[(r / group_rows) * kHeadSelWords + SEL_CUT];
     int cg = 0, ce = 0;
     for (int j = lane; j < nb; j += 64) {
         uint32_t key = order_key(p[r * nb + j]);
@@ -314,9 +317,10 @@ __global__ __launch_bounds__(1024) void k_row_scan(const int32_t *__restrict__ g
     if (threadIdx.x == 0) row_ptr[rows] = (int32_t)kept_total;
 }
 
-// Per row (one wave): write the kept key blocks in ascending order.
+// Per row (one wave): write the kept key blocks in ascending order.  tie_base
+// counts the cut ties before the row within its group; K bounds col_idx.
 __global__ __launch_bounds__(256) void k_row_scatter(const float *__restrict__ p, int nb,
-                                                     int64_t rows,
+                                                     int64_t rows, int64_t group_rows, int64_t K,
                                                      const uint32_t *__restrict__ sel,
                                                      const int32_t *__restrict__ tie_base,
                                                      const int32_t *__restrict__ row_ptr,
@@ -324,9 +328,9 @@ __global__ __launch_bounds__(256) void k_row_scatter(const float *__restrict__ p
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= rows) return;
     const int lane = threadIdx.x & 63;
-    const uint32_t cut = sel[SEL_CUT];
-    const int64_t ties = sel[SEL_TIES];
-    const int64_t K = sel[SEL_K];
+    const uint32_t *gs = sel + (r / group_rows) * kHeadSelWords;
+    const uint32_t cut = gs[SEL_CUT];
+    const int64_t ties = gs[SEL_TIES];
     int64_t tie = tie_base[r];
     int64_t out = row_ptr[r];
     const uint64_t lt = lanemask_lt();
@@ -344,6 +348,107 @@ __global__ __launch_bounds__(256) void k_row_scatter(const float *__restrict__ p
         out += __popcll(km);
         tie += __popcll(eqm);
     }
+}
+
+// ------------------------------------------------- uniform per-head budget --
+// One workgroup per head: the k_h-th largest order key of the head's nb*nb
+// scores by the same three digit passes, with the histogram in LDS.  State
+// words at hsel[h * kHeadSelWords]: cut key, count above it, ties to keep, k_h.
+__global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ p, int nb,
+                                                      int64_t k_h,
+                                                      uint32_t *__restrict__ hsel) {
+    __shared__ uint32_t hist[kRadixBins];
+    __shared__ uint32_t win[2];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int64_t per = (int64_t)nb * nb;
+    const float *ph = p + (int64_t)h * per;
+    uint32_t *out = hsel + (int64_t)h * kHeadSelWords;
+    if (k_h <= 0) {   // nothing kept: no score is above the cut, no tie is kept
+        if (tid == 0) {
+            out[SEL_CUT] = 0xFFFFFFFFu;
+            out[SEL_ABOVE] = 0;
+            out[SEL_TIES] = 0;
+            out[SEL_K] = 0;
+        }
+        return;
+    }
+    uint32_t prefix = 0;
+    int64_t remain = k_h;   // rank wanted inside the prefix bucket, counted from the top
+    for (int pass = 0; pass < 3; ++pass) {
+        int shift;
+        uint32_t hi_mask, dmask;
+        digit_of_pass(pass, shift, hi_mask, dmask);
+        for (int b = tid; b < kRadixBins; b += 1024) hist[b] = 0;
+        __syncthreads();
+        for (int64_t x = tid; x < per; x += 1024) {
+            const uint32_t key = order_key(ph[x]);
+            if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        // Bins in descending order; thread t owns ranks 2t and 2t+1.
+        const int nbins = (int)dmask + 1;
+        const int r0 = 2 * tid, r1 = r0 + 1;
+        const int b0 = nbins - 1 - r0, b1 = nbins - 1 - r1;
+        const int64_t c0 = r0 < nbins ? hist[b0] : 0;
+        const int64_t c1 = r1 < nbins ? hist[b1] : 0;
+        int64_t total;
+        const int64_t before = block_exclusive_scan_1024(c0 + c1, &total);
+        if (r0 < nbins && before < remain && remain <= before + c0) {
+            win[0] = (uint32_t)b0;
+            win[1] = (uint32_t)(remain - before);
+        } else if (r1 < nbins && before + c0 < remain && remain <= before + c0 + c1) {
+            win[0] = (uint32_t)b1;
+            win[1] = (uint32_t)(remain - before - c0);
+        }
+        __syncthreads();
+        prefix |= win[0] << shift;
+        remain = win[1];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        out[SEL_CUT] = prefix;
+        out[SEL_ABOVE] = (uint32_t)(k_h - remain);
+        out[SEL_TIES] = (uint32_t)remain;
+        out[SEL_K] = (uint32_t)k_h;
+    }
+}
+
+// One workgroup per head: cut ties before each row within the head (flat
+// order) and the row's kept count, written over gt.
+__global__ __launch_bounds__(1024) void k_head_ties(int32_t *__restrict__ gt,
+                                                    const int32_t *__restrict__ eq, int nb,
+                                                    const uint32_t *__restrict__ hsel,
+                                                    int32_t *__restrict__ tie_base) {
+    const int h = blockIdx.x, i = threadIdx.x;
+    const int64_t r = (int64_t)h * nb + i;
+    const int64_t ties = hsel[(int64_t)h * kHeadSelWords + SEL_TIES];
+    const int e = i < nb ? eq[r] : 0;
+    int64_t total;
+    const int64_t before = block_exclusive_scan_1024(e, &total);
+    if (i < nb) {
+        int64_t take = ties - before;
+        take = take < 0 ? 0 : (take > e ? e : take);
+        tie_base[r] = (int32_t)before;
+        gt[r] = (int32_t)(gt[r] + take);
+    }
+}
+
+// One block: row_ptr as the exclusive prefix of the kept counts.
+__global__ __launch_bounds__(1024) void k_kept_scan(const int32_t *__restrict__ kept,
+                                                    int64_t rows,
+                                                    int32_t *__restrict__ row_ptr) {
+    const int64_t per = (rows + 1023) / 1024;
+    const int64_t lo = min(rows, (int64_t)threadIdx.x * per);
+    const int64_t hi = min(rows, lo + per);
+    int64_t local = 0;
+    for (int64_t r = lo; r < hi; ++r) local += kept[r];
+    int64_t total;
+    int64_t out = block_exclusive_scan_1024(local, &total);
+    for (int64_t r = lo; r < hi; ++r) {
+        row_ptr[r] = (int32_t)out;
+        out += kept[r];
+    }
+    if (threadIdx.x == 0) row_ptr[rows] = (int32_t)total;
 }
 
 // --------------------------------------------------------------------- plan --
@@ -503,10 +608,30 @@ hipError_t launch_select(const Dims &D, int64_t K, const float *p, char *ws, con
         }
     }
     const unsigned row_grid = (unsigned)((rows + 3) / 4);
-    hipLaunchKernelGGL(k_row_count, dim3(row_grid), dim3(256), 0, s, p, D.nb, rows, sel, gt, eq);
+    hipLaunchKernelGGL(k_row_count, dim3(row_grid), dim3(256), 0, s, p, D.nb, rows, rows, sel, gt,
+                       eq);
     hipLaunchKernelGGL(k_row_scan, dim3(1), dim3(1024), 0, s, gt, eq, rows, sel, tie_base, row_ptr);
-    hipLaunchKernelGGL(k_row_scatter, dim3(row_grid), dim3(256), 0, s, p, D.nb, rows, sel, tie_base,
-                       row_ptr, col_idx);
+    hipLaunchKernelGGL(k_row_scatter, dim3(row_grid), dim3(256), 0, s, p, D.nb, rows, rows, K, sel,
+                       tie_base, row_ptr, col_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, char *ws,
+                                  const WsLayout &w, int32_t *row_ptr, int32_t *col_idx,
+                                  hipStream_t s) {
+    uint32_t *hsel = reinterpret_cast<uint32_t *>(ws + w.hsel);
+    int32_t *gt = reinterpret_cast<int32_t *>(ws + w.gt);
+    int32_t *eq = reinterpret_cast<int32_t *>(ws + w.eq);
+    int32_t *tie_base = reinterpret_cast<int32_t *>(ws + w.tie_base);
+    const int64_t rows = D.rows();
+    const unsigned row_grid = (unsigned)((rows + 3) / 4);
+    hipLaunchKernelGGL(k_head_select, dim3(D.H), dim3(1024), 0, s, p, D.nb, k_h, hsel);
+    hipLaunchKernelGGL(k_row_count, dim3(row_grid), dim3(256), 0, s, p, D.nb, rows,
+                       (int64_t)D.nb, hsel, gt, eq);
+    hipLaunchKernelGGL(k_head_ties, dim3(D.H), dim3(1024), 0, s, gt, eq, D.nb, hsel, tie_base);
+    hipLaunchKernelGGL(k_kept_scan, dim3(1), dim3(1024), 0, s, gt, rows, row_ptr);
+    hipLaunchKernelGGL(k_row_scatter, dim3(row_grid), dim3(256), 0, s, p, D.nb, rows,
+                       (int64_t)D.nb, k_h * D.H, hsel, tie_base, row_ptr, col_idx);
     return hipGetLastError();
 }
 

@@ -76,6 +76,9 @@ typedef struct {
     int32_t dense_steps;
     int32_t refresh_every;
     double sparsity;    /* s in [0, 1): fraction of the H*nb*nb blocks dropped */
+    int32_t per_head_budget;  /* 0: head-adaptive global budget (Step-dLLM);
+                                 1: the uniform per-head budget it is compared
+                                 with (see stepdllm_build_mask_per_head) */
 } stepdllm_schedule;
 
 /* Byte offsets of the intermediates inside a workspace (read-only views for
@@ -89,6 +92,9 @@ typedef struct {
     int64_t work;       /* int32 [8 * cap]: attention work order, cap =
                            ceil(H/8) * nb positions per die; -1 = padding        */
     int64_t work_meta;  /* int32 [16]: [0] cap, [1] number of non-empty rows      */
+    int64_t head_select;/* uint32 [H, 8]: per-head select state under the uniform
+                           budget: [h*8 + 0] cut key, [+1] count above the cut,
+                           [+2] ties kept at the cut, [+3] k_h                    */
     int64_t total;      /* == stepdllm_workspace_bytes()                          */
 } stepdllm_ws_layout;
 
@@ -125,6 +131,26 @@ int stepdllm_build_mask(const stepdllm_dims *dims, double sparsity,
 int stepdllm_select_mask(const stepdllm_dims *dims, double sparsity,
                          const float *scores, void *ws, size_t ws_bytes,
                          int32_t *row_ptr, int32_t *col_idx, void *stream);
+
+/* The uniform per-head budget, the baseline that the Step-dLLM abstract sets
+ * its head-adaptive budget against: every head keeps the same number
+ * k_h = ceil((1 - s) * nb^2) of its own nb^2 pooled scores (a guard of
+ * 1e-9 * nb^2 is subtracted first), largest first, ties by lowest index.
+ * Host only.  Returns H * k_h (the length of col_idx), or a negative status. */
+int64_t stepdllm_keep_count_per_head(const stepdllm_dims *dims, double sparsity);
+
+/* stepdllm_build_mask with the uniform per-head budget: same arguments,
+ * outputs and work order; col_idx holds H * k_h entries. */
+int stepdllm_build_mask_per_head(const stepdllm_dims *dims, double sparsity,
+                                 const uint16_t *q, const uint16_t *k,
+                                 void *ws, size_t ws_bytes,
+                                 int32_t *row_ptr, int32_t *col_idx,
+                                 float *scores_out, void *stream);
+
+/* stepdllm_select_mask with the uniform per-head budget. */
+int stepdllm_select_mask_per_head(const stepdllm_dims *dims, double sparsity,
+                                  const float *scores, void *ws, size_t ws_bytes,
+                                  int32_t *row_ptr, int32_t *col_idx, void *stream);
 
 /* Work order for a caller-built mask (row_ptr as above).  The GPU's 8 dies
  * (XCDs) each have their own L2 and take workgroups round robin, so all rows

@@ -83,14 +83,14 @@ def check_outputs_np(g, o_ref, token_sel=None):
 class GpuMask:
     """Run the library's anchor-step mask build and fetch every output."""
 
-    def __init__(self, q, k, blk, sparsity, scores_copy=True):
+    def __init__(self, q, k, blk, sparsity, scores_copy=True, per_head=False):
         self.dims = B.dims_of(q, k, blk)
-        self.buf = B.MaskBuffers(self.dims, sparsity, device=q.device)
+        self.buf = B.MaskBuffers(self.dims, sparsity, device=q.device, per_head=per_head)
         H, nb = q.shape[0], q.shape[1] // blk
         self.scores_out = (torch.empty(H * nb * nb, dtype=torch.float32, device=q.device)
                            if scores_copy else None)
         B.build_mask(self.dims, sparsity, q, k, self.buf.ws, self.buf.row_ptr,
-                     self.buf.col_idx, self.scores_out)
+                     self.buf.col_idx, self.scores_out, per_head=per_head)
         torch.cuda.synchronize()
         self.K = self.buf.K
         self.H, self.nb = H, nb

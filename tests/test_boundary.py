@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = B.load()
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(B.EXPORTS) == names
@@ -41,6 +41,16 @@ def test_keep_count_matches_exact_rationals(name):
     for s in w.sparsities:
         want = math.ceil((1 - Fraction(str(s))) * w.H * w.nb * w.nb)
         assert B.keep_count(dims(w.H, w.Hkv, w.L, w.d, w.B), s) == want
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_per_head_keep_count_matches_exact_rationals(name, olib):
+    import oracle as O
+    w = WORKLOADS[name]
+    for s in w.sparsities:
+        k_h = math.ceil((1 - Fraction(str(s))) * w.nb * w.nb)
+        assert O.keep_count(w.nb * w.nb, s, olib) == k_h
+        assert B.keep_count(dims(w.H, w.Hkv, w.L, w.d, w.B), s, per_head=True) == w.H * k_h
 
 
 def test_keep_count_edges():
@@ -74,11 +84,13 @@ def test_workspace_layout():
     for w in WORKLOADS.values():
         d = dims(w.H, w.Hkv, w.L, w.d, w.B)
         lay = B.workspace_layout(d)
-        offs = [lay.pooled_q, lay.pooled_k, lay.scores, lay.select, lay.work, lay.work_meta]
+        offs = [lay.pooled_q, lay.pooled_k, lay.scores, lay.select, lay.work, lay.work_meta,
+                lay.head_select]
         assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
         assert lay.total == B.workspace_bytes(d)
         assert lay.scores - lay.pooled_k >= w.Hkv * w.nb * w.d * 4
         assert lay.select - lay.scores >= w.H * w.nb * w.nb * 4
+        assert lay.total - lay.head_select >= w.H * 8 * 4
 
 
 def test_entry_points_reject_bad_arguments_before_launch():
@@ -92,6 +104,9 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.stepdllm_dense_attn(r(d), FAKE, FAKE, FAKE, None, None) == B.EINVAL
     assert lib.stepdllm_select_mask(r(d), 0.5, None, FAKE, ws_need, FAKE, FAKE, None) == B.EINVAL
     assert lib.stepdllm_plan(r(d), None, FAKE, ws_need, None) == B.EINVAL
+    assert lib.stepdllm_build_mask_per_head(r(d), 0.5, None, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL
+    assert lib.stepdllm_select_mask_per_head(r(d), 0.5, FAKE, FAKE, ws_need - 1, FAKE, FAKE, None) == B.EWORKSPACE
+    assert lib.stepdllm_keep_count_per_head(r(d), 1.0) == B.EINVAL
     # sparsity out of range
     for s in (-0.5, 1.0, float("nan")):
         assert lib.stepdllm_build_mask(r(d), s, FAKE, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL
@@ -107,10 +122,10 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.stepdllm_dense_attn(r(bad), FAKE, FAKE, FAKE, FAKE, None) == B.EUNSUPPORTED
 
 
-def _driver(d, dense, every, s, ws_bytes=None):
+def _driver(d, dense, every, s, ws_bytes=None, per_head=0):
     lib = B.load()
     h = ctypes.c_void_p()
-    sched = B.Schedule(dense, every, s)
+    sched = B.Schedule(dense, every, s, per_head)
     st = lib.stepdllm_driver_create(ctypes.byref(h), ctypes.byref(d), ctypes.byref(sched), FAKE,
                                     B.workspace_bytes(d) if ws_bytes is None else ws_bytes,
                                     FAKE, FAKE)
@@ -148,6 +163,10 @@ def test_driver_rejects_reuse_before_anchor_and_bad_schedules():
     assert _driver(d, 0, -4, 0.5)[0] == B.EINVAL
     assert _driver(d, 0, 4, 1.0)[0] == B.EINVAL
     assert _driver(d, 0, 4, 0.5, ws_bytes=16)[0] == B.EWORKSPACE
+    assert _driver(d, 0, 4, 0.5, per_head=2)[0] == B.EINVAL
+    st, h = _driver(d, 0, 4, 0.5, per_head=1)
+    assert st == B.OK
+    lib.stepdllm_driver_destroy(h)
 
 
 def test_status_strings():
