@@ -389,6 +389,65 @@ void oracle_dense_attn(const float *q, const float *k, const float *v, int H,
     free(z);
 }
 
+/* ------------------------------------------------------------ mask quality --- */
+/* True block attention mass, fp64: A[h,i,j] is the mean over the B query
+ * tokens t of block i of the full bidirectional softmax probability that t
+ * puts on the B key tokens of block j (head h, key head g(h)).  This is the
+ * block-level map of the exact attention that a pooled mask approximates
+ * (the post-downsampling comparison of the BA-Att abstract).  Each row of A
+ * sums to 1.  rows: optional list of rows r = h*nb + i to compute (others are
+ * left untouched); A is [H, nb, nb]. */
+void oracle_block_mass(const float *q, const float *k, int H, int Hkv, int L,
+                       int d, int B, const int32_t *rows, int n_rows, double *A)
+{
+    int nb = L / B, G = H / Hkv;
+    int total = rows ? n_rows : H * nb;
+    double scale = 1.0 / sqrt((double)d);
+    double *z = (double *)malloc(sizeof(double) * (size_t)L);
+    for (int x = 0; x < total; ++x) {
+        int r = rows ? rows[x] : x;
+        int h = r / nb, i = r % nb, g = h / G;
+        const float *kh = k + (int64_t)g * L * d;
+        double *arow = A + (int64_t)r * nb;
+        for (int j = 0; j < nb; ++j)
+            arow[j] = 0.0;
+        for (int t = i * B; t < (i + 1) * B; ++t) {
+            const float *qt = q + ((int64_t)h * L + t) * d;
+            double m = -INFINITY;
+            for (int u = 0; u < L; ++u) {
+                const float *ku = kh + (int64_t)u * d;
+                double dot = 0.0;
+                for (int c = 0; c < d; ++c)
+                    dot += (double)qt[c] * (double)ku[c];
+                z[u] = dot * scale;
+                if (z[u] > m)
+                    m = z[u];
+            }
+            double l = 0.0;
+            for (int u = 0; u < L; ++u) {
+                z[u] = exp(z[u] - m);
+                l += z[u];
+            }
+            for (int u = 0; u < L; ++u)
+                arow[u / B] += z[u] / l / B;
+        }
+    }
+    free(z);
+}
+
+/* Recall of a mask: per row, the block mass A[h,i,j] summed over the row's
+ * kept blocks j (1 when the kept blocks hold all of the row's attention). */
+void oracle_mask_recall(const double *A, int rows, int nb, const int32_t *row_ptr,
+                        const int32_t *col_idx, double *recall)
+{
+    for (int r = 0; r < rows; ++r) {
+        double acc = 0.0;
+        for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e)
+            acc += A[(int64_t)r * nb + col_idx[e]];
+        recall[r] = acc;
+    }
+}
+
 /* ----------------------------------------------------------------- driver --- */
 /* What a denoising step runs ([SD] anchors + reuse; [SP] dense warm-up then
  * one mask reused): 0 = dense attention, 1 = anchor (rebuild the mask from

@@ -47,6 +47,8 @@ def _bind(lib):
         "oracle_sparse_attn": (None, [f32p, f32p, f32p, ci, ci, ci, ci, ci, i32p, i32p, vp, ci, f64p]),
         "oracle_dense_attn": (None, [f32p, f32p, f32p, ci, ci, ci, ci, ci, vp, ci, f64p]),
         "oracle_step_kind": (ci, [ci, ci, ci]),
+        "oracle_block_mass": (None, [f32p, f32p, ci, ci, ci, ci, ci, vp, ci, f64p]),
+        "oracle_mask_recall": (None, [f64p, ci, ci, i32p, i32p, f64p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -206,6 +208,34 @@ def step_kind(step, dense_steps, refresh_every, lib=None):
     return int(lib.oracle_step_kind(int(step), int(dense_steps), int(refresh_every)))
 
 
+def block_mass(q, k, B, rows=None, lib=None, out=None):
+    """True block attention mass A [H, nb, nb] (fp64): mean over each query
+    block's tokens of the full softmax probability on each key block.  rows:
+    optional row ids h*nb + i to compute (others stay as in `out`, else 0)."""
+    lib = lib or load()
+    q, k = _f32(q), _f32(k)
+    H, L, d = q.shape
+    nb = L // B
+    A = np.zeros((H, nb, nb), np.float64) if out is None else out
+    rp, nr, keep = _rows_arg(rows)
+    lib.oracle_block_mass(q, k, H, k.shape[0], L, d, B, rp, nr, A)
+    return A
+
+
+def mask_recall(A, row_ptr, col_idx, lib=None):
+    """Per-row recall [H*nb] (fp64): the block mass on each row's kept blocks."""
+    lib = lib or load()
+    A = np.ascontiguousarray(A, dtype=np.float64)
+    H, nb, _ = A.shape
+    rec = np.empty(H * nb, np.float64)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    if ci.size == 0:
+        ci = np.zeros(1, np.int32)
+    lib.oracle_mask_recall(A, H * nb, nb, np.ascontiguousarray(row_ptr, dtype=np.int32), ci, rec)
+    return rec
+
+
 __all__ = ["build", "load", "pool", "scores", "keep_count", "select", "select_per_head",
            "cut_value", "csr",
-           "build_mask", "plan", "sparse_attn", "dense_attn", "step_kind"]
+           "build_mask", "plan", "sparse_attn", "dense_attn", "step_kind", "block_mass",
+           "mask_recall"]

@@ -375,6 +375,52 @@ def pin_worked_w1_per_head(lib):
     assert np.all(o[1, 2 * B:] == 0)
 
 
+def pin_block_mass(lib):
+    """A[h,i,j]: whole-matrix fp64 softmax (numpy matmul, a different
+    formulation) summed over blocks; rows sum to 1; Q = 0 gives 1/nb; the W1
+    concentrated head in closed form; a row subset equals the full map."""
+    rng = np.random.default_rng(RNG_SEEDS[1] + 21)
+    H, Hkv, L, d, B = 4, 2, 256, 64, 64
+    nb = L // B
+    q = _rand((H, L, d), rng) * 2.0
+    k = _rand((Hkv, L, d), rng)
+    A = O.block_mass(q, k, B, lib=lib)
+    want = np.zeros_like(A)
+    for h in range(H):
+        S = q[h].astype(np.float64) @ k[h // (H // Hkv)].astype(np.float64).T / math.sqrt(d)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        want[h] = P.reshape(nb, B, nb, B).sum(axis=(1, 3)) / B
+    assert np.max(np.abs(A - want)) < 1e-12
+    assert np.max(np.abs(A.sum(axis=2) - 1.0)) < 1e-12
+    rows = [1, 6, 13]
+    part = O.block_mass(q, k, B, rows=rows, lib=lib)
+    for r in range(H * nb):
+        got = part.reshape(H * nb, nb)[r]
+        assert np.array_equal(got, A.reshape(H * nb, nb)[r]) if r in rows else not got.any()
+    assert np.max(np.abs(O.block_mass(np.zeros_like(q), k, B, lib=lib) - 1.0 / nb)) < 1e-15
+    qw, kw, _, _ = worked_example_w1()
+    Aw = O.block_mass(qw, kw, 64, lib=lib)
+    e = math.exp(-50)
+    for i in range(4):
+        for j in range(4):
+            w = 1 / (1 + 3 * e) if i == j else e / (1 + 3 * e)
+            assert abs(Aw[0, i, j] / w - 1) < 1e-12, (i, j)
+
+
+def pin_mask_recall(lib):
+    rng = np.random.default_rng(RNG_SEEDS[1] + 22)
+    A = rng.random((3, 5, 5))
+    A /= A.sum(axis=2, keepdims=True)
+    keep = (rng.random((3, 5, 5)) < 0.4).astype(np.uint8)
+    keep[0, 1, :] = 0        # an empty row recalls nothing
+    keep[2, 3, :] = 1        # a full row recalls everything
+    rp, ci = O.csr(keep, lib)
+    rec = O.mask_recall(A, rp, ci, lib)
+    assert np.allclose(rec, (A * keep).sum(axis=2).reshape(-1), rtol=0, atol=1e-15)
+    assert rec[1] == 0.0 and abs(rec[2 * 5 + 3] - 1.0) < 1e-15
+
+
 def pin_worked_w2(lib):
     """Q = 0 for every head: every score is 1/nb and the mask is the first K
     flat indices, whatever the sparsity."""
@@ -441,4 +487,4 @@ def pin_step_kind(lib):
 ALL_PINS = [pin_keep_count, pin_pool, pin_scores, pin_select, pin_select_per_head, pin_csr,
             pin_plan, pin_worked_w1_per_head,
             pin_attention_brute, pin_attention_closed_forms, pin_worked_w1, pin_worked_w2,
-            pin_build_mask_brute, pin_step_kind]
+            pin_build_mask_brute, pin_step_kind, pin_block_mass, pin_mask_recall]

@@ -52,6 +52,12 @@ MUTANTS = [
      "int h = r / nb, i = r % nb, g = h % Hkv;", 1),
     ("attn_wrong_query_block", "for (int t = i * B; t < (i + 1) * B; ++t)\n            attend_token(q + ((int64_t)h * L + t) * d, kh, vh, d, toks, ntok",
      "for (int t = i * B; t < (i + 1) * B; ++t)\n            attend_token(q + ((int64_t)h * L + (t + B) % L) * d, kh, vh, d, toks, ntok", 0),
+    ("mass_not_averaged", "arow[u / B] += z[u] / l / B;", "arow[u / B] += z[u] / l;", 0),
+    ("mass_key_block_modulo", "arow[u / B] += z[u] / l / B;", "arow[u % nb] += z[u] / l / B;", 0),
+    ("mass_gqa_modulo", "int h = r / nb, i = r % nb, g = h / G;\n        const float *kh = k + (int64_t)g * L * d;\n        double *arow",
+     "int h = r / nb, i = r % nb, g = h % Hkv;\n        const float *kh = k + (int64_t)g * L * d;\n        double *arow", 0),
+    ("recall_skips_last", "for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e)",
+     "for (int32_t e = row_ptr[r]; e + 1 < row_ptr[r + 1]; ++e)", 0),
     ("driver_period_from_zero", "since % refresh_every == 0", "step % refresh_every == 0", 0),
 ]
 
