@@ -45,6 +45,10 @@ def parse_args():
     p.add_argument("--dense-iters", type=int, default=5)
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--mask-quality", action="store_true",
+                   help="instead of the timing run: recall of the mask in use at every step "
+                        "against the true block attention mass of that step (anchors and "
+                        "staleness across each refresh interval)")
     p.add_argument("--per-head-budget", action="store_true",
                    help="uniform per-head budget (the baseline the head-adaptive one is "
                         "compared with) instead of the global budget")
@@ -116,6 +120,87 @@ def cpu_baseline(inputs0, w, sparsity, flops_per_step, budget_s, per_head=False)
     }
 
 
+def mask_quality(args, w, sparsity, dev, T):
+    """Recall of the mask in use at each denoising step: the share of the true
+    block attention mass (full softmax map of that step's Q/K) that the kept
+    blocks hold, averaged over all rows (an empty row recalls 0)."""
+    import torch
+    from block_sparse_attention_pooled_amd import binding as B
+    from block_sparse_attention_pooled_amd.inputs import Trajectory
+
+    dims = B.make_dims(w.H, w.Hkv, w.L, w.d, w.B)
+    drv = B.Driver(dims, w.dense_steps, w.refresh_every, sparsity, device=dev,
+                   per_head_budget=args.per_head_budget)
+    o = torch.empty(w.H, w.L, w.d, dtype=torch.bfloat16, device=dev)
+    mass = torch.empty(w.H * w.nb * w.nb, dtype=torch.float32, device=dev)
+    rec = torch.empty(w.H * w.nb, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    traj = Trajectory(w, dev)
+    # The best mask of the same budget: top-K of the true mass map itself.
+    best_rp = torch.empty(w.H * w.nb + 1, dtype=torch.int32, device=dev)
+    best_ci = torch.empty(max(drv.K, 1), dtype=torch.int32, device=dev)
+    best_ws = torch.empty(B.workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    best_at_anchor = []
+    per_step, kinds, mass_ms = [], [], []
+    since_anchor = []
+    last_anchor = None
+    for t in range(T):
+        q, k, v = traj.next()
+        kind = drv.step_kind(t)
+        drv.step(t, q, k, v, o, stream)
+        if kind == 0:
+            continue
+        if kind == 1:
+            last_anchor = t
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        B.block_mass(dims, q, k, mass, stream)
+        b.record(stream)
+        B.mask_recall(dims, mass, drv.row_ptr, drv.col_idx, rec, nnz=drv.K, stream=stream)
+        torch.cuda.synchronize()
+        mass_ms.append(a.elapsed_time(b))
+        per_step.append(float(rec.mean()))
+        if kind == 1:
+            B.select_mask(dims, sparsity, mass, best_ws, best_rp, best_ci, stream=stream,
+                          per_head=args.per_head_budget)
+            B.mask_recall(dims, mass, best_rp, best_ci, rec, nnz=drv.K, stream=stream)
+            torch.cuda.synchronize()
+            best_at_anchor.append(float(rec.mean()))
+        kinds.append(kind)
+        since_anchor.append(t - last_anchor)
+    R = w.refresh_every if w.refresh_every > 0 else max(since_anchor) + 1
+    by_offset = []
+    for off in range(R):
+        xs = [r for r, s in zip(per_step, since_anchor) if s == off]
+        by_offset.append(round(sum(xs) / len(xs), 5) if xs else None)
+    at_anchor = [r for r, kd in zip(per_step, kinds) if kd == 1]
+    last_in = [r for r, s in zip(per_step, since_anchor) if s == R - 1]
+    mass_flops = 4.0 * w.H * w.L * w.L * w.d          # two score passes
+    mms = sorted(mass_ms)[len(mass_ms) // 2]
+    result = {
+        "metric": "mask recall: share of the true block attention mass on the kept blocks",
+        "value": round(sum(per_step) / len(per_step), 5),
+        "unit": "fraction",
+        "higher_is_better": True,
+        "n_gpus": 1,
+        "steps": len(per_step),
+        "data": "synthetic",
+        "config": {"workload": w.name, "H": w.H, "L": w.L, "d": w.d, "block": w.B,
+                   "sparsity": sparsity, "kept_blocks": drv.K,
+                   "budget": "per_head" if args.per_head_budget else "global",
+                   "refresh_every": w.refresh_every, "dense_steps": w.dense_steps},
+        "recall_at_anchors": round(sum(at_anchor) / len(at_anchor), 5),
+        "best_recall_same_budget_at_anchors": round(sum(best_at_anchor) / len(best_at_anchor), 5),
+        "random_mask_recall": round(drv.K / (w.H * w.nb * w.nb), 5),
+        "recall_last_step_of_interval": round(sum(last_in) / len(last_in), 5) if last_in else None,
+        "recall_by_steps_since_anchor": by_offset,
+        "recall_per_step": [round(x, 5) for x in per_step],
+        "block_mass_ms": round(mms, 4),
+        "block_mass_tflops": round(mass_flops / (mms * 1e-3) / 1e12, 2),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -132,6 +217,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     T = args.traj_steps or w.steps
+    if args.mask_quality:
+        mask_quality(args, w, sparsity, dev, T)
+        return
 
     # Inputs for every step of the trajectory, resident in HBM before timing.
     traj = Trajectory(w, dev)

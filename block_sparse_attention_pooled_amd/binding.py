@@ -66,6 +66,8 @@ def load():
         "stepdllm_plan": (i32, [D, _vp, _vp, sz, _vp]),
         "stepdllm_sparse_attn": (i32, [D, _vp, _vp, _vp, _vp, _vp, i64, _vp, sz, _vp, _vp]),
         "stepdllm_dense_attn": (i32, [D, _vp, _vp, _vp, _vp, _vp]),
+        "stepdllm_block_mass": (i32, [D, _vp, _vp, _vp, _vp]),
+        "stepdllm_mask_recall": (i32, [D, _vp, _vp, _vp, i64, _vp, _vp]),
         "stepdllm_driver_create": (i32, [ctypes.POINTER(_vp), D, ctypes.POINTER(Schedule), _vp,
                                          sz, _vp, _vp]),
         "stepdllm_driver_step_kind": (i32, [_vp, ctypes.c_int32]),
@@ -84,7 +86,8 @@ def load():
 EXPORTS = ["stepdllm_keep_count", "stepdllm_workspace_bytes", "stepdllm_workspace_layout",
            "stepdllm_build_mask", "stepdllm_select_mask", "stepdllm_keep_count_per_head",
            "stepdllm_build_mask_per_head", "stepdllm_select_mask_per_head", "stepdllm_plan",
-           "stepdllm_sparse_attn", "stepdllm_dense_attn", "stepdllm_driver_create",
+           "stepdllm_sparse_attn", "stepdllm_dense_attn", "stepdllm_block_mass",
+           "stepdllm_mask_recall", "stepdllm_driver_create",
            "stepdllm_driver_step_kind", "stepdllm_step", "stepdllm_driver_destroy",
            "stepdllm_status_string"]
 
@@ -189,6 +192,23 @@ def dense_attn(dims, q, k, v, o, stream=None):
     _check(load().stepdllm_dense_attn(
         ctypes.byref(dims), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
         _ptr(o, bf, "o"), _stream(stream)), "stepdllm_dense_attn")
+
+
+def block_mass(dims, q, k, mass, stream=None):
+    """True block attention mass, fp32 [H, nb, nb], into `mass`."""
+    bf = torch.bfloat16
+    _check(load().stepdllm_block_mass(ctypes.byref(dims), _ptr(q, bf, "q"), _ptr(k, bf, "k"),
+                                      _ptr(mass, torch.float32, "mass"), _stream(stream)),
+           "stepdllm_block_mass")
+
+
+def mask_recall(dims, mass, row_ptr, col_idx, recall, nnz=None, stream=None):
+    """Per-row recall [H*nb] of the mask (row_ptr, col_idx) against `mass`."""
+    nnz = col_idx.numel() if nnz is None else int(nnz)
+    _check(load().stepdllm_mask_recall(
+        ctypes.byref(dims), _ptr(mass, torch.float32, "mass"),
+        _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"), nnz,
+        _ptr(recall, torch.float32, "recall"), _stream(stream)), "stepdllm_mask_recall")
 
 
 class Driver:

@@ -223,6 +223,26 @@ int stepdllm_dense_attn(const stepdllm_dims *dims, const uint16_t *q, const uint
     return hip_status(sd::launch_dense_attn(D, q, k, v, o, static_cast<hipStream_t>(stream)));
 }
 
+int stepdllm_block_mass(const stepdllm_dims *dims, const uint16_t *q, const uint16_t *k,
+                        float *mass, void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!q || !k || !mass) return STEPDLLM_EINVAL;
+    return hip_status(sd::launch_block_mass(D, q, k, mass, static_cast<hipStream_t>(stream)));
+}
+
+int stepdllm_mask_recall(const stepdllm_dims *dims, const float *mass, const int32_t *row_ptr,
+                         const int32_t *col_idx, int64_t nnz, float *recall, void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!mass || !row_ptr || !col_idx || !recall) return STEPDLLM_EINVAL;
+    if (nnz < 0 || nnz > D.n_scores()) return STEPDLLM_EINVAL;
+    return hip_status(sd::launch_mask_recall(D, mass, row_ptr, col_idx, nnz, recall,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int stepdllm_driver_create(stepdllm_driver **out, const stepdllm_dims *dims,
                            const stepdllm_schedule *schedule, void *ws, size_t ws_bytes,
                            int32_t *row_ptr, int32_t *col_idx) {

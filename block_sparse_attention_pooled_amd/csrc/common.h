@@ -83,6 +83,13 @@ hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, ch
 hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, char *ws, const WsLayout &w,
                        hipStream_t s);
 
+// Mask quality launches (quality_kernels.hip).
+hipError_t launch_block_mass(const Dims &D, const uint16_t *q, const uint16_t *k, float *mass,
+                             hipStream_t s);
+hipError_t launch_mask_recall(const Dims &D, const float *mass, const int32_t *row_ptr,
+                              const int32_t *col_idx, int64_t nnz, float *recall,
+                              hipStream_t s);
+
 // Attention launches (attn_kernels.hip).
 hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                               const uint16_t *v, const int32_t *row_ptr, const int32_t *col_idx,

@@ -16,6 +16,13 @@ and evaluation data are not available:
   per element ("attention patterns are only locally consistent across steps",
   Step-dLLM abstract), with an abrupt full redraw of Q and K at chosen steps
   ("shift abruptly at certain transitions").
+* Block structure (the structured 8K variant only, for the mask-quality
+  measurement): each key head g draws a unit direction e[g, j] per key block j;
+  every key token of block j gets + a * e[g, j], and every query token of block
+  i of head h gets + a * (sum of e[g(h), j] over its target blocks j: its own
+  block and 4 random ones), with a = structure * (4 * sqrt(d))^(1/2), so a
+  target pair scores about +4 * structure^2 before the head temperature.  The
+  targets and directions are redrawn with Q and K.
 """
 from dataclasses import dataclass, field
 import math
@@ -40,6 +47,7 @@ class Workload:
     drift: float           # per-step drift std (0 = static)
     resample_steps: tuple = field(default=())
     seed: int = 0
+    structure: float = 0.0  # block-affinity strength (0 = i.i.d. inputs)
 
     @property
     def nb(self):
@@ -61,6 +69,11 @@ WORKLOADS = {
                             sparsities=(0.9,), steps=256, dense_steps=0, refresh_every=32,
                             temperatures=True, sinks=False, drift=0.02,
                             resample_steps=(64, 160), seed=1003),
+    "stepdllm_8k_structured": Workload("stepdllm_8k_structured", H=32, Hkv=32, L=8192, d=128,
+                                       B=64, sparsities=(0.9,), steps=256, dense_steps=0,
+                                       refresh_every=32, temperatures=True, sinks=False,
+                                       drift=0.02, resample_steps=(80, 176), seed=1006,
+                                       structure=1.0),
     "dream_gqa_8k": Workload("dream_gqa_8k", H=28, Hkv=4, L=8192, d=128, B=64,
                              sparsities=(0.7, 0.8, 0.9, 0.95), steps=64, dense_steps=0,
                              refresh_every=16, temperatures=True, sinks=False, drift=0.02,
@@ -92,28 +105,36 @@ class Trajectory:
                       else torch.ones(w.H, dtype=torch.float32)).to(self.device)
         self.gen = torch.Generator(device=self.device).manual_seed(w.seed)
         self.step = 0
-        self.q = self._draw_q()
-        self.k = self._draw_k()
+        self.q, self.k = self._draw_qk()
         self.v = self._randn(w.Hkv, w.L, w.d)
 
     def _randn(self, *shape):
         return torch.randn(*shape, generator=self.gen, device=self.device, dtype=torch.float32)
 
-    def _draw_q(self):
-        return self._randn(self.w.H, self.w.L, self.w.d) * self.temps.view(-1, 1, 1)
-
-    def _draw_k(self):
-        k = self._randn(self.w.Hkv, self.w.L, self.w.d)
-        if self.w.sinks:
+    def _draw_qk(self):
+        w = self.w
+        q = self._randn(w.H, w.L, w.d)
+        k = self._randn(w.Hkv, w.L, w.d)
+        if w.sinks:
             k[:, 0:4, :] *= 4.0
-        return k
+        if w.structure:
+            a = w.structure * math.sqrt(4.0 * math.sqrt(w.d))
+            e = self._randn(w.Hkv, w.nb, w.d)
+            e = e / e.norm(dim=-1, keepdim=True)
+            k += a * e.repeat_interleave(w.B, dim=1)
+            tgt = torch.randint(0, w.nb, (w.H, w.nb, 4), generator=self.gen, device=self.device)
+            own = torch.arange(w.nb, device=self.device).view(1, w.nb, 1).expand(w.H, w.nb, 1)
+            tgt = torch.cat([own, tgt], dim=2)                        # [H, nb, 5]
+            g = torch.arange(w.H, device=self.device) // (w.H // w.Hkv)
+            dirs = e[g.view(-1, 1, 1), tgt]                            # [H, nb, 5, d]
+            q += a * dirs.sum(dim=2).repeat_interleave(w.B, dim=1)
+        return q * self.temps.view(-1, 1, 1), k
 
     def next(self):
         """bf16 (q, k, v) for the current step, then advance the state."""
         w = self.w
         if self.step in w.resample_steps:
-            self.q = self._draw_q()
-            self.k = self._draw_k()
+            self.q, self.k = self._draw_qk()
         out = (self.q.to(torch.bfloat16), self.k.to(torch.bfloat16), self.v.to(torch.bfloat16))
         if w.drift:
             self.q += w.drift * self._randn(*self.q.shape)

@@ -185,6 +185,29 @@ int stepdllm_dense_attn(const stepdllm_dims *dims, const uint16_t *q,
                         const uint16_t *k, const uint16_t *v, uint16_t *o,
                         void *stream);
 
+/* Mask quality (a diagnostic, off the per-step path).  The BA-Att abstract
+ * compares block selection in the pooled, pre-downsampled space with the
+ * block map of the exact attention; Step-dLLM reuses one mask across a
+ * refresh interval.  stepdllm_block_mass writes the true block attention mass
+ *   mass[h,i,j] = (1/B) sum_{t in q-block i} sum_{u in k-block j}
+ *                 softmax_u(q_t . k_u / sqrt(d))       (all L keys, key head
+ *                                                       h / (H/Hkv))
+ * fp32 [H, nb, nb] (caller-owned device memory; each row sums to 1 up to fp32
+ * rounding).  q [H,L,d], k [Hkv,L,d] bf16.  Scores on bf16 MFMA with fp32
+ * accumulation; exact per-query max and normaliser (two passes over the keys);
+ * deterministic. */
+int stepdllm_block_mass(const stepdllm_dims *dims, const uint16_t *q,
+                        const uint16_t *k, float *mass, void *stream);
+
+/* Recall of a block mask against a block mass map: recall[r] (fp32, [H*nb])
+ * is the sum of mass[r, j] over the kept blocks j of row r (1 when the kept
+ * blocks hold all of the row's attention, 0 for an empty row).  row_ptr /
+ * col_idx as for stepdllm_sparse_attn; list positions at or past nnz are not
+ * read and block ids outside [0, nb) add nothing. */
+int stepdllm_mask_recall(const stepdllm_dims *dims, const float *mass,
+                         const int32_t *row_ptr, const int32_t *col_idx,
+                         int64_t nnz, float *recall, void *stream);
+
 /* Step driver: a small host object owned by the library; device buffers
  * (workspace, row_ptr [H*nb+1], col_idx [K]) stay owned by the caller and
  * must outlive the driver.  stepdllm_step runs what the schedule asks for at

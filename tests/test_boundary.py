@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = B.load()
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(B.EXPORTS) == names
@@ -107,6 +107,10 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.stepdllm_build_mask_per_head(r(d), 0.5, None, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL
     assert lib.stepdllm_select_mask_per_head(r(d), 0.5, FAKE, FAKE, ws_need - 1, FAKE, FAKE, None) == B.EWORKSPACE
     assert lib.stepdllm_keep_count_per_head(r(d), 1.0) == B.EINVAL
+    assert lib.stepdllm_block_mass(r(d), FAKE, None, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_block_mass(r(dims(2, 2, 256, 80, 64)), FAKE, FAKE, FAKE, None) == B.EUNSUPPORTED
+    assert lib.stepdllm_mask_recall(r(d), FAKE, FAKE, FAKE, 33, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_mask_recall(r(d), FAKE, None, FAKE, 16, FAKE, None) == B.EINVAL
     # sparsity out of range
     for s in (-0.5, 1.0, float("nan")):
         assert lib.stepdllm_build_mask(r(d), s, FAKE, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL

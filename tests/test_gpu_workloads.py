@@ -111,3 +111,12 @@ def test_dream_gqa_8k(sparsity):
 def test_long_64k_dense_then_sparse():
     w = WORKLOADS["long_64k"]
     _run(w, w.sparsities[0], 27, mask_steps={26}, out_steps={0, 26, 27}, heads=())
+
+
+@pytest.mark.timeout(900)
+def test_stepdllm_8k_structured_across_a_redraw():
+    """Block-structured inputs (concentrated attention); Q/K are redrawn at
+    step 80, inside the interval of the anchor at 64, so step 95 runs on a
+    stale mask and step 96 rebuilds it."""
+    w = WORKLOADS["stepdllm_8k_structured"]
+    _run(w, w.sparsities[0], 96, mask_steps={0, 96}, out_steps={0, 95, 96}, heads=(0, 5))
