@@ -191,10 +191,11 @@ def pin_csr(lib):
         assert np.array_equal(col_idx[row_ptr[r]:row_ptr[r + 1]], np.nonzero(flat[r])[0])
 
 
-def _plan_spec(lens, H, nb):
-    """The work-order spec written out in Python: heads by kept blocks
-    (descending, then id) to the least-loaded die with room for ceil(H/8)
-    heads; each die lists its heads in that order, rows by length desc."""
+def _die_lists(lens, H, nb):
+    """The die lists of the work-order spec written out in Python: heads by kept
+    blocks (descending, then id) to the least-loaded die with room for
+    ceil(H/8) heads; each die lists its heads in that order, rows by length
+    desc, ties by row id."""
     cap_h = -(-H // 8)
     kept = [int(sum(lens[h * nb:(h + 1) * nb])) for h in range(H)]
     dies = [[] for _ in range(8)]
@@ -203,30 +204,60 @@ def _plan_spec(lens, H, nb):
         x = min((x for x in range(8) if len(dies[x]) < cap_h), key=lambda x: (load[x], x))
         dies[x].append(h)
         load[x] += kept[h]
-    work = [-1] * (8 * cap_h * nb)
-    for x in range(8):
-        rows = [r for h in dies[x] for r in sorted(range(h * nb, (h + 1) * nb),
-                                                    key=lambda r: (-lens[r], r))]
-        work[x * cap_h * nb: x * cap_h * nb + len(rows)] = rows
-    return work
+    return [[r for h in dies[x] for r in sorted(range(h * nb, (h + 1) * nb),
+                                                 key=lambda r: (-lens[r], r))]
+            for x in range(8)]
+
+
+def _check_rounds(work, lists, lens, P, capP):
+    """Each die's positions k*P + s hold its list dealt in rounds of P: round k
+    holds exactly the list's rows k*P .. k*P+P-1, at most one per slot, and the
+    earlier (longer) a row is in its round, the lighter the slot it goes to."""
+    for x, lst in enumerate(lists):
+        seg = list(work[x * capP:(x + 1) * capP])
+        assert sorted(r for r in seg if r >= 0) == sorted(lst)
+        load = [0] * P
+        for k in range(-(-len(lst) // P)):
+            got = {s: seg[k * P + s] for s in range(P) if seg[k * P + s] >= 0}
+            want_rows = lst[k * P:(k + 1) * P]
+            assert sorted(got.values()) == sorted(want_rows)
+            slot_of = {r: s for s, r in got.items()}
+            keys = [(load[slot_of[r]], slot_of[r]) for r in want_rows]
+            assert keys == sorted(keys), (x, k)
+            for r in want_rows:
+                load[slot_of[r]] += int(lens[r]) + 1
+        assert all(r == -1 for r in seg[-(-len(lst) // P) * P:])
 
 
 def pin_plan(lib):
     # Hand-derived: H=3, nb=4, one head per die.  Kept per head: 5, 9, 5, so
     # head 1 -> die 0, head 0 -> die 1, head 2 -> die 2; dies 3..7 stay empty.
+    # With P = 4 slots each die's 4 rows form one round on fresh slots.
     lens = np.array([2, 0, 3, 0,   4, 1, 4, 0,   1, 1, 1, 2])
     row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    work, n = O.plan(row_ptr, 3, 4, lib)
+    work, n = O.plan(row_ptr, 3, 4, 4, lib)
     want = [4, 6, 5, 7,   2, 0, 1, 3,   11, 8, 9, 10] + [-1] * 20
     assert list(work) == want and n == 9
-    # Spec in Python on random shapes (several heads per die, LPT balancing).
+    # Hand-derived rounds: one head of 5 rows, lengths 4, 3, 2, 2, 1, P = 2.
+    # Round 0: rows 0, 1 to fresh slots 0, 1 (loads 5, 4).  Round 1: slot 1 is
+    # lighter, so row 2 -> slot 1 and row 3 -> slot 0 (loads 8, 7).  Round 2:
+    # row 4 -> slot 1; slot 0 idles.
+    lens = np.array([4, 3, 2, 2, 1])
+    row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    work, n = O.plan(row_ptr, 1, 5, 2, lib)
+    assert list(work[:6]) == [0, 1, 3, 2, -1, 4] and all(w == -1 for w in work[6:])
+    assert len(work) == 8 * 6 and n == 5
+    # Properties on random shapes and slot counts (several heads per die).
     rng = np.random.default_rng(RNG_SEEDS[1] + 7)
-    for H, nb in ((20, 6), (28, 9), (8, 5), (33, 3)):
+    for H, nb, P in ((20, 6, 4), (28, 9, 5), (8, 5, 16), (33, 3, 2), (17, 12, 7)):
         lens = rng.integers(0, nb + 1, size=H * nb) * (rng.random(H * nb) < 0.7)
         lens[: nb] = 0                                  # one head keeps nothing
         row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-        work, n = O.plan(row_ptr, H, nb, lib)
-        assert list(work) == _plan_spec(lens, H, nb), (H, nb)
+        work, n = O.plan(row_ptr, H, nb, P, lib)
+        cap = -(-H // 8) * nb
+        capP = -(-cap // P) * P
+        assert len(work) == 8 * capP
+        _check_rounds(work, _die_lists(lens, H, nb), lens, P, capP)
         assert n == int((lens > 0).sum())
         assert sorted(int(r) for r in work if r >= 0) == list(range(H * nb))
 
