@@ -284,7 +284,12 @@ class MaskBuffers:
         return self.view(self.layout.select, 16, torch.int32)
 
     def work_cap(self):
-        return -(-self.dims.n_q_heads // 8) * self.nb
+        """Positions per die of the last plan (capP), from the plan's meta words."""
+        return int(self.work_meta()[0].item())
+
+    def work_slots(self):
+        """Slots per die P of the last plan."""
+        return int(self.work_meta()[2].item())
 
     def work(self):
         return self.view(self.layout.work, 8 * self.work_cap(), torch.int32)

@@ -82,7 +82,8 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ row_ptr,
     const int32_t *__restrict__ col_idx, const int32_t *__restrict__ work,
-    uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx, float scale_log2) {
+    uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx, int64_t capP,
+    float scale_log2) {
     constexpr int NT = QW / 32;                 // 32-query tiles per wave
     constexpr int WQ = BLK / QW;                // query slices (= waves) per block
     constexpr int KS = D / 16;                  // k steps of the score product
@@ -114,10 +115,10 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
             row = b;
         }
     } else {
-        // Workgroup b runs on die b % kDies: take that die's list.
-        const int64_t cap = (int64_t)((H + kDies - 1) / kDies) * nb;
+        // Workgroup b runs on die b % kDies: take position b / kDies of that
+        // die's list (capP positions per die).
         const int b = blockIdx.x;
-        row = __builtin_amdgcn_readfirstlane(work[(b % kDies) * cap + b / kDies]);
+        row = __builtin_amdgcn_readfirstlane(work[(b % kDies) * capP + b / kDies]);
         if (row < 0 || row >= H * nb) return;   // padding (or a malformed order): nothing to do
     }
     const int h = row / nb, blk = row % nb, g = h / G;
@@ -448,11 +449,35 @@ hipError_t launch_attn_t(const Dims &Dm, const uint16_t *q, const uint16_t *k, c
                          const int32_t *row_ptr, const int32_t *col_idx, const int32_t *work,
                          int n_idx, uint16_t *o, hipStream_t s) {
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    const unsigned grid = (unsigned)(DENSE ? Dm.rows() : kDies * Dm.die_cap());
+    const int64_t P = DENSE ? 1 : attn_slots_per_die(Dm);
+    const int64_t capP = (Dm.die_cap() + P - 1) / P * P;
+    const unsigned grid = (unsigned)(DENSE ? Dm.rows() : kDies * capP);
     hipLaunchKernelGGL((k_attn<D, BLK, QW, DENSE>), dim3(grid), dim3(BLK / QW * 64),
                        0, s, q, k, v, row_ptr, col_idx, work, o, Dm.L, Dm.nb, Dm.G, Dm.H,
-                       n_idx, scale_log2);
+                       n_idx, capP, scale_log2);
     return hipGetLastError();
+}
+
+// Resident workgroups of the sparse kernel per CU (occupancy API) times the
+// CUs of one die, cached per device and shape class.
+template <int D, int BLK>
+int slots_per_die_t() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    static int cache[64];
+    if (cache[dev] > 0) return cache[dev];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(&k_attn<D, BLK, kQW, false>), BLK / kQW * 64,
+            0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 1;
+    }
+    int p = cus / kDies * per_cu;
+    p = p < 1 ? 1 : (p > kMaxSlots ? kMaxSlots : p);
+    cache[dev] = p;
+    return p;
 }
 
 template <bool DENSE>
@@ -469,6 +494,13 @@ hipError_t launch_attn(const Dims &D, const uint16_t *q, const uint16_t *k, cons
 }
 
 }  // namespace
+
+int attn_slots_per_die(const Dims &D) {
+    if (D.d == 128 && D.B == 64) return slots_per_die_t<128, 64>();
+    if (D.d == 128 && D.B == 128) return slots_per_die_t<128, 128>();
+    if (D.d == 64 && D.B == 64) return slots_per_die_t<64, 64>();
+    return slots_per_die_t<64, 128>();
+}
 
 hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                               const uint16_t *v, const int32_t *row_ptr, const int32_t *col_idx,

@@ -468,21 +468,27 @@ constexpr int kPlanThreads = 512;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict__ row_ptr,
-                                                       int H, int nb,
+                                                       int H, int nb, int P,
                                                        int32_t *__restrict__ work,
                                                        int32_t *__restrict__ meta) {
+    static_assert(kPlanWaves == kDies, "one wave per die deals the rounds");
     __shared__ int32_t kept[kMaxHeads];
     __shared__ int32_t order[kMaxHeads];
     __shared__ int32_t head_base[kMaxHeads];
     __shared__ int32_t next[kPlanWaves][kMaxBlocks + 1];
+    __shared__ int32_t die_count[kDies];
+    __shared__ int32_t slot_load[kDies][kMaxSlots];
+    __shared__ int32_t slot_of_rank[kDies][kMaxSlots];
+    __shared__ int32_t round_rows[kDies][kMaxSlots];
     __shared__ int32_t nonempty;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cap_h = (H + kDies - 1) / kDies;
     const int64_t cap = (int64_t)cap_h * nb;
+    const int64_t capP = (cap + P - 1) / P * P;
     if (tid == 0) nonempty = 0;
     for (int h = tid; h < H; h += kPlanThreads)
         kept[h] = row_ptr[(int64_t)(h + 1) * nb] - row_ptr[(int64_t)h * nb];
-    for (int64_t p = tid; p < kDies * cap; p += kPlanThreads) work[p] = -1;
+    for (int64_t p = tid; p < kDies * capP; p += kPlanThreads) work[p] = -1;
     __syncthreads();
     for (int h = tid; h < H; h += kPlanThreads) {
         int rank = 0;
@@ -503,10 +509,11 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict
             int best = -1;
             for (int x = 0; x < kDies; ++x)
                 if (count[x] < cap_h && (best < 0 || load[x] < load[best])) best = x;
-            head_base[h] = (int32_t)(best * cap + (int64_t)count[best] * nb);
+            head_base[h] = (int32_t)(best * capP + (int64_t)count[best] * nb);
             ++count[best];
             load[best] += kept[h];
         }
+        for (int x = 0; x < kDies; ++x) die_count[x] = count[x];
     }
     __syncthreads();
     const uint64_t lt = lanemask_lt();
@@ -554,9 +561,45 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict
     }
     atomicAdd(&nonempty, my_nonempty);
     __syncthreads();
+    // Deal each die's list in rounds of P rows (wave x, die x): the round's
+    // rows in list order go to the slots ranked by load (ascending, ties by
+    // slot); slot s's row of round k lands at k*P + s.  Dies run different
+    // numbers of rounds, so the steps of a round are ordered by LDS waits
+    // within the wave (LDS requests of a wave complete in order), not by
+    // workgroup barriers.
+    {
+        const int x = wave;
+        const int64_t m = (int64_t)die_count[x] * nb;
+        int32_t *seg = work + (int64_t)x * capP;
+        int32_t *ld = slot_load[x], *by_rank = slot_of_rank[x], *rows = round_rows[x];
+        for (int sl = lane; sl < P; sl += 64) ld[sl] = 0;
+        for (int64_t k0 = 0; k0 < m; k0 += P) {
+            const int64_t cnt = min((int64_t)P, m - k0);
+            for (int t = lane; t < P; t += 64) rows[t] = t < cnt ? seg[k0 + t] : -1;
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            for (int sl = lane; sl < P; sl += 64) {
+                const int l0 = ld[sl];
+                int rank = 0;
+                for (int s2 = 0; s2 < P; ++s2) {
+                    const int l2 = ld[s2];
+                    rank += (l2 < l0) || (l2 == l0 && s2 < sl);
+                }
+                by_rank[rank] = sl;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            for (int t = lane; t < P; t += 64) {
+                const int sl = by_rank[t];
+                const int r = rows[t];
+                seg[k0 + sl] = r;
+                if (r >= 0) ld[sl] += row_ptr[r + 1] - row_ptr[r] + 1;
+            }
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        }
+    }
     if (tid == 0) {
-        meta[0] = (int32_t)cap;
+        meta[0] = (int32_t)capP;
         meta[1] = nonempty;
+        meta[2] = P;
     }
 }
 
@@ -639,7 +682,8 @@ hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, char *ws, const Ws
                        hipStream_t s) {
     int32_t *work = reinterpret_cast<int32_t *>(ws + w.work);
     int32_t *meta = reinterpret_cast<int32_t *>(ws + w.work_meta);
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.H, D.nb, work,
+    const int P = attn_slots_per_die(D);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.H, D.nb, P, work,
                        meta);
     return hipGetLastError();
 }

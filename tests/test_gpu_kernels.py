@@ -105,10 +105,12 @@ def test_plan_matches_oracle(shape):
     q, k, v = _qkv(shape, 303)
     m = PT.GpuMask(q, k, blk, 0.8)
     rp, _ = m.csr()
-    work_ref, n_ref = O.plan(rp, H, L // blk)
-    assert np.array_equal(m.buf.work().cpu().numpy(), work_ref)
     meta = m.buf.work_meta().cpu().numpy()
-    assert int(meta[0]) == m.buf.work_cap() and int(meta[1]) == n_ref
+    P = int(meta[2])
+    assert 1 <= P <= 512
+    work_ref, n_ref = O.plan(rp, H, L // blk, P)
+    assert np.array_equal(m.buf.work().cpu().numpy(), work_ref)
+    assert int(meta[0]) * 8 == work_ref.size and int(meta[1]) == n_ref
 
 
 @pytest.mark.parametrize("H,nb", [(64, 320), (28, 129), (3, 1024), (13, 7)])
@@ -122,7 +124,7 @@ def test_plan_many_rows_and_lengths(H, nb):
     buf = B.MaskBuffers(dims, 0.5, device=DEV)
     B.plan(dims, torch.from_numpy(rp).to(DEV), buf.ws)
     torch.cuda.synchronize()
-    work_ref, n_ref = O.plan(rp, H, nb)
+    work_ref, n_ref = O.plan(rp, H, nb, buf.work_slots())
     assert np.array_equal(buf.work().cpu().numpy(), work_ref)
     assert int(buf.work_meta().cpu().numpy()[1]) == n_ref
 
