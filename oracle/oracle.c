@@ -225,14 +225,15 @@ int64_t oracle_build_mask_per_head(const float *q, const float *k, int H, int Hk
  * rows of a head share one die's L2 and each slot gets an even share:
  *  - heads are taken in order of kept blocks (descending, ties by head id) and
  *    each goes to the die with the fewest kept blocks so far among those that
- *    hold fewer than ceil(H/8) heads (ties: lowest die);
+ *    hold fewer than cap_h = min(H, ceil(H/8) + 2) heads (ties: lowest die);
+ *    the slack over ceil(H/8) lets the greedy balance skewed heads;
  *  - die x's list is its heads in that order, each head's rows by list
  *    length descending (ties by row id);
  *  - the list is dealt in rounds of P consecutive rows: the rows of a round,
  *    in list order, go to the slots in order of their load so far (ascending,
  *    ties: lowest slot), and a slot's load grows by the row's length + 1;
  *  - the row that slot s takes in round k sits at work[x*capP + k*P + s],
- *    capP = ceil(cap/P)*P, cap = ceil(H/8)*nb; positions without a row hold -1.
+ *    capP = ceil(cap/P)*P, cap = cap_h*nb; positions without a row hold -1.
  * Returns the number of rows with at least one kept block. */
 static const int32_t *g_row_ptr;
 static const int64_t *g_head_kept;
@@ -268,7 +269,9 @@ enum { ORACLE_DIES = 8 };
 
 int32_t oracle_plan(const int32_t *row_ptr, int H, int nb, int P, int32_t *work)
 {
-    int cap_heads = (H + ORACLE_DIES - 1) / ORACLE_DIES;
+    int cap_heads = (H + ORACLE_DIES - 1) / ORACLE_DIES + 2;
+    if (cap_heads > H)
+        cap_heads = H;
     int64_t cap = (int64_t)cap_heads * nb;
     int64_t capP = (cap + P - 1) / P * P;
     int64_t *kept = (int64_t *)malloc(sizeof(int64_t) * (size_t)H);

@@ -166,10 +166,10 @@ DIES = 8
 
 def plan(row_ptr, H, nb, P, lib=None):
     """-> (work [8 * capP] int32 with -1 padding, n_nonempty); capP =
-    ceil(ceil(H/8) * nb / P) * P, P slots per die."""
+    ceil(min(H, ceil(H/8) + 2) * nb / P) * P, P slots per die."""
     lib = lib or load()
     row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
-    cap = -(-H // DIES) * nb
+    cap = min(H, -(-H // DIES) + 2) * nb
     capP = -(-cap // P) * P
     work = np.empty(DIES * capP, np.int32)
     n = lib.oracle_plan(row_ptr, int(H), int(nb), int(P), work)

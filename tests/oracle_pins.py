@@ -194,9 +194,9 @@ def pin_csr(lib):
 def _die_lists(lens, H, nb):
     """The die lists of the work-order spec written out in Python: heads by kept
     blocks (descending, then id) to the least-loaded die with room for
-    ceil(H/8) heads; each die lists its heads in that order, rows by length
-    desc, ties by row id."""
-    cap_h = -(-H // 8)
+    min(H, ceil(H/8) + 2) heads; each die lists its heads in that order, rows
+    by length desc, ties by row id."""
+    cap_h = min(H, -(-H // 8) + 2)
     kept = [int(sum(lens[h * nb:(h + 1) * nb])) for h in range(H)]
     dies = [[] for _ in range(8)]
     load = [0] * 8
@@ -232,12 +232,31 @@ def _check_rounds(work, lists, lens, P, capP):
 def pin_plan(lib):
     # Hand-derived: H=3, nb=4, one head per die.  Kept per head: 5, 9, 5, so
     # head 1 -> die 0, head 0 -> die 1, head 2 -> die 2; dies 3..7 stay empty.
-    # With P = 4 slots each die's 4 rows form one round on fresh slots.
+    # A die may hold min(3, 1 + 2) = 3 heads, so 12 positions; with P = 4 slots
+    # each die's 4 rows form one round on fresh slots.
     lens = np.array([2, 0, 3, 0,   4, 1, 4, 0,   1, 1, 1, 2])
     row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     work, n = O.plan(row_ptr, 3, 4, 4, lib)
-    want = [4, 6, 5, 7,   2, 0, 1, 3,   11, 8, 9, 10] + [-1] * 20
+    pad = [-1] * 8
+    want = [4, 6, 5, 7] + pad + [2, 0, 1, 3] + pad + [11, 8, 9, 10] + pad + [-1] * 60
     assert list(work) == want and n == 9
+    # Head cap slack: 12 heads of kept 30, 1, 1, ..., 1 with 8 dies: each die
+    # may hold min(12, 2 + 2) = 4 heads.  Head 0 -> die 0 (30); heads 1..7 ->
+    # dies 1..7; heads 8..11 (1 block each) go to the lightest dies, 1..4,
+    # never to die 0.
+    lens = np.zeros(12 * 2, np.int64)
+    lens[0], lens[1] = 20, 10
+    for h in range(1, 12):
+        lens[2 * h] = 1
+    row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    work, n = O.plan(row_ptr, 12, 2, 8, lib)
+    capP = 8
+    die_rows = [sorted(int(r) for r in work[x * capP:(x + 1) * capP] if r >= 0) for x in range(8)]
+    assert die_rows[0] == [0, 1]
+    for x in range(1, 5):
+        assert die_rows[x] == sorted([2 * x, 2 * x + 1, 2 * (x + 7), 2 * (x + 7) + 1]), x
+    for x in range(5, 8):
+        assert die_rows[x] == [2 * x, 2 * x + 1], x
     # Hand-derived rounds: one head of 5 rows, lengths 4, 3, 2, 2, 1, P = 2.
     # Round 0: rows 0, 1 to fresh slots 0, 1 (loads 5, 4).  Round 1: slot 1 is
     # lighter, so row 2 -> slot 1 and row 3 -> slot 0 (loads 8, 7).  Round 2:
@@ -254,7 +273,7 @@ def pin_plan(lib):
         lens[: nb] = 0                                  # one head keeps nothing
         row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
         work, n = O.plan(row_ptr, H, nb, P, lib)
-        cap = -(-H // 8) * nb
+        cap = min(H, -(-H // 8) + 2) * nb
         capP = -(-cap // P) * P
         assert len(work) == 8 * capP
         _check_rounds(work, _die_lists(lens, H, nb), lens, P, capP)
