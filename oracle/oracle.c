@@ -221,23 +221,19 @@ int64_t oracle_build_mask_per_head(const float *q, const float *k, int H, int Hk
 
 /* ------------------------------------------------------------------- plan --- */
 /* Work order for the attention launch on a GPU made of 8 dies (XCDs) that take
- * workgroups round robin, with P resident workgroup slots per die, so that all
- * rows of a head share one die's L2 and each slot gets an even share:
+ * workgroups round robin, so that all rows of a head share one die's L2 and
+ * each die's rows start longest first:
  *  - heads are taken in order of kept blocks (descending, ties by head id) and
  *    each goes to the die with the fewest kept blocks so far among those that
  *    hold fewer than cap_h = min(H, ceil(H/8) + 2) heads (ties: lowest die);
  *    the slack over ceil(H/8) lets the greedy balance skewed heads;
  *  - die x's list is its heads in that order, each head's rows by list
  *    length descending (ties by row id);
- *  - the list is dealt in rounds of P consecutive rows: the rows of a round,
- *    in list order, go to the slots in order of their load so far (ascending,
- *    ties: lowest slot), and a slot's load grows by the row's length + 1;
- *  - the row that slot s takes in round k sits at work[x*capP + k*P + s],
- *    capP = ceil(cap/P)*P, cap = cap_h*nb; positions without a row hold -1.
+ *  - list x fills work[x*cap .. x*cap + cap), cap = cap_h*nb, and unused
+ *    positions hold -1.
  * Returns the number of rows with at least one kept block. */
 static const int32_t *g_row_ptr;
 static const int64_t *g_head_kept;
-static const int64_t *g_slot_load;
 
 static int by_len_desc_row_asc(const void *pa, const void *pb)
 {
@@ -257,29 +253,17 @@ static int by_kept_desc_head_asc(const void *pa, const void *pb)
     return (a < b) ? -1 : (a > b);
 }
 
-static int by_load_asc_slot_asc(const void *pa, const void *pb)
-{
-    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
-    if (g_slot_load[a] < g_slot_load[b]) return -1;
-    if (g_slot_load[a] > g_slot_load[b]) return 1;
-    return (a < b) ? -1 : (a > b);
-}
-
 enum { ORACLE_DIES = 8 };
 
-int32_t oracle_plan(const int32_t *row_ptr, int H, int nb, int P, int32_t *work)
+int32_t oracle_plan(const int32_t *row_ptr, int H, int nb, int32_t *work)
 {
     int cap_heads = (H + ORACLE_DIES - 1) / ORACLE_DIES + 2;
     if (cap_heads > H)
         cap_heads = H;
     int64_t cap = (int64_t)cap_heads * nb;
-    int64_t capP = (cap + P - 1) / P * P;
     int64_t *kept = (int64_t *)malloc(sizeof(int64_t) * (size_t)H);
     int32_t *heads = (int32_t *)malloc(sizeof(int32_t) * (size_t)H);
     int32_t *die_heads = (int32_t *)malloc(sizeof(int32_t) * (size_t)(ORACLE_DIES * cap_heads));
-    int32_t *list = (int32_t *)malloc(sizeof(int32_t) * (size_t)cap);
-    int64_t *slot_load = (int64_t *)malloc(sizeof(int64_t) * (size_t)P);
-    int32_t *slots = (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
     int64_t load[ORACLE_DIES] = {0};
     int count[ORACLE_DIES] = {0};
     int32_t n_nonempty = 0;
@@ -300,41 +284,22 @@ int32_t oracle_plan(const int32_t *row_ptr, int H, int nb, int P, int32_t *work)
         die_heads[best * cap_heads + count[best]++] = heads[a];
         load[best] += kept[heads[a]];
     }
-    for (int64_t p = 0; p < ORACLE_DIES * capP; ++p)
+    for (int64_t p = 0; p < ORACLE_DIES * cap; ++p)
         work[p] = -1;
     g_row_ptr = row_ptr;
-    g_slot_load = slot_load;
     for (int x = 0; x < ORACLE_DIES; ++x) {
-        /* the die's list */
-        int64_t m = 0;
+        int32_t *out = work + x * cap;
         for (int c = 0; c < count[x]; ++c) {
             int h = die_heads[x * cap_heads + c];
             for (int i = 0; i < nb; ++i)
-                list[m + i] = h * nb + i;
-            qsort(list + m, (size_t)nb, sizeof(int32_t), by_len_desc_row_asc);
-            m += nb;
-        }
-        /* rounds of P rows to the slots by load */
-        for (int s = 0; s < P; ++s)
-            slot_load[s] = 0;
-        for (int64_t k = 0; k * P < m; ++k) {
-            for (int s = 0; s < P; ++s)
-                slots[s] = s;
-            qsort(slots, (size_t)P, sizeof(int32_t), by_load_asc_slot_asc);
-            for (int t = 0; t < P && k * P + t < m; ++t) {
-                int32_t r = list[k * P + t];
-                int s = slots[t];
-                work[x * capP + k * P + s] = r;
-                slot_load[s] += row_ptr[r + 1] - row_ptr[r] + 1;
-            }
+                out[i] = h * nb + i;
+            qsort(out, (size_t)nb, sizeof(int32_t), by_len_desc_row_asc);
+            out += nb;
         }
     }
     free(kept);
     free(heads);
     free(die_heads);
-    free(list);
-    free(slot_load);
-    free(slots);
     return n_nonempty;
 }
 

@@ -209,76 +209,54 @@ def _die_lists(lens, H, nb):
             for x in range(8)]
 
 
-def _check_rounds(work, lists, lens, P, capP):
-    """Each die's positions k*P + s hold its list dealt in rounds of P: round k
-    holds exactly the list's rows k*P .. k*P+P-1, at most one per slot, and the
-    earlier (longer) a row is in its round, the lighter the slot it goes to."""
-    for x, lst in enumerate(lists):
-        seg = list(work[x * capP:(x + 1) * capP])
-        assert sorted(r for r in seg if r >= 0) == sorted(lst)
-        load = [0] * P
-        for k in range(-(-len(lst) // P)):
-            got = {s: seg[k * P + s] for s in range(P) if seg[k * P + s] >= 0}
-            want_rows = lst[k * P:(k + 1) * P]
-            assert sorted(got.values()) == sorted(want_rows)
-            slot_of = {r: s for s, r in got.items()}
-            keys = [(load[slot_of[r]], slot_of[r]) for r in want_rows]
-            assert keys == sorted(keys), (x, k)
-            for r in want_rows:
-                load[slot_of[r]] += int(lens[r]) + 1
-        assert all(r == -1 for r in seg[-(-len(lst) // P) * P:])
-
-
 def pin_plan(lib):
     # Hand-derived: H=3, nb=4, one head per die.  Kept per head: 5, 9, 5, so
     # head 1 -> die 0, head 0 -> die 1, head 2 -> die 2; dies 3..7 stay empty.
-    # A die may hold min(3, 1 + 2) = 3 heads, so 12 positions; with P = 4 slots
-    # each die's 4 rows form one round on fresh slots.
+    # A die may hold min(3, 1 + 2) = 3 heads, so 12 positions per die.
     lens = np.array([2, 0, 3, 0,   4, 1, 4, 0,   1, 1, 1, 2])
     row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    work, n = O.plan(row_ptr, 3, 4, 4, lib)
+    work, n = O.plan(row_ptr, 3, 4, lib)
     pad = [-1] * 8
     want = [4, 6, 5, 7] + pad + [2, 0, 1, 3] + pad + [11, 8, 9, 10] + pad + [-1] * 60
     assert list(work) == want and n == 9
     # Head cap slack: 12 heads of kept 30, 1, 1, ..., 1 with 8 dies: each die
     # may hold min(12, 2 + 2) = 4 heads.  Head 0 -> die 0 (30); heads 1..7 ->
     # dies 1..7; heads 8..11 (1 block each) go to the lightest dies, 1..4,
-    # never to die 0.
+    # never to die 0.  Within a die, heads in assignment order.
     lens = np.zeros(12 * 2, np.int64)
     lens[0], lens[1] = 20, 10
     for h in range(1, 12):
         lens[2 * h] = 1
     row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    work, n = O.plan(row_ptr, 12, 2, 8, lib)
-    capP = 8
-    die_rows = [sorted(int(r) for r in work[x * capP:(x + 1) * capP] if r >= 0) for x in range(8)]
-    assert die_rows[0] == [0, 1]
+    work, n = O.plan(row_ptr, 12, 2, lib)
+    cap = 8
+    assert len(work) == 8 * cap and n == 13
+    assert list(work[:cap]) == [0, 1] + [-1] * 6
     for x in range(1, 5):
-        assert die_rows[x] == sorted([2 * x, 2 * x + 1, 2 * (x + 7), 2 * (x + 7) + 1]), x
+        assert list(work[x * cap:(x + 1) * cap]) == [2 * x, 2 * x + 1, 2 * (x + 7),
+                                                     2 * (x + 7) + 1] + [-1] * 4, x
     for x in range(5, 8):
-        assert die_rows[x] == [2 * x, 2 * x + 1], x
-    # Hand-derived rounds: one head of 5 rows, lengths 4, 3, 2, 2, 1, P = 2.
-    # Round 0: rows 0, 1 to fresh slots 0, 1 (loads 5, 4).  Round 1: slot 1 is
-    # lighter, so row 2 -> slot 1 and row 3 -> slot 0 (loads 8, 7).  Round 2:
-    # row 4 -> slot 1; slot 0 idles.
-    lens = np.array([4, 3, 2, 2, 1])
+        assert list(work[x * cap:(x + 1) * cap]) == [2 * x, 2 * x + 1] + [-1] * 6, x
+    # Hand-derived row order: one head of 5 rows with lengths 2, 4, 1, 3, 2:
+    # longest first, the two of length 2 by row id.
+    lens = np.array([2, 4, 1, 3, 2])
     row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    work, n = O.plan(row_ptr, 1, 5, 2, lib)
-    assert list(work[:6]) == [0, 1, 3, 2, -1, 4] and all(w == -1 for w in work[6:])
-    assert len(work) == 8 * 6 and n == 5
-    # Properties on random shapes and slot counts (several heads per die).
+    work, n = O.plan(row_ptr, 1, 5, lib)
+    assert list(work[:5]) == [1, 3, 0, 4, 2] and all(w == -1 for w in work[5:])
+    assert len(work) == 8 * 5 and n == 5
+    # Random shapes (several heads per die) against the spec written out.
     rng = np.random.default_rng(RNG_SEEDS[1] + 7)
-    for H, nb, P in ((20, 6, 4), (28, 9, 5), (8, 5, 16), (33, 3, 2), (17, 12, 7)):
+    for H, nb in ((20, 6), (28, 9), (8, 5), (33, 3), (17, 12)):
         lens = rng.integers(0, nb + 1, size=H * nb) * (rng.random(H * nb) < 0.7)
         lens[: nb] = 0                                  # one head keeps nothing
         row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-        work, n = O.plan(row_ptr, H, nb, P, lib)
+        work, n = O.plan(row_ptr, H, nb, lib)
         cap = min(H, -(-H // 8) + 2) * nb
-        capP = -(-cap // P) * P
-        assert len(work) == 8 * capP
-        _check_rounds(work, _die_lists(lens, H, nb), lens, P, capP)
+        want = []
+        for lst in _die_lists(lens, H, nb):
+            want += lst + [-1] * (cap - len(lst))
+        assert list(work) == want
         assert n == int((lens > 0).sum())
-        assert sorted(int(r) for r in work if r >= 0) == list(range(H * nb))
 
 
 # --------------------------------------------------------------- attention --

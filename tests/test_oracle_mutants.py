@@ -39,10 +39,6 @@ MUTANTS = [
     ("csr_transposed", "if (keep[(int64_t)r * nb + j])", "if (keep[(int64_t)j * nb + r])", 0),
     ("plan_ascending", "if (la > lb) return -1;", "if (la < lb) return -1;", 0),
     ("plan_most_loaded_die", "load[x] < load[best]", "load[x] > load[best]", 0),
-    ("plan_heaviest_slot_first", "if (g_slot_load[a] < g_slot_load[b]) return -1;\n    if (g_slot_load[a] > g_slot_load[b]) return 1;",
-     "if (g_slot_load[a] < g_slot_load[b]) return 1;\n    if (g_slot_load[a] > g_slot_load[b]) return -1;", 0),
-    ("plan_slot_load_ignores_length", "slot_load[s] += row_ptr[r + 1] - row_ptr[r] + 1;",
-     "slot_load[s] += 1;", 0),
     ("plan_heads_ascending",
      "if (g_head_kept[a] > g_head_kept[b]) return -1;\n    if (g_head_kept[a] < g_head_kept[b]) return 1;",
      "if (g_head_kept[a] > g_head_kept[b]) return 1;\n    if (g_head_kept[a] < g_head_kept[b]) return -1;", 0),
