@@ -284,12 +284,9 @@ class MaskBuffers:
         return self.view(self.layout.select, 16, torch.int32)
 
     def work_cap(self):
-        """Positions per die of the last plan (capP), from the plan's meta words."""
-        return int(self.work_meta()[0].item())
-
-    def work_slots(self):
-        """Slots per die P of the last plan."""
-        return int(self.work_meta()[2].item())
+        """Positions per die of the work order: min(H, ceil(H/8) + 2) * nb."""
+        H = self.dims.n_q_heads
+        return min(H, -(-H // 8) + 2) * self.nb
 
     def work(self):
         return self.view(self.layout.work, 8 * self.work_cap(), torch.int32)

@@ -34,7 +34,10 @@
 //  * fp32 accumulation and softmax (exp2 with log2(e)/sqrt(d) folded in); the
 //    running max is raised only when a chunk exceeds it by more than 8 (log2
 //    units), so the O^T rescale is rare; the normaliser sums the bf16-rounded
-//    weights that enter the product.  bf16 round-to-nearest-even output.
+//    weights that enter the product.  bf16 round-to-nearest-even output,
+//    staged through the (then free) rings so that every store writes whole
+//    rows: scattered 8-byte stores from the accumulator layout cost the
+//    memory path far more than their bytes.
 #include "common.h"
 
 namespace sd {
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ row_ptr,
     const int32_t *__restrict__ col_idx, const int32_t *__restrict__ work,
-    uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx, int64_t capP,
+    uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx, int64_t cap,
     float scale_log2) {
     constexpr int NT = QW / 32;                 // 32-query tiles per wave
     constexpr int WQ = BLK / QW;                // query slices (= waves) per block
@@ -95,8 +98,9 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     constexpr int LOADS = kChunk / ROWS_PER_LOAD;   // wave loads per tile
     // A three-stage K ring and a two-stage V ring, shared by the WQ waves of
     // the workgroup.
-    __shared__ __attribute__((aligned(16))) uint16_t kring[3 * TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t vring[2 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t rings[5 * TILE];
+    uint16_t *const kring = rings;
+    uint16_t *const vring = rings + 3 * TILE;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -116,9 +120,9 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         }
     } else {
         // Workgroup b runs on die b % kDies: take position b / kDies of that
-        // die's list (capP positions per die).
+        // die's list (cap positions per die).
         const int b = blockIdx.x;
-        row = __builtin_amdgcn_readfirstlane(work[(b % kDies) * capP + b / kDies]);
+        row = __builtin_amdgcn_readfirstlane(work[(b % kDies) * cap + b / kDies]);
         if (row < 0 || row >= H * nb) return;   // padding (or a malformed order): nothing to do
     }
     const int h = row / nb, blk = row % nb, g = h / G;
@@ -422,12 +426,22 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) l_run[nt] += __shfl_xor(l_run[nt], 32);
 
-    // O = O^T / l, rounded to bf16: lane holds query col (32*nt + col) and 4
-    // consecutive dims per group of 4 accumulators.
-    uint16_t *orow = o + qbase;
+    // O = O^T / l, rounded to bf16, staged through LDS so that every store
+    // writes whole rows.  Lane holds query col (32*nt + col) and 4 consecutive
+    // dims per group of 4 accumulators; the wave's 32 x D tile goes into the
+    // rings (every wave has finished reading them after the sync), row-major
+    // with 16-byte segment s of row r stored at s ^ (r % segments), then each
+    // lane reads back 16 contiguous bytes and the wave stores 64 x 16 bytes
+    // of consecutive rows per instruction.
+    sync();
+    constexpr int SEGS = D / 8;                 // 16-byte segments per row
+    constexpr int RPI = 64 / SEGS;              // rows per store instruction
+    static_assert(WQ * QW * D <= 5 * TILE, "the staged tiles fit in the rings");
+    uint16_t *ot = rings + wq * QW * D;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const float inv_l = 1.0f / l_run[nt];
+        const int r = 32 * nt + col;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -437,10 +451,19 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
                                     ((uint32_t)bf16_rne(oacc[mt][nt][i + 1] * inv_l) << 16);
                 const uint32_t hi = (uint32_t)bf16_rne(oacc[mt][nt][i + 2] * inv_l) |
                                     ((uint32_t)bf16_rne(oacc[mt][nt][i + 3] * inv_l) << 16);
-                const int qr = 32 * nt + col;
-                const int dcol = 32 * mt + 8 * i4 + 4 * hh;
-                *reinterpret_cast<uint2 *>(orow + (int64_t)qr * D + dcol) = make_uint2(lo, hi);
+                const int seg = 4 * mt + i4;    // dims 8*seg .. +8; this lane's half is 4*hh
+                *reinterpret_cast<uint2 *>(ot + r * D + 8 * (seg ^ (r & (SEGS - 1))) + 4 * hh) =
+                    make_uint2(lo, hi);
             }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    uint16_t *orow = o + qbase;
+#pragma unroll
+    for (int t = 0; t < QW / RPI; ++t) {
+        const int r = t * RPI + lane / SEGS, sg = lane % SEGS;
+        const uint4 val =
+            *reinterpret_cast<const uint4 *>(ot + r * D + 8 * (sg ^ (r & (SEGS - 1))));
+        *reinterpret_cast<uint4 *>(orow + (int64_t)r * D + 8 * sg) = val;
     }
 }
 
@@ -449,35 +472,12 @@ hipError_t launch_attn_t(const Dims &Dm, const uint16_t *q, const uint16_t *k, c
                          const int32_t *row_ptr, const int32_t *col_idx, const int32_t *work,
                          int n_idx, uint16_t *o, hipStream_t s) {
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    const int64_t P = DENSE ? 1 : attn_slots_per_die(Dm);
-    const int64_t capP = (Dm.die_cap() + P - 1) / P * P;
-    const unsigned grid = (unsigned)(DENSE ? Dm.rows() : kDies * capP);
+    const int64_t cap = Dm.die_cap();
+    const unsigned grid = (unsigned)(DENSE ? Dm.rows() : kDies * cap);
     hipLaunchKernelGGL((k_attn<D, BLK, QW, DENSE>), dim3(grid), dim3(BLK / QW * 64),
                        0, s, q, k, v, row_ptr, col_idx, work, o, Dm.L, Dm.nb, Dm.G, Dm.H,
-                       n_idx, capP, scale_log2);
+                       n_idx, cap, scale_log2);
     return hipGetLastError();
-}
-
-// Resident workgroups of the sparse kernel per CU (occupancy API) times the
-// CUs of one die, cached per device and shape class.
-template <int D, int BLK>
-int slots_per_die_t() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
-    static int cache[64];
-    if (cache[dev] > 0) return cache[dev];
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&k_attn<D, BLK, kQW, false>), BLK / kQW * 64,
-            0) != hipSuccess) {
-        (void)hipGetLastError();
-        return 1;
-    }
-    int p = cus / kDies * per_cu;
-    p = p < 1 ? 1 : (p > kMaxSlots ? kMaxSlots : p);
-    cache[dev] = p;
-    return p;
 }
 
 template <bool DENSE>
@@ -494,13 +494,6 @@ hipError_t launch_attn(const Dims &D, const uint16_t *q, const uint16_t *k, cons
 }
 
 }  // namespace
-
-int attn_slots_per_die(const Dims &D) {
-    if (D.d == 128 && D.B == 64) return slots_per_die_t<128, 64>();
-    if (D.d == 128 && D.B == 128) return slots_per_die_t<128, 128>();
-    if (D.d == 64 && D.B == 64) return slots_per_die_t<64, 64>();
-    return slots_per_die_t<64, 128>();
-}
 
 hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                               const uint16_t *v, const int32_t *row_ptr, const int32_t *col_idx,

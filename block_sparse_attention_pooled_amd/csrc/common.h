@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace sd {
 
 constexpr int kWave = 64;            // CDNA wavefront width
@@ -13,7 +15,6 @@ constexpr int kDies = 8;             // XCDs: workgroup b of a launch runs on di
 constexpr int kRadixBins = 2048;     // 11-bit digits (11 + 11 + 10 = 32 bits)
 constexpr int kSelectWords = 16;     // select state words in the workspace
 constexpr int kHeadSelWords = 8;     // per-head select state words (uniform budget)
-constexpr int kMaxSlots = 512;       // most resident attention workgroups per die
 
 // Select state words.
 enum SelectWord {
@@ -29,8 +30,11 @@ enum SelectWord {
 struct Dims {
     int H, Hkv, L, d, B, nb, G;
     int64_t rows() const { return (int64_t)H * nb; }
-    // Work-order positions per die (rows of ceil(H / kDies) heads).
-    int64_t die_cap() const { return (int64_t)((H + kDies - 1) / kDies) * nb; }
+    // Heads a die may take in the work order: ceil(H / kDies) plus two of
+    // slack for balancing, at most H.
+    int die_heads() const { return std::min(H, (H + kDies - 1) / kDies + 2); }
+    // Work-order positions per die (rows of die_heads() heads).
+    int64_t die_cap() const { return (int64_t)die_heads() * nb; }
     int64_t n_scores() const { return (int64_t)H * nb * nb; }
 };
 
@@ -53,7 +57,7 @@ inline WsLayout ws_layout(const Dims &D) {
     w.gt = take(D.rows() * 4);
     w.eq = take(D.rows() * 4);
     w.tie_base = take(D.rows() * 4);
-    w.work = take(kDies * (D.die_cap() + kMaxSlots) * 4);   // 8 * capP, capP < cap + P
+    w.work = take(kDies * D.die_cap() * 4);
     w.work_meta = take(16 * 4);
     w.hsel = take((int64_t)D.H * kHeadSelWords * 4);
     w.total = off;
@@ -92,9 +96,6 @@ hipError_t launch_mask_recall(const Dims &D, const float *mass, const int32_t *r
                               hipStream_t s);
 
 // Attention launches (attn_kernels.hip).
-// Resident sparse-attention workgroups per die on the current device for these
-// shapes (the plan deals each die's rows to that many slots); in [1, kMaxSlots].
-int attn_slots_per_die(const Dims &D);
 hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                               const uint16_t *v, const int32_t *row_ptr, const int32_t *col_idx,
                               const int32_t *work, int64_t n_idx, uint16_t *o, hipStream_t s);

@@ -457,38 +457,37 @@ __global__ __launch_bounds__(1024) void k_kept_scan(const int32_t *__restrict__ 
 // rows of a head go to one die so that the head's K/V stay in that die's L2:
 //  * heads are ranked by kept blocks (descending, ties by head id) and, in
 //    that order, each goes to the die with the fewest kept blocks so far among
-//    those holding fewer than ceil(H / kDies) heads (ties: lowest die);
+//    those holding fewer than min(H, ceil(H / kDies) + 2) heads (ties: lowest
+//    die);
 //  * die x's list is its heads in assignment order, each head's rows by list
-//    length descending (ties by row id), at work[x*cap ...], cap =
-//    ceil(H / kDies) * nb; unused positions hold -1.
-// One workgroup: heads are ranked in parallel, assigned by one thread, then
-// each wave sorts whole heads with a stable counting sort (length histogram,
-// descending bucket starts, ranks among equal lengths from wave ballots).
+//    length descending (ties by row id), at work[x*cap ..], cap = (heads a die
+//    may hold) * nb; unused positions hold -1.
+// One workgroup: heads are ranked in parallel and assigned by one wave (die
+// loads and counts in registers), then each wave sorts whole heads with a
+// stable counting sort (length histogram, descending bucket starts, ranks
+// among equal lengths from wave ballots).
 constexpr int kPlanThreads = 512;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict__ row_ptr,
-                                                       int H, int nb, int P,
+                                                       int H, int nb,
                                                        int32_t *__restrict__ work,
                                                        int32_t *__restrict__ meta) {
-    static_assert(kPlanWaves == kDies, "one wave per die deals the rounds");
     __shared__ int32_t kept[kMaxHeads];
     __shared__ int32_t order[kMaxHeads];
     __shared__ int32_t head_base[kMaxHeads];
+    // Per wave: the sort's histogram (and row_ptr staging) and list lengths.
     __shared__ int32_t next[kPlanWaves][kMaxBlocks + 1];
+    __shared__ int16_t lens[kPlanWaves][kMaxBlocks];
     __shared__ int32_t die_count[kDies];
-    __shared__ int32_t slot_load[kDies][kMaxSlots];
-    __shared__ int32_t slot_of_rank[kDies][kMaxSlots];
-    __shared__ int32_t round_rows[kDies][kMaxSlots];
     __shared__ int32_t nonempty;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int cap_h = (H + kDies - 1) / kDies;
+    const int cap_h = min(H, (H + kDies - 1) / kDies + 2);
     const int64_t cap = (int64_t)cap_h * nb;
-    const int64_t capP = (cap + P - 1) / P * P;
     if (tid == 0) nonempty = 0;
     for (int h = tid; h < H; h += kPlanThreads)
         kept[h] = row_ptr[(int64_t)(h + 1) * nb] - row_ptr[(int64_t)h * nb];
-    for (int64_t p = tid; p < kDies * capP; p += kPlanThreads) work[p] = -1;
+    for (int64_t p = tid; p < kDies * cap; p += kPlanThreads) work[p] = -1;
     __syncthreads();
     for (int h = tid; h < H; h += kPlanThreads) {
         int rank = 0;
@@ -497,36 +496,72 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict
         order[rank] = h;
     }
     __syncthreads();
-    if (tid == 0) {
+    if (wave == 0) {
+        // Uniform in the wave: die loads and head counts, indexed only by
+        // unrolled loops so they stay in registers.
         int64_t load[kDies];
         int count[kDies];
+#pragma unroll
         for (int x = 0; x < kDies; ++x) {
             load[x] = 0;
             count[x] = 0;
         }
-        for (int a = 0; a < H; ++a) {
-            const int h = order[a];
-            int best = -1;
-            for (int x = 0; x < kDies; ++x)
-                if (count[x] < cap_h && (best < 0 || load[x] < load[best])) best = x;
-            head_base[h] = (int32_t)(best * capP + (int64_t)count[best] * nb);
-            ++count[best];
-            load[best] += kept[h];
+        for (int a0 = 0; a0 < H; a0 += 64) {
+            const int my_h = a0 + lane < H ? order[a0 + lane] : 0;
+            const int my_kept = kept[my_h];
+            const int n = min(64, H - a0);
+            for (int a = 0; a < n; ++a) {
+                const int h = __builtin_amdgcn_readlane(my_h, a);
+                const int kh = __builtin_amdgcn_readlane(my_kept, a);
+                int best = 0;
+                int64_t best_key = INT64_MAX;
+#pragma unroll
+                for (int x = 0; x < kDies; ++x) {
+                    const int64_t key = count[x] < cap_h ? load[x] * kDies + x : INT64_MAX;
+                    if (key < best_key) {
+                        best_key = key;
+                        best = x;
+                    }
+                }
+                int base = 0;
+#pragma unroll
+                for (int x = 0; x < kDies; ++x)
+                    if (x == best) {
+                        base = (int)(x * cap + (int64_t)count[x] * nb);
+                        ++count[x];
+                        load[x] += kh;
+                    }
+                if (lane == 0) head_base[h] = base;
+            }
         }
-        for (int x = 0; x < kDies; ++x) die_count[x] = count[x];
+        if (lane == 0)
+#pragma unroll
+            for (int x = 0; x < kDies; ++x) die_count[x] = count[x];
     }
     __syncthreads();
     const uint64_t lt = lanemask_lt();
     int32_t *nx = next[wave];
+    int16_t *ln = lens[wave];
     int my_nonempty = 0;
     for (int h = wave; h < H; h += kPlanWaves) {
         const int64_t r0 = (int64_t)h * nb;
-        for (int l = lane; l <= nb; l += 64) nx[l] = 0;
+        // Stage row_ptr[r0 .. r0 + nb] in nx (loads issued together), then
+        // the list lengths in ln.  A wave's LDS requests complete in order.
+        for (int c = 0; c <= nb; c += 512) {
+            int v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = row_ptr[r0 + min(c + lane + 64 * j, nb)];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (c + lane + 64 * j <= nb) nx[c + lane + 64 * j] = v[j];
+        }
         for (int i = lane; i < nb; i += 64) {
-            const int len = row_ptr[r0 + i + 1] - row_ptr[r0 + i];
-            atomicAdd(&nx[len], 1);
+            const int len = nx[i + 1] - nx[i];
+            ln[i] = (int16_t)len;
             my_nonempty += len > 0;
         }
+        for (int l = lane; l <= nb; l += 64) nx[l] = 0;
+        for (int i = lane; i < nb; i += 64) atomicAdd(&nx[ln[i]], 1);
         // Bucket starts, longest lists first: nx[l] = rows with length > l.
         int carry = 0;
         for (int c0 = nb; c0 >= 0; c0 -= 64) {
@@ -545,7 +580,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict
         for (int i0 = 0; i0 < nb; i0 += 64) {
             const int i = i0 + lane;
             const bool valid = i < nb;
-            const int len = valid ? row_ptr[r0 + i + 1] - row_ptr[r0 + i] : 0;
+            const int len = valid ? ln[i] : 0;
             uint64_t same = __ballot(valid);
 #pragma unroll
             for (int bit = 0; bit < 11; ++bit) {
@@ -561,45 +596,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict
     }
     atomicAdd(&nonempty, my_nonempty);
     __syncthreads();
-    // Deal each die's list in rounds of P rows (wave x, die x): the round's
-    // rows in list order go to the slots ranked by load (ascending, ties by
-    // slot); slot s's row of round k lands at k*P + s.  Dies run different
-    // numbers of rounds, so the steps of a round are ordered by LDS waits
-    // within the wave (LDS requests of a wave complete in order), not by
-    // workgroup barriers.
-    {
-        const int x = wave;
-        const int64_t m = (int64_t)die_count[x] * nb;
-        int32_t *seg = work + (int64_t)x * capP;
-        int32_t *ld = slot_load[x], *by_rank = slot_of_rank[x], *rows = round_rows[x];
-        for (int sl = lane; sl < P; sl += 64) ld[sl] = 0;
-        for (int64_t k0 = 0; k0 < m; k0 += P) {
-            const int64_t cnt = min((int64_t)P, m - k0);
-            for (int t = lane; t < P; t += 64) rows[t] = t < cnt ? seg[k0 + t] : -1;
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-            for (int sl = lane; sl < P; sl += 64) {
-                const int l0 = ld[sl];
-                int rank = 0;
-                for (int s2 = 0; s2 < P; ++s2) {
-                    const int l2 = ld[s2];
-                    rank += (l2 < l0) || (l2 == l0 && s2 < sl);
-                }
-                by_rank[rank] = sl;
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            for (int t = lane; t < P; t += 64) {
-                const int sl = by_rank[t];
-                const int r = rows[t];
-                seg[k0 + sl] = r;
-                if (r >= 0) ld[sl] += row_ptr[r + 1] - row_ptr[r] + 1;
-            }
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        }
-    }
     if (tid == 0) {
-        meta[0] = (int32_t)capP;
+        meta[0] = (int32_t)cap;
         meta[1] = nonempty;
-        meta[2] = P;
     }
 }
 
@@ -682,9 +681,7 @@ hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, char *ws, const Ws
                        hipStream_t s) {
     int32_t *work = reinterpret_cast<int32_t *>(ws + w.work);
     int32_t *meta = reinterpret_cast<int32_t *>(ws + w.work_meta);
-    const int P = attn_slots_per_die(D);
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.H, D.nb, P, work,
-                       meta);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.H, D.nb, work, meta);
     return hipGetLastError();
 }
 

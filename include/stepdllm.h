@@ -89,11 +89,10 @@ typedef struct {
     int64_t scores;     /* fp32 [H, nb, nb]: row-softmaxed pooled scores          */
     int64_t select;     /* uint32 [16]: [0] cut key, [1] count above the cut,
                            [2] ties kept at the cut, [3] K                        */
-    int64_t work;       /* int32 [8 * capP]: attention work order, capP =
-                           ceil(cap / P) * P positions per die, cap =
-                           ceil(H/8) * nb, P slots per die; -1 = padding         */
-    int64_t work_meta;  /* int32 [16]: [0] capP, [1] number of non-empty rows,
-                           [2] P                                                  */
+    int64_t work;       /* int32 [8 * cap]: attention work order, cap =
+                           min(H, ceil(H/8) + 2) * nb positions per die;
+                           -1 = padding                                           */
+    int64_t work_meta;  /* int32 [16]: [0] cap, [1] number of non-empty rows      */
     int64_t head_select;/* uint32 [H, 8]: per-head select state under the uniform
                            budget: [h*8 + 0] cut key, [+1] count above the cut,
                            [+2] ties kept at the cut, [+3] k_h                    */
@@ -158,13 +157,12 @@ int stepdllm_select_mask_per_head(const stepdllm_dims *dims, double sparsity,
  * (XCDs) each have their own L2 and take workgroups round robin, so all rows
  * of a head go to one die: heads are ranked by kept blocks (descending, ties
  * by id) and each goes to the least-loaded die that holds fewer than
- * ceil(H/8) heads (ties: lowest die); a die's list is its heads in that
- * order, each head's rows by list length descending (ties by row id).  The
- * list is dealt to P slots per die (P = resident attention workgroups per die
- * on the current device) in rounds of P rows: a round's rows, in list order,
- * go to the slots by load so far (ascending, ties: lowest slot; a row adds its
- * length + 1), and slot s's row of round k is at position k*P + s.  The order
- * is for the device that is current when it is built. */
+ * min(H, ceil(H/8) + 2) heads (ties: lowest die); a die's list is its heads in that
+ * order, each head's rows by list length descending (ties by row id), at
+ * positions [x*cap, x*cap + cap) of the work order.  Workgroup b of the
+ * sparse launch takes position b / 8 of die b % 8's list, so each die starts
+ * its longest rows first and the hardware hands the next row to whichever
+ * workgroup slot frees first. */
 int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr,
                   void *ws, size_t ws_bytes, void *stream);
 
