@@ -16,6 +16,8 @@
  *        precomputed sparse pattern reused for all later steps.
  *  [BA]  "Block Approximate Sparse Attention (BA-Att)" abstract: blocks are
  *        scored in a block-wise pre-downsampled space.
+ *  [PC]  "PulseCol" abstract: periodically refreshed column-sparse attention
+ *        (the column-sparse variant below).
  *
  * The pages do not say how blocks are scored; the reading taken here is:
  * mean-pool Q and K over each block of B tokens, score pooled pairs with
@@ -450,6 +452,134 @@ void oracle_mask_recall(const double *A, int rows, int nb, const int32_t *row_pt
             acc += A[(int64_t)r * nb + col_idx[e]];
         recall[r] = acc;
     }
+}
+
+/* --------------------------------------------------------- column-sparse --- */
+/* [PC] "PulseCol" abstract: column-sparse attention (individual key columns
+ * instead of blocks), its pattern found at an early denoising step, reused,
+ * and refreshed at a few intermediate steps.  The pages do not say how the
+ * columns are scored or counted; the reading taken mirrors the block path:
+ *  - each query block's pooled query (block mean, as in oracle_pool) is
+ *    rounded to bf16, the matrix-core input type, and scored against every
+ *    key token u with q.k_u / sqrt(d), softmaxed over all L keys;
+ *  - the column mass c[h,u] is the mean of those probabilities over the nb
+ *    pooled queries of head h (an estimate of the share of the head's
+ *    attention that lands on key u); each head's masses sum to 1;
+ *  - head h keeps its k_c = ceil((1-s) * L) largest columns (value
+ *    descending, index ascending), the same count for every head;
+ *  - every query token of head h attends to exactly the kept key tokens. */
+
+/* Round to the nearest bf16, ties to even (finite inputs). */
+static float bf16_round(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    memcpy(&x, &u, sizeof u);
+    return x;
+}
+
+void oracle_bf16_round(const float *x, int64_t n, float *y)
+{
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = bf16_round(x[i]);
+}
+
+/* c: [H, L] fp64 column masses. */
+void oracle_col_scores(const float *q, const float *k, int H, int Hkv, int L,
+                       int d, int B, double *c)
+{
+    int nb = L / B, G = H / Hkv;
+    double scale = 1.0 / sqrt((double)d);
+    float *qb = (float *)malloc(sizeof(float) * (size_t)H * nb * d);
+    double *z = (double *)malloc(sizeof(double) * (size_t)L);
+    oracle_pool(q, H, L, d, B, qb);
+    for (int64_t x = 0; x < (int64_t)H * nb * d; ++x)
+        qb[x] = bf16_round(qb[x]);
+    for (int h = 0; h < H; ++h) {
+        int g = h / G;
+        const float *kh = k + (int64_t)g * L * d;
+        double *ch = c + (int64_t)h * L;
+        for (int u = 0; u < L; ++u)
+            ch[u] = 0.0;
+        for (int i = 0; i < nb; ++i) {
+            const float *a = qb + ((int64_t)h * nb + i) * d;
+            double m = -INFINITY;
+            for (int u = 0; u < L; ++u) {
+                const float *ku = kh + (int64_t)u * d;
+                double dot = 0.0;
+                for (int e = 0; e < d; ++e)
+                    dot += (double)a[e] * (double)ku[e];
+                z[u] = dot * scale;
+                if (z[u] > m)
+                    m = z[u];
+            }
+            double l = 0.0;
+            for (int u = 0; u < L; ++u) {
+                z[u] = exp(z[u] - m);
+                l += z[u];
+            }
+            for (int u = 0; u < L; ++u)
+                ch[u] += z[u] / l / nb;
+        }
+    }
+    free(qb);
+    free(z);
+}
+
+/* Per head, the k_c largest of the head's L column masses (fp32, the
+ * precision the GPU decides in) under (value descending, index ascending),
+ * listed in ascending column order: cols [H, k_c]. */
+void oracle_col_select(const float *c, int H, int L, int64_t k_c, int32_t *cols)
+{
+    uint8_t *keep = (uint8_t *)malloc((size_t)L);
+    for (int h = 0; h < H; ++h) {
+        oracle_select(c + (int64_t)h * L, L, k_c, keep);
+        int64_t n = 0;
+        for (int u = 0; u < L; ++u)
+            if (keep[u])
+                cols[(int64_t)h * k_c + n++] = u;
+    }
+    free(keep);
+}
+
+/* The whole column mask: masses in fp64, rounded to fp32 (c_out, [H, L]),
+ * then the per-head select.  Returns k_c. */
+int64_t oracle_build_col_mask(const float *q, const float *k, int H, int Hkv,
+                              int L, int d, int B, double s, float *c_out,
+                              int32_t *cols)
+{
+    int64_t k_c = oracle_keep_count(L, s);
+    double *c = (double *)malloc(sizeof(double) * (size_t)H * L);
+    oracle_col_scores(q, k, H, Hkv, L, d, B, c);
+    for (int64_t x = 0; x < (int64_t)H * L; ++x)
+        c_out[x] = (float)c[x];
+    oracle_col_select(c_out, H, L, k_c, cols);
+    free(c);
+    return k_c;
+}
+
+/* Column-sparse attention for the listed rows r = h*nb + i (all when rows ==
+ * NULL): each query token of block i in head h attends to the key tokens
+ * cols[h*k_c .. h*k_c + k_c) of key head h / (H/Hkv).  o: [H, L, d] fp64. */
+void oracle_col_attn(const float *q, const float *k, const float *v, int H,
+                     int Hkv, int L, int d, int B, const int32_t *cols,
+                     int64_t k_c, const int32_t *rows, int n_rows, double *o)
+{
+    int nb = L / B, G = H / Hkv;
+    int total = rows ? n_rows : H * nb;
+    double *z = (double *)malloc(sizeof(double) * (size_t)(k_c > 0 ? k_c : 1));
+    for (int x = 0; x < total; ++x) {
+        int r = rows ? rows[x] : x;
+        int h = r / nb, i = r % nb, g = h / G;
+        const float *kh = k + (int64_t)g * L * d;
+        const float *vh = v + (int64_t)g * L * d;
+        for (int t = i * B; t < (i + 1) * B; ++t)
+            attend_token(q + ((int64_t)h * L + t) * d, kh, vh, d,
+                         cols + (int64_t)h * k_c, (int)k_c, z,
+                         o + ((int64_t)h * L + t) * d);
+    }
+    free(z);
 }
 
 /* ----------------------------------------------------------------- driver --- */

@@ -49,6 +49,11 @@ def _bind(lib):
         "oracle_step_kind": (ci, [ci, ci, ci]),
         "oracle_block_mass": (None, [f32p, f32p, ci, ci, ci, ci, ci, vp, ci, f64p]),
         "oracle_mask_recall": (None, [f64p, ci, ci, i32p, i32p, f64p]),
+        "oracle_bf16_round": (None, [f32p, ci64, f32p]),
+        "oracle_col_scores": (None, [f32p, f32p, ci, ci, ci, ci, ci, f64p]),
+        "oracle_col_select": (None, [f32p, ci, ci, ci64, i32p]),
+        "oracle_build_col_mask": (ci64, [f32p, f32p, ci, ci, ci, ci, ci, cd, f32p, i32p]),
+        "oracle_col_attn": (None, [f32p, f32p, f32p, ci, ci, ci, ci, ci, i32p, ci64, vp, ci, f64p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -236,7 +241,70 @@ def mask_recall(A, row_ptr, col_idx, lib=None):
     return rec
 
 
+def bf16_round(x, lib=None):
+    """Round fp32 values to the nearest bf16 (ties to even), as fp32."""
+    lib = lib or load()
+    x = _f32(x)
+    y = np.empty_like(x)
+    lib.oracle_bf16_round(x.reshape(-1), int(x.size), y.reshape(-1))
+    return y
+
+
+def col_scores(q, k, B, lib=None):
+    """Column masses c [H, L] (fp64) of the column-sparse variant: the mean over
+    each head's bf16-rounded pooled queries of the softmax over all key
+    tokens."""
+    lib = lib or load()
+    q, k = _f32(q), _f32(k)
+    H, L, d = q.shape
+    c = np.empty((H, L), np.float64)
+    lib.oracle_col_scores(q, k, H, k.shape[0], L, d, B, c)
+    return c
+
+
+def col_select(c, k_c, lib=None):
+    """Per head, the k_c largest fp32 column masses (ties to the lowest index),
+    ascending: cols [H, k_c] int32."""
+    lib = lib or load()
+    c = _f32(c)
+    H, L = c.shape
+    cols = np.empty((H, max(int(k_c), 0)), np.int32)
+    lib.oracle_col_select(c, H, L, int(k_c), cols if cols.size else np.zeros(1, np.int32))
+    return cols
+
+
+def build_col_mask(q, k, B, sparsity, lib=None):
+    """-> (c fp32 [H, L], cols [H, k_c] int32, k_c) for the column-sparse variant."""
+    lib = lib or load()
+    q, k = _f32(q), _f32(k)
+    H, L, d = q.shape
+    k_c = int(lib.oracle_keep_count(L, float(sparsity)))
+    c = np.empty((H, L), np.float32)
+    cols = np.empty((H, k_c), np.int32)
+    got = lib.oracle_build_col_mask(q, k, H, k.shape[0], L, d, B, float(sparsity), c,
+                                    cols if cols.size else np.zeros(1, np.int32))
+    assert got == k_c
+    return c, cols, k_c
+
+
+def col_attn(q, k, v, B, cols, rows=None, lib=None, out=None):
+    """fp64 column-sparse attention: every query of head h attends to the key
+    tokens cols[h] (ascending); only the listed rows h*nb + i are written."""
+    lib = lib or load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    H, L, d = q.shape
+    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    k_c = cols.shape[1] if cols.ndim == 2 else 0
+    if out is None:
+        out = np.zeros((H, L, d), np.float64)
+    rptr, nrows, _keep = _rows_arg(rows)
+    lib.oracle_col_attn(q, k, v, H, k.shape[0], L, d, B,
+                        cols if cols.size else np.zeros(1, np.int32), int(k_c), rptr, nrows, out)
+    return out
+
+
 __all__ = ["build", "load", "pool", "scores", "keep_count", "select", "select_per_head",
            "cut_value", "csr",
            "build_mask", "plan", "sparse_attn", "dense_attn", "step_kind", "block_mass",
-           "mask_recall"]
+           "mask_recall", "bf16_round", "col_scores", "col_select", "build_col_mask",
+           "col_attn"]

@@ -512,7 +512,128 @@ def pin_step_kind(lib):
     assert kinds == [0, 0, 0, 1, 2, 2, 2, 1, 2, 2, 2, 1]
 
 
+# ----------------------------------------------------------- column-sparse --
+def _torch_bf16(x):
+    """bf16 rounding by torch (an independent implementation), as fp32."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).to(
+        torch.float32).numpy()
+
+
+def pin_bf16_round(lib):
+    rng = np.random.default_rng(RNG_SEEDS[0] + 11)
+    x = np.concatenate([rng.standard_normal(4000).astype(np.float32) * 10.0 ** rng.integers(-6, 6, 4000),
+                        np.float32([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -8 + 2 ** -16,
+                                    0.0, -0.0, 65504.0, 1e-30])]).astype(np.float32)
+    got = O.bf16_round(x, lib)
+    assert np.array_equal(got.view(np.uint32), _torch_bf16(x).view(np.uint32))
+    # Ties to even, by hand: 1 + 2^-8 is halfway between 1 and 1 + 2^-7.
+    assert got[4000] == 1.0 and got[4001] == np.float32(1 + 2 ** -6)
+
+
+def _pooled_bf16(q, B, lib):
+    return _torch_bf16(O.pool(q, B, lib))
+
+
+def _softmax_rows(z):
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def worked_example_w3():
+    """One head, L = 128, B = 64, d = 64: every query is 2*e0; key 5 is 3*e0,
+    key 70 is 2*e0, every other key is 0.  Scores q.k/8 are 0.75 (key 5), 0.5
+    (key 70) and 0 elsewhere, so with D = e^0.75 + e^0.5 + 126 the column
+    masses are e^0.75/D, e^0.5/D and 1/D."""
+    L, d = 128, 64
+    q = np.zeros((1, L, d), np.float32)
+    q[0, :, 0] = 2.0
+    k = np.zeros((1, L, d), np.float32)
+    k[0, 5, 0], k[0, 70, 0] = 3.0, 2.0
+    v = np.zeros((1, L, d), np.float32)
+    v[0, :, 1] = np.arange(L, dtype=np.float32) / 64.0
+    v[0, :, 2] = 1.0
+    return q, k, v
+
+
+def pin_col_scores(lib):
+    # Q = 0: every column gets 1/L.
+    rng = np.random.default_rng(RNG_SEEDS[1] + 11)
+    k = _rand((2, 256, 64), rng)
+    c = O.col_scores(np.zeros((4, 256, 64), np.float32), k, 64, lib)
+    assert np.max(np.abs(c - 1.0 / 256)) < 1e-15
+    # Whole-matrix numpy fp64 on torch-rounded pooled queries, with GQA and
+    # head temperatures; each head's masses sum to 1.
+    for (H, Hkv, L, d, B, qs) in ((4, 2, 320, 64, 64, 2.0), (3, 1, 256, 128, 128, 0.5),
+                                  (2, 2, 192, 64, 64, 4.0)):
+        q, k = _rand((H, L, d), rng, qs), _rand((Hkv, L, d), rng)
+        got = O.col_scores(q, k, B, lib)
+        qb = _pooled_bf16(q, B, lib).astype(np.float64)
+        for h in range(H):
+            z = qb[h] @ k[h // (H // Hkv)].astype(np.float64).T / math.sqrt(d)
+            want = _softmax_rows(z).mean(axis=0)
+            assert np.max(np.abs(got[h] - want) / want) < 1e-12, (H, Hkv, L, d, B, h)
+        assert np.max(np.abs(got.sum(axis=1) - 1.0)) < 1e-12
+    # W3 in closed form.
+    q, k, _ = worked_example_w3()
+    c = O.col_scores(q, k, 64, lib)[0]
+    D = math.exp(0.75) + math.exp(0.5) + 126
+    want = np.full(128, 1 / D)
+    want[5], want[70] = math.exp(0.75) / D, math.exp(0.5) / D
+    assert np.max(np.abs(c - want)) < 1e-15
+
+
+def pin_col_select(lib):
+    rng = np.random.default_rng(RNG_SEEDS[2] + 11)
+    H, L = 3, 200
+    vals = rng.integers(0, 6, size=(H, L)).astype(np.float32) / 8.0   # heavy ties
+    vals[1] = rng.random(L).astype(np.float32)
+    for k_c in (0, 1, 7, 64, 199, 200):
+        got = O.col_select(vals, k_c, lib)
+        assert got.shape == (H, k_c)
+        for h in range(H):
+            order = np.lexsort((np.arange(L), -vals[h].astype(np.float64)))
+            assert np.array_equal(got[h], np.sort(order[:k_c])), (k_c, h)
+    # W3: k_c = 2 keeps keys 5 and 70; k_c = 3 adds the lowest-index tie, 0.
+    q, k, _ = worked_example_w3()
+    for s, want in ((1 - 2 / 128, [5, 70]), (1 - 3 / 128, [0, 5, 70]), (0.0, list(range(128)))):
+        c, cols, k_c = O.build_col_mask(q, k, 64, s, lib)
+        assert k_c == len(want) and list(cols[0]) == want, (s, list(cols[0]))
+
+
+def pin_col_attention(lib):
+    rng = np.random.default_rng(RNG_SEEDS[0] + 12)
+    for (H, Hkv, L, d, B, k_c) in ((4, 2, 256, 64, 64, 37), (3, 1, 256, 128, 128, 5),
+                                   (2, 2, 192, 64, 64, 1)):
+        q, k, v = _rand((H, L, d), rng), _rand((Hkv, L, d), rng), _rand((Hkv, L, d), rng)
+        cols = np.stack([np.sort(rng.choice(L, k_c, replace=False)) for _ in range(H)]).astype(np.int32)
+        mask = np.zeros((H, L, L), bool)
+        for h in range(H):
+            mask[h][:, cols[h]] = True
+        got = O.col_attn(q, k, v, B, cols, lib=lib)
+        want = brute_attention(q, k, v, mask)
+        assert np.max(np.abs(got - want)) < 1e-12, (H, Hkv, L, d, B, k_c)
+        # A subset of rows writes only those rows.
+        rows = np.array([1, L // B + 2], np.int32) % (H * (L // B))
+        part = O.col_attn(q, k, v, B, cols, rows=rows, lib=lib)
+        for r in rows:
+            h, i = divmod(int(r), L // B)
+            assert np.array_equal(part[h, i * B:(i + 1) * B], got[h, i * B:(i + 1) * B])
+    # Every column kept is dense attention.
+    q, k, v = _rand((2, 128, 64), rng), _rand((2, 128, 64), rng), _rand((2, 128, 64), rng)
+    allc = np.tile(np.arange(128, dtype=np.int32), (2, 1))
+    assert np.max(np.abs(O.col_attn(q, k, v, 64, allc, lib=lib) - O.dense_attn(q, k, v, 64, lib=lib))) < 1e-13
+    # W3: columns 5 and 70 with weights e^0.75 : e^0.5 for every query.
+    q, k, v = worked_example_w3()
+    o = O.col_attn(q, k, v, 64, np.array([[5, 70]], np.int32), lib=lib)[0]
+    w5 = math.exp(0.75) / (math.exp(0.75) + math.exp(0.5))
+    assert np.max(np.abs(o[:, 1] - (w5 * 5 + (1 - w5) * 70) / 64)) < 1e-15
+    assert np.max(np.abs(o[:, 2] - 1.0)) < 1e-15 and np.all(o[:, 0] == 0) and np.all(o[:, 3:] == 0)
+
+
 ALL_PINS = [pin_keep_count, pin_pool, pin_scores, pin_select, pin_select_per_head, pin_csr,
             pin_plan, pin_worked_w1_per_head,
             pin_attention_brute, pin_attention_closed_forms, pin_worked_w1, pin_worked_w2,
-            pin_build_mask_brute, pin_step_kind, pin_block_mass, pin_mask_recall]
+            pin_build_mask_brute, pin_step_kind, pin_block_mass, pin_mask_recall,
+            pin_bf16_round, pin_col_scores, pin_col_select, pin_col_attention]

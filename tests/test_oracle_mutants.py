@@ -59,6 +59,20 @@ MUTANTS = [
     ("recall_skips_last", "for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e)",
      "for (int32_t e = row_ptr[r]; e + 1 < row_ptr[r + 1]; ++e)", 0),
     ("driver_period_from_zero", "since % refresh_every == 0", "step % refresh_every == 0", 0),
+    ("bf16_truncates", "u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;",
+     "u = u & 0xFFFF0000u;", 0),
+    ("bf16_ties_up", "u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;",
+     "u = (u + 0x8000u) & 0xFFFF0000u;", 0),
+    ("col_pooled_not_rounded", "qb[x] = bf16_round(qb[x]);", "qb[x] = qb[x];", 0),
+    ("col_mass_unnormalised", "ch[u] += z[u] / l / nb;", "ch[u] += z[u] / nb;", 0),
+    ("col_mass_sum_not_mean", "ch[u] += z[u] / l / nb;", "ch[u] += z[u] / l;", 0),
+    ("col_gqa_modulo", "int g = h / G;\n        const float *kh = k + (int64_t)g * L * d;\n        double *ch",
+     "int g = h % Hkv;\n        const float *kh = k + (int64_t)g * L * d;\n        double *ch", 0),
+    ("col_select_head_0", "oracle_select(c + (int64_t)h * L, L, k_c, keep);",
+     "oracle_select(c, L, k_c, keep);", 0),
+    ("col_attn_head_0_columns", "cols + (int64_t)h * k_c, (int)k_c, z,", "cols, (int)k_c, z,", 0),
+    ("col_attn_drops_last_column", "cols + (int64_t)h * k_c, (int)k_c, z,",
+     "cols + (int64_t)h * k_c, (int)k_c - 1, z,", 0),
 ]
 
 
