@@ -25,13 +25,14 @@ class Dims(ctypes.Structure):
 
 class Schedule(ctypes.Structure):
     _fields_ = [("dense_steps", ctypes.c_int32), ("refresh_every", ctypes.c_int32),
-                ("sparsity", ctypes.c_double), ("per_head_budget", ctypes.c_int32)]
+                ("sparsity", ctypes.c_double), ("per_head_budget", ctypes.c_int32),
+                ("column_sparse", ctypes.c_int32)]
 
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("pooled_q", "pooled_k", "scores", "select", "work", "work_meta",
-                 "head_select", "total")]
+                 "head_select", "col_scores", "col_stats", "total")]
 
 
 class StepDLLMError(RuntimeError):
@@ -68,6 +69,10 @@ def load():
         "stepdllm_dense_attn": (i32, [D, _vp, _vp, _vp, _vp, _vp]),
         "stepdllm_block_mass": (i32, [D, _vp, _vp, _vp, _vp]),
         "stepdllm_mask_recall": (i32, [D, _vp, _vp, _vp, i64, _vp, _vp]),
+        "stepdllm_keep_count_columns": (i64, [D, dbl]),
+        "stepdllm_build_col_mask": (i32, [D, dbl, _vp, _vp, _vp, sz, _vp, _vp, _vp]),
+        "stepdllm_select_col_mask": (i32, [D, dbl, _vp, _vp, sz, _vp, _vp]),
+        "stepdllm_col_attn": (i32, [D, _vp, _vp, _vp, _vp, i64, _vp, _vp]),
         "stepdllm_driver_create": (i32, [ctypes.POINTER(_vp), D, ctypes.POINTER(Schedule), _vp,
                                          sz, _vp, _vp]),
         "stepdllm_driver_step_kind": (i32, [_vp, ctypes.c_int32]),
@@ -87,7 +92,8 @@ EXPORTS = ["stepdllm_keep_count", "stepdllm_workspace_bytes", "stepdllm_workspac
            "stepdllm_build_mask", "stepdllm_select_mask", "stepdllm_keep_count_per_head",
            "stepdllm_build_mask_per_head", "stepdllm_select_mask_per_head", "stepdllm_plan",
            "stepdllm_sparse_attn", "stepdllm_dense_attn", "stepdllm_block_mass",
-           "stepdllm_mask_recall", "stepdllm_driver_create",
+           "stepdllm_mask_recall", "stepdllm_keep_count_columns", "stepdllm_build_col_mask",
+           "stepdllm_select_col_mask", "stepdllm_col_attn", "stepdllm_driver_create",
            "stepdllm_driver_step_kind", "stepdllm_step", "stepdllm_driver_destroy",
            "stepdllm_status_string"]
 
@@ -211,24 +217,69 @@ def mask_recall(dims, mass, row_ptr, col_idx, recall, nnz=None, stream=None):
         _ptr(recall, torch.float32, "recall"), _stream(stream)), "stepdllm_mask_recall")
 
 
+def keep_count_columns(dims, sparsity):
+    """k_c: key columns kept per head by the column-sparse variant."""
+    r = load().stepdllm_keep_count_columns(ctypes.byref(dims), float(sparsity))
+    if r < 0:
+        raise StepDLLMError(int(r), "stepdllm_keep_count_columns")
+    return int(r)
+
+
+def build_col_mask(dims, sparsity, q, k, ws, cols, scores_out=None, stream=None):
+    """Column mask: per head the k_c kept key columns, ascending, into cols [H, k_c]."""
+    bf = torch.bfloat16
+    _check(load().stepdllm_build_col_mask(
+        ctypes.byref(dims), float(sparsity), _ptr(q, bf, "q"), _ptr(k, bf, "k"),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _ptr(cols, torch.int32, "cols"),
+        _ptr(scores_out, torch.float32, "scores_out"), _stream(stream)),
+        "stepdllm_build_col_mask")
+
+
+def select_col_mask(dims, sparsity, scores, ws, cols, stream=None):
+    _check(load().stepdllm_select_col_mask(
+        ctypes.byref(dims), float(sparsity), _ptr(scores, torch.float32, "scores"),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _ptr(cols, torch.int32, "cols"),
+        _stream(stream)), "stepdllm_select_col_mask")
+
+
+def col_attn(dims, q, k, v, cols, o, k_c=None, stream=None):
+    """Every query of head h over the key tokens cols[h] ([H, k_c] int32)."""
+    bf = torch.bfloat16
+    k_c = (cols.shape[-1] if cols.dim() == 2 else 0) if k_c is None else int(k_c)
+    _check(load().stepdllm_col_attn(
+        ctypes.byref(dims), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
+        _ptr(cols, torch.int32, "cols") if cols.numel() else None, k_c, _ptr(o, bf, "o"),
+        _stream(stream)), "stepdllm_col_attn")
+
+
 class Driver:
     """Owns the C driver handle; buffers are torch device tensors kept alive here."""
 
     def __init__(self, dims, dense_steps, refresh_every, sparsity, device="cuda",
-                 per_head_budget=False):
+                 per_head_budget=False, column_sparse=False):
         self.dims = dims
-        self.K = keep_count(dims, sparsity, per_head_budget)
+        self.column_sparse = bool(column_sparse)
+        if self.column_sparse:
+            self.k_c = keep_count_columns(dims, sparsity)
+            self.K = self.k_c * dims.n_q_heads
+        else:
+            self.K = keep_count(dims, sparsity, per_head_budget)
         rows = dims.n_q_heads * (dims.seq_len // dims.block)
         self.ws = torch.empty(workspace_bytes(dims), dtype=torch.uint8, device=device)
-        self.row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=device)
+        self.row_ptr = None if self.column_sparse else torch.empty(rows + 1, dtype=torch.int32,
+                                                                   device=device)
         self.col_idx = torch.empty(max(self.K, 1), dtype=torch.int32, device=device)
         self._h = _vp()
         sched = Schedule(int(dense_steps), int(refresh_every), float(sparsity),
-                         int(bool(per_head_budget)))
+                         int(bool(per_head_budget)), int(self.column_sparse))
         _check(load().stepdllm_driver_create(
             ctypes.byref(self._h), ctypes.byref(dims), ctypes.byref(sched), self.ws.data_ptr(),
-            self.ws.numel(), self.row_ptr.data_ptr(), self.col_idx.data_ptr()),
-            "stepdllm_driver_create")
+            self.ws.numel(), None if self.row_ptr is None else self.row_ptr.data_ptr(),
+            self.col_idx.data_ptr()), "stepdllm_driver_create")
+
+    def cols(self):
+        """Column mode: the kept columns [H, k_c] of the last anchor."""
+        return self.col_idx[:self.K].view(self.dims.n_q_heads, self.k_c)
 
     def step_kind(self, step):
         r = load().stepdllm_driver_step_kind(self._h, int(step))

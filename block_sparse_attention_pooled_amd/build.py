@@ -8,7 +8,8 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["mask_kernels.hip", "attn_kernels.hip", "quality_kernels.hip", "api.hip"]
+SOURCES = ["mask_kernels.hip", "attn_kernels.hip", "quality_kernels.hip", "col_kernels.hip",
+           "api.hip"]
 LIB = os.path.join(PKG, "libstepdllm.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 

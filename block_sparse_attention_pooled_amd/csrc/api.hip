@@ -61,6 +61,15 @@ int64_t keep_count_per_head(const Dims &D, double s) {
     return k > (int64_t)D.nb * D.nb ? (int64_t)D.nb * D.nb : k;
 }
 
+// Column-sparse variant: k_c of each head's L key columns.
+int64_t keep_count_columns(const Dims &D, double s) {
+    const double n = (double)D.L;
+    const double x = (1.0 - s) * n - 1e-9 * n;
+    if (x <= 0.0) return 0;
+    int64_t k = (int64_t)ceil(x);
+    return k > D.L ? D.L : k;
+}
+
 bool sparsity_ok(double s) { return s >= 0.0 && s < 1.0; }   // false for NaN
 
 int hip_status(hipError_t e) { return e == hipSuccess ? STEPDLLM_OK : STEPDLLM_EHIP; }
@@ -106,6 +115,36 @@ int select_mask(const stepdllm_dims *dims, double sparsity, bool per_head, const
                            col_idx, static_cast<hipStream_t>(stream));
 }
 
+int build_col_mask(const stepdllm_dims *dims, double sparsity, const uint16_t *q,
+                   const uint16_t *k, void *ws, size_t ws_bytes, int32_t *cols,
+                   float *scores_out, void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!sparsity_ok(sparsity) || !q || !k || !ws || !cols) return STEPDLLM_EINVAL;
+    WsLayout w = sd::ws_layout(D);
+    if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
+    char *base = static_cast<char *>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *qb = reinterpret_cast<float *>(base + w.qb);
+    float *c = scores_out ? scores_out : reinterpret_cast<float *>(base + w.col_scores);
+    if ((st = hip_status(sd::launch_pool_q(D, q, qb, s)))) return st;
+    if ((st = hip_status(sd::launch_col_scores(D, qb, k, base, w, c, s)))) return st;
+    return hip_status(
+        sd::launch_col_select(D, keep_count_columns(D, sparsity), c, base, w, cols, s));
+}
+
+int col_attn(const stepdllm_dims *dims, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+             const int32_t *cols, int64_t k_c, uint16_t *o, void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!q || !k || !v || !o || (k_c > 0 && !cols)) return STEPDLLM_EINVAL;
+    if (k_c < 0 || k_c > D.L) return STEPDLLM_EINVAL;
+    return hip_status(sd::launch_col_attn(D, q, k, v, cols, k_c, o,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 struct stepdllm_driver {
@@ -136,6 +175,14 @@ int64_t stepdllm_keep_count_per_head(const stepdllm_dims *dims, double sparsity)
     return keep_count_per_head(D, sparsity) * D.H;
 }
 
+int64_t stepdllm_keep_count_columns(const stepdllm_dims *dims, double sparsity) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!sparsity_ok(sparsity)) return STEPDLLM_EINVAL;
+    return keep_count_columns(D, sparsity);
+}
+
 int64_t stepdllm_workspace_bytes(const stepdllm_dims *dims) {
     Dims D;
     int st = check_dims(dims, &D);
@@ -156,6 +203,8 @@ int stepdllm_workspace_layout(const stepdllm_dims *dims, stepdllm_ws_layout *out
     out->work = w.work;
     out->work_meta = w.work_meta;
     out->head_select = w.hsel;
+    out->col_scores = w.col_scores;
+    out->col_stats = w.col_stats;
     out->total = w.total;
     return STEPDLLM_OK;
 }
@@ -223,6 +272,31 @@ int stepdllm_dense_attn(const stepdllm_dims *dims, const uint16_t *q, const uint
     return hip_status(sd::launch_dense_attn(D, q, k, v, o, static_cast<hipStream_t>(stream)));
 }
 
+int stepdllm_build_col_mask(const stepdllm_dims *dims, double sparsity, const uint16_t *q,
+                            const uint16_t *k, void *ws, size_t ws_bytes, int32_t *cols,
+                            float *scores_out, void *stream) {
+    return build_col_mask(dims, sparsity, q, k, ws, ws_bytes, cols, scores_out, stream);
+}
+
+int stepdllm_select_col_mask(const stepdllm_dims *dims, double sparsity, const float *scores,
+                             void *ws, size_t ws_bytes, int32_t *cols, void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!sparsity_ok(sparsity) || !scores || !ws || !cols) return STEPDLLM_EINVAL;
+    WsLayout w = sd::ws_layout(D);
+    if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
+    return hip_status(sd::launch_col_select(D, keep_count_columns(D, sparsity), scores,
+                                            static_cast<char *>(ws), w, cols,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int stepdllm_col_attn(const stepdllm_dims *dims, const uint16_t *q, const uint16_t *k,
+                      const uint16_t *v, const int32_t *cols, int64_t k_c, uint16_t *o,
+                      void *stream) {
+    return col_attn(dims, q, k, v, cols, k_c, o, stream);
+}
+
 int stepdllm_block_mass(const stepdllm_dims *dims, const uint16_t *q, const uint16_t *k,
                         float *mass, void *stream) {
     Dims D;
@@ -251,11 +325,14 @@ int stepdllm_driver_create(stepdllm_driver **out, const stepdllm_dims *dims,
     Dims D;
     int st = check_dims(dims, &D);
     if (st) return st;
-    if (!schedule || !ws || !row_ptr || !col_idx) return STEPDLLM_EINVAL;
+    if (!schedule || !ws || !col_idx) return STEPDLLM_EINVAL;
     if (!sparsity_ok(schedule->sparsity) || schedule->dense_steps < 0 ||
         schedule->refresh_every < 0 ||
-        (schedule->per_head_budget != 0 && schedule->per_head_budget != 1))
+        (schedule->per_head_budget != 0 && schedule->per_head_budget != 1) ||
+        (schedule->column_sparse != 0 && schedule->column_sparse != 1) ||
+        (schedule->column_sparse && schedule->per_head_budget))
         return STEPDLLM_EINVAL;
+    if (!schedule->column_sparse && !row_ptr) return STEPDLLM_EINVAL;
     if ((int64_t)ws_bytes < sd::ws_layout(D).total) return STEPDLLM_EWORKSPACE;
     stepdllm_driver *drv = static_cast<stepdllm_driver *>(malloc(sizeof(stepdllm_driver)));
     if (!drv) return STEPDLLM_EINVAL;
@@ -265,8 +342,9 @@ int stepdllm_driver_create(stepdllm_driver **out, const stepdllm_dims *dims,
     drv->ws_bytes = ws_bytes;
     drv->row_ptr = row_ptr;
     drv->col_idx = col_idx;
-    drv->K = schedule->per_head_budget ? keep_count_per_head(D, schedule->sparsity) * D.H
-                                       : keep_count(D, schedule->sparsity);
+    drv->K = schedule->column_sparse     ? keep_count_columns(D, schedule->sparsity)
+             : schedule->per_head_budget ? keep_count_per_head(D, schedule->sparsity) * D.H
+                                         : keep_count(D, schedule->sparsity);
     drv->have_mask = false;
     *out = drv;
     return STEPDLLM_OK;
@@ -289,13 +367,19 @@ int stepdllm_step(stepdllm_driver *drv, int32_t step, const uint16_t *q, const u
     stepdllm_dims dims = {drv->D.H, drv->D.Hkv, drv->D.L, drv->D.d, drv->D.B};
     if (kind == 0) return stepdllm_dense_attn(&dims, q, k, v, o, stream);
     if (kind == 1) {
-        int st = build_mask(&dims, drv->sched.sparsity, drv->sched.per_head_budget != 0, q, k,
-                            drv->ws, drv->ws_bytes, drv->row_ptr, drv->col_idx, nullptr, stream);
+        int st = drv->sched.column_sparse
+                     ? build_col_mask(&dims, drv->sched.sparsity, q, k, drv->ws, drv->ws_bytes,
+                                      drv->col_idx, nullptr, stream)
+                     : build_mask(&dims, drv->sched.sparsity, drv->sched.per_head_budget != 0, q,
+                                  k, drv->ws, drv->ws_bytes, drv->row_ptr, drv->col_idx, nullptr,
+                                  stream);
         if (st) return st;
         drv->have_mask = true;
     } else if (!drv->have_mask) {
         return STEPDLLM_ESTATE;
     }
+    if (drv->sched.column_sparse)
+        return col_attn(&dims, q, k, v, drv->col_idx, drv->K, o, stream);
     return stepdllm_sparse_attn(&dims, q, k, v, drv->row_ptr, drv->col_idx, drv->K, drv->ws,
                                 drv->ws_bytes, o, stream);
 }

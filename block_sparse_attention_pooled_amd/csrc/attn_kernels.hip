@@ -38,6 +38,14 @@
 //    staged through the (then free) rings so that every store writes whole
 //    rows: scattered 8-byte stores from the accumulator layout cost the
 //    memory path far more than their bytes.
+//
+// Column mode: the column-sparse variant ("PulseCol", abstract: individual
+// key columns kept instead of blocks).  Every query of head h attends to the
+// k_c key tokens listed for the head; a chunk is 32 consecutive list entries
+// and each lane's rows of a K/V tile are gathered by buffer->LDS loads whose
+// per-lane offsets come from the list.  The list entries a step needs are
+// loaded one step ahead; a short last chunk has its missing keys' scores set
+// to -inf, so they get weight 0.
 #include "common.h"
 
 namespace sd {
@@ -53,6 +61,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kChunk = 32;          // keys per wave step
 constexpr int kQW = 32;             // query rows per wave
+
+// Which keys a row walks.
+constexpr int kModeSparse = 0;      // the kept blocks of the row (CSR lists, work order)
+constexpr int kModeDense = 1;       // every key block
+constexpr int kModeCols = 2;        // the head's kept key columns (col_idx = [H, n_idx])
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
@@ -80,7 +93,7 @@ __device__ __forceinline__ int swz_v(int row) {
     return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
-template <int D, int BLK, int QW, bool DENSE>
+template <int D, int BLK, int QW, int MODE>
 __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ row_ptr,
@@ -96,6 +109,8 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     constexpr int NSEG = D / 8;                 // 16-byte segments per row
     constexpr int ROWS_PER_LOAD = 64 / NSEG;    // rows covered by one wave load
     constexpr int LOADS = kChunk / ROWS_PER_LOAD;   // wave loads per tile
+    constexpr bool SPARSE = MODE == kModeSparse;
+    constexpr bool COLS = MODE == kModeCols;
     // A three-stage K ring and a two-stage V ring, shared by the WQ waves of
     // the workgroup.
     __shared__ __attribute__((aligned(16))) uint16_t rings[5 * TILE];
@@ -110,7 +125,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
 
     // Row of this workgroup.
     int row;
-    if (DENSE) {
+    if (!SPARSE) {
         const int b = blockIdx.x;
         if ((H & 7) == 0) {   // keep each head's rows on one XCD (round-robin dispatch)
             const int x = b & 7, kk = b >> 3;
@@ -131,11 +146,15 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     const int64_t kvbase = (int64_t)g * L * D;
 
     int e_begin = 0, e_end = nb;
-    if (!DENSE) {
+    if (SPARSE) {
         e_begin = max(__builtin_amdgcn_readfirstlane(row_ptr[row]), 0);
         e_end = min(__builtin_amdgcn_readfirstlane(row_ptr[row + 1]), n_idx);
     }
-    if (e_end <= e_begin) {     // no kept block: the row attends to nothing
+    // The row's chunks: every 32-key chunk of every kept block e, in order
+    // (column mode: 32 consecutive entries of the head's column list).
+    const int n_total = COLS ? (n_idx + kChunk - 1) / kChunk
+                             : (e_end > e_begin ? (e_end - e_begin) * CPB : 0);
+    if (n_total <= 0) {     // no kept key: the row attends to nothing
         const uint4 z = make_uint4(0, 0, 0, 0);
         for (int x = lane; x < QW * D / 8; x += 64)
             *reinterpret_cast<uint4 *>(o + qbase + (int64_t)x * 8) = z;
@@ -156,7 +175,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     // also wait on every LDS read in flight).  Loaded after Q, so the first
     // wait on them also retires the Q loads before the loop.
     int ids = 0, ids_grp = 0;
-    if (!DENSE) {
+    if (SPARSE) {
         const int e = e_begin + lane;
         ids = e < e_end ? col_idx[e] : 0;
     }
@@ -175,12 +194,10 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         l_run[nt] = 0.0f;
     }
 
-    // The row's chunks: every 32-key chunk of every kept block e, in order.
-    const int n_total = (e_end - e_begin) * CPB;
     auto chunk_key0 = [&](int n) -> int {
         const int e_rel = n / CPB;
         int j;
-        if (DENSE) {
+        if (!SPARSE) {
             j = e_begin + e_rel;
         } else {
             const int grp = e_rel >> 6;
@@ -233,6 +250,47 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
             load_lds16(v_rsrc, vring + st * TILE + t * 512, v_voff,
                        off + t * ROWS_PER_LOAD * D * 2);
         }
+    };
+    // Column mode: list entry 32*c + r is the token of row r of chunk c.  A
+    // lane's row in its wave load tt is (tt*WQ + wq)*ROWS_PER_LOAD + r_in;
+    // entries past the list read 0 (a valid token whose weight is masked).
+    const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(col_idx + (COLS ? (int64_t)h * n_idx : 0)), 0, COLS ? n_idx * 4 : 0,
+        0x00020000);
+    const uint32_t tok_voff = (uint32_t)((wq * ROWS_PER_LOAD + r_in) * 4);
+    auto load_tok = [&](int c, int (&tok)[MY_LOADS]) {
+#pragma unroll
+        for (int tt = 0; tt < MY_LOADS; ++tt)
+            tok[tt] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+                c_rsrc, tok_voff + tt * WQ * ROWS_PER_LOAD * 4, c * kChunk * 4, 0);
+    };
+    // Gathered rows: the token's row in the key head, at the segment the
+    // contiguous loads would use.  Tokens outside the head read zeros.
+    auto issue_k_tok = [&](const int (&tok)[MY_LOADS], int st) {
+#pragma unroll
+        for (int tt = 0; tt < MY_LOADS; ++tt) {
+            const int t = tt * WQ + wq;
+            load_lds16(k_rsrc, kring + st * TILE + t * 512,
+                       (uint32_t)tok[tt] * (D * 2) + (k_voff[tt] - r_in * D * 2), 0);
+        }
+    };
+    auto issue_v_tok = [&](const int (&tok)[MY_LOADS], int st) {
+#pragma unroll
+        for (int tt = 0; tt < MY_LOADS; ++tt) {
+            const int t = tt * WQ + wq;
+            load_lds16(v_rsrc, vring + st * TILE + t * 512,
+                       (uint32_t)tok[tt] * (D * 2) + (v_voff - r_in * D * 2), 0);
+        }
+    };
+    // Valid keys of the last chunk (column mode); accumulator i of a lane is
+    // key 8*(i/4) + 4*hh + i%4 of the chunk.
+    const int tail = COLS ? n_idx - (n_total - 1) * kChunk : kChunk;
+    auto mask_tail = [&](f32x16 (&sacc)[NT]) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (8 * (i >> 2) + 4 * hh + (i & 3) >= tail) sacc[nt][i] = -INFINITY;
     };
 
     // K as the A operand of the score product: lane row = key col, dims
@@ -374,6 +432,9 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     // read wait for every buffer->LDS load in flight.  FULL steps have every
     // chunk up to n+3; the last steps are guarded.
     bf16x8 kf[KS];
+    // Column mode: tokens of the next V load (chunk n+1) and K load (chunk
+    // n+3), loaded during the previous step.
+    int tok_v[MY_LOADS], tok_k[MY_LOADS];
     auto step = [&](int n, bool full, f32x16 (&s_cur)[NT], f32x16 (&s_next)[NT]) {
         const bool has1 = full || n + 1 < n_total;
         const bool has2 = full || n + 2 < n_total;
@@ -381,16 +442,24 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         sync();
         // Keys of the next loads first: a reload of the ids waits on vector
         // memory, which is idle right after the sync.
-        const int key1 = has1 ? chunk_key0(n + 1) : 0;
-        const int key3 = has3 ? chunk_key0(n + 3) : 0;
+        const int key1 = (!COLS && has1) ? chunk_key0(n + 1) : 0;
+        const int key3 = (!COLS && has3) ? chunk_key0(n + 3) : 0;
         bf16x8 vf[MT][2];
         bf16x8 pf[NT][2];
         read_v(n & 1, vf);
         if (has1) scores(kf, s_next);
+        if (COLS && has1 && n + 1 == n_total - 1 && tail < kChunk) mask_tail(s_next);
         weights(s_cur, pf);
         if (has2) read_k((n + 2) % 3, kf);
-        if (has1) issue_v(key1, (n + 1) & 1);
-        if (has3) issue_k(key3, n % 3);
+        if (COLS) {
+            if (has1) issue_v_tok(tok_v, (n + 1) & 1);
+            if (has3) issue_k_tok(tok_k, n % 3);
+            if (n + 2 < n_total) load_tok(n + 2, tok_v);
+            if (n + 4 < n_total) load_tok(n + 4, tok_k);
+        } else {
+            if (has1) issue_v(key1, (n + 1) & 1);
+            if (has3) issue_k(key3, n % 3);
+        }
         pv(vf, pf);
         if (has1) update_max(s_next);
     };
@@ -398,7 +467,17 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     f32x16 sA[NT], sB[NT];
     // Prologue: K(0..2) and V(0) in flight; S(0) and its max; K(1) into
     // registers.
-    {
+    if (COLS) {
+        int t0[MY_LOADS], t2[MY_LOADS];
+        load_tok(0, t0);
+        load_tok(1, tok_v);
+        load_tok(2, t2);
+        load_tok(3, tok_k);
+        issue_k_tok(t0, 0);
+        issue_v_tok(t0, 0);
+        if (n_total > 1) issue_k_tok(tok_v, 1);
+        if (n_total > 2) issue_k_tok(t2, 2);
+    } else {
         const int key0 = chunk_key0(0);
         issue_k(key0, 0);
         issue_v(key0, 0);
@@ -408,6 +487,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     sync();
     read_k(0, kf);
     scores(kf, sA);
+    if (COLS && n_total == 1 && tail < kChunk) mask_tail(sA);
     if (n_total > 1) read_k(1, kf);
     update_max(sA);
 
@@ -467,30 +547,30 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     }
 }
 
-template <int D, int BLK, int QW, bool DENSE>
+template <int D, int BLK, int QW, int MODE>
 hipError_t launch_attn_t(const Dims &Dm, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const int32_t *row_ptr, const int32_t *col_idx, const int32_t *work,
                          int n_idx, uint16_t *o, hipStream_t s) {
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int64_t cap = Dm.die_cap();
-    const unsigned grid = (unsigned)(DENSE ? Dm.rows() : kDies * cap);
-    hipLaunchKernelGGL((k_attn<D, BLK, QW, DENSE>), dim3(grid), dim3(BLK / QW * 64),
+    const unsigned grid = (unsigned)(MODE != kModeSparse ? Dm.rows() : kDies * cap);
+    hipLaunchKernelGGL((k_attn<D, BLK, QW, MODE>), dim3(grid), dim3(BLK / QW * 64),
                        0, s, q, k, v, row_ptr, col_idx, work, o, Dm.L, Dm.nb, Dm.G, Dm.H,
                        n_idx, cap, scale_log2);
     return hipGetLastError();
 }
 
-template <bool DENSE>
+template <int MODE>
 hipError_t launch_attn(const Dims &D, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                        const int32_t *row_ptr, const int32_t *col_idx, const int32_t *work,
                        int n_idx, uint16_t *o, hipStream_t s) {
     if (D.d == 128 && D.B == 64)
-        return launch_attn_t<128, 64, kQW, DENSE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
+        return launch_attn_t<128, 64, kQW, MODE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
     if (D.d == 128 && D.B == 128)
-        return launch_attn_t<128, 128, kQW, DENSE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
+        return launch_attn_t<128, 128, kQW, MODE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
     if (D.d == 64 && D.B == 64)
-        return launch_attn_t<64, 64, kQW, DENSE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
-    return launch_attn_t<64, 128, kQW, DENSE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
+        return launch_attn_t<64, 64, kQW, MODE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
+    return launch_attn_t<64, 128, kQW, MODE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
 }
 
 }  // namespace
@@ -498,12 +578,18 @@ hipError_t launch_attn(const Dims &D, const uint16_t *q, const uint16_t *k, cons
 hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                               const uint16_t *v, const int32_t *row_ptr, const int32_t *col_idx,
                               const int32_t *work, int64_t n_idx, uint16_t *o, hipStream_t s) {
-    return launch_attn<false>(D, q, k, v, row_ptr, col_idx, work, (int)n_idx, o, s);
+    return launch_attn<kModeSparse>(D, q, k, v, row_ptr, col_idx, work, (int)n_idx, o, s);
 }
 
 hipError_t launch_dense_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                              const uint16_t *v, uint16_t *o, hipStream_t s) {
-    return launch_attn<true>(D, q, k, v, nullptr, nullptr, nullptr, 0, o, s);
+    return launch_attn<kModeDense>(D, q, k, v, nullptr, nullptr, nullptr, 0, o, s);
+}
+
+hipError_t launch_col_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
+                           const uint16_t *v, const int32_t *cols, int64_t k_c, uint16_t *o,
+                           hipStream_t s) {
+    return launch_attn<kModeCols>(D, q, k, v, nullptr, cols, nullptr, (int)k_c, o, s);
 }
 
 }  // namespace sd

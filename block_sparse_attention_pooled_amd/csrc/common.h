@@ -40,7 +40,8 @@ struct Dims {
 
 // Workspace carve-up (byte offsets, 256-byte aligned).
 struct WsLayout {
-    int64_t qb, kb, p, hist, sel, gt, eq, tie_base, work, work_meta, hsel, total;
+    int64_t qb, kb, p, hist, sel, gt, eq, tie_base, work, work_meta, hsel, col_scores, col_stats,
+        total;
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -60,6 +61,8 @@ inline WsLayout ws_layout(const Dims &D) {
     w.work = take(kDies * D.die_cap() * 4);
     w.work_meta = take(16 * 4);
     w.hsel = take((int64_t)D.H * kHeadSelWords * 4);
+    w.col_scores = take((int64_t)D.H * D.L * 4);   // column masses (column-sparse variant)
+    w.col_stats = take(D.rows() * 8);              // per pooled query: max, normaliser
     w.total = off;
     return w;
 }
@@ -88,6 +91,16 @@ hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, ch
 hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, char *ws, const WsLayout &w,
                        hipStream_t s);
 
+// Column-sparse variant.  Block means of Q only (mask_kernels.hip).
+hipError_t launch_pool_q(const Dims &D, const uint16_t *q, float *qb, hipStream_t s);
+// Per head, the k_c largest of the head's L column masses c, listed ascending
+// in cols [H, k_c] (mask_kernels.hip).
+hipError_t launch_col_select(const Dims &D, int64_t k_c, const float *c, char *ws,
+                             const WsLayout &w, int32_t *cols, hipStream_t s);
+// Column masses c [H, L] of the pooled queries qb (col_kernels.hip).
+hipError_t launch_col_scores(const Dims &D, const float *qb, const uint16_t *k, char *ws,
+                             const WsLayout &w, float *c, hipStream_t s);
+
 // Mask quality launches (quality_kernels.hip).
 hipError_t launch_block_mass(const Dims &D, const uint16_t *q, const uint16_t *k, float *mass,
                              hipStream_t s);
@@ -101,5 +114,9 @@ hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *
                               const int32_t *work, int64_t n_idx, uint16_t *o, hipStream_t s);
 hipError_t launch_dense_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                              const uint16_t *v, uint16_t *o, hipStream_t s);
+// Every query of head h over the key tokens cols[h*k_c .. h*k_c + k_c).
+hipError_t launch_col_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
+                           const uint16_t *v, const int32_t *cols, int64_t k_c, uint16_t *o,
+                           hipStream_t s);
 
 }  // namespace sd

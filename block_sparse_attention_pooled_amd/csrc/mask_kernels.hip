@@ -354,13 +354,12 @@ __global__ __launch_bounds__(256) void k_row_scatter(const float *__restrict__ p
 // One workgroup per head: the k_h-th largest order key of the head's nb*nb
 // scores by the same three digit passes, with the histogram in LDS.  State
 // words at hsel[h * kHeadSelWords]: cut key, count above it, ties to keep, k_h.
-__global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ p, int nb,
+__global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ p, int64_t per,
                                                       int64_t k_h,
                                                       uint32_t *__restrict__ hsel) {
     __shared__ uint32_t hist[kRadixBins];
     __shared__ uint32_t win[2];
     const int h = blockIdx.x, tid = threadIdx.x;
-    const int64_t per = (int64_t)nb * nb;
     const float *ph = p + (int64_t)h * per;
     uint32_t *out = hsel + (int64_t)h * kHeadSelWords;
     if (k_h <= 0) {   // nothing kept: no score is above the cut, no tie is kept
@@ -449,6 +448,47 @@ __global__ __launch_bounds__(1024) void k_kept_scan(const int32_t *__restrict__ 
         out += kept[r];
     }
     if (threadIdx.x == 0) row_ptr[rows] = (int32_t)total;
+}
+
+// ------------------------------------------------------------ column lists --
+// Column-sparse variant ("PulseCol" abstract: column-sparse attention): head
+// h keeps the k_c largest of its L column masses, the per-head select state
+// (cut key, ties kept at the cut) coming from k_head_select.  One workgroup
+// per head; thread t owns a contiguous run of columns.  Ties at the cut are
+// kept in ascending column order, so the kept set is the top-k_c under
+// (value descending, index ascending) and the list comes out ascending.
+__global__ __launch_bounds__(1024) void k_col_compact(const float *__restrict__ c, int L,
+                                                      const uint32_t *__restrict__ hsel,
+                                                      int64_t k_c, int32_t *__restrict__ cols) {
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const float *ch = c + (int64_t)h * L;
+    const uint32_t cut = hsel[(int64_t)h * kHeadSelWords + SEL_CUT];
+    const int64_t ties = hsel[(int64_t)h * kHeadSelWords + SEL_TIES];
+    const int per = (L + 1023) / 1024;
+    const int lo = min(L, tid * per), hi = min(L, lo + per);
+    int64_t n_eq = 0;
+    for (int u = lo; u < hi; ++u) n_eq += order_key(ch[u]) == cut;
+    int64_t total;
+    const int64_t eq_before = block_exclusive_scan_1024(n_eq, &total);
+    int64_t n_keep = 0, e = eq_before;
+    for (int u = lo; u < hi; ++u) {
+        const uint32_t key = order_key(ch[u]);
+        if (key > cut) {
+            ++n_keep;
+        } else if (key == cut) {
+            n_keep += e < ties;
+            ++e;
+        }
+    }
+    int64_t out = block_exclusive_scan_1024(n_keep, &total);
+    int32_t *dst = cols + (int64_t)h * k_c;
+    e = eq_before;
+    for (int u = lo; u < hi; ++u) {
+        const uint32_t key = order_key(ch[u]);
+        bool keep = key > cut;
+        if (key == cut) keep = e++ < ties;
+        if (keep && out < k_c) dst[out++] = u;
+    }
 }
 
 // --------------------------------------------------------------------- plan --
@@ -619,6 +659,27 @@ hipError_t launch_pool(const Dims &D, const uint16_t *q, const uint16_t *k, floa
     return hipGetLastError();
 }
 
+hipError_t launch_pool_q(const Dims &D, const uint16_t *q, float *qb, hipStream_t s) {
+    const int64_t nq = (int64_t)D.H * D.nb * (D.d / 8);
+    const int64_t grid = (nq + 255) / 256;
+    if (D.d == 128)
+        hipLaunchKernelGGL(k_pool<128>, dim3((unsigned)grid), dim3(256), 0, s, q, nullptr, qb,
+                           nullptr, D.L, D.B, nq, (int64_t)0);
+    else
+        hipLaunchKernelGGL(k_pool<64>, dim3((unsigned)grid), dim3(256), 0, s, q, nullptr, qb,
+                           nullptr, D.L, D.B, nq, (int64_t)0);
+    return hipGetLastError();
+}
+
+hipError_t launch_col_select(const Dims &D, int64_t k_c, const float *c, char *ws,
+                             const WsLayout &w, int32_t *cols, hipStream_t s) {
+    uint32_t *hsel = reinterpret_cast<uint32_t *>(ws + w.hsel);
+    hipLaunchKernelGGL(k_head_select, dim3(D.H), dim3(1024), 0, s, c, (int64_t)D.L, k_c, hsel);
+    if (k_c > 0)
+        hipLaunchKernelGGL(k_col_compact, dim3(D.H), dim3(1024), 0, s, c, D.L, hsel, k_c, cols);
+    return hipGetLastError();
+}
+
 hipError_t launch_scores(const Dims &D, const float *qb, const float *kb, float *p, float *copy,
                          hipStream_t s) {
     const int tiles = (D.nb + kScoreRows - 1) / kScoreRows;
@@ -667,7 +728,8 @@ hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, ch
     int32_t *tie_base = reinterpret_cast<int32_t *>(ws + w.tie_base);
     const int64_t rows = D.rows();
     const unsigned row_grid = (unsigned)((rows + 3) / 4);
-    hipLaunchKernelGGL(k_head_select, dim3(D.H), dim3(1024), 0, s, p, D.nb, k_h, hsel);
+    hipLaunchKernelGGL(k_head_select, dim3(D.H), dim3(1024), 0, s, p, (int64_t)D.nb * D.nb, k_h,
+                       hsel);
     hipLaunchKernelGGL(k_row_count, dim3(row_grid), dim3(256), 0, s, p, D.nb, rows,
                        (int64_t)D.nb, hsel, gt, eq);
     hipLaunchKernelGGL(k_head_ties, dim3(D.H), dim3(1024), 0, s, gt, eq, D.nb, hsel, tie_base);

@@ -15,6 +15,9 @@
  *    sparse pattern computed once and reused for all later steps.
  *  - "Block Approximate Sparse Attention (BA-Att)" abstract: blocks are
  *    selected in a block-wise pre-downsampled (pooled) space.
+ *  - "PulseCol" abstract: periodically refreshed column-sparse attention
+ *    (individual key columns kept instead of blocks); the column-sparse
+ *    entry points below.
  * The pages leave the block score open; this library scores a (query block,
  * key block) pair by the mean-pooled queries and keys, Qb . Kb^T / sqrt(d),
  * softmaxed over key blocks per (head, query block), and keeps the
@@ -79,6 +82,11 @@ typedef struct {
     int32_t per_head_budget;  /* 0: head-adaptive global budget (Step-dLLM);
                                  1: the uniform per-head budget it is compared
                                  with (see stepdllm_build_mask_per_head) */
+    int32_t column_sparse;    /* 0: block mask; 1: column mask (PulseCol
+                                 variant): anchors run stepdllm_build_col_mask,
+                                 sparse steps stepdllm_col_attn; col_idx holds
+                                 H * k_c entries, row_ptr is unused (may be
+                                 NULL); per_head_budget must be 0 */
 } stepdllm_schedule;
 
 /* Byte offsets of the intermediates inside a workspace (read-only views for
@@ -95,7 +103,12 @@ typedef struct {
     int64_t work_meta;  /* int32 [16]: [0] cap, [1] number of non-empty rows      */
     int64_t head_select;/* uint32 [H, 8]: per-head select state under the uniform
                            budget: [h*8 + 0] cut key, [+1] count above the cut,
-                           [+2] ties kept at the cut, [+3] k_h                    */
+                           [+2] ties kept at the cut, [+3] k_h; the column mask
+                           uses it with k_c                                       */
+    int64_t col_scores; /* fp32 [H, L]: column masses of the last column mask
+                           built without scores_out                               */
+    int64_t col_stats;  /* fp32 [H, nb, 2]: per pooled query, max (log2 units)
+                           and normaliser of its scores over all keys             */
     int64_t total;      /* == stepdllm_workspace_bytes()                          */
 } stepdllm_ws_layout;
 
@@ -190,6 +203,46 @@ int stepdllm_dense_attn(const stepdllm_dims *dims, const uint16_t *q,
                         const uint16_t *k, const uint16_t *v, uint16_t *o,
                         void *stream);
 
+/* Column-sparse variant ("PulseCol" abstract: column-sparse attention whose
+ * pattern is found at an early step, reused, and refreshed at a few
+ * intermediate steps).  The page leaves the column score open; the reading
+ * here mirrors the block path's pooled scoring:
+ *   c[h,u] = (1/nb) sum_i softmax_u(qb[h,i] . k_u / sqrt(d))
+ * over all L key tokens u of key head h / (H/Hkv), qb[h,i] the mean of query
+ * block i rounded to bf16; each head keeps the same number
+ * k_c = ceil((1 - s) * L) of its columns (a guard of 1e-9 * L is subtracted
+ * first), largest mass first, ties by lowest column, and every query of the
+ * head attends to exactly those key tokens.
+ * Host only.  Returns k_c, or a negative status. */
+int64_t stepdllm_keep_count_columns(const stepdllm_dims *dims, double sparsity);
+
+/* Column mask of one step: q [H,L,d], k [Hkv,L,d] bf16 -> cols int32
+ * [H, k_c] (out; head h's kept columns, ascending).  scores_out (nullable):
+ * fp32 [H, L] receives c (otherwise c stays in the workspace).  Masses on
+ * bf16 MFMA with fp32 accumulation, exact per-pooled-query max and normaliser
+ * (two passes over the keys), deterministic.  Uses the workspace. */
+int stepdllm_build_col_mask(const stepdllm_dims *dims, double sparsity,
+                            const uint16_t *q, const uint16_t *k,
+                            void *ws, size_t ws_bytes, int32_t *cols,
+                            float *scores_out, void *stream);
+
+/* The selection half on caller-given masses scores [H, L] fp32 (finite):
+ * per head the k_c largest (ties by lowest column), ascending in cols. */
+int stepdllm_select_col_mask(const stepdllm_dims *dims, double sparsity,
+                             const float *scores, void *ws, size_t ws_bytes,
+                             int32_t *cols, void *stream);
+
+/* Column-sparse attention: every token t of head h attends to the key tokens
+ * cols[h*k_c .. h*k_c + k_c) of key head h / (H/Hkv),
+ *   o_t = sum_a softmax_a(q_t . k_{cols[a]} / sqrt(d)) v_{cols[a]},
+ * k_c in [0, L] (0 gives zeros).  Entries are expected in [0, L); any other
+ * entry reads zero K and V rows (no fault, output unspecified).  Same
+ * arithmetic as stepdllm_sparse_attn; K/V rows are gathered per entry. */
+int stepdllm_col_attn(const stepdllm_dims *dims, const uint16_t *q,
+                      const uint16_t *k, const uint16_t *v,
+                      const int32_t *cols, int64_t k_c, uint16_t *o,
+                      void *stream);
+
 /* Mask quality (a diagnostic, off the per-step path).  The BA-Att abstract
  * compares block selection in the pooled, pre-downsampled space with the
  * block map of the exact attention; Step-dLLM reuses one mask across a
@@ -214,7 +267,8 @@ int stepdllm_mask_recall(const stepdllm_dims *dims, const float *mass,
                          int64_t nnz, float *recall, void *stream);
 
 /* Step driver: a small host object owned by the library; device buffers
- * (workspace, row_ptr [H*nb+1], col_idx [K]) stay owned by the caller and
+ * (workspace, row_ptr [H*nb+1], col_idx [K]; column mode: col_idx [H*k_c]
+ * and no row_ptr) stay owned by the caller and
  * must outlive the driver.  stepdllm_step runs what the schedule asks for at
  * step `step` (dense / anchor: build mask + sparse / reuse: sparse) and
  * returns STEPDLLM_ESTATE for a reuse step before any anchor.  A driver is

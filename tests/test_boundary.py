@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = B.load()
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(B.EXPORTS) == names
@@ -90,7 +90,21 @@ def test_workspace_layout():
         assert lay.total == B.workspace_bytes(d)
         assert lay.scores - lay.pooled_k >= w.Hkv * w.nb * w.d * 4
         assert lay.select - lay.scores >= w.H * w.nb * w.nb * 4
-        assert lay.total - lay.head_select >= w.H * 8 * 4
+        assert lay.col_scores - lay.head_select >= w.H * 8 * 4
+        assert lay.col_stats - lay.col_scores >= w.H * w.L * 4
+        assert lay.total - lay.col_stats >= w.H * w.nb * 8
+        assert lay.head_select < lay.col_scores < lay.col_stats < lay.total
+        assert lay.col_scores % 256 == 0 and lay.col_stats % 256 == 0
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_column_keep_count_matches_exact_rationals(name, olib):
+    import oracle as O
+    w = WORKLOADS[name]
+    for s in w.sparsities:
+        k_c = math.ceil((1 - Fraction(str(s))) * w.L)
+        assert O.keep_count(w.L, s, olib) == k_c
+        assert B.keep_count_columns(dims(w.H, w.Hkv, w.L, w.d, w.B), s) == k_c
 
 
 def test_entry_points_reject_bad_arguments_before_launch():
@@ -111,6 +125,20 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.stepdllm_block_mass(r(dims(2, 2, 256, 80, 64)), FAKE, FAKE, FAKE, None) == B.EUNSUPPORTED
     assert lib.stepdllm_mask_recall(r(d), FAKE, FAKE, FAKE, 33, FAKE, None) == B.EINVAL
     assert lib.stepdllm_mask_recall(r(d), FAKE, None, FAKE, 16, FAKE, None) == B.EINVAL
+    # column-sparse entry points
+    assert lib.stepdllm_keep_count_columns(r(d), 1.0) == B.EINVAL
+    assert lib.stepdllm_keep_count_columns(r(d), 0.0) == 256
+    assert lib.stepdllm_build_col_mask(r(d), 0.5, FAKE, None, FAKE, ws_need, FAKE, None, None) == B.EINVAL
+    assert lib.stepdllm_build_col_mask(r(d), 0.5, FAKE, FAKE, FAKE, ws_need, None, None, None) == B.EINVAL
+    assert lib.stepdllm_build_col_mask(r(d), 0.5, FAKE, FAKE, FAKE, ws_need - 1, FAKE, None, None) == B.EWORKSPACE
+    assert lib.stepdllm_build_col_mask(r(d), 1.0, FAKE, FAKE, FAKE, ws_need, FAKE, None, None) == B.EINVAL
+    assert lib.stepdllm_select_col_mask(r(d), 0.5, None, FAKE, ws_need, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_select_col_mask(r(d), 0.5, FAKE, FAKE, 8, FAKE, None) == B.EWORKSPACE
+    assert lib.stepdllm_col_attn(r(d), FAKE, FAKE, FAKE, FAKE, 257, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_col_attn(r(d), FAKE, FAKE, FAKE, FAKE, -1, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_col_attn(r(d), FAKE, FAKE, FAKE, None, 4, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_col_attn(r(d), FAKE, FAKE, None, FAKE, 4, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_col_attn(r(dims(2, 2, 256, 80, 64)), FAKE, FAKE, FAKE, FAKE, 4, FAKE, None) == B.EUNSUPPORTED
     # sparsity out of range
     for s in (-0.5, 1.0, float("nan")):
         assert lib.stepdllm_build_mask(r(d), s, FAKE, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL
@@ -126,13 +154,13 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.stepdllm_dense_attn(r(bad), FAKE, FAKE, FAKE, FAKE, None) == B.EUNSUPPORTED
 
 
-def _driver(d, dense, every, s, ws_bytes=None, per_head=0):
+def _driver(d, dense, every, s, ws_bytes=None, per_head=0, columns=0, row_ptr=FAKE):
     lib = B.load()
     h = ctypes.c_void_p()
-    sched = B.Schedule(dense, every, s, per_head)
+    sched = B.Schedule(dense, every, s, per_head, columns)
     st = lib.stepdllm_driver_create(ctypes.byref(h), ctypes.byref(d), ctypes.byref(sched), FAKE,
                                     B.workspace_bytes(d) if ws_bytes is None else ws_bytes,
-                                    FAKE, FAKE)
+                                    row_ptr, FAKE)
     return st, h
 
 
@@ -171,6 +199,16 @@ def test_driver_rejects_reuse_before_anchor_and_bad_schedules():
     st, h = _driver(d, 0, 4, 0.5, per_head=1)
     assert st == B.OK
     lib.stepdllm_driver_destroy(h)
+    # Column mode: no row_ptr needed; the per-head block budget does not apply.
+    assert _driver(d, 0, 4, 0.5, columns=2)[0] == B.EINVAL
+    assert _driver(d, 0, 4, 0.5, columns=1, per_head=1)[0] == B.EINVAL
+    assert _driver(d, 0, 4, 0.5, row_ptr=None)[0] == B.EINVAL
+    st, h = _driver(d, 0, 4, 0.5, columns=1, row_ptr=None)
+    assert st == B.OK
+    try:
+        assert lib.stepdllm_step(h, 1, FAKE, FAKE, FAKE, FAKE, None) == B.ESTATE
+    finally:
+        lib.stepdllm_driver_destroy(h)
 
 
 def test_status_strings():
