@@ -27,10 +27,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "block-sparse attn ms/step + effective TFLOP/s, L=8192 H=32 d=128 90% sparse"
+METRIC_COLS = ("column-sparse attn (PulseCol variant) ms/step + effective TFLOP/s, "
+               "L=8192 H=32 d=128 90% of key columns dropped")
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_pooled_amd", "csrc", "attn_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_stepdllm_8k_traffic.json")
+TRAFFIC_FILE_COLS = os.path.join(ROOT, "profiles", "col_attn_stepdllm_8k_traffic.json")
 
 
 def parse_args():
@@ -52,6 +55,9 @@ def parse_args():
     p.add_argument("--per-head-budget", action="store_true",
                    help="uniform per-head budget (the baseline the head-adaptive one is "
                         "compared with) instead of the global budget")
+    p.add_argument("--columns", action="store_true",
+                   help="the column-sparse variant (PulseCol): per head the ceil((1-s)L) key "
+                        "columns of largest pooled-query mass, refreshed at the same anchors")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (for counter calibration)")
     return p.parse_args()
@@ -61,11 +67,11 @@ def src_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def traffic_record():
+def traffic_record(path=TRAFFIC_FILE):
     """HBM bytes per attention launch from committed counter runs, if they were
     taken on the current kernel source; else None."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != src_sha(ATTN_SRC):
@@ -116,6 +122,49 @@ def cpu_baseline(inputs0, w, sparsity, flops_per_step, budget_s, per_head=False)
                    f"{period} steps) + fp64 sparse attention on {done_rows} of {nonempty.size} "
                    f"non-empty rows ({done_pairs} of {K} kept blocks, {t_attn:.2f} s), "
                    f"extrapolated to one step by kept blocks"),
+        "ms_per_step": round(t_step * 1e3, 3),
+    }
+
+
+def cpu_baseline_cols(inputs0, w, sparsity, flops_per_step, budget_s):
+    """The column-sparse variant's oracle on the host cores: one full column
+    mask build on step-0 Q/K plus attention on a deterministic sample of query
+    blocks, extrapolated to one step by query blocks (the mask build amortised
+    over the refresh period)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import oracle as O
+    from block_sparse_attention_pooled_amd.inputs import to_host_f32
+
+    q, k, v = (to_host_f32(x) for x in inputs0)
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    _, cols, k_c = O.build_col_mask(q, k, w.B, sparsity)
+    t_mask = time.perf_counter() - t0
+    rows_all = w.H * w.nb
+    order = np.random.default_rng(w.seed).permutation(rows_all)
+    out = np.zeros(q.shape, np.float64)
+    done = 0
+    batch = threads * 2
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        while done < rows_all and time.perf_counter() - t0 < budget_s:
+            chunk = order[done:done + batch]
+            list(ex.map(lambda r: O.col_attn(q, k, v, w.B, cols, rows=[int(r)], out=out), chunk))
+            done += chunk.size
+    t_attn = time.perf_counter() - t0
+    period = w.refresh_every if w.refresh_every > 0 else w.steps
+    t_step = t_attn * rows_all / max(done, 1) + t_mask / period
+    return {
+        "value": round(flops_per_step / t_step / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"one full column mask build on the step-0 Q/K ({t_mask:.2f} s, amortised "
+                   f"over {period} steps) + fp64 column attention on {done} of {rows_all} "
+                   f"query blocks ({k_c} columns per head, {t_attn:.2f} s), extrapolated to "
+                   f"one step by query blocks"),
         "ms_per_step": round(t_step * 1e3, 3),
     }
 
@@ -220,6 +269,10 @@ def main():
     if args.mask_quality:
         mask_quality(args, w, sparsity, dev, T)
         return
+    if args.columns and args.per_head_budget:
+        print("bench.py: --columns already keeps the same number of columns per head",
+              file=sys.stderr)
+        sys.exit(2)
 
     # Inputs for every step of the trajectory, resident in HBM before timing.
     traj = Trajectory(w, dev)
@@ -228,7 +281,7 @@ def main():
     torch.cuda.synchronize()
     dims = B.make_dims(w.H, w.Hkv, w.L, w.d, w.B)
     drv = B.Driver(dims, w.dense_steps, w.refresh_every, sparsity, device=dev,
-                   per_head_budget=args.per_head_budget)
+                   per_head_budget=args.per_head_budget, column_sparse=args.columns)
     o = torch.empty(w.H, w.L, w.d, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -265,12 +318,17 @@ def main():
     n_anchor = sum(1 for kd in kinds if kd == 1)
 
     Kkept = drv.K
-    # Kept blocks per head in the mask left by the last anchor before timing ended.
-    rp = drv.row_ptr.cpu()
-    per_head = [int(rp[(h + 1) * w.nb] - rp[h * w.nb]) for h in range(w.H)]
+    if args.columns:
+        # Every query token attends to the k_c kept columns of its head.
+        per_head = [drv.k_c] * w.H
+        flops_step = 4.0 * w.L * w.d * drv.k_c * w.H
+    else:
+        # Kept blocks per head in the mask left by the last anchor before timing ended.
+        rp = drv.row_ptr.cpu()
+        per_head = [int(rp[(h + 1) * w.nb] - rp[h * w.nb]) for h in range(w.H)]
+        flops_step = 4.0 * w.B * w.B * w.d * Kkept
     ph_mean = sum(per_head) / len(per_head)
     ph_cv = (sum((x - ph_mean) ** 2 for x in per_head) / len(per_head)) ** 0.5 / ph_mean
-    flops_step = 4.0 * w.B * w.B * w.d * Kkept
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
     # Same-GPU dense baseline on the step-0 inputs.
@@ -297,10 +355,13 @@ def main():
         del src, dst
 
     attn_tflops = flops_step / (attn_ms * 1e-3) / 1e12 if attn_ms else None
-    trec = traffic_record()
+    trec = None
+    if (w.name, w.d, w.B, sparsity) == ("stepdllm_8k", 128, 64, 0.9):
+        trec = traffic_record(TRAFFIC_FILE_COLS if args.columns else TRAFFIC_FILE)
+    mode = "cols" if args.columns else "sparse"
     roofline = {
         "bound": "mfma",
-        "kernel": "k_attn<128,64,sparse>" if (w.d, w.B) == (128, 64) else "k_attn",
+        "kernel": f"k_attn<{w.d},{w.B},{mode}>",
         "achieved": round(attn_tflops, 3) if attn_tflops else None,
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
@@ -311,7 +372,7 @@ def main():
     }
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC_COLS if args.columns else METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -324,8 +385,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "H": w.H, "Hkv": w.Hkv, "L": w.L, "d": w.d, "block": w.B,
-                   "sparsity": sparsity, "kept_blocks": Kkept,
-                   "budget": "per_head" if args.per_head_budget else "global",
+                   "sparsity": sparsity,
+                   **({"kept_columns_per_head": drv.k_c} if args.columns
+                      else {"kept_blocks": Kkept}),
+                   "budget": ("columns" if args.columns else
+                              "per_head" if args.per_head_budget else "global"),
                    "refresh_every": w.refresh_every, "dense_steps": w.dense_steps,
                    "distinct_input_steps": T, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
@@ -341,7 +405,10 @@ def main():
         "speedup_vs_dense_kernel": round(dense_ms / attn_ms, 3) if attn_ms else None,
         "speedup_vs_dense_per_step": round(dense_ms / ms_per_step, 3),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.columns:
+        result["cpu_baseline"] = cpu_baseline_cols(inputs[0], w, sparsity, flops_step,
+                                                   args.cpu_budget_s)
+    elif not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inputs[0], w, sparsity, flops_step, args.cpu_budget_s,
                                               per_head=args.per_head_budget)
     else:
