@@ -454,8 +454,10 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         if (COLS) {
             if (has1) issue_v_tok(tok_v, (n + 1) & 1);
             if (has3) issue_k_tok(tok_k, n % 3);
-            if (n + 2 < n_total) load_tok(n + 2, tok_v);
-            if (n + 4 < n_total) load_tok(n + 4, tok_k);
+            // A FULL step has chunks up to n+4 (the loop runs while n+4 <
+            // n_total); a tail step never needs chunk n+4.
+            if (full || n + 2 < n_total) load_tok(n + 2, tok_v);
+            if (full) load_tok(n + 4, tok_k);
         } else {
             if (has1) issue_v(key1, (n + 1) & 1);
             if (has3) issue_k(key3, n % 3);

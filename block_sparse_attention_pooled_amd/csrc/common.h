@@ -36,12 +36,14 @@ struct Dims {
     // Work-order positions per die (rows of die_heads() heads).
     int64_t die_cap() const { return (int64_t)die_heads() * nb; }
     int64_t n_scores() const { return (int64_t)H * nb * nb; }
+    // Key splits of the column-mass statistics pass (1024 keys each).
+    int64_t col_splits() const { return ((int64_t)L + 1023) / 1024; }
 };
 
 // Workspace carve-up (byte offsets, 256-byte aligned).
 struct WsLayout {
     int64_t qb, kb, p, hist, sel, gt, eq, tie_base, work, work_meta, hsel, col_scores, col_stats,
-        total;
+        col_part, col_q16, total;
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -62,7 +64,9 @@ inline WsLayout ws_layout(const Dims &D) {
     w.work_meta = take(16 * 4);
     w.hsel = take((int64_t)D.H * kHeadSelWords * 4);
     w.col_scores = take((int64_t)D.H * D.L * 4);   // column masses (column-sparse variant)
-    w.col_stats = take(D.rows() * 8);              // per pooled query: max, normaliser
+    w.col_stats = take(D.rows() * 8);              // per pooled query: max, 1 / normaliser
+    w.col_part = take(D.rows() * D.col_splits() * 8);   // per key split: max, normaliser
+    w.col_q16 = take((int64_t)D.H * ((D.nb + 31) / 32) * 32 * D.d * 2);   // bf16 pooled Q
     w.total = off;
     return w;
 }
