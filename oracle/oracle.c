@@ -582,6 +582,50 @@ void oracle_col_attn(const float *q, const float *k, const float *v, int H,
     free(z);
 }
 
+/* Recall of a column mask (mask quality, as oracle_mask_recall for blocks):
+ * for row r = h*nb + i, the mean over the B query tokens t of block i of the
+ * full bidirectional softmax probability that t puts on the kept key tokens
+ * cols[h*k_c .. h*k_c + k_c) (all L keys in the normaliser), fp64.  1 when the
+ * kept columns hold all of the rows' attention. */
+void oracle_col_recall(const float *q, const float *k, int H, int Hkv, int L,
+                       int d, int B, const int32_t *cols, int64_t k_c,
+                       const int32_t *rows, int n_rows, double *recall)
+{
+    int nb = L / B, G = H / Hkv;
+    int total = rows ? n_rows : H * nb;
+    double scale = 1.0 / sqrt((double)d);
+    double *z = (double *)malloc(sizeof(double) * (size_t)L);
+    for (int x = 0; x < total; ++x) {
+        int r = rows ? rows[x] : x;
+        int h = r / nb, i = r % nb, g = h / G;
+        const float *kh = k + (int64_t)g * L * d;
+        const int32_t *ch = cols + (int64_t)h * k_c;
+        double acc = 0.0;
+        for (int t = i * B; t < (i + 1) * B; ++t) {
+            const float *qt = q + ((int64_t)h * L + t) * d;
+            double m = -INFINITY;
+            for (int u = 0; u < L; ++u) {
+                const float *ku = kh + (int64_t)u * d;
+                double dot = 0.0;
+                for (int e = 0; e < d; ++e)
+                    dot += (double)qt[e] * (double)ku[e];
+                z[u] = dot * scale;
+                if (z[u] > m)
+                    m = z[u];
+            }
+            double l = 0.0;
+            for (int u = 0; u < L; ++u)
+                l += exp(z[u] - m);
+            double kept = 0.0;
+            for (int64_t a = 0; a < k_c; ++a)
+                kept += exp(z[ch[a]] - m);
+            acc += kept / l;
+        }
+        recall[r] = acc / B;
+    }
+    free(z);
+}
+
 /* ----------------------------------------------------------------- driver --- */
 /* What a denoising step runs ([SD] anchors + reuse; [SP] dense warm-up then
  * one mask reused): 0 = dense attention, 1 = anchor (rebuild the mask from

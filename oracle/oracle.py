@@ -54,6 +54,7 @@ def _bind(lib):
         "oracle_col_select": (None, [f32p, ci, ci, ci64, i32p]),
         "oracle_build_col_mask": (ci64, [f32p, f32p, ci, ci, ci, ci, ci, cd, f32p, i32p]),
         "oracle_col_attn": (None, [f32p, f32p, f32p, ci, ci, ci, ci, ci, i32p, ci64, vp, ci, f64p]),
+        "oracle_col_recall": (None, [f32p, f32p, ci, ci, ci, ci, ci, i32p, ci64, vp, ci, f64p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -303,8 +304,25 @@ def col_attn(q, k, v, B, cols, rows=None, lib=None, out=None):
     return out
 
 
+def col_recall(q, k, B, cols, rows=None, lib=None, out=None):
+    """Recall of a column mask per row h*nb + i (fp64 [H*nb]): the mean over the
+    block's query tokens of the full-softmax probability on the kept columns
+    cols[h].  Only the listed rows are written."""
+    lib = lib or load()
+    q, k = _f32(q), _f32(k)
+    H, L, d = q.shape
+    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    k_c = cols.shape[1] if cols.ndim == 2 else 0
+    if out is None:
+        out = np.zeros(H * (L // B), np.float64)
+    rptr, nrows, _keep = _rows_arg(rows)
+    lib.oracle_col_recall(q, k, H, k.shape[0], L, d, B,
+                          cols if cols.size else np.zeros(1, np.int32), int(k_c), rptr, nrows, out)
+    return out
+
+
 __all__ = ["build", "load", "pool", "scores", "keep_count", "select", "select_per_head",
            "cut_value", "csr",
            "build_mask", "plan", "sparse_attn", "dense_attn", "step_kind", "block_mass",
            "mask_recall", "bf16_round", "col_scores", "col_select", "build_col_mask",
-           "col_attn"]
+           "col_attn", "col_recall"]

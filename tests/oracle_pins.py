@@ -632,8 +632,39 @@ def pin_col_attention(lib):
     assert np.max(np.abs(o[:, 2] - 1.0)) < 1e-15 and np.all(o[:, 0] == 0) and np.all(o[:, 3:] == 0)
 
 
+def pin_col_recall(lib):
+    rng = np.random.default_rng(RNG_SEEDS[1] + 12)
+    for (H, Hkv, L, d, B, qs) in ((4, 2, 256, 64, 64, 2.0), (3, 1, 256, 128, 128, 1.0)):
+        nb = L // B
+        q, k = _rand((H, L, d), rng, qs), _rand((Hkv, L, d), rng)
+        allc = np.tile(np.arange(L, dtype=np.int32), (H, 1))
+        assert np.max(np.abs(O.col_recall(q, k, B, allc, lib=lib) - 1.0)) < 1e-12
+        assert np.all(O.col_recall(q, k, B, np.zeros((H, 0), np.int32), lib=lib) == 0)
+        # Whole-matrix numpy fp64: softmax rows, summed over the kept columns,
+        # averaged over each query block.
+        k_c = 37
+        cols = np.stack([np.sort(rng.choice(L, k_c, replace=False)) for _ in range(H)]).astype(np.int32)
+        got = O.col_recall(q, k, B, cols, lib=lib)
+        for h in range(H):
+            p = _softmax_rows(q[h].astype(np.float64) @ k[h // (H // Hkv)].astype(np.float64).T
+                              / math.sqrt(d))
+            want = p[:, cols[h]].sum(axis=1).reshape(nb, B).mean(axis=1)
+            assert np.max(np.abs(got[h * nb:(h + 1) * nb] - want)) < 1e-12, (H, h)
+        # Keeping whole key blocks (the same blocks for every row of a head)
+        # recalls the block attention mass of those blocks.
+        blocks = [np.sort(rng.choice(nb, 2, replace=False)) for _ in range(H)]
+        bcols = np.stack([np.concatenate([np.arange(j * B, (j + 1) * B) for j in bl])
+                          for bl in blocks]).astype(np.int32)
+        A = O.block_mass(q, k, B, lib=lib)
+        want = np.concatenate([A[h][:, blocks[h]].sum(axis=1) for h in range(H)])
+        assert np.max(np.abs(O.col_recall(q, k, B, bcols, lib=lib) - want)) < 1e-12
+        # A row subset writes only those rows.
+        part = O.col_recall(q, k, B, cols, rows=[1, H * nb - 1], lib=lib)
+        assert part[1] == got[1] and part[-1] == got[-1] and part[0] == 0
+
+
 ALL_PINS = [pin_keep_count, pin_pool, pin_scores, pin_select, pin_select_per_head, pin_csr,
             pin_plan, pin_worked_w1_per_head,
             pin_attention_brute, pin_attention_closed_forms, pin_worked_w1, pin_worked_w2,
             pin_build_mask_brute, pin_step_kind, pin_block_mass, pin_mask_recall,
-            pin_bf16_round, pin_col_scores, pin_col_select, pin_col_attention]
+            pin_bf16_round, pin_col_scores, pin_col_select, pin_col_attention, pin_col_recall]

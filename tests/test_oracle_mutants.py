@@ -71,6 +71,11 @@ MUTANTS = [
     ("col_select_head_0", "oracle_select(c + (int64_t)h * L, L, k_c, keep);",
      "oracle_select(c, L, k_c, keep);", 0),
     ("col_attn_head_0_columns", "cols + (int64_t)h * k_c, (int)k_c, z,", "cols, (int)k_c, z,", 0),
+    ("col_recall_not_averaged", "recall[r] = acc / B;", "recall[r] = acc;", 0),
+    ("col_recall_head_0_columns", "const int32_t *ch = cols + (int64_t)h * k_c;",
+     "const int32_t *ch = cols;", 0),
+    ("col_recall_normalised_over_kept", "            for (int u = 0; u < L; ++u)\n                l += exp(z[u] - m);",
+     "            for (int64_t a = 0; a < k_c; ++a)\n                l += exp(z[ch[a]] - m);", 0),
     ("col_attn_drops_last_column", "cols + (int64_t)h * k_c, (int)k_c, z,",
      "cols + (int64_t)h * k_c, (int)k_c - 1, z,", 0),
 ]
