@@ -179,7 +179,7 @@ def mask_quality(args, w, sparsity, dev, T):
 
     dims = B.make_dims(w.H, w.Hkv, w.L, w.d, w.B)
     drv = B.Driver(dims, w.dense_steps, w.refresh_every, sparsity, device=dev,
-                   per_head_budget=args.per_head_budget)
+                   per_head_budget=args.per_head_budget, column_sparse=args.columns)
     o = torch.empty(w.H, w.L, w.d, dtype=torch.bfloat16, device=dev)
     mass = torch.empty(w.H * w.nb * w.nb, dtype=torch.float32, device=dev)
     rec = torch.empty(w.H * w.nb, dtype=torch.float32, device=dev)
@@ -202,6 +202,17 @@ def mask_quality(args, w, sparsity, dev, T):
         if kind == 1:
             last_anchor = t
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.columns:
+            # Recall of the kept columns straight from this step's Q/K.
+            a.record(stream)
+            B.col_recall(dims, q, k, drv.cols(), rec, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            mass_ms.append(a.elapsed_time(b))
+            per_step.append(float(rec.mean()))
+            kinds.append(kind)
+            since_anchor.append(t - last_anchor)
+            continue
         a.record(stream)
         B.block_mass(dims, q, k, mass, stream)
         b.record(stream)
@@ -225,9 +236,13 @@ def mask_quality(args, w, sparsity, dev, T):
     at_anchor = [r for r, kd in zip(per_step, kinds) if kd == 1]
     last_in = [r for r, s in zip(per_step, since_anchor) if s == R - 1]
     mass_flops = 4.0 * w.H * w.L * w.L * w.d          # two score passes
+    if args.columns:                                  # one full pass, then the kept columns
+        mass_flops = 2.0 * w.H * w.L * w.d * (w.L + drv.k_c)
     mms = sorted(mass_ms)[len(mass_ms) // 2]
     result = {
-        "metric": "mask recall: share of the true block attention mass on the kept blocks",
+        "metric": ("mask recall: share of the exact attention on the kept key columns"
+                   if args.columns else
+                   "mask recall: share of the true block attention mass on the kept blocks"),
         "value": round(sum(per_step) / len(per_step), 5),
         "unit": "fraction",
         "higher_is_better": True,
@@ -235,17 +250,23 @@ def mask_quality(args, w, sparsity, dev, T):
         "steps": len(per_step),
         "data": "synthetic",
         "config": {"workload": w.name, "H": w.H, "L": w.L, "d": w.d, "block": w.B,
-                   "sparsity": sparsity, "kept_blocks": drv.K,
-                   "budget": "per_head" if args.per_head_budget else "global",
+                   "sparsity": sparsity,
+                   **({"kept_columns_per_head": drv.k_c} if args.columns
+                      else {"kept_blocks": drv.K}),
+                   "budget": ("columns" if args.columns else
+                              "per_head" if args.per_head_budget else "global"),
                    "refresh_every": w.refresh_every, "dense_steps": w.dense_steps},
         "recall_at_anchors": round(sum(at_anchor) / len(at_anchor), 5),
-        "best_recall_same_budget_at_anchors": round(sum(best_at_anchor) / len(best_at_anchor), 5),
-        "random_mask_recall": round(drv.K / (w.H * w.nb * w.nb), 5),
+        "best_recall_same_budget_at_anchors": (
+            round(sum(best_at_anchor) / len(best_at_anchor), 5) if best_at_anchor else None),
+        "random_mask_recall": round(drv.k_c / w.L if args.columns
+                                    else drv.K / (w.H * w.nb * w.nb), 5),
         "recall_last_step_of_interval": round(sum(last_in) / len(last_in), 5) if last_in else None,
         "recall_by_steps_since_anchor": by_offset,
         "recall_per_step": [round(x, 5) for x in per_step],
-        "block_mass_ms": round(mms, 4),
-        "block_mass_tflops": round(mass_flops / (mms * 1e-3) / 1e12, 2),
+        ("col_recall_ms" if args.columns else "block_mass_ms"): round(mms, 4),
+        ("col_recall_tflops" if args.columns else "block_mass_tflops"):
+            round(mass_flops / (mms * 1e-3) / 1e12, 2),
     }
     print(json.dumps(result), flush=True)
 

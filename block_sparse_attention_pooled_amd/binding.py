@@ -73,6 +73,7 @@ def load():
         "stepdllm_build_col_mask": (i32, [D, dbl, _vp, _vp, _vp, sz, _vp, _vp, _vp]),
         "stepdllm_select_col_mask": (i32, [D, dbl, _vp, _vp, sz, _vp, _vp]),
         "stepdllm_col_attn": (i32, [D, _vp, _vp, _vp, _vp, i64, _vp, _vp]),
+        "stepdllm_col_recall": (i32, [D, _vp, _vp, _vp, i64, _vp, _vp]),
         "stepdllm_driver_create": (i32, [ctypes.POINTER(_vp), D, ctypes.POINTER(Schedule), _vp,
                                          sz, _vp, _vp]),
         "stepdllm_driver_step_kind": (i32, [_vp, ctypes.c_int32]),
@@ -93,7 +94,8 @@ EXPORTS = ["stepdllm_keep_count", "stepdllm_workspace_bytes", "stepdllm_workspac
            "stepdllm_build_mask_per_head", "stepdllm_select_mask_per_head", "stepdllm_plan",
            "stepdllm_sparse_attn", "stepdllm_dense_attn", "stepdllm_block_mass",
            "stepdllm_mask_recall", "stepdllm_keep_count_columns", "stepdllm_build_col_mask",
-           "stepdllm_select_col_mask", "stepdllm_col_attn", "stepdllm_driver_create",
+           "stepdllm_select_col_mask", "stepdllm_col_attn", "stepdllm_col_recall",
+           "stepdllm_driver_create",
            "stepdllm_driver_step_kind", "stepdllm_step", "stepdllm_driver_destroy",
            "stepdllm_status_string"]
 
@@ -250,6 +252,16 @@ def col_attn(dims, q, k, v, cols, o, k_c=None, stream=None):
         ctypes.byref(dims), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
         _ptr(cols, torch.int32, "cols") if cols.numel() else None, k_c, _ptr(o, bf, "o"),
         _stream(stream)), "stepdllm_col_attn")
+
+
+def col_recall(dims, q, k, cols, recall, k_c=None, stream=None):
+    """Per-row recall [H*nb] of the column mask cols ([H, k_c] int32)."""
+    bf = torch.bfloat16
+    k_c = (cols.shape[-1] if cols.dim() == 2 else 0) if k_c is None else int(k_c)
+    _check(load().stepdllm_col_recall(
+        ctypes.byref(dims), _ptr(q, bf, "q"), _ptr(k, bf, "k"),
+        _ptr(cols, torch.int32, "cols") if cols.numel() else None, k_c,
+        _ptr(recall, torch.float32, "recall"), _stream(stream)), "stepdllm_col_recall")
 
 
 class Driver:

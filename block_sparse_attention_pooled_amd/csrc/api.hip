@@ -306,6 +306,17 @@ int stepdllm_block_mass(const stepdllm_dims *dims, const uint16_t *q, const uint
     return hip_status(sd::launch_block_mass(D, q, k, mass, static_cast<hipStream_t>(stream)));
 }
 
+int stepdllm_col_recall(const stepdllm_dims *dims, const uint16_t *q, const uint16_t *k,
+                        const int32_t *cols, int64_t k_c, float *recall, void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!q || !k || !recall || (k_c > 0 && !cols)) return STEPDLLM_EINVAL;
+    if (k_c < 0 || k_c > D.L) return STEPDLLM_EINVAL;
+    return hip_status(sd::launch_col_recall(D, q, k, cols, k_c, recall,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int stepdllm_mask_recall(const stepdllm_dims *dims, const float *mass, const int32_t *row_ptr,
                          const int32_t *col_idx, int64_t nnz, float *recall, void *stream) {
     Dims D;

@@ -108,6 +108,10 @@ hipError_t launch_col_scores(const Dims &D, const float *qb, const uint16_t *k, 
 // Mask quality launches (quality_kernels.hip).
 hipError_t launch_block_mass(const Dims &D, const uint16_t *q, const uint16_t *k, float *mass,
                              hipStream_t s);
+// Recall of a column mask per row: mean over the query block of the full
+// softmax probability on cols[h*k_c .. +k_c).
+hipError_t launch_col_recall(const Dims &D, const uint16_t *q, const uint16_t *k,
+                             const int32_t *cols, int64_t k_c, float *recall, hipStream_t s);
 hipError_t launch_mask_recall(const Dims &D, const float *mass, const int32_t *row_ptr,
                               const int32_t *col_idx, int64_t nnz, float *recall,
                               hipStream_t s);

@@ -151,6 +151,143 @@ __global__ __launch_bounds__(BLK / 32 * 64) void k_block_mass(
     }
 }
 
+// Recall of a column mask (the column-sparse variant, "PulseCol" abstract):
+// per row (head, query block), the mean over its query tokens of the full
+// softmax probability on the head's kept key columns.  Same workgroup shape
+// and pass 1 as k_block_mass (exact max and normaliser over all L keys); pass
+// 2 walks only the kept columns, 32 list entries at a time, each lane
+// gathering its key's K row, and entries past the list count nothing.
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK / 32 * 64) void k_col_recall(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const int32_t *__restrict__ cols, int64_t k_c, float *__restrict__ recall, int L, int nb,
+    int G, int H, float scale_log2) {
+    constexpr int WQ = BLK / 32;
+    constexpr int KS = D / 16;
+    __shared__ float part[WQ];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, hh = lane >> 5;
+
+    int row = blockIdx.x;
+    if ((H & 7) == 0) {   // keep each head's rows on one XCD (round-robin dispatch)
+        const int x = row & 7, kk = row >> 3;
+        row = (x + 8 * (kk / nb)) * nb + kk % nb;
+    }
+    const int h = row / nb, blk = row % nb, g = h / G;
+    const int64_t qbase = ((int64_t)h * L + (int64_t)blk * BLK + 32 * wave) * D;
+    const uint16_t *kh = k + (int64_t)g * L * D;
+    const __amdgpu_buffer_rsrc_t k_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)kh, 0, L * D * 2, 0x00020000);
+
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+        qf[s] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4 *>(q + qbase + (int64_t)col * D + 16 * s + 8 * hh));
+    const uint32_t k_voff = (uint32_t)(col * D * 2 + 16 * hh);
+    auto load_k = [&](int c, bf16x8 (&kf)[KS]) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            kf[s] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, k_voff,
+                                                              c * kMassChunk * D * 2 + 32 * s, 0));
+    };
+    auto scores = [&](const bf16x8 (&kf)[KS], f32x16 &sacc) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
+    };
+
+    // Pass 1: per query column, max m and sum l of 2^(s*scale - m) over all keys.
+    const int n_chunks = L / kMassChunk;
+    bf16x8 ka[KS], kb[KS];
+    float m = -INFINITY, l = 0.0f;
+    auto pass1 = [&](const bf16x8 (&kf)[KS]) {
+        f32x16 sacc;
+        scores(kf, sacc);
+        float cm = sacc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) cm = fmaxf(cm, sacc[i]);
+        const float m_new = fmaxf(m, cm * scale_log2);
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc += __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -m_new));
+        l = l * __builtin_amdgcn_exp2f(m - m_new) + acc;
+        m = m_new;
+    };
+    load_k(0, ka);
+    for (int c = 0; c < n_chunks; c += 2) {
+        if (c + 1 < n_chunks) load_k(c + 1, kb);
+        pass1(ka);
+        if (c + 1 < n_chunks) {
+            if (c + 2 < n_chunks) load_k(c + 2, ka);
+            pass1(kb);
+        }
+    }
+    {
+        const float m2 = __shfl_xor(m, 32), l2 = __shfl_xor(l, 32);
+        const float mm = fmaxf(m, m2);
+        l = l * __builtin_amdgcn_exp2f(m - mm) + l2 * __builtin_amdgcn_exp2f(m2 - mm);
+        m = mm;
+    }
+
+    // Pass 2: the kept columns.  Lane row col of chunk c is list entry 32*c + col.
+    const int32_t *ch = cols + (int64_t)h * k_c;
+    const int n_cc = (int)((k_c + kMassChunk - 1) / kMassChunk);
+    auto load_kc = [&](int c, bf16x8 (&kf)[KS]) {
+        const int64_t a = (int64_t)c * kMassChunk + col;
+        int tok = a < k_c ? ch[a] : 0;
+        tok = min(max(tok, 0), L - 1);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            kf[s] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4 *>(kh + (int64_t)tok * D + 16 * s + 8 * hh));
+    };
+    float acc = 0.0f;
+    auto pass2 = [&](int c, const bf16x8 (&kf)[KS]) {
+        f32x16 sacc;
+        scores(kf, sacc);
+        // Accumulator i of this lane is key 8*(i/4) + 4*hh + i%4 of the chunk.
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if ((int64_t)c * kMassChunk + 8 * (i >> 2) + 4 * hh + (i & 3) < k_c)
+                acc += __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -m));
+    };
+    if (n_cc > 0) load_kc(0, ka);
+    for (int c = 0; c < n_cc; c += 2) {
+        if (c + 1 < n_cc) load_kc(c + 1, kb);
+        pass2(c, ka);
+        if (c + 1 < n_cc) {
+            if (c + 2 < n_cc) load_kc(c + 2, ka);
+            pass2(c + 1, kb);
+        }
+    }
+    float p = acc / l;
+    p += __shfl_xor(p, 32);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) p += __shfl_xor(p, o);
+    if (lane == 0) part[wave] = p;
+    __syncthreads();
+    if (tid == 0) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WQ; ++w) s += part[w];
+        recall[row] = s * (1.0f / BLK);
+    }
+}
+
+template <int D, int BLK>
+hipError_t launch_col_recall_t(const Dims &Dm, const uint16_t *q, const uint16_t *k,
+                               const int32_t *cols, int64_t k_c, float *recall, hipStream_t s) {
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    hipLaunchKernelGGL((k_col_recall<D, BLK>), dim3((unsigned)Dm.rows()), dim3(BLK / 32 * 64), 0,
+                       s, q, k, cols, k_c, recall, Dm.L, Dm.nb, Dm.G, Dm.H, scale_log2);
+    return hipGetLastError();
+}
+
 // One wave per row: the mass on the row's kept blocks.  List positions at or
 // past nnz are not read; block ids outside [0, nb) add nothing.
 __global__ __launch_bounds__(256) void k_mask_recall(const float *__restrict__ mass, int64_t rows,
@@ -189,6 +326,15 @@ hipError_t launch_block_mass(const Dims &D, const uint16_t *q, const uint16_t *k
     if (D.d == 128 && D.B == 128) return launch_mass_t<128, 128>(D, q, k, mass, s);
     if (D.d == 64 && D.B == 64) return launch_mass_t<64, 64>(D, q, k, mass, s);
     return launch_mass_t<64, 128>(D, q, k, mass, s);
+}
+
+hipError_t launch_col_recall(const Dims &D, const uint16_t *q, const uint16_t *k,
+                             const int32_t *cols, int64_t k_c, float *recall, hipStream_t s) {
+    if (D.d == 128 && D.B == 64) return launch_col_recall_t<128, 64>(D, q, k, cols, k_c, recall, s);
+    if (D.d == 128 && D.B == 128)
+        return launch_col_recall_t<128, 128>(D, q, k, cols, k_c, recall, s);
+    if (D.d == 64 && D.B == 64) return launch_col_recall_t<64, 64>(D, q, k, cols, k_c, recall, s);
+    return launch_col_recall_t<64, 128>(D, q, k, cols, k_c, recall, s);
 }
 
 hipError_t launch_mask_recall(const Dims &D, const float *mass, const int32_t *row_ptr,

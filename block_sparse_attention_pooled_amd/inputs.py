@@ -23,6 +23,13 @@ and evaluation data are not available:
   block and 4 random ones), with a = structure * (4 * sqrt(d))^(1/2), so a
   target pair scores about +4 * structure^2 before the head temperature.  The
   targets and directions are redrawn with Q and K.
+* Column structure (the column-structured 8K variant only): each key head g
+  draws one unit direction e[g] and L/64 heavy key tokens at random positions
+  (not block-aligned); each heavy key gets + a * e[g] and every query token of
+  a head of group g gets + a * e[g], with a = columns * (4 * sqrt(d))^(1/2),
+  so every query scores its group's heavy keys about +4 * columns^2 higher:
+  "vertical" attention shared by all queries, the case column sparsity
+  ("PulseCol" abstract) is made for.  Redrawn with Q and K.
 """
 from dataclasses import dataclass, field
 import math
@@ -48,6 +55,7 @@ class Workload:
     resample_steps: tuple = field(default=())
     seed: int = 0
     structure: float = 0.0  # block-affinity strength (0 = i.i.d. inputs)
+    columns: float = 0.0    # heavy-column strength (0 = none)
 
     @property
     def nb(self):
@@ -74,6 +82,11 @@ WORKLOADS = {
                                        refresh_every=32, temperatures=True, sinks=False,
                                        drift=0.02, resample_steps=(80, 176), seed=1006,
                                        structure=1.0),
+    "stepdllm_8k_columns": Workload("stepdllm_8k_columns", H=32, Hkv=32, L=8192, d=128,
+                                    B=64, sparsities=(0.9,), steps=256, dense_steps=0,
+                                    refresh_every=32, temperatures=True, sinks=False,
+                                    drift=0.02, resample_steps=(80, 176), seed=1007,
+                                    columns=1.0),
     "dream_gqa_8k": Workload("dream_gqa_8k", H=28, Hkv=4, L=8192, d=128, B=64,
                              sparsities=(0.7, 0.8, 0.9, 0.95), steps=64, dense_steps=0,
                              refresh_every=16, temperatures=True, sinks=False, drift=0.02,
@@ -128,6 +141,17 @@ class Trajectory:
             g = torch.arange(w.H, device=self.device) // (w.H // w.Hkv)
             dirs = e[g.view(-1, 1, 1), tgt]                            # [H, nb, 5, d]
             q += a * dirs.sum(dim=2).repeat_interleave(w.B, dim=1)
+        if w.columns:
+            a = w.columns * math.sqrt(4.0 * math.sqrt(w.d))
+            e = self._randn(w.Hkv, w.d)
+            e = e / e.norm(dim=-1, keepdim=True)
+            n_heavy = w.L // 64
+            heavy = torch.argsort(torch.rand(w.Hkv, w.L, generator=self.gen, device=self.device),
+                                  dim=1)[:, :n_heavy]                 # [Hkv, L/64] distinct
+            k[torch.arange(w.Hkv, device=self.device).view(-1, 1), heavy] += a * e.view(
+                w.Hkv, 1, w.d)
+            g = torch.arange(w.H, device=self.device) // (w.H // w.Hkv)
+            q += a * e[g].view(w.H, 1, w.d)
         return q * self.temps.view(-1, 1, 1), k
 
     def next(self):

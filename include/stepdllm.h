@@ -266,6 +266,19 @@ int stepdllm_mask_recall(const stepdllm_dims *dims, const float *mass,
                          const int32_t *row_ptr, const int32_t *col_idx,
                          int64_t nnz, float *recall, void *stream);
 
+/* Recall of a column mask (the column-sparse variant's counterpart of
+ * stepdllm_mask_recall): recall[r] (fp32, [H*nb]) for row r = h*nb + i is
+ *   (1/B) sum_{t in q-block i} sum_{a < k_c} softmax_u(q_t . k_u / sqrt(d))
+ *                                            at u = cols[h*k_c + a]
+ * (all L keys of key head h / (H/Hkv) in the softmax): the share of the
+ * row's exact attention on the kept columns.  Entries are expected distinct
+ * and in [0, L); others are clamped into range.  Exact per-token max and
+ * normaliser over all keys (bf16 MFMA, fp32), then the kept columns only;
+ * deterministic. */
+int stepdllm_col_recall(const stepdllm_dims *dims, const uint16_t *q,
+                        const uint16_t *k, const int32_t *cols, int64_t k_c,
+                        float *recall, void *stream);
+
 /* Step driver: a small host object owned by the library; device buffers
  * (workspace, row_ptr [H*nb+1], col_idx [K]; column mode: col_idx [H*k_c]
  * and no row_ptr) stay owned by the caller and

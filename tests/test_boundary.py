@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = B.load()
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(B.EXPORTS) == names
@@ -139,6 +139,9 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.stepdllm_col_attn(r(d), FAKE, FAKE, FAKE, None, 4, FAKE, None) == B.EINVAL
     assert lib.stepdllm_col_attn(r(d), FAKE, FAKE, None, FAKE, 4, FAKE, None) == B.EINVAL
     assert lib.stepdllm_col_attn(r(dims(2, 2, 256, 80, 64)), FAKE, FAKE, FAKE, FAKE, 4, FAKE, None) == B.EUNSUPPORTED
+    assert lib.stepdllm_col_recall(r(d), FAKE, FAKE, None, 4, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_col_recall(r(d), FAKE, FAKE, FAKE, 257, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_col_recall(r(d), FAKE, FAKE, FAKE, 4, None, None) == B.EINVAL
     # sparsity out of range
     for s in (-0.5, 1.0, float("nan")):
         assert lib.stepdllm_build_mask(r(d), s, FAKE, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL

@@ -242,11 +242,12 @@ def test_column_driver_matches_oracle(shape, s):
 
 
 @pytest.mark.timeout(900)
-def test_column_mask_8k_anchor():
-    """The 8K workload's step-0 inputs at 90%: every mass against the fp64
-    oracle, the lists against the oracle's (near-ties listed), and sampled
-    rows of the attention."""
-    w = WORKLOADS["stepdllm_8k"]
+@pytest.mark.parametrize("name", ["stepdllm_8k", "stepdllm_8k_columns"])
+def test_column_mask_8k_anchor(name):
+    """An 8K workload's step-0 inputs at 90% (i.i.d., and with heavy key
+    columns): every mass against the fp64 oracle, the lists against the
+    oracle's (near-ties listed), and sampled rows of the attention."""
+    w = WORKLOADS[name]
     s = w.sparsities[0]
     traj = Trajectory(w, DEV)
     q, k, v = traj.next()
@@ -270,3 +271,58 @@ def test_column_mask_8k_anchor():
     want = np.zeros((w.H, w.L, w.d), np.float64)
     PT.oracle_rows_parallel(O.col_attn, rows, q=qf, k=kf, v=vf, B=w.B, cols=cols, out=want)
     PT.check_outputs(o, want, PT.token_mask_for_rows(rows, w.H, w.nb, w.B))
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=SHAPE_IDS)
+def test_column_recall_matches_oracle(shape):
+    """Recall of column masks against the fp64 oracle; every column recalls 1,
+    none 0; whole key blocks recall the GPU's block attention mass."""
+    H, Hkv, L, d, blk, _ = shape
+    q, k, _ = _qkv(shape, 616)
+    dims = B.dims_of(q, k, blk)
+    nb = L // blk
+    rng = np.random.default_rng(L + 7)
+    qf, kf = PT.oracle_inputs(q, k)
+    rec = torch.empty(H * nb, dtype=torch.float32, device=DEV)
+    for k_c in (1, 33, L // 4):
+        cols = _random_cols(H, L, k_c, rng)
+        B.col_recall(dims, q, k, torch.from_numpy(cols).to(DEV), rec)
+        torch.cuda.synchronize()
+        want = O.col_recall(qf, kf, blk, cols)
+        assert np.max(np.abs(rec.cpu().numpy() - want)) < 1e-4, k_c
+    allc = torch.arange(L, dtype=torch.int32, device=DEV).repeat(H, 1).contiguous()
+    B.col_recall(dims, q, k, allc, rec)
+    torch.cuda.synchronize()
+    assert float((rec - 1.0).abs().max()) < 1e-4
+    B.col_recall(dims, q, k, torch.empty((H, 0), dtype=torch.int32, device=DEV), rec, k_c=0)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(rec)) == 0
+    blocks = [np.sort(rng.choice(nb, min(2, nb), replace=False)) for _ in range(H)]
+    bcols = np.stack([np.concatenate([np.arange(j * blk, (j + 1) * blk) for j in bl])
+                      for bl in blocks]).astype(np.int32)
+    mass = torch.empty(H * nb * nb, dtype=torch.float32, device=DEV)
+    B.block_mass(dims, q, k, mass)
+    B.col_recall(dims, q, k, torch.from_numpy(bcols).to(DEV), rec)
+    torch.cuda.synchronize()
+    A = mass.cpu().numpy().reshape(H, nb, nb)
+    want = np.concatenate([A[h][:, blocks[h]].sum(axis=1) for h in range(H)])
+    assert np.max(np.abs(rec.cpu().numpy() - want)) < 1e-5
+
+
+@pytest.mark.timeout(600)
+def test_column_recall_8k_sampled_rows():
+    """The 8K anchor's column mask: recall of sampled rows against the oracle."""
+    w = WORKLOADS["stepdllm_8k"]
+    traj = Trajectory(w, DEV)
+    q, k, _ = traj.next()
+    m = GpuCols(q, k, w.B, w.sparsities[0])
+    rec = torch.empty(w.H * w.nb, dtype=torch.float32, device=DEV)
+    B.col_recall(m.dims, q, k, m.cols_t(), rec)
+    torch.cuda.synchronize()
+    got = rec.cpu().numpy()
+    assert np.all((got > 0) & (got <= 1.0 + 1e-5))
+    rows = np.random.default_rng(8).choice(w.H * w.nb, size=48, replace=False).astype(np.int32)
+    qf, kf = PT.oracle_inputs(q, k)
+    want = np.zeros(w.H * w.nb, np.float64)
+    PT.oracle_rows_parallel(O.col_recall, rows, q=qf, k=kf, B=w.B, cols=m.cols(), out=want)
+    assert np.max(np.abs(got[rows] - want[rows])) < 1e-4
