@@ -79,6 +79,21 @@ def traffic_record(path=TRAFFIC_FILE):
     return rec
 
 
+def sustained_mfma_rate():
+    """Run the package's MFMA-rate probe (built beside the library): the bf16
+    MFMA rate and shader clock the GPU holds under a pure MFMA load, for
+    random and for zero operands.  None if the probe is not built."""
+    import subprocess
+    exe = os.path.join(ROOT, "block_sparse_attention_pooled_amd", "mfma_rate")
+    if not os.path.exists(exe):
+        return None
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        print(f"bench.py: mfma_rate failed: {r.stderr.strip()}", file=sys.stderr)
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def cpu_baseline(inputs0, w, sparsity, flops_per_step, budget_s, per_head=False):
     """The oracle as it stands, on the host cores: one full mask build on step-0
     Q/K plus sparse attention on a deterministic sample of rows, extrapolated
@@ -391,6 +406,16 @@ def main():
         "algorithmic_flops_per_launch": flops_step,
         "kernel_ms": round(attn_ms, 5) if attn_ms else None,
     }
+    # What the chip sustains under pure MFMA load (power-limited clock with
+    # real-valued operands), measured after the timed region.
+    rate = sustained_mfma_rate()
+    if rate:
+        roofline["sustained_mfma"] = {
+            "random_bf16_tflops": rate["random"]["tflops"], "random_ghz": rate["random"]["ghz"],
+            "zero_bf16_tflops": rate["zero"]["tflops"], "zero_ghz": rate["zero"]["ghz"],
+            "probe": "block_sparse_attention_pooled_amd/mfma_rate"}
+        if attn_tflops:
+            roofline["frac_of_sustained_random"] = round(attn_tflops / rate["random"]["tflops"], 4)
 
     result = {
         "metric": METRIC_COLS if args.columns else METRIC,

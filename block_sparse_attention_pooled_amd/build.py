@@ -11,6 +11,10 @@ CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["mask_kernels.hip", "attn_kernels.hip", "quality_kernels.hip", "col_kernels.hip",
            "api.hip"]
 LIB = os.path.join(PKG, "libstepdllm.so")
+# A standalone measurement aid (sustained MFMA rate and shader clock), not
+# linked into the library.
+PROBE_SRC = "mfma_rate.hip"
+PROBE = os.path.join(PKG, "mfma_rate")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -45,8 +49,13 @@ def build(extra_flags=(), verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    cmd = [HIPCC, *FLAGS, *extra_flags, os.path.join(CSRC, PROBE_SRC), "-o", PROBE + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE)
     return LIB
 
 
