@@ -43,7 +43,7 @@ struct Dims {
 // Workspace carve-up (byte offsets, 256-byte aligned).
 struct WsLayout {
     int64_t qb, kb, p, hist, sel, gt, eq, tie_base, work, work_meta, hsel, col_scores, col_stats,
-        col_part, col_q16, total;
+        col_part, col_q16, plan_sorted, plan_nonempty, total;
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -67,6 +67,8 @@ inline WsLayout ws_layout(const Dims &D) {
     w.col_stats = take(D.rows() * 8);              // per pooled query: max, 1 / normaliser
     w.col_part = take(D.rows() * D.col_splits() * 8);   // per key split: max, normaliser
     w.col_q16 = take((int64_t)D.H * ((D.nb + 31) / 32) * 32 * D.d * 2);   // bf16 pooled Q
+    w.plan_sorted = take(D.rows() * 4);            // each head's rows, longest list first
+    w.plan_nonempty = take((int64_t)D.H * 4);      // non-empty rows per head
     w.total = off;
     return w;
 }

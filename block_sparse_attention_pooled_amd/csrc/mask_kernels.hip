@@ -502,24 +502,96 @@ __global__ __launch_bounds__(1024) void k_col_compact(const float *__restrict__ 
 //  * die x's list is its heads in assignment order, each head's rows by list
 //    length descending (ties by row id), at work[x*cap ..], cap = (heads a die
 //    may hold) * nb; unused positions hold -1.
-// One workgroup: heads are ranked in parallel and assigned by one wave (die
-// loads and counts in registers), then each wave sorts whole heads with a
-// stable counting sort (length histogram, descending bucket starts, ranks
-// among equal lengths from wave ballots).
+// Two launches.  k_plan_sort, one wave per head: the head's rows by list
+// length descending, ties by row id, with a stable counting sort (length
+// histogram, descending bucket starts, ranks among equal lengths from wave
+// ballots), and the head's count of non-empty rows.  k_plan, one workgroup:
+// heads are ranked in parallel, assigned to dies by one wave with one die per
+// lane (the least-loaded open die found by a three-step 8-lane argmin), and
+// every head's sorted rows are copied to its die positions.
+__global__ __launch_bounds__(64) void k_plan_sort(const int32_t *__restrict__ row_ptr, int nb,
+                                                  int32_t *__restrict__ sorted,
+                                                  int32_t *__restrict__ nonempty) {
+    __shared__ int32_t nx[kMaxBlocks + 1];   // histogram, first staging row_ptr
+    __shared__ int16_t ln[kMaxBlocks];
+    const int lane = threadIdx.x, h = blockIdx.x;
+    const uint64_t lt = lanemask_lt();
+    const int64_t r0 = (int64_t)h * nb;
+    // Stage row_ptr[r0 .. r0 + nb] (loads issued together), then the lengths.
+    // A wave's LDS requests complete in order.
+    for (int c = 0; c <= nb; c += 512) {
+        int v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = row_ptr[r0 + min(c + lane + 64 * j, nb)];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (c + lane + 64 * j <= nb) nx[c + lane + 64 * j] = v[j];
+    }
+    int my_nonempty = 0;
+    for (int i = lane; i < nb; i += 64) {
+        const int len = nx[i + 1] - nx[i];
+        ln[i] = (int16_t)len;
+        my_nonempty += len > 0;
+    }
+    for (int l = lane; l <= nb; l += 64) nx[l] = 0;
+    for (int i = lane; i < nb; i += 64) atomicAdd(&nx[ln[i]], 1);
+    // Bucket starts, longest lists first: nx[l] = rows with length > l.
+    int carry = 0;
+    for (int c0 = nb; c0 >= 0; c0 -= 64) {
+        const int l = c0 - lane;
+        const int cnt = l >= 0 ? nx[l] : 0;
+        int inc = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o);
+            if (lane >= o) inc += y;
+        }
+        if (l >= 0) nx[l] = carry + inc - cnt;
+        carry += __shfl(inc, 63);
+    }
+    for (int i0 = 0; i0 < nb; i0 += 64) {
+        const int i = i0 + lane;
+        const bool valid = i < nb;
+        const int len = valid ? ln[i] : 0;
+        uint64_t same = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 11; ++bit) {
+            const bool mine = (len >> bit) & 1;
+            const uint64_t b = __ballot(valid && mine);
+            same &= mine ? b : ~b;
+        }
+        const int rank = __popcll(same & lt);
+        const int pos = valid ? nx[len] + rank : 0;
+        if (valid && pos < nb) sorted[r0 + pos] = (int32_t)(r0 + i);
+        if (valid && rank == 0) nx[len] += __popcll(same);
+    }
+    const int total = wave_sum(my_nonempty);
+    if (lane == 0) nonempty[h] = total;
+}
+
+// One step of the die argmin: take the (load, die) pair of the lane that
+// dpp_ctrl names when it is smaller.
+template <int CTRL>
+__device__ __forceinline__ void argmin_step(int &load, int &die) {
+    const int l2 = __builtin_amdgcn_update_dpp(0, load, CTRL, 0xF, 0xF, false);
+    const int d2 = __builtin_amdgcn_update_dpp(0, die, CTRL, 0xF, 0xF, false);
+    const bool take = l2 < load || (l2 == load && d2 < die);
+    load = take ? l2 : load;
+    die = take ? d2 : die;
+}
+
 constexpr int kPlanThreads = 512;
-constexpr int kPlanWaves = kPlanThreads / 64;
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict__ row_ptr,
                                                        int H, int nb,
+                                                       const int32_t *__restrict__ sorted,
+                                                       const int32_t *__restrict__ ne_head,
                                                        int32_t *__restrict__ work,
                                                        int32_t *__restrict__ meta) {
+    static_assert(kDies == 8, "the die argmin covers 8 lanes");
     __shared__ int32_t kept[kMaxHeads];
     __shared__ int32_t order[kMaxHeads];
     __shared__ int32_t head_base[kMaxHeads];
-    // Per wave: the sort's histogram (and row_ptr staging) and list lengths.
-    __shared__ int32_t next[kPlanWaves][kMaxBlocks + 1];
-    __shared__ int16_t lens[kPlanWaves][kMaxBlocks];
-    __shared__ int32_t die_count[kDies];
     __shared__ int32_t nonempty;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cap_h = min(H, (H + kDies - 1) / kDies + 2);
@@ -534,18 +606,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict
         for (int o = 0; o < H; ++o)
             rank += (kept[o] > kept[h]) || (kept[o] == kept[h] && o < h);
         order[rank] = h;
+        atomicAdd(&nonempty, ne_head[h]);
     }
     __syncthreads();
     if (wave == 0) {
-        // Uniform in the wave: die loads and head counts, indexed only by
-        // unrolled loops so they stay in registers.
-        int64_t load[kDies];
-        int count[kDies];
-#pragma unroll
-        for (int x = 0; x < kDies; ++x) {
-            load[x] = 0;
-            count[x] = 0;
-        }
+        // Lane x < 8 holds die x: its kept blocks so far and its head count.
+        // Loads stay below 2^31 (at most H*nb*nb kept blocks in all).
+        int my_load = 0, my_count = 0;
         for (int a0 = 0; a0 < H; a0 += 64) {
             const int my_h = a0 + lane < H ? order[a0 + lane] : 0;
             const int my_kept = kept[my_h];
@@ -553,89 +620,26 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict
             for (int a = 0; a < n; ++a) {
                 const int h = __builtin_amdgcn_readlane(my_h, a);
                 const int kh = __builtin_amdgcn_readlane(my_kept, a);
-                int best = 0;
-                int64_t best_key = INT64_MAX;
-#pragma unroll
-                for (int x = 0; x < kDies; ++x) {
-                    const int64_t key = count[x] < cap_h ? load[x] * kDies + x : INT64_MAX;
-                    if (key < best_key) {
-                        best_key = key;
-                        best = x;
-                    }
+                int load = (lane < kDies && my_count < cap_h) ? my_load : INT_MAX;
+                int die = lane;
+                argmin_step<0xB1>(load, die);    // quad_perm [1,0,3,2]
+                argmin_step<0x4E>(load, die);    // quad_perm [2,3,0,1]
+                argmin_step<0x141>(load, die);   // row_half_mirror: lane i <-> 7 - i
+                const int best = __builtin_amdgcn_readlane(die, 0);
+                if (lane == best) {
+                    head_base[h] = (int32_t)(best * cap + (int64_t)my_count * nb);
+                    ++my_count;
+                    my_load += kh;
                 }
-                int base = 0;
-#pragma unroll
-                for (int x = 0; x < kDies; ++x)
-                    if (x == best) {
-                        base = (int)(x * cap + (int64_t)count[x] * nb);
-                        ++count[x];
-                        load[x] += kh;
-                    }
-                if (lane == 0) head_base[h] = base;
             }
         }
-        if (lane == 0)
-#pragma unroll
-            for (int x = 0; x < kDies; ++x) die_count[x] = count[x];
     }
     __syncthreads();
-    const uint64_t lt = lanemask_lt();
-    int32_t *nx = next[wave];
-    int16_t *ln = lens[wave];
-    int my_nonempty = 0;
-    for (int h = wave; h < H; h += kPlanWaves) {
-        const int64_t r0 = (int64_t)h * nb;
-        // Stage row_ptr[r0 .. r0 + nb] in nx (loads issued together), then
-        // the list lengths in ln.  A wave's LDS requests complete in order.
-        for (int c = 0; c <= nb; c += 512) {
-            int v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = row_ptr[r0 + min(c + lane + 64 * j, nb)];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (c + lane + 64 * j <= nb) nx[c + lane + 64 * j] = v[j];
-        }
-        for (int i = lane; i < nb; i += 64) {
-            const int len = nx[i + 1] - nx[i];
-            ln[i] = (int16_t)len;
-            my_nonempty += len > 0;
-        }
-        for (int l = lane; l <= nb; l += 64) nx[l] = 0;
-        for (int i = lane; i < nb; i += 64) atomicAdd(&nx[ln[i]], 1);
-        // Bucket starts, longest lists first: nx[l] = rows with length > l.
-        int carry = 0;
-        for (int c0 = nb; c0 >= 0; c0 -= 64) {
-            const int l = c0 - lane;
-            const int cnt = l >= 0 ? nx[l] : 0;
-            int inc = cnt;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(inc, o);
-                if (lane >= o) inc += y;
-            }
-            if (l >= 0) nx[l] = carry + inc - cnt;
-            carry += __shfl(inc, 63);
-        }
-        const int32_t base = head_base[h];
-        for (int i0 = 0; i0 < nb; i0 += 64) {
-            const int i = i0 + lane;
-            const bool valid = i < nb;
-            const int len = valid ? ln[i] : 0;
-            uint64_t same = __ballot(valid);
-#pragma unroll
-            for (int bit = 0; bit < 11; ++bit) {
-                const bool mine = (len >> bit) & 1;
-                const uint64_t b = __ballot(valid && mine);
-                same &= mine ? b : ~b;
-            }
-            const int rank = __popcll(same & lt);
-            const int pos = valid ? nx[len] + rank : 0;
-            if (valid && pos < nb) work[(int64_t)base + pos] = (int32_t)(r0 + i);
-            if (valid && rank == 0) nx[len] += __popcll(same);
-        }
+    const int64_t rows = (int64_t)H * nb;
+    for (int64_t x = tid; x < rows; x += kPlanThreads) {
+        const int h = (int)(x / nb), i = (int)(x % nb);
+        work[(int64_t)head_base[h] + i] = sorted[x];
     }
-    atomicAdd(&nonempty, my_nonempty);
-    __syncthreads();
     if (tid == 0) {
         meta[0] = (int32_t)cap;
         meta[1] = nonempty;
@@ -743,7 +747,11 @@ hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, char *ws, const Ws
                        hipStream_t s) {
     int32_t *work = reinterpret_cast<int32_t *>(ws + w.work);
     int32_t *meta = reinterpret_cast<int32_t *>(ws + w.work_meta);
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.H, D.nb, work, meta);
+    int32_t *sorted = reinterpret_cast<int32_t *>(ws + w.plan_sorted);
+    int32_t *ne_head = reinterpret_cast<int32_t *>(ws + w.plan_nonempty);
+    hipLaunchKernelGGL(k_plan_sort, dim3(D.H), dim3(64), 0, s, row_ptr, D.nb, sorted, ne_head);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.H, D.nb, sorted,
+                       ne_head, work, meta);
     return hipGetLastError();
 }
 
