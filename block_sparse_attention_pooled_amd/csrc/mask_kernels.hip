@@ -54,16 +54,17 @@ __device__ int64_t block_exclusive_scan_1024(int64_t x, int64_t *total) {
 }
 
 // ------------------------------------------------------------------- pool --
-// One thread owns 8 consecutive columns of one (head, block) and adds the B
+// One thread owns 4 consecutive columns of one (head, block) and adds the B
 // rows in ascending token order in fp32, then scales by 1/B (a power of two,
-// exact).  A wave covers 8 (d=64) or 4 (d=128) blocks with 128/256-byte
-// contiguous segments per load.
+// exact).  A wave covers 4 (d=64) or 2 (d=128) blocks with 128/256-byte
+// contiguous segments per load, and a thread keeps a whole 64-row batch of
+// loads in flight.
 template <int D>
 __global__ __launch_bounds__(256) void k_pool(const uint16_t *__restrict__ q,
                                               const uint16_t *__restrict__ k,
                                               float *__restrict__ qb, float *__restrict__ kb,
                                               int L, int B, int64_t nq_items, int64_t nk_items) {
-    constexpr int CG = D / 8;
+    constexpr int CG = D / 4;   // 4-column groups per row
     int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const uint16_t *src = q;
     float *dst = qb;
@@ -78,24 +79,30 @@ __global__ __launch_bounds__(256) void k_pool(const uint16_t *__restrict__ q,
     const int nb = L / B;
     const int64_t head = hb / nb;
     const int blk = (int)(hb % nb);
-    const uint4 *p = reinterpret_cast<const uint4 *>(src + (head * L + (int64_t)blk * B) * D) + cg;
-    float acc[8];
+    const uint2 *p = reinterpret_cast<const uint2 *>(src + (head * L + (int64_t)blk * B) * D) + cg;
+    float acc[4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
-#pragma unroll 8
-    for (int t = 0; t < B; ++t) {
-        const uint4 u = p[(int64_t)t * CG];
-        uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int c = 0; c < 4; ++c) acc[c] = 0.0f;
+    // Batches of 64 rows: all of a batch's loads are in flight before the
+    // first add; the adds still run in ascending token order.
+    constexpr int kBatch = 64;   // B is 64 or 128
+    for (int t0 = 0; t0 < B; t0 += kBatch) {
+        uint2 u[kBatch];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            acc[2 * c] = acc[2 * c] + bf16_bits_to_float(w[c] & 0xFFFFu);
-            acc[2 * c + 1] = acc[2 * c + 1] + bf16_bits_to_float(w[c] >> 16);
+        for (int j = 0; j < kBatch; ++j) u[j] = p[(int64_t)(t0 + j) * CG];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const uint32_t w[2] = {u[j].x, u[j].y};
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                acc[2 * c] = acc[2 * c] + bf16_bits_to_float(w[c] & 0xFFFFu);
+                acc[2 * c + 1] = acc[2 * c + 1] + bf16_bits_to_float(w[c] >> 16);
+            }
         }
     }
     const float inv_b = 1.0f / (float)B;
-    float4 *out = reinterpret_cast<float4 *>(dst + hb * D + cg * 8);
-    out[0] = make_float4(acc[0] * inv_b, acc[1] * inv_b, acc[2] * inv_b, acc[3] * inv_b);
-    out[1] = make_float4(acc[4] * inv_b, acc[5] * inv_b, acc[6] * inv_b, acc[7] * inv_b);
+    *reinterpret_cast<float4 *>(dst + hb * D + cg * 4) =
+        make_float4(acc[0] * inv_b, acc[1] * inv_b, acc[2] * inv_b, acc[3] * inv_b);
 }
 
 // ---------------------------------------------------------- score + softmax --
@@ -651,7 +658,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict
 // ------------------------------------------------------------------ launches --
 hipError_t launch_pool(const Dims &D, const uint16_t *q, const uint16_t *k, float *qb, float *kb,
                        hipStream_t s) {
-    const int64_t cg = D.d / 8;
+    const int64_t cg = D.d / 4;
     const int64_t nq = (int64_t)D.H * D.nb * cg, nk = (int64_t)D.Hkv * D.nb * cg;
     const int64_t grid = (nq + nk + 255) / 256;
     if (D.d == 128)
@@ -664,7 +671,7 @@ hipError_t launch_pool(const Dims &D, const uint16_t *q, const uint16_t *k, floa
 }
 
 hipError_t launch_pool_q(const Dims &D, const uint16_t *q, float *qb, hipStream_t s) {
-    const int64_t nq = (int64_t)D.H * D.nb * (D.d / 8);
+    const int64_t nq = (int64_t)D.H * D.nb * (D.d / 4);
     const int64_t grid = (nq + 255) / 256;
     if (D.d == 128)
         hipLaunchKernelGGL(k_pool<128>, dim3((unsigned)grid), dim3(256), 0, s, q, nullptr, qb,
