@@ -56,6 +56,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define SD_LDS __attribute__((address_space(3)))
 #define SD_GLOBAL __attribute__((address_space(1)))
 
@@ -69,6 +70,13 @@ constexpr int kModeCols = 2;        // the head's kept key columns (col_idx = [H
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
+}
+
+// O is written once and read by a later kernel: non-temporal stores stream it
+// out instead of leaving dirty lines in this die's L2 for the end-of-kernel
+// write-back.
+__device__ __forceinline__ void store_nt(uint16_t *p, uint4 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float x) {
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     if (n_total <= 0) {     // no kept key: the row attends to nothing
         const uint4 z = make_uint4(0, 0, 0, 0);
         for (int x = lane; x < QW * D / 8; x += 64)
-            *reinterpret_cast<uint4 *>(o + qbase + (int64_t)x * 8) = z;
+            store_nt(o + qbase + (int64_t)x * 8, z);
         return;
     }
 
@@ -545,7 +553,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         const int r = t * RPI + lane / SEGS, sg = lane % SEGS;
         const uint4 val =
             *reinterpret_cast<const uint4 *>(ot + r * D + 8 * (sg ^ (r & (SEGS - 1))));
-        *reinterpret_cast<uint4 *>(orow + (int64_t)r * D + 8 * sg) = val;
+        store_nt(orow + (int64_t)r * D + 8 * sg, val);
     }
 }
 
