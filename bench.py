@@ -205,6 +205,7 @@ def mask_quality(args, w, sparsity, dev, T):
     best_ci = torch.empty(max(drv.K, 1), dtype=torch.int32, device=dev)
     best_ws = torch.empty(B.workspace_bytes(dims), dtype=torch.uint8, device=dev)
     best_at_anchor = []
+    overlap, prev_keep = [], None      # kept set shared with the previous anchor
     per_step, kinds, mass_ms = [], [], []
     since_anchor = []
     last_anchor = None
@@ -216,6 +217,17 @@ def mask_quality(args, w, sparsity, dev, T):
             continue
         if kind == 1:
             last_anchor = t
+            if args.columns:
+                cols = drv.cols().cpu()
+                keep = set((cols + (torch.arange(w.H).view(-1, 1) * w.L)).view(-1).tolist())
+            else:
+                rp = drv.row_ptr.cpu()
+                ci = drv.col_idx[:drv.K].cpu()
+                rows = torch.repeat_interleave(torch.arange(w.H * w.nb), rp[1:] - rp[:-1])
+                keep = set((rows * w.nb + ci.long()).tolist())
+            if prev_keep is not None:
+                overlap.append(round(len(keep & prev_keep) / max(len(keep), 1), 5))
+            prev_keep = keep
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if args.columns:
             # Recall of the kept columns straight from this step's Q/K.
@@ -278,6 +290,7 @@ def mask_quality(args, w, sparsity, dev, T):
                                     else drv.K / (w.H * w.nb * w.nb), 5),
         "recall_last_step_of_interval": round(sum(last_in) / len(last_in), 5) if last_in else None,
         "recall_by_steps_since_anchor": by_offset,
+        "anchor_overlap_with_previous": overlap,
         "recall_per_step": [round(x, 5) for x in per_step],
         ("col_recall_ms" if args.columns else "block_mass_ms"): round(mms, 4),
         ("col_recall_tflops" if args.columns else "block_mass_tflops"):
@@ -448,6 +461,8 @@ def main():
         "roofline": roofline,
         "kept_per_head": {"min": min(per_head), "max": max(per_head),
                           "cv": round(ph_cv, 4)},
+        "empty_rows": (None if args.columns else
+                       int((drv.row_ptr[1:] == drv.row_ptr[:-1]).sum().item())),
         "anchor_step_ms": round(anchor_ms, 5) if anchor_ms else None,
         "mask_build_ms": round(anchor_ms - attn_ms, 5) if (anchor_ms and attn_ms) else None,
         "anchors_timed": n_anchor,
