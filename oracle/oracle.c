@@ -225,8 +225,11 @@ int64_t oracle_build_mask_per_head(const float *q, const float *k, int H, int Hk
 /* Work order for the attention launch on a GPU made of 8 dies (XCDs) that take
  * workgroups round robin, so that all rows of a head share one die's L2 and
  * each die's rows start longest first:
- *  - heads are taken in order of kept blocks (descending, ties by head id) and
- *    each goes to the die with the fewest kept blocks so far among those that
+ *  - a head weighs w = (B/32)*kept + 4*nonempty: its kept blocks in 32-key
+ *    steps plus four steps for each row with a kept block, the fixed start-up
+ *    and write-out of a row (B is a multiple of 32);
+ *  - heads are taken in order of weight (descending, ties by head id) and
+ *    each goes to the die with the least weight so far among those that
  *    hold fewer than cap_h = min(H, ceil(H/8) + 2) heads (ties: lowest die);
  *    the slack over ceil(H/8) lets the greedy balance skewed heads;
  *  - die x's list is its heads in that order, each head's rows by list
@@ -235,7 +238,7 @@ int64_t oracle_build_mask_per_head(const float *q, const float *k, int H, int Hk
  *    positions hold -1.
  * Returns the number of rows with at least one kept block. */
 static const int32_t *g_row_ptr;
-static const int64_t *g_head_kept;
+static const int64_t *g_head_weight;
 
 static int by_len_desc_row_asc(const void *pa, const void *pb)
 {
@@ -247,44 +250,46 @@ static int by_len_desc_row_asc(const void *pa, const void *pb)
     return (a < b) ? -1 : (a > b);
 }
 
-static int by_kept_desc_head_asc(const void *pa, const void *pb)
+static int by_weight_desc_head_asc(const void *pa, const void *pb)
 {
     int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
-    if (g_head_kept[a] > g_head_kept[b]) return -1;
-    if (g_head_kept[a] < g_head_kept[b]) return 1;
+    if (g_head_weight[a] > g_head_weight[b]) return -1;
+    if (g_head_weight[a] < g_head_weight[b]) return 1;
     return (a < b) ? -1 : (a > b);
 }
 
 enum { ORACLE_DIES = 8 };
 
-int32_t oracle_plan(const int32_t *row_ptr, int H, int nb, int32_t *work)
+int32_t oracle_plan(const int32_t *row_ptr, int H, int nb, int B, int32_t *work)
 {
     int cap_heads = (H + ORACLE_DIES - 1) / ORACLE_DIES + 2;
     if (cap_heads > H)
         cap_heads = H;
     int64_t cap = (int64_t)cap_heads * nb;
-    int64_t *kept = (int64_t *)malloc(sizeof(int64_t) * (size_t)H);
+    int64_t *weight = (int64_t *)malloc(sizeof(int64_t) * (size_t)H);
     int32_t *heads = (int32_t *)malloc(sizeof(int32_t) * (size_t)H);
     int32_t *die_heads = (int32_t *)malloc(sizeof(int32_t) * (size_t)(ORACLE_DIES * cap_heads));
     int64_t load[ORACLE_DIES] = {0};
     int count[ORACLE_DIES] = {0};
     int32_t n_nonempty = 0;
     for (int h = 0; h < H; ++h) {
-        kept[h] = row_ptr[(h + 1) * nb] - row_ptr[h * nb];
+        int64_t kept = row_ptr[(h + 1) * nb] - row_ptr[h * nb];
+        int64_t rows = 0;
+        for (int i = 0; i < nb; ++i)
+            rows += row_ptr[h * nb + i + 1] > row_ptr[h * nb + i];
+        weight[h] = (B / 32) * kept + 4 * rows;
+        n_nonempty += (int32_t)rows;
         heads[h] = h;
     }
-    for (int r = 0; r < H * nb; ++r)
-        if (row_ptr[r + 1] > row_ptr[r])
-            ++n_nonempty;
-    g_head_kept = kept;
-    qsort(heads, (size_t)H, sizeof(int32_t), by_kept_desc_head_asc);
+    g_head_weight = weight;
+    qsort(heads, (size_t)H, sizeof(int32_t), by_weight_desc_head_asc);
     for (int a = 0; a < H; ++a) {
         int best = -1;
         for (int x = 0; x < ORACLE_DIES; ++x)
             if (count[x] < cap_heads && (best < 0 || load[x] < load[best]))
                 best = x;
         die_heads[best * cap_heads + count[best]++] = heads[a];
-        load[best] += kept[heads[a]];
+        load[best] += weight[heads[a]];
     }
     for (int64_t p = 0; p < ORACLE_DIES * cap; ++p)
         work[p] = -1;
@@ -299,7 +304,7 @@ int32_t oracle_plan(const int32_t *row_ptr, int H, int nb, int32_t *work)
             out += nb;
         }
     }
-    free(kept);
+    free(weight);
     free(heads);
     free(die_heads);
     return n_nonempty;

@@ -43,7 +43,7 @@ def _bind(lib):
         "oracle_build_mask": (ci64, [f32p, f32p, ci, ci, ci, ci, ci, cd, f32p, f32p, f32p, i32p, i32p]),
         "oracle_build_mask_per_head": (ci64, [f32p, f32p, ci, ci, ci, ci, ci, cd, f32p, f32p, f32p,
                                               i32p, i32p]),
-        "oracle_plan": (ctypes.c_int32, [i32p, ci, ci, i32p]),
+        "oracle_plan": (ctypes.c_int32, [i32p, ci, ci, ci, i32p]),
         "oracle_sparse_attn": (None, [f32p, f32p, f32p, ci, ci, ci, ci, ci, i32p, i32p, vp, ci, f64p]),
         "oracle_dense_attn": (None, [f32p, f32p, f32p, ci, ci, ci, ci, ci, vp, ci, f64p]),
         "oracle_step_kind": (ci, [ci, ci, ci]),
@@ -170,14 +170,14 @@ def build_mask(q, k, B, sparsity, lib=None, per_head=False):
 DIES = 8
 
 
-def plan(row_ptr, H, nb, lib=None):
+def plan(row_ptr, H, nb, B, lib=None):
     """-> (work [8 * cap] int32 with -1 padding, n_nonempty); cap =
-    min(H, ceil(H/8) + 2) * nb."""
+    min(H, ceil(H/8) + 2) * nb; heads weigh (B/32)*kept + 4*nonempty rows."""
     lib = lib or load()
     row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
     cap = min(H, -(-H // DIES) + 2) * nb
     work = np.empty(DIES * cap, np.int32)
-    n = lib.oracle_plan(row_ptr, int(H), int(nb), work)
+    n = lib.oracle_plan(row_ptr, int(H), int(nb), int(B), work)
     return work, int(n)
 
 

@@ -191,44 +191,83 @@ def pin_csr(lib):
         assert np.array_equal(col_idx[row_ptr[r]:row_ptr[r + 1]], np.nonzero(flat[r])[0])
 
 
-def _die_lists(lens, H, nb):
-    """The die lists of the work-order spec written out in Python: heads by kept
-    blocks (descending, then id) to the least-loaded die with room for
-    min(H, ceil(H/8) + 2) heads; each die lists its heads in that order, rows
-    by length desc, ties by row id."""
+def _die_lists(lens, H, nb, B):
+    """The die lists of the work-order spec written out in Python: heads by
+    weight (B/32)*kept + 4*nonempty rows (descending, then id) to the
+    least-loaded die with room for min(H, ceil(H/8) + 2) heads; each die lists
+    its heads in that order, rows by length desc, ties by row id."""
     cap_h = min(H, -(-H // 8) + 2)
-    kept = [int(sum(lens[h * nb:(h + 1) * nb])) for h in range(H)]
+    weight = [(B // 32) * int(sum(lens[h * nb:(h + 1) * nb]))
+              + 4 * int(sum(1 for r in range(h * nb, (h + 1) * nb) if lens[r] > 0))
+              for h in range(H)]
     dies = [[] for _ in range(8)]
     load = [0] * 8
-    for h in sorted(range(H), key=lambda h: (-kept[h], h)):
+    for h in sorted(range(H), key=lambda h: (-weight[h], h)):
         x = min((x for x in range(8) if len(dies[x]) < cap_h), key=lambda x: (load[x], x))
         dies[x].append(h)
-        load[x] += kept[h]
+        load[x] += weight[h]
     return [[r for h in dies[x] for r in sorted(range(h * nb, (h + 1) * nb),
                                                  key=lambda r: (-lens[r], r))]
             for x in range(8)]
 
 
 def pin_plan(lib):
-    # Hand-derived: H=3, nb=4, one head per die.  Kept per head: 5, 9, 5, so
-    # head 1 -> die 0, head 0 -> die 1, head 2 -> die 2; dies 3..7 stay empty.
-    # A die may hold min(3, 1 + 2) = 3 heads, so 12 positions per die.
+    # Hand-derived: H=3, nb=4, B=64 (2 steps of 32 keys per block), one head
+    # per die.  Kept blocks per head 5, 9, 5 over 2, 3, 4 non-empty rows, so
+    # the weights are 2*5 + 4*2 = 18, 2*9 + 4*3 = 30, 2*5 + 4*4 = 26: head 1 ->
+    # die 0, head 2 -> die 1, head 0 -> die 2 (by kept blocks alone, heads 0
+    # and 2 would tie and head 0 would come first); dies 3..7 stay empty.  A
+    # die may hold min(3, 1 + 2) = 3 heads, so 12 positions per die.
     lens = np.array([2, 0, 3, 0,   4, 1, 4, 0,   1, 1, 1, 2])
     row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    work, n = O.plan(row_ptr, 3, 4, lib)
+    work, n = O.plan(row_ptr, 3, 4, 64, lib)
     pad = [-1] * 8
-    want = [4, 6, 5, 7] + pad + [2, 0, 1, 3] + pad + [11, 8, 9, 10] + pad + [-1] * 60
+    want = [4, 6, 5, 7] + pad + [11, 8, 9, 10] + pad + [2, 0, 1, 3] + pad + [-1] * 60
     assert list(work) == want and n == 9
-    # Head cap slack: 12 heads of kept 30, 1, 1, ..., 1 with 8 dies: each die
-    # may hold min(12, 2 + 2) = 4 heads.  Head 0 -> die 0 (30); heads 1..7 ->
-    # dies 1..7; heads 8..11 (1 block each) go to the lightest dies, 1..4,
-    # never to die 0.  Within a die, heads in assignment order.
+    # The same mask with B=128 (4 steps per block): weights 28, 48, 36, same
+    # order.
+    work, n = O.plan(row_ptr, 3, 4, 128, lib)
+    assert list(work) == want and n == 9
+    # Block size decides: head 0 keeps two rows of 1 block, head 1 one row of
+    # 4.  B=64: weights 2*2 + 8 = 12 and 2*4 + 4 = 12 tie, head 0 -> die 0.
+    # B=128: 4*2 + 8 = 16 against 4*4 + 4 = 20, head 1 -> die 0.
+    lens = np.array([1, 1, 4, 0])
+    row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    work, n = O.plan(row_ptr, 2, 2, 64, lib)
+    assert list(work) == [0, 1, -1, -1, 2, 3, -1, -1] + [-1] * 24 and n == 3
+    work, n = O.plan(row_ptr, 2, 2, 128, lib)
+    assert list(work) == [2, 3, -1, -1, 0, 1, -1, -1] + [-1] * 24 and n == 3
+    # Hand-derived die choice: H=9, nb=4, B=64, 4 positions per head, a die
+    # may hold min(9, 2 + 2) = 4 heads (16 positions).  Head 0 keeps one row of
+    # 3 blocks (weight 6 + 4 = 10), head 1 three rows of 1 block (6 + 12 =
+    # 18), heads 2..7 one row of 4 blocks (8 + 4 = 12), head 8 one row of 1
+    # block (2 + 4 = 6).  Order: head 1, heads 2..7, head 0, head 8; heads
+    # 1..7 take dies 0..6, head 0 die 7 (load 10) and head 8 the least-loaded
+    # die, die 7.  (By kept blocks alone, head 8 would join head 0 on die 6.)
+    lens = np.zeros(9 * 4, np.int64)
+    lens[0] = 3
+    lens[4:7] = 1
+    for h in range(2, 8):
+        lens[4 * h] = 4
+    lens[32] = 1
+    row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    work, n = O.plan(row_ptr, 9, 4, 64, lib)
+    assert n == 11 and len(work) == 8 * 16
+    assert list(work[:16]) == [4, 5, 6, 7] + [-1] * 12
+    for x in range(1, 7):
+        assert list(work[16 * x:16 * (x + 1)]) == [4 * (x + 1) + c for c in range(4)] + [-1] * 12, x
+    assert list(work[112:]) == [0, 1, 2, 3, 32, 33, 34, 35] + [-1] * 8
+    # Head cap slack: 12 heads of kept 30, 1, 1, ..., 1 with 8 dies (weights
+    # 2*30 + 4*2 = 68 and 2 + 4 = 6): each die may hold min(12, 2 + 2) = 4
+    # heads.  Head 0 -> die 0; heads 1..7 -> dies 1..7; heads 8..11 go to the
+    # lightest dies, 1..4, never to die 0.  Within a die, heads in assignment
+    # order.
     lens = np.zeros(12 * 2, np.int64)
     lens[0], lens[1] = 20, 10
     for h in range(1, 12):
         lens[2 * h] = 1
     row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    work, n = O.plan(row_ptr, 12, 2, lib)
+    work, n = O.plan(row_ptr, 12, 2, 64, lib)
     cap = 8
     assert len(work) == 8 * cap and n == 13
     assert list(work[:cap]) == [0, 1] + [-1] * 6
@@ -241,19 +280,19 @@ def pin_plan(lib):
     # longest first, the two of length 2 by row id.
     lens = np.array([2, 4, 1, 3, 2])
     row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    work, n = O.plan(row_ptr, 1, 5, lib)
+    work, n = O.plan(row_ptr, 1, 5, 64, lib)
     assert list(work[:5]) == [1, 3, 0, 4, 2] and all(w == -1 for w in work[5:])
     assert len(work) == 8 * 5 and n == 5
     # Random shapes (several heads per die) against the spec written out.
     rng = np.random.default_rng(RNG_SEEDS[1] + 7)
-    for H, nb in ((20, 6), (28, 9), (8, 5), (33, 3), (17, 12)):
+    for H, nb, B in ((20, 6, 64), (28, 9, 128), (8, 5, 64), (33, 3, 64), (17, 12, 128)):
         lens = rng.integers(0, nb + 1, size=H * nb) * (rng.random(H * nb) < 0.7)
         lens[: nb] = 0                                  # one head keeps nothing
         row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-        work, n = O.plan(row_ptr, H, nb, lib)
+        work, n = O.plan(row_ptr, H, nb, B, lib)
         cap = min(H, -(-H // 8) + 2) * nb
         want = []
-        for lst in _die_lists(lens, H, nb):
+        for lst in _die_lists(lens, H, nb, B):
             want += lst + [-1] * (cap - len(lst))
         assert list(work) == want
         assert n == int((lens > 0).sum())

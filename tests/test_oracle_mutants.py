@@ -40,8 +40,11 @@ MUTANTS = [
     ("plan_ascending", "if (la > lb) return -1;", "if (la < lb) return -1;", 0),
     ("plan_most_loaded_die", "load[x] < load[best]", "load[x] > load[best]", 0),
     ("plan_heads_ascending",
-     "if (g_head_kept[a] > g_head_kept[b]) return -1;\n    if (g_head_kept[a] < g_head_kept[b]) return 1;",
-     "if (g_head_kept[a] > g_head_kept[b]) return 1;\n    if (g_head_kept[a] < g_head_kept[b]) return -1;", 0),
+     "if (g_head_weight[a] > g_head_weight[b]) return -1;\n    if (g_head_weight[a] < g_head_weight[b]) return 1;",
+     "if (g_head_weight[a] > g_head_weight[b]) return 1;\n    if (g_head_weight[a] < g_head_weight[b]) return -1;", 0),
+    ("plan_weight_kept_only", "weight[h] = (B / 32) * kept + 4 * rows;", "weight[h] = kept;", 0),
+    ("plan_weight_no_row_cost", "weight[h] = (B / 32) * kept + 4 * rows;", "weight[h] = (B / 32) * kept;", 0),
+    ("plan_weight_steps_ignore_block", "weight[h] = (B / 32) * kept + 4 * rows;", "weight[h] = 2 * kept + 4 * rows;", 0),
     ("attn_block_index_not_scaled", "toks[ntok++] = col_idx[e] * B + t;",
      "toks[ntok++] = col_idx[e] + t;", 0),
     ("attn_no_scale", "double scale = 1.0 / sqrt((double)d);", "double scale = 1.0;", 0),
