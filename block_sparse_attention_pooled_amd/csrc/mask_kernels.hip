@@ -502,10 +502,12 @@ __global__ __launch_bounds__(1024) void k_col_compact(const float *__restrict__ 
 // Work order for the attention launch.  The GPU has kDies dies (XCDs), each
 // with its own L2, and workgroup b of a launch runs on die b % kDies.  All
 // rows of a head go to one die so that the head's K/V stay in that die's L2:
-//  * heads are ranked by kept blocks (descending, ties by head id) and, in
-//    that order, each goes to the die with the fewest kept blocks so far among
-//    those holding fewer than min(H, ceil(H / kDies) + 2) heads (ties: lowest
-//    die);
+//  * a head weighs (B/32) * kept + 4 * nonempty: the 32-key steps of its
+//    kept blocks plus four steps per row that keeps a block, for the row's
+//    fixed start-up and write-out;
+//  * heads are ranked by weight (descending, ties by head id) and, in that
+//    order, each goes to the die with the least weight so far among those
+//    holding fewer than min(H, ceil(H / kDies) + 2) heads (ties: lowest die);
 //  * die x's list is its heads in assignment order, each head's rows by list
 //    length descending (ties by row id), at work[x*cap ..], cap = (heads a die
 //    may hold) * nb; unused positions hold -1.
@@ -579,8 +581,10 @@ __global__ __launch_bounds__(64) void k_plan_sort(const int32_t *__restrict__ ro
 // One step of the die argmin: take the (load, die) pair of the lane that
 // dpp_ctrl names when it is smaller.
 template <int CTRL>
-__device__ __forceinline__ void argmin_step(int &load, int &die) {
-    const int l2 = __builtin_amdgcn_update_dpp(0, load, CTRL, 0xF, 0xF, false);
+__device__ __forceinline__ void argmin_step(int64_t &load, int &die) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)load, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(load >> 32), CTRL, 0xF, 0xF, false);
+    const int64_t l2 = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
     const int d2 = __builtin_amdgcn_update_dpp(0, die, CTRL, 0xF, 0xF, false);
     const bool take = l2 < load || (l2 == load && d2 < die);
     load = take ? l2 : load;
@@ -590,13 +594,13 @@ __device__ __forceinline__ void argmin_step(int &load, int &die) {
 constexpr int kPlanThreads = 512;
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict__ row_ptr,
-                                                       int H, int nb,
+                                                       int H, int nb, int steps_per_block,
                                                        const int32_t *__restrict__ sorted,
                                                        const int32_t *__restrict__ ne_head,
                                                        int32_t *__restrict__ work,
                                                        int32_t *__restrict__ meta) {
     static_assert(kDies == 8, "the die argmin covers 8 lanes");
-    __shared__ int32_t kept[kMaxHeads];
+    __shared__ int64_t weight[kMaxHeads];
     __shared__ int32_t order[kMaxHeads];
     __shared__ int32_t head_base[kMaxHeads];
     __shared__ int32_t nonempty;
@@ -605,29 +609,33 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict
     const int64_t cap = (int64_t)cap_h * nb;
     if (tid == 0) nonempty = 0;
     for (int h = tid; h < H; h += kPlanThreads)
-        kept[h] = row_ptr[(int64_t)(h + 1) * nb] - row_ptr[(int64_t)h * nb];
+        weight[h] = (int64_t)steps_per_block *
+                        (row_ptr[(int64_t)(h + 1) * nb] - row_ptr[(int64_t)h * nb]) +
+                    4 * (int64_t)ne_head[h];
     for (int64_t p = tid; p < kDies * cap; p += kPlanThreads) work[p] = -1;
     __syncthreads();
     for (int h = tid; h < H; h += kPlanThreads) {
         int rank = 0;
         for (int o = 0; o < H; ++o)
-            rank += (kept[o] > kept[h]) || (kept[o] == kept[h] && o < h);
+            rank += (weight[o] > weight[h]) || (weight[o] == weight[h] && o < h);
         order[rank] = h;
         atomicAdd(&nonempty, ne_head[h]);
     }
     __syncthreads();
     if (wave == 0) {
-        // Lane x < 8 holds die x: its kept blocks so far and its head count.
-        // Loads stay below 2^31 (at most H*nb*nb kept blocks in all).
-        int my_load = 0, my_count = 0;
+        // Lane x < 8 holds die x: its weight so far and its head count.
+        int64_t my_load = 0;
+        int my_count = 0;
         for (int a0 = 0; a0 < H; a0 += 64) {
             const int my_h = a0 + lane < H ? order[a0 + lane] : 0;
-            const int my_kept = kept[my_h];
+            const int64_t my_w = weight[my_h];
             const int n = min(64, H - a0);
             for (int a = 0; a < n; ++a) {
                 const int h = __builtin_amdgcn_readlane(my_h, a);
-                const int kh = __builtin_amdgcn_readlane(my_kept, a);
-                int load = (lane < kDies && my_count < cap_h) ? my_load : INT_MAX;
+                const int64_t wh = (int64_t)(
+                    ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(my_w >> 32), a) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_w, a));
+                int64_t load = (lane < kDies && my_count < cap_h) ? my_load : INT64_MAX;
                 int die = lane;
                 argmin_step<0xB1>(load, die);    // quad_perm [1,0,3,2]
                 argmin_step<0x4E>(load, die);    // quad_perm [2,3,0,1]
@@ -636,7 +644,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict
                 if (lane == best) {
                     head_base[h] = (int32_t)(best * cap + (int64_t)my_count * nb);
                     ++my_count;
-                    my_load += kh;
+                    my_load += wh;
                 }
             }
         }
@@ -757,8 +765,8 @@ hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, char *ws, const Ws
     int32_t *sorted = reinterpret_cast<int32_t *>(ws + w.plan_sorted);
     int32_t *ne_head = reinterpret_cast<int32_t *>(ws + w.plan_nonempty);
     hipLaunchKernelGGL(k_plan_sort, dim3(D.H), dim3(64), 0, s, row_ptr, D.nb, sorted, ne_head);
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.H, D.nb, sorted,
-                       ne_head, work, meta);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.H, D.nb, D.B / 32,
+                       sorted, ne_head, work, meta);
     return hipGetLastError();
 }
 

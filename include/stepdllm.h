@@ -168,9 +168,11 @@ int stepdllm_select_mask_per_head(const stepdllm_dims *dims, double sparsity,
 
 /* Work order for a caller-built mask (row_ptr as above).  The GPU's 8 dies
  * (XCDs) each have their own L2 and take workgroups round robin, so all rows
- * of a head go to one die: heads are ranked by kept blocks (descending, ties
- * by id) and each goes to the least-loaded die that holds fewer than
- * min(H, ceil(H/8) + 2) heads (ties: lowest die); a die's list is its heads in that
+ * of a head go to one die.  A head weighs (B/32) * kept blocks + 4 * rows that
+ * keep a block (its 32-key steps plus a fixed start-up and write-out per row);
+ * heads are ranked by weight (descending, ties by id) and each goes to the
+ * least-loaded die that holds fewer than min(H, ceil(H/8) + 2) heads (ties:
+ * lowest die); a die's list is its heads in that
  * order, each head's rows by list length descending (ties by row id), at
  * positions [x*cap, x*cap + cap) of the work order.  Workgroup b of the
  * sparse launch takes position b / 8 of die b % 8's list, so each die starts
