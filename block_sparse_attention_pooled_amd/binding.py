@@ -32,7 +32,7 @@ class Schedule(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("pooled_q", "pooled_k", "scores", "select", "work", "work_meta",
-                 "head_select", "col_scores", "col_stats", "total")]
+                 "head_select", "col_scores", "col_stats", "work_rec", "total")]
 
 
 class StepDLLMError(RuntimeError):
@@ -64,8 +64,8 @@ def load():
         "stepdllm_select_mask": (i32, [D, dbl, _vp, _vp, sz, _vp, _vp, _vp]),
         "stepdllm_build_mask_per_head": (i32, [D, dbl, _vp, _vp, _vp, sz, _vp, _vp, _vp, _vp]),
         "stepdllm_select_mask_per_head": (i32, [D, dbl, _vp, _vp, sz, _vp, _vp, _vp]),
-        "stepdllm_plan": (i32, [D, _vp, _vp, sz, _vp]),
-        "stepdllm_sparse_attn": (i32, [D, _vp, _vp, _vp, _vp, _vp, i64, _vp, sz, _vp, _vp]),
+        "stepdllm_plan": (i32, [D, _vp, _vp, i64, _vp, sz, _vp]),
+        "stepdllm_sparse_attn": (i32, [D, _vp, _vp, _vp, _vp, i64, _vp, sz, _vp, _vp]),
         "stepdllm_dense_attn": (i32, [D, _vp, _vp, _vp, _vp, _vp]),
         "stepdllm_block_mass": (i32, [D, _vp, _vp, _vp, _vp]),
         "stepdllm_mask_recall": (i32, [D, _vp, _vp, _vp, i64, _vp, _vp]),
@@ -178,19 +178,24 @@ def select_mask(dims, sparsity, scores, ws, row_ptr, col_idx, stream=None, per_h
         _ptr(col_idx, torch.int32, "col_idx"), _stream(stream)), fn)
 
 
-def plan(dims, row_ptr, ws, stream=None):
+def plan(dims, row_ptr, col_idx, ws, nnz=None, stream=None):
+    """Work order and records of the mask row_ptr / col_idx; nnz defaults to
+    col_idx.numel()."""
+    nnz = col_idx.numel() if nnz is None else int(nnz)
     _check(load().stepdllm_plan(ctypes.byref(dims), _ptr(row_ptr, torch.int32, "row_ptr"),
+                                _ptr(col_idx, torch.int32, "col_idx"), nnz,
                                 _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
            "stepdllm_plan")
 
 
-def sparse_attn(dims, q, k, v, row_ptr, col_idx, ws, o, nnz=None, stream=None):
-    """nnz defaults to col_idx.numel()."""
+def sparse_attn(dims, q, k, v, col_idx, ws, o, nnz=None, stream=None):
+    """Sparse attention on the mask whose plan is in ws (col_idx: its lists);
+    nnz defaults to col_idx.numel()."""
     bf = torch.bfloat16
     nnz = col_idx.numel() if nnz is None else int(nnz)
     _check(load().stepdllm_sparse_attn(
         ctypes.byref(dims), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
-        _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"), nnz,
+        _ptr(col_idx, torch.int32, "col_idx"), nnz,
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _ptr(o, bf, "o"), _stream(stream)),
         "stepdllm_sparse_attn")
 
@@ -356,6 +361,10 @@ class MaskBuffers:
 
     def work_meta(self):
         return self.view(self.layout.work_meta, 16, torch.int32)
+
+    def work_rec(self):
+        """[8 * cap, 4] int32: row, list begin, list end, first two block ids."""
+        return self.view(self.layout.work_rec, 32 * self.work_cap(), torch.int32).view(-1, 4)
 
     def head_select(self):
         return self.view(self.layout.head_select, 8 * self.dims.n_q_heads, torch.int32)

@@ -76,12 +76,13 @@ int hip_status(hipError_t e) { return e == hipSuccess ? STEPDLLM_OK : STEPDLLM_E
 
 int select_and_plan(const Dims &D, double sparsity, bool per_head, const float *p, char *ws,
                     const WsLayout &w, int32_t *row_ptr, int32_t *col_idx, hipStream_t s) {
+    const int64_t k_h = per_head ? keep_count_per_head(D, sparsity) : 0;
+    const int64_t K = per_head ? k_h * D.H : keep_count(D, sparsity);
     int st = hip_status(
-        per_head ? sd::launch_select_per_head(D, keep_count_per_head(D, sparsity), p, ws, w,
-                                              row_ptr, col_idx, s)
-                 : sd::launch_select(D, keep_count(D, sparsity), p, ws, w, row_ptr, col_idx, s));
+        per_head ? sd::launch_select_per_head(D, k_h, p, ws, w, row_ptr, col_idx, s)
+                 : sd::launch_select(D, K, p, ws, w, row_ptr, col_idx, s));
     if (st) return st;
-    return hip_status(sd::launch_plan(D, row_ptr, ws, w, s));
+    return hip_status(sd::launch_plan(D, row_ptr, col_idx, K, ws, w, s));
 }
 
 int build_mask(const stepdllm_dims *dims, double sparsity, bool per_head, const uint16_t *q,
@@ -205,6 +206,7 @@ int stepdllm_workspace_layout(const stepdllm_dims *dims, stepdllm_ws_layout *out
     out->head_select = w.hsel;
     out->col_scores = w.col_scores;
     out->col_stats = w.col_stats;
+    out->work_rec = w.work_rec;
     out->total = w.total;
     return STEPDLLM_OK;
 }
@@ -235,31 +237,31 @@ int stepdllm_select_mask_per_head(const stepdllm_dims *dims, double sparsity,
     return select_mask(dims, sparsity, true, scores, ws, ws_bytes, row_ptr, col_idx, stream);
 }
 
-int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr, void *ws, size_t ws_bytes,
-                  void *stream) {
+int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr, const int32_t *col_idx,
+                  int64_t nnz, void *ws, size_t ws_bytes, void *stream) {
     Dims D;
     int st = check_dims(dims, &D);
     if (st) return st;
-    if (!row_ptr || !ws) return STEPDLLM_EINVAL;
-    WsLayout w = sd::ws_layout(D);
-    if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
-    return hip_status(
-        sd::launch_plan(D, row_ptr, static_cast<char *>(ws), w, static_cast<hipStream_t>(stream)));
-}
-
-int stepdllm_sparse_attn(const stepdllm_dims *dims, const uint16_t *q, const uint16_t *k,
-                         const uint16_t *v, const int32_t *row_ptr, const int32_t *col_idx,
-                         int64_t nnz, const void *ws, size_t ws_bytes, uint16_t *o,
-                         void *stream) {
-    Dims D;
-    int st = check_dims(dims, &D);
-    if (st) return st;
-    if (!q || !k || !v || !row_ptr || !col_idx || !ws || !o) return STEPDLLM_EINVAL;
+    if (!row_ptr || !col_idx || !ws) return STEPDLLM_EINVAL;
     if (nnz < 0 || nnz > D.n_scores()) return STEPDLLM_EINVAL;
     WsLayout w = sd::ws_layout(D);
     if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
-    const int32_t *work = reinterpret_cast<const int32_t *>(static_cast<const char *>(ws) + w.work);
-    return hip_status(sd::launch_sparse_attn(D, q, k, v, row_ptr, col_idx, work, nnz, o,
+    return hip_status(sd::launch_plan(D, row_ptr, col_idx, nnz, static_cast<char *>(ws), w,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int stepdllm_sparse_attn(const stepdllm_dims *dims, const uint16_t *q, const uint16_t *k,
+                         const uint16_t *v, const int32_t *col_idx, int64_t nnz,
+                         const void *ws, size_t ws_bytes, uint16_t *o, void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!q || !k || !v || !col_idx || !ws || !o) return STEPDLLM_EINVAL;
+    if (nnz < 0 || nnz > D.n_scores()) return STEPDLLM_EINVAL;
+    WsLayout w = sd::ws_layout(D);
+    if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
+    const int4 *recs = reinterpret_cast<const int4 *>(static_cast<const char *>(ws) + w.work_rec);
+    return hip_status(sd::launch_sparse_attn(D, q, k, v, col_idx, recs, nnz, o,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -391,8 +393,8 @@ int stepdllm_step(stepdllm_driver *drv, int32_t step, const uint16_t *q, const u
     }
     if (drv->sched.column_sparse)
         return col_attn(&dims, q, k, v, drv->col_idx, drv->K, o, stream);
-    return stepdllm_sparse_attn(&dims, q, k, v, drv->row_ptr, drv->col_idx, drv->K, drv->ws,
-                                drv->ws_bytes, o, stream);
+    return stepdllm_sparse_attn(&dims, q, k, v, drv->col_idx, drv->K, drv->ws, drv->ws_bytes, o,
+                                stream);
 }
 
 int stepdllm_driver_destroy(stepdllm_driver *drv) {

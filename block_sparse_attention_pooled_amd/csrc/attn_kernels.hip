@@ -15,6 +15,10 @@
 //    merged; a workgroup is the BLK / 32 waves of one query block.  Under 256
 //    VGPRs per wave, so two waves share each SIMD; with 40 KiB of LDS per
 //    workgroup, four 64-row workgroups fit on a CU.
+//  * In sparse mode a workgroup starts from the plan's record for its work
+//    position (row, list bounds, first two block ids), so its first K/V loads
+//    leave one load after it starts; the rest of the list is read 64 ids at a
+//    time into one register.
 //  * Scores are computed transposed, S^T = K . Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K is the A operand, Q^T the B operand (held in
 //    registers for the whole row).  In the accumulator layout every lane holds
@@ -104,9 +108,8 @@ __device__ __forceinline__ int swz_v(int row) {
 template <int D, int BLK, int QW, int MODE>
 __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const int32_t *__restrict__ row_ptr,
-    const int32_t *__restrict__ col_idx, const int32_t *__restrict__ work,
-    uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx, int64_t cap,
+    const uint16_t *__restrict__ v, const int32_t *__restrict__ col_idx,
+    const int4 *__restrict__ recs, uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx, int64_t cap,
     float scale_log2) {
     constexpr int NT = QW / 32;                 // 32-query tiles per wave
     constexpr int WQ = BLK / QW;                // query slices (= waves) per block
@@ -131,8 +134,10 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     const int wq = wave;
     const int col = lane & 31, hh = lane >> 5;
 
-    // Row of this workgroup.
+    // Row of this workgroup and, in sparse mode, its list bounds and first
+    // two block ids from the work record.
     int row;
+    int rec_begin = 0, rec_end = 0, rec_ids = 0;
     if (!SPARSE) {
         const int b = blockIdx.x;
         if ((H & 7) == 0) {   // keep each head's rows on one XCD (round-robin dispatch)
@@ -143,10 +148,15 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         }
     } else {
         // Workgroup b runs on die b % kDies: take position b / kDies of that
-        // die's list (cap positions per die).
+        // die's list (cap positions per die).  One record holds everything
+        // the first K/V loads need, so they leave one load after the start.
         const int b = blockIdx.x;
-        row = __builtin_amdgcn_readfirstlane(work[(b % kDies) * cap + b / kDies]);
+        const int4 rc = recs[(b % kDies) * cap + b / kDies];
+        row = __builtin_amdgcn_readfirstlane(rc.x);
         if (row < 0 || row >= H * nb) return;   // padding (or a malformed order): nothing to do
+        rec_begin = __builtin_amdgcn_readfirstlane(rc.y);
+        rec_end = __builtin_amdgcn_readfirstlane(rc.z);
+        rec_ids = __builtin_amdgcn_readfirstlane(rc.w);
     }
     const int h = row / nb, blk = row % nb, g = h / G;
     const int q0 = blk * BLK + QW * wq;
@@ -155,8 +165,8 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
 
     int e_begin = 0, e_end = nb;
     if (SPARSE) {
-        e_begin = max(__builtin_amdgcn_readfirstlane(row_ptr[row]), 0);
-        e_end = min(__builtin_amdgcn_readfirstlane(row_ptr[row + 1]), n_idx);
+        e_begin = max(rec_begin, 0);
+        e_end = min(rec_end, n_idx);
     }
     // The row's chunks: every 32-key chunk of every kept block e, in order
     // (column mode: 32 consecutive entries of the head's column list).
@@ -207,6 +217,8 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         int j;
         if (!SPARSE) {
             j = e_begin + e_rel;
+        } else if (e_rel < 2) {   // the record's ids: no wait on the list load
+            j = (rec_ids >> (16 * e_rel)) & 0xFFFF;
         } else {
             const int grp = e_rel >> 6;
             if (grp != ids_grp) {
@@ -559,47 +571,47 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
 
 template <int D, int BLK, int QW, int MODE>
 hipError_t launch_attn_t(const Dims &Dm, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                         const int32_t *row_ptr, const int32_t *col_idx, const int32_t *work,
-                         int n_idx, uint16_t *o, hipStream_t s) {
+                         const int32_t *col_idx, const int4 *recs, int n_idx, uint16_t *o,
+                         hipStream_t s) {
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int64_t cap = Dm.die_cap();
     const unsigned grid = (unsigned)(MODE != kModeSparse ? Dm.rows() : kDies * cap);
     hipLaunchKernelGGL((k_attn<D, BLK, QW, MODE>), dim3(grid), dim3(BLK / QW * 64),
-                       0, s, q, k, v, row_ptr, col_idx, work, o, Dm.L, Dm.nb, Dm.G, Dm.H,
+                       0, s, q, k, v, col_idx, recs, o, Dm.L, Dm.nb, Dm.G, Dm.H,
                        n_idx, cap, scale_log2);
     return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t launch_attn(const Dims &D, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                       const int32_t *row_ptr, const int32_t *col_idx, const int32_t *work,
-                       int n_idx, uint16_t *o, hipStream_t s) {
+                       const int32_t *col_idx, const int4 *recs, int n_idx, uint16_t *o,
+                       hipStream_t s) {
     if (D.d == 128 && D.B == 64)
-        return launch_attn_t<128, 64, kQW, MODE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
+        return launch_attn_t<128, 64, kQW, MODE>(D, q, k, v, col_idx, recs, n_idx, o, s);
     if (D.d == 128 && D.B == 128)
-        return launch_attn_t<128, 128, kQW, MODE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
+        return launch_attn_t<128, 128, kQW, MODE>(D, q, k, v, col_idx, recs, n_idx, o, s);
     if (D.d == 64 && D.B == 64)
-        return launch_attn_t<64, 64, kQW, MODE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
-    return launch_attn_t<64, 128, kQW, MODE>(D, q, k, v, row_ptr, col_idx, work, n_idx, o, s);
+        return launch_attn_t<64, 64, kQW, MODE>(D, q, k, v, col_idx, recs, n_idx, o, s);
+    return launch_attn_t<64, 128, kQW, MODE>(D, q, k, v, col_idx, recs, n_idx, o, s);
 }
 
 }  // namespace
 
 hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
-                              const uint16_t *v, const int32_t *row_ptr, const int32_t *col_idx,
-                              const int32_t *work, int64_t n_idx, uint16_t *o, hipStream_t s) {
-    return launch_attn<kModeSparse>(D, q, k, v, row_ptr, col_idx, work, (int)n_idx, o, s);
+                              const uint16_t *v, const int32_t *col_idx, const int4 *recs,
+                              int64_t n_idx, uint16_t *o, hipStream_t s) {
+    return launch_attn<kModeSparse>(D, q, k, v, col_idx, recs, (int)n_idx, o, s);
 }
 
 hipError_t launch_dense_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                              const uint16_t *v, uint16_t *o, hipStream_t s) {
-    return launch_attn<kModeDense>(D, q, k, v, nullptr, nullptr, nullptr, 0, o, s);
+    return launch_attn<kModeDense>(D, q, k, v, nullptr, nullptr, 0, o, s);
 }
 
 hipError_t launch_col_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                            const uint16_t *v, const int32_t *cols, int64_t k_c, uint16_t *o,
                            hipStream_t s) {
-    return launch_attn<kModeCols>(D, q, k, v, nullptr, cols, nullptr, (int)k_c, o, s);
+    return launch_attn<kModeCols>(D, q, k, v, cols, nullptr, (int)k_c, o, s);
 }
 
 }  // namespace sd

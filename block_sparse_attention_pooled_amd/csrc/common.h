@@ -43,7 +43,7 @@ struct Dims {
 // Workspace carve-up (byte offsets, 256-byte aligned).
 struct WsLayout {
     int64_t qb, kb, p, hist, sel, gt, eq, tie_base, work, work_meta, hsel, col_scores, col_stats,
-        col_part, col_q16, plan_sorted, plan_nonempty, total;
+        col_part, col_q16, plan_sorted, plan_nonempty, work_rec, total;
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -67,8 +67,9 @@ inline WsLayout ws_layout(const Dims &D) {
     w.col_stats = take(D.rows() * 8);              // per pooled query: max, 1 / normaliser
     w.col_part = take(D.rows() * D.col_splits() * 8);   // per key split: max, normaliser
     w.col_q16 = take((int64_t)D.H * ((D.nb + 31) / 32) * 32 * D.d * 2);   // bf16 pooled Q
-    w.plan_sorted = take(D.rows() * 4);            // each head's rows, longest list first
+    w.plan_sorted = take(D.rows() * 16);           // each head's row records, longest list first
     w.plan_nonempty = take((int64_t)D.H * 4);      // non-empty rows per head
+    w.work_rec = take(kDies * D.die_cap() * 16);   // int4 record per work position
     w.total = off;
     return w;
 }
@@ -94,8 +95,11 @@ hipError_t launch_select(const Dims &D, int64_t K, const float *p, char *ws, con
 hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, char *ws,
                                   const WsLayout &w, int32_t *row_ptr, int32_t *col_idx,
                                   hipStream_t s);
-hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, char *ws, const WsLayout &w,
-                       hipStream_t s);
+// Work order of the mask row_ptr / col_idx (nnz list entries): the row ids
+// into w.work and one record per position into w.work_rec (row, list begin,
+// list end, first two block ids in 16 bits each; row -1 for padding).
+hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, const int32_t *col_idx,
+                       int64_t nnz, char *ws, const WsLayout &w, hipStream_t s);
 
 // Column-sparse variant.  Block means of Q only (mask_kernels.hip).
 hipError_t launch_pool_q(const Dims &D, const uint16_t *q, float *qb, hipStream_t s);
@@ -119,9 +123,10 @@ hipError_t launch_mask_recall(const Dims &D, const float *mass, const int32_t *r
                               hipStream_t s);
 
 // Attention launches (attn_kernels.hip).
+// Rows, list bounds and first block ids from the work records of the plan.
 hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
-                              const uint16_t *v, const int32_t *row_ptr, const int32_t *col_idx,
-                              const int32_t *work, int64_t n_idx, uint16_t *o, hipStream_t s);
+                              const uint16_t *v, const int32_t *col_idx, const int4 *recs,
+                              int64_t n_idx, uint16_t *o, hipStream_t s);
 hipError_t launch_dense_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                              const uint16_t *v, uint16_t *o, hipStream_t s);
 // Every query of head h over the key tokens cols[h*k_c .. h*k_c + k_c).

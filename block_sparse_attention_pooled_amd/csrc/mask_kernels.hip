@@ -510,19 +510,28 @@ __global__ __launch_bounds__(1024) void k_col_compact(const float *__restrict__ 
 //    holding fewer than min(H, ceil(H / kDies) + 2) heads (ties: lowest die);
 //  * die x's list is its heads in assignment order, each head's rows by list
 //    length descending (ties by row id), at work[x*cap ..], cap = (heads a die
-//    may hold) * nb; unused positions hold -1.
-// Two launches.  k_plan_sort, one wave per head: the head's rows by list
-// length descending, ties by row id, with a stable counting sort (length
-// histogram, descending bucket starts, ranks among equal lengths from wave
-// ballots), and the head's count of non-empty rows.  k_plan, one workgroup:
-// heads are ranked in parallel, assigned to dies by one wave with one die per
-// lane (the least-loaded open die found by a three-step 8-lane argmin), and
-// every head's sorted rows are copied to its die positions.
-__global__ __launch_bounds__(64) void k_plan_sort(const int32_t *__restrict__ row_ptr, int nb,
-                                                  int32_t *__restrict__ sorted,
+//    may hold) * nb; unused positions hold -1;
+//  * beside it, work_rec holds one record per position for the attention
+//    launch: row, list begin, list end (clamped into [0, nnz]) and the row's
+//    first two block ids (16 bits each, clamped into [0, nb)), so that a
+//    workgroup's first K/V loads need one load, not a chain of three; padding
+//    records have row -1.
+// Two launches.  k_plan_sort, one wave per head: the head's row records, its
+// rows by list length descending, ties by row id, with a stable counting sort
+// (length histogram, descending bucket starts, ranks among equal lengths from
+// wave ballots), and the head's count of non-empty rows.  k_plan, one
+// workgroup: heads are ranked in parallel, assigned to dies by one wave with
+// one die per lane (the least-loaded open die found by a three-step 8-lane
+// argmin), and every head's sorted records are copied to its die positions.
+__global__ __launch_bounds__(64) void k_plan_sort(const int32_t *__restrict__ row_ptr,
+                                                  const int32_t *__restrict__ col_idx,
+                                                  int64_t nnz, int nb,
+                                                  int4 *__restrict__ sorted,
                                                   int32_t *__restrict__ nonempty) {
+    constexpr int kRowsPerLane = kMaxBlocks / 64;
     __shared__ int32_t nx[kMaxBlocks + 1];   // histogram, first staging row_ptr
     __shared__ int16_t ln[kMaxBlocks];
+    __shared__ int4 rec[kMaxBlocks];
     const int lane = threadIdx.x, h = blockIdx.x;
     const uint64_t lt = lanemask_lt();
     const int64_t r0 = (int64_t)h * nb;
@@ -536,10 +545,34 @@ __global__ __launch_bounds__(64) void k_plan_sort(const int32_t *__restrict__ ro
         for (int j = 0; j < 8; ++j)
             if (c + lane + 64 * j <= nb) nx[c + lane + 64 * j] = v[j];
     }
+    // Records: list bounds clamped into [0, nnz], the first two ids of the
+    // list (all loads of a lane issued together).
+    int lo[kRowsPerLane], hi[kRowsPerLane], id0[kRowsPerLane], id1[kRowsPerLane];
+#pragma unroll
+    for (int t = 0; t < kRowsPerLane; ++t) {
+        const int i = lane + 64 * t;
+        lo[t] = hi[t] = id0[t] = id1[t] = 0;
+        if (i < nb) {
+            lo[t] = max(nx[i], 0);
+            hi[t] = (int)min((int64_t)nx[i + 1], nnz);
+            if (hi[t] > lo[t]) {
+                id0[t] = col_idx[lo[t]];
+                if (hi[t] - lo[t] > 1) id1[t] = col_idx[lo[t] + 1];
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kRowsPerLane; ++t) {
+        const int i = lane + 64 * t;
+        if (i < nb) {
+            const int a = min(max(id0[t], 0), nb - 1), b = min(max(id1[t], 0), nb - 1);
+            rec[i] = make_int4((int)r0 + i, lo[t], hi[t], a | (b << 16));
+        }
+    }
     int my_nonempty = 0;
     for (int i = lane; i < nb; i += 64) {
-        const int len = nx[i + 1] - nx[i];
-        ln[i] = (int16_t)len;
+        const int64_t len = (int64_t)nx[i + 1] - nx[i];
+        ln[i] = (int16_t)min(max(len, (int64_t)0), (int64_t)nb);
         my_nonempty += len > 0;
     }
     for (int l = lane; l <= nb; l += 64) nx[l] = 0;
@@ -571,7 +604,7 @@ __global__ __launch_bounds__(64) void k_plan_sort(const int32_t *__restrict__ ro
         }
         const int rank = __popcll(same & lt);
         const int pos = valid ? nx[len] + rank : 0;
-        if (valid && pos < nb) sorted[r0 + pos] = (int32_t)(r0 + i);
+        if (valid && pos < nb) sorted[r0 + pos] = rec[i];
         if (valid && rank == 0) nx[len] += __popcll(same);
     }
     const int total = wave_sum(my_nonempty);
@@ -595,9 +628,10 @@ constexpr int kPlanThreads = 512;
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict__ row_ptr,
                                                        int H, int nb, int steps_per_block,
-                                                       const int32_t *__restrict__ sorted,
+                                                       const int4 *__restrict__ sorted,
                                                        const int32_t *__restrict__ ne_head,
                                                        int32_t *__restrict__ work,
+                                                       int4 *__restrict__ work_rec,
                                                        int32_t *__restrict__ meta) {
     static_assert(kDies == 8, "the die argmin covers 8 lanes");
     __shared__ int64_t weight[kMaxHeads];
@@ -612,7 +646,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict
         weight[h] = (int64_t)steps_per_block *
                         (row_ptr[(int64_t)(h + 1) * nb] - row_ptr[(int64_t)h * nb]) +
                     4 * (int64_t)ne_head[h];
-    for (int64_t p = tid; p < kDies * cap; p += kPlanThreads) work[p] = -1;
+    for (int64_t p = tid; p < kDies * cap; p += kPlanThreads) {
+        work[p] = -1;
+        work_rec[p] = make_int4(-1, 0, 0, 0);
+    }
     __syncthreads();
     for (int h = tid; h < H; h += kPlanThreads) {
         int rank = 0;
@@ -653,7 +690,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t *__restrict
     const int64_t rows = (int64_t)H * nb;
     for (int64_t x = tid; x < rows; x += kPlanThreads) {
         const int h = (int)(x / nb), i = (int)(x % nb);
-        work[(int64_t)head_base[h] + i] = sorted[x];
+        const int4 rc = sorted[x];
+        work[(int64_t)head_base[h] + i] = rc.x;
+        work_rec[(int64_t)head_base[h] + i] = rc;
     }
     if (tid == 0) {
         meta[0] = (int32_t)cap;
@@ -758,15 +797,17 @@ hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, ch
     return hipGetLastError();
 }
 
-hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, char *ws, const WsLayout &w,
-                       hipStream_t s) {
+hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, const int32_t *col_idx,
+                       int64_t nnz, char *ws, const WsLayout &w, hipStream_t s) {
     int32_t *work = reinterpret_cast<int32_t *>(ws + w.work);
+    int4 *work_rec = reinterpret_cast<int4 *>(ws + w.work_rec);
     int32_t *meta = reinterpret_cast<int32_t *>(ws + w.work_meta);
-    int32_t *sorted = reinterpret_cast<int32_t *>(ws + w.plan_sorted);
+    int4 *sorted = reinterpret_cast<int4 *>(ws + w.plan_sorted);
     int32_t *ne_head = reinterpret_cast<int32_t *>(ws + w.plan_nonempty);
-    hipLaunchKernelGGL(k_plan_sort, dim3(D.H), dim3(64), 0, s, row_ptr, D.nb, sorted, ne_head);
+    hipLaunchKernelGGL(k_plan_sort, dim3(D.H), dim3(64), 0, s, row_ptr, col_idx, nnz, D.nb,
+                       sorted, ne_head);
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.H, D.nb, D.B / 32,
-                       sorted, ne_head, work, meta);
+                       sorted, ne_head, work, work_rec, meta);
     return hipGetLastError();
 }
 

@@ -109,6 +109,11 @@ typedef struct {
                            built without scores_out                               */
     int64_t col_stats;  /* fp32 [H, nb, 2]: per pooled query, max (log2 units)
                            and normaliser of its scores over all keys             */
+    int64_t work_rec;   /* int32 [8 * cap, 4]: per work position, the record the
+                           sparse launch reads: row (-1 = padding), list begin,
+                           list end (both clamped into [0, nnz]), first two
+                           block ids (bits 0-15 and 16-31, clamped into
+                           [0, nb); 0 where the list is shorter)                 */
     int64_t total;      /* == stepdllm_workspace_bytes()                          */
 } stepdllm_ws_layout;
 
@@ -166,7 +171,8 @@ int stepdllm_select_mask_per_head(const stepdllm_dims *dims, double sparsity,
                                   const float *scores, void *ws, size_t ws_bytes,
                                   int32_t *row_ptr, int32_t *col_idx, void *stream);
 
-/* Work order for a caller-built mask (row_ptr as above).  The GPU's 8 dies
+/* Work order for a caller-built mask (row_ptr as above; col_idx holds nnz
+ * list entries).  The GPU's 8 dies
  * (XCDs) each have their own L2 and take workgroups round robin, so all rows
  * of a head go to one die.  A head weighs (B/32) * kept blocks + 4 * rows that
  * keep a block (its 32-key steps plus a fixed start-up and write-out per row);
@@ -177,16 +183,24 @@ int stepdllm_select_mask_per_head(const stepdllm_dims *dims, double sparsity,
  * positions [x*cap, x*cap + cap) of the work order.  Workgroup b of the
  * sparse launch takes position b / 8 of die b % 8's list, so each die starts
  * its longest rows first and the hardware hands the next row to whichever
- * workgroup slot frees first. */
+ * workgroup slot frees first.  Beside the order, each position gets a record
+ * (work_rec in the layout) of the row's list bounds and first two block ids,
+ * so the plan describes this mask's contents, not only its row lengths: plan
+ * again after any change to row_ptr or col_idx.  Memory safety on malformed
+ * masks: list positions outside [0, nnz) are not read. */
 int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr,
+                  const int32_t *col_idx, int64_t nnz,
                   void *ws, size_t ws_bytes, void *stream);
 
 /* Block-sparse bidirectional attention (the fused kernel of the Step-dLLM
  * abstract): for each token t of query block i in head h,
  *   o_t = sum_u softmax_u(q_t . k_u / sqrt(d)) v_u
  * over the tokens u of the key blocks listed for row h*nb + i, from key head
- * h / (H/Hkv).  A row with no kept block outputs zeros.  Reads the work order
- * that stepdllm_build_mask / select_mask / plan left in ws.
+ * h / (H/Hkv).  A row with no kept block outputs zeros.  The mask is the one
+ * whose plan stepdllm_build_mask / select_mask / plan left in ws: the launch
+ * takes each row's list bounds and first two block ids from the plan's
+ * records and the rest of the list from col_idx, which must be the array the
+ * plan was made from, unchanged since.
  * nnz is the length of col_idx (row_ptr[H*nb] for a well-formed mask, K for a
  * built one).  Memory safety on malformed masks: list positions at or past nnz
  * are not read, and block ids outside [0, nb) are clamped into range (the
@@ -195,8 +209,8 @@ int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr,
  * and softmax; o rounded to nearest-even bf16. */
 int stepdllm_sparse_attn(const stepdllm_dims *dims, const uint16_t *q,
                          const uint16_t *k, const uint16_t *v,
-                         const int32_t *row_ptr, const int32_t *col_idx,
-                         int64_t nnz, const void *ws, size_t ws_bytes,
+                         const int32_t *col_idx, int64_t nnz,
+                         const void *ws, size_t ws_bytes,
                          uint16_t *o, void *stream);
 
 /* Dense bidirectional attention, every block kept: the same-GPU baseline that

@@ -93,8 +93,10 @@ def test_workspace_layout():
         assert lay.col_scores - lay.head_select >= w.H * 8 * 4
         assert lay.col_stats - lay.col_scores >= w.H * w.L * 4
         assert lay.total - lay.col_stats >= w.H * w.nb * 8
-        assert lay.head_select < lay.col_scores < lay.col_stats < lay.total
-        assert lay.col_scores % 256 == 0 and lay.col_stats % 256 == 0
+        assert lay.head_select < lay.col_scores < lay.col_stats < lay.work_rec < lay.total
+        assert lay.col_scores % 256 == 0 and lay.col_stats % 256 == 0 and lay.work_rec % 256 == 0
+        cap = min(w.H, -(-w.H // 8) + 2) * w.nb
+        assert lay.total - lay.work_rec >= 8 * cap * 16
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -114,10 +116,14 @@ def test_entry_points_reject_bad_arguments_before_launch():
     r = ctypes.byref
     # null pointers
     assert lib.stepdllm_build_mask(r(d), 0.5, None, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL
-    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, None, FAKE, FAKE, 16, FAKE, ws_need, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, None, FAKE, 16, FAKE, ws_need, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, FAKE, None, 16, FAKE, ws_need, FAKE, None) == B.EINVAL
     assert lib.stepdllm_dense_attn(r(d), FAKE, FAKE, FAKE, None, None) == B.EINVAL
     assert lib.stepdllm_select_mask(r(d), 0.5, None, FAKE, ws_need, FAKE, FAKE, None) == B.EINVAL
-    assert lib.stepdllm_plan(r(d), None, FAKE, ws_need, None) == B.EINVAL
+    assert lib.stepdllm_plan(r(d), None, FAKE, 16, FAKE, ws_need, None) == B.EINVAL
+    assert lib.stepdllm_plan(r(d), FAKE, None, 16, FAKE, ws_need, None) == B.EINVAL
+    assert lib.stepdllm_plan(r(d), FAKE, FAKE, 33, FAKE, ws_need, None) == B.EINVAL
+    assert lib.stepdllm_plan(r(d), FAKE, FAKE, -1, FAKE, ws_need, None) == B.EINVAL
     assert lib.stepdllm_build_mask_per_head(r(d), 0.5, None, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL
     assert lib.stepdllm_select_mask_per_head(r(d), 0.5, FAKE, FAKE, ws_need - 1, FAKE, FAKE, None) == B.EWORKSPACE
     assert lib.stepdllm_keep_count_per_head(r(d), 1.0) == B.EINVAL
@@ -147,11 +153,11 @@ def test_entry_points_reject_bad_arguments_before_launch():
         assert lib.stepdllm_build_mask(r(d), s, FAKE, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL
     # workspace too small
     assert lib.stepdllm_build_mask(r(d), 0.5, FAKE, FAKE, FAKE, ws_need - 1, FAKE, FAKE, None, None) == B.EWORKSPACE
-    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 8, FAKE, None) == B.EWORKSPACE
-    assert lib.stepdllm_plan(r(d), FAKE, FAKE, 0, None) == B.EWORKSPACE
+    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, FAKE, FAKE, 16, FAKE, 8, FAKE, None) == B.EWORKSPACE
+    assert lib.stepdllm_plan(r(d), FAKE, FAKE, 16, FAKE, 0, None) == B.EWORKSPACE
     # nnz outside [0, H*nb*nb]
-    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, FAKE, FAKE, FAKE, 33, FAKE, ws_need, FAKE, None) == B.EINVAL
-    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, ws_need, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, FAKE, FAKE, 33, FAKE, ws_need, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, FAKE, FAKE, -1, FAKE, ws_need, FAKE, None) == B.EINVAL
     # unsupported dims on a compute entry point
     bad = dims(2, 2, 256, 80, 64)
     assert lib.stepdllm_dense_attn(r(bad), FAKE, FAKE, FAKE, FAKE, None) == B.EUNSUPPORTED

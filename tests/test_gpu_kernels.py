@@ -104,27 +104,47 @@ def test_plan_matches_oracle(shape):
     H, Hkv, L, d, blk, _ = shape
     q, k, v = _qkv(shape, 303)
     m = PT.GpuMask(q, k, blk, 0.8)
-    rp, _ = m.csr()
+    rp, ci = m.csr()
     meta = m.buf.work_meta().cpu().numpy()
-    work_ref, n_ref = O.plan(rp, H, L // blk)
+    work_ref, n_ref = O.plan(rp, H, L // blk, blk)
     assert np.array_equal(m.buf.work().cpu().numpy(), work_ref)
     assert int(meta[0]) * 8 == work_ref.size and int(meta[1]) == n_ref
+    _check_records(m.buf.work_rec().cpu().numpy(), work_ref, rp, ci)
 
 
-@pytest.mark.parametrize("H,nb", [(64, 320), (28, 129), (3, 1024), (13, 7)])
-def test_plan_many_rows_and_lengths(H, nb):
+@pytest.mark.parametrize("H,nb,blk", [(64, 320, 64), (28, 129, 128), (3, 1024, 64), (13, 7, 128)])
+def test_plan_many_rows_and_lengths(H, nb, blk):
     """Injected lists with every length 0..nb, ragged head counts per die."""
     rng = np.random.default_rng(9)
     lens = rng.integers(0, nb + 1, size=H * nb)
     lens[rng.random(H * nb) < 0.3] = 0
     rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    dims = B.make_dims(H, H, nb * 64, 64, 64)
+    ci = rng.integers(0, nb, size=max(int(rp[-1]), 1)).astype(np.int32)
+    dims = B.make_dims(H, H, nb * blk, 64, blk)
     buf = B.MaskBuffers(dims, 0.5, device=DEV)
-    B.plan(dims, torch.from_numpy(rp).to(DEV), buf.ws)
+    B.plan(dims, torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV), buf.ws,
+           nnz=int(rp[-1]))
     torch.cuda.synchronize()
-    work_ref, n_ref = O.plan(rp, H, nb)
+    work_ref, n_ref = O.plan(rp, H, nb, blk)
     assert np.array_equal(buf.work().cpu().numpy(), work_ref)
     assert int(buf.work_meta().cpu().numpy()[1]) == n_ref
+    _check_records(buf.work_rec().cpu().numpy(), work_ref, rp, ci)
+
+
+def _check_records(rec, work, rp, ci):
+    """Each work position's record: row, list bounds, first two block ids
+    (16 bits each, 0 past the list); padding has row -1 and zeros."""
+    assert rec.shape == (work.size, 4)
+    assert np.array_equal(rec[:, 0], work)
+    pad = work < 0
+    assert np.all(rec[pad, 1:] == 0)
+    rows = work[~pad]
+    lo, hi = rp[rows], rp[rows + 1]
+    assert np.array_equal(rec[~pad, 1], lo) and np.array_equal(rec[~pad, 2], hi)
+    ci_pad = np.concatenate([ci, [0, 0]])
+    id0 = np.where(hi > lo, ci_pad[lo], 0)
+    id1 = np.where(hi > lo + 1, ci_pad[np.minimum(lo + 1, ci_pad.size - 1)], 0)
+    assert np.array_equal(rec[~pad, 3], id0 | (id1 << 16))
 
 
 def _attn_case(shape, s, seed):
@@ -144,9 +164,9 @@ def test_sparse_attention_on_oracle_mask(shape, s):
     buf = B.MaskBuffers(dims, s, device=DEV)
     rp = torch.from_numpy(ref["row_ptr"]).to(DEV)
     ci = torch.from_numpy(np.concatenate([ref["col_idx"], [0]]).astype(np.int32)).to(DEV)
-    B.plan(dims, rp, buf.ws)
+    B.plan(dims, rp, ci, buf.ws, nnz=ref["K"])
     o = torch.full_like(q, float("nan"))
-    B.sparse_attn(dims, q, k, v, rp, ci, buf.ws, o, nnz=ref["K"])
+    B.sparse_attn(dims, q, k, v, ci, buf.ws, o, nnz=ref["K"])
     torch.cuda.synchronize()
     o_ref = O.sparse_attn(qf, kf, vf, blk, ref["row_ptr"], ref["col_idx"])
     PT.check_outputs(o, o_ref)
@@ -174,7 +194,7 @@ def test_sparsity_zero_equals_dense(shape):
     buf = B.MaskBuffers(dims, 0.0, device=DEV)
     B.build_mask(dims, 0.0, q, k, buf.ws, buf.row_ptr, buf.col_idx)
     o_s, o_d = torch.empty_like(q), torch.empty_like(q)
-    B.sparse_attn(dims, q, k, v, buf.row_ptr, buf.col_idx, buf.ws, o_s)
+    B.sparse_attn(dims, q, k, v, buf.col_idx, buf.ws, o_s)
     B.dense_attn(dims, q, k, v, o_d)
     torch.cuda.synchronize()
     assert torch.equal(o_s, o_d)
@@ -197,9 +217,9 @@ def test_dropped_block_is_detected():
     buf = B.MaskBuffers(dims, 0.75, device=DEV)
     rpt = torch.from_numpy(rp_mut).to(DEV)
     cit = torch.from_numpy(ci_mut.astype(np.int32)).to(DEV)
-    B.plan(dims, rpt, buf.ws)
+    B.plan(dims, rpt, cit, buf.ws)
     o = torch.empty_like(q)
-    B.sparse_attn(dims, q, k, v, rpt, cit, buf.ws, o)
+    B.sparse_attn(dims, q, k, v, cit, buf.ws, o)
     torch.cuda.synchronize()
     o_ref = O.sparse_attn(qf, kf, vf, blk, ref["row_ptr"], ref["col_idx"])
     with pytest.raises(AssertionError):
@@ -215,7 +235,7 @@ def test_worked_example_w1_on_gpu():
     m = PT.GpuMask(qd, kd, 64, 0.5)
     assert np.array_equal(m.keep(), keep_want)
     o = torch.empty_like(qd)
-    B.sparse_attn(m.dims, qd, kd, vd, m.buf.row_ptr, m.buf.col_idx, m.buf.ws, o)
+    B.sparse_attn(m.dims, qd, kd, vd, m.buf.col_idx, m.buf.ws, o)
     torch.cuda.synchronize()
     on = o.cpu().to(torch.float64).numpy()
     for i in range(4):
@@ -235,13 +255,13 @@ def test_constant_values_and_zero_queries():
     vc = torch.full_like(v, -1.5)
     m = PT.GpuMask(q, k, blk, 0.7)
     o = torch.empty_like(q)
-    B.sparse_attn(m.dims, q, k, vc, m.buf.row_ptr, m.buf.col_idx, m.buf.ws, o)
+    B.sparse_attn(m.dims, q, k, vc, m.buf.col_idx, m.buf.ws, o)
     torch.cuda.synchronize()
     nonempty = np.diff(m.csr()[0]) > 0
     on = o.cpu().to(torch.float32).numpy().reshape(H * (L // blk), blk, d)
     assert np.all(np.abs(on[nonempty] + 1.5) <= 1.5 * 2.0 ** -7) and np.all(on[~nonempty] == 0)
     z = torch.zeros_like(q)
-    B.sparse_attn(m.dims, z, k, v, m.buf.row_ptr, m.buf.col_idx, m.buf.ws, o)
+    B.sparse_attn(m.dims, z, k, v, m.buf.col_idx, m.buf.ws, o)
     torch.cuda.synchronize()
     qf, kf, vf = PT.oracle_inputs(z, k, v)
     rp, ci = m.csr()
@@ -255,7 +275,7 @@ def test_determinism():
     for _ in range(2):
         m = PT.GpuMask(q, k, 64, 0.9)
         o = torch.empty_like(q)
-        B.sparse_attn(m.dims, q, k, v, m.buf.row_ptr, m.buf.col_idx, m.buf.ws, o)
+        B.sparse_attn(m.dims, q, k, v, m.buf.col_idx, m.buf.ws, o)
         torch.cuda.synchronize()
         outs.append((m.P(), m.csr(), m.buf.work().cpu().numpy(), o.cpu()))
     a, b = outs
