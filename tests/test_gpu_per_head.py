@@ -68,7 +68,7 @@ def test_per_head_selection_bit_exact_on_gpu_scores(shape, s):
     assert np.array_equal(rp, rp_ref) and np.array_equal(ci, ci_ref)
     _check_head_state(m.buf.head_select().cpu().numpy(), P, k_h)
     # The work order is the usual plan of this mask.
-    work_ref, n_ref = O.plan(rp, H, m.nb)
+    work_ref, n_ref = O.plan(rp, H, m.nb, blk)
     assert np.array_equal(m.buf.work().cpu().numpy(), work_ref)
 
 

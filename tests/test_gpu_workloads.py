@@ -38,7 +38,7 @@ def _check_anchor(drv, w, sparsity, q, k, label):
     assert np.array_equal(O.select(P_gpu, K), keep)
     rel = float(np.max(np.abs(P_gpu.astype(np.float64) - ref["P"]) / ref["P"]))
     assert rel < 4e-6, rel
-    work_ref, n_ref = O.plan(rp, w.H, w.nb)
+    work_ref, n_ref = O.plan(rp, w.H, w.nb, w.B)
     work = drv.ws[lay.work:lay.work + 4 * work_ref.size].view(torch.int32).cpu().numpy()
     assert np.array_equal(work, work_ref)
     print(f"{label}: K={K} near-tie differences={len(listed)} {listed[:8]} "
