@@ -74,13 +74,16 @@ bool sparsity_ok(double s) { return s >= 0.0 && s < 1.0; }   // false for NaN
 
 int hip_status(hipError_t e) { return e == hipSuccess ? STEPDLLM_OK : STEPDLLM_EHIP; }
 
+// state_ready: the global select state was already prepared (by the score
+// launch of build_mask).
 int select_and_plan(const Dims &D, double sparsity, bool per_head, const float *p, char *ws,
-                    const WsLayout &w, int32_t *row_ptr, int32_t *col_idx, hipStream_t s) {
+                    const WsLayout &w, int32_t *row_ptr, int32_t *col_idx, bool state_ready,
+                    hipStream_t s) {
     const int64_t k_h = per_head ? keep_count_per_head(D, sparsity) : 0;
     const int64_t K = per_head ? k_h * D.H : keep_count(D, sparsity);
     int st = hip_status(
         per_head ? sd::launch_select_per_head(D, k_h, p, ws, w, row_ptr, col_idx, s)
-                 : sd::launch_select(D, K, p, ws, w, row_ptr, col_idx, s));
+                 : sd::launch_select(D, K, p, ws, w, row_ptr, col_idx, state_ready, s));
     if (st) return st;
     return hip_status(sd::launch_plan(D, row_ptr, col_idx, K, ws, w, s));
 }
@@ -100,8 +103,10 @@ int build_mask(const stepdllm_dims *dims, double sparsity, bool per_head, const 
     float *kb = reinterpret_cast<float *>(base + w.kb);
     float *p = reinterpret_cast<float *>(base + w.p);
     if ((st = hip_status(sd::launch_pool(D, q, k, qb, kb, s)))) return st;
-    if ((st = hip_status(sd::launch_scores(D, qb, kb, p, scores_out, s)))) return st;
-    return select_and_plan(D, sparsity, per_head, p, base, w, row_ptr, col_idx, s);
+    const int64_t sel_init_K = per_head ? -1 : keep_count(D, sparsity);
+    if ((st = hip_status(sd::launch_scores(D, qb, kb, p, scores_out, base, w, sel_init_K, s))))
+        return st;
+    return select_and_plan(D, sparsity, per_head, p, base, w, row_ptr, col_idx, !per_head, s);
 }
 
 int select_mask(const stepdllm_dims *dims, double sparsity, bool per_head, const float *scores,
@@ -113,7 +118,7 @@ int select_mask(const stepdllm_dims *dims, double sparsity, bool per_head, const
     WsLayout w = sd::ws_layout(D);
     if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
     return select_and_plan(D, sparsity, per_head, scores, static_cast<char *>(ws), w, row_ptr,
-                           col_idx, static_cast<hipStream_t>(stream));
+                           col_idx, false, static_cast<hipStream_t>(stream));
 }
 
 int build_col_mask(const stepdllm_dims *dims, double sparsity, const uint16_t *q,

@@ -13,8 +13,9 @@ constexpr int kMaxBlocks = 1024;     // largest nb = L / B supported
 constexpr int kMaxHeads = 1024;      // largest number of query heads supported
 constexpr int kDies = 8;             // XCDs: workgroup b of a launch runs on die b % 8
 constexpr int kRadixBins = 2048;     // 11-bit digits (11 + 11 + 10 = 32 bits)
-constexpr int kSelectWords = 16;     // select state words in the workspace
+constexpr int kSelectWords = 32;     // select state words in the workspace
 constexpr int kHeadSelWords = 8;     // per-head select state words (uniform budget)
+constexpr int kCompactRows = 16;     // rows per workgroup of the list compaction
 
 // Select state words.
 enum SelectWord {
@@ -24,6 +25,8 @@ enum SelectWord {
     SEL_K = 3,        // K
     SEL_PREFIX = 4,   // running prefix during the radix passes
     SEL_REMAIN = 5,   // K minus the count already above the prefix bucket
+    SEL_PASS = 8,     // 8..16: state entering digit pass 0..2 (prefix, count
+                      // above the prefix, rank wanted inside it), 3 words each
 };
 
 // Shapes after validation, with derived sizes.
@@ -43,7 +46,7 @@ struct Dims {
 // Workspace carve-up (byte offsets, 256-byte aligned).
 struct WsLayout {
     int64_t qb, kb, p, hist, sel, gt, eq, tie_base, work, work_meta, hsel, col_scores, col_stats,
-        col_part, col_q16, plan_sorted, plan_nonempty, work_rec, total;
+        col_part, col_q16, plan_head_base, work_rec, row_agg, total;
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -67,9 +70,10 @@ inline WsLayout ws_layout(const Dims &D) {
     w.col_stats = take(D.rows() * 8);              // per pooled query: max, 1 / normaliser
     w.col_part = take(D.rows() * D.col_splits() * 8);   // per key split: max, normaliser
     w.col_q16 = take((int64_t)D.H * ((D.nb + 31) / 32) * 32 * D.d * 2);   // bf16 pooled Q
-    w.plan_sorted = take(D.rows() * 16);           // each head's row records, longest list first
-    w.plan_nonempty = take((int64_t)D.H * 4);      // non-empty rows per head
+    w.plan_head_base = take((int64_t)D.H * 4);     // each head's first work position
     w.work_rec = take(kDies * D.die_cap() * 16);   // int4 record per work position
+    // per compaction workgroup: above-cut and at-cut counts of its rows
+    w.row_agg = take(2 * ((D.rows() + kCompactRows - 1) / kCompactRows) * 4);
     w.total = off;
     return w;
 }
@@ -87,10 +91,12 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
 // Mask-building launches (mask_kernels.hip).
 hipError_t launch_pool(const Dims &D, const uint16_t *q, const uint16_t *k, float *qb, float *kb,
                        hipStream_t s);
+// With sel_init_K >= 0 the launch also prepares the global select state in ws
+// for a budget of sel_init_K (then launch_select may skip its own init).
 hipError_t launch_scores(const Dims &D, const float *qb, const float *kb, float *p, float *copy,
-                         hipStream_t s);
+                         char *ws, const WsLayout &w, int64_t sel_init_K, hipStream_t s);
 hipError_t launch_select(const Dims &D, int64_t K, const float *p, char *ws, const WsLayout &w,
-                         int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
+                         int32_t *row_ptr, int32_t *col_idx, bool state_ready, hipStream_t s);
 // Uniform per-head budget: head h keeps its k_h largest scores.
 hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, char *ws,
                                   const WsLayout &w, int32_t *row_ptr, int32_t *col_idx,

@@ -95,8 +95,9 @@ typedef struct {
     int64_t pooled_q;   /* fp32 [H, nb, d]: block means of Q                      */
     int64_t pooled_k;   /* fp32 [Hkv, nb, d]: block means of K                    */
     int64_t scores;     /* fp32 [H, nb, nb]: row-softmaxed pooled scores          */
-    int64_t select;     /* uint32 [16]: [0] cut key, [1] count above the cut,
-                           [2] ties kept at the cut, [3] K                        */
+    int64_t select;     /* uint32 [32]: [0] cut key, [1] count above the cut,
+                           [2] ties kept at the cut, [3] K; the other words
+                           are the select's working state                        */
     int64_t work;       /* int32 [8 * cap]: attention work order, cap =
                            min(H, ceil(H/8) + 2) * nb positions per die;
                            -1 = padding                                           */
