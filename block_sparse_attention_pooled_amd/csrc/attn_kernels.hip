@@ -253,22 +253,20 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         k_voff[tt] = (uint32_t)(r_in * D * 2 + 16 * (sp ^ swz_k<D>(r)));
     }
     const uint32_t v_voff = (uint32_t)(r_in * D * 2 + 16 * (sp ^ swz_v<D>(r_in)));
-    auto issue_k = [&](int key0, int st) {
+    auto issue_k = [&](int key0, uint16_t *dst) {
         const uint32_t off = (uint32_t)key0 * (D * 2);
 #pragma unroll
         for (int tt = 0; tt < MY_LOADS; ++tt) {
             const int t = tt * WQ + wq;
-            load_lds16(k_rsrc, kring + st * TILE + t * 512, k_voff[tt],
-                       off + t * ROWS_PER_LOAD * D * 2);
+            load_lds16(k_rsrc, dst + t * 512, k_voff[tt], off + t * ROWS_PER_LOAD * D * 2);
         }
     };
-    auto issue_v = [&](int key0, int st) {
+    auto issue_v = [&](int key0, uint16_t *dst) {
         const uint32_t off = (uint32_t)key0 * (D * 2);
 #pragma unroll
         for (int tt = 0; tt < MY_LOADS; ++tt) {
             const int t = tt * WQ + wq;
-            load_lds16(v_rsrc, vring + st * TILE + t * 512, v_voff,
-                       off + t * ROWS_PER_LOAD * D * 2);
+            load_lds16(v_rsrc, dst + t * 512, v_voff, off + t * ROWS_PER_LOAD * D * 2);
         }
     };
     // Column mode: list entry 32*c + r is the token of row r of chunk c.  A
@@ -286,19 +284,19 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     };
     // Gathered rows: the token's row in the key head, at the segment the
     // contiguous loads would use.  Tokens outside the head read zeros.
-    auto issue_k_tok = [&](const int (&tok)[MY_LOADS], int st) {
+    auto issue_k_tok = [&](const int (&tok)[MY_LOADS], uint16_t *dst) {
 #pragma unroll
         for (int tt = 0; tt < MY_LOADS; ++tt) {
             const int t = tt * WQ + wq;
-            load_lds16(k_rsrc, kring + st * TILE + t * 512,
+            load_lds16(k_rsrc, dst + t * 512,
                        (uint32_t)tok[tt] * (D * 2) + (k_voff[tt] - r_in * D * 2), 0);
         }
     };
-    auto issue_v_tok = [&](const int (&tok)[MY_LOADS], int st) {
+    auto issue_v_tok = [&](const int (&tok)[MY_LOADS], uint16_t *dst) {
 #pragma unroll
         for (int tt = 0; tt < MY_LOADS; ++tt) {
             const int t = tt * WQ + wq;
-            load_lds16(v_rsrc, vring + st * TILE + t * 512,
+            load_lds16(v_rsrc, dst + t * 512,
                        (uint32_t)tok[tt] * (D * 2) + (v_voff - r_in * D * 2), 0);
         }
     };
@@ -315,8 +313,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
 
     // K as the A operand of the score product: lane row = key col, dims
     // 16*s + 8*hh.
-    auto read_k = [&](int st, bf16x8 (&kf)[KS]) {
-        const uint16_t *kt = kring + st * TILE;
+    auto read_k = [&](const uint16_t *kt, bf16x8 (&kf)[KS]) {
 #pragma unroll
         for (int s = 0; s < KS; ++s)
             kf[s] = __builtin_bit_cast(
@@ -328,8 +325,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     // 8-byte pieces addressed by lanes 4k + i/4, k = 0..3.  Addressing lane
     // (group gq, index i) points at key row 16*ks + 8*r + 4*(gq/2) + i/4,
     // dims 32*mt + 16*(gq%2) + 4*(i%4) .. +4.
-    auto read_v = [&](int st, bf16x8 (&vf)[MT][2]) {
-        const uint16_t *vt = vring + st * TILE;
+    auto read_v = [&](const uint16_t *vt, bf16x8 (&vf)[MT][2]) {
         const int gq = lane >> 4, i16 = lane & 15;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -448,13 +444,45 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     //   S(n+1) has consumed K(n+1); load V(n+1) (its stage was read in step
     //   n-1) and K(n+3) (stage of K(n), read in step n-2); O^T += V(n) . P(n)
     //   on the matrix cores while the max of S(n+1) is taken; rare rescale.
-    // Every LDS read of a step precedes its loads: the compiler makes an LDS
-    // read wait for every buffer->LDS load in flight.  FULL steps have every
-    // chunk up to n+3; the last steps are guarded.
+    // The loads and the LDS reads of a step touch different stages, so their
+    // order inside the step is left to the compiler (see body below).  FULL
+    // steps have every chunk up to n+3; the last steps are guarded.
     bf16x8 kf[KS];
     // Column mode: tokens of the next V load (chunk n+1) and K load (chunk
     // n+3), loaded during the previous step.
     int tok_v[MY_LOADS], tok_k[MY_LOADS];
+    // One step's work on the rings.  The stages it loads (K(n+3), V(n+1)) and
+    // the stages it reads (V(n), K(n+2)) are always different, and every load
+    // of an earlier step has landed at the sync before it.  Passing the four
+    // stages as restrict pointers tells the compiler so: it then neither makes
+    // each LDS read wait for every buffer->LDS load in flight nor has to keep
+    // the loads after the reads, and the step needs fewer registers (no
+    // instance spills).
+    auto body = [&](int n, bool full, bool has1, bool has2, bool has3, int key1, int key3,
+                    uint16_t *__restrict__ kdst, uint16_t *__restrict__ vdst,
+                    const uint16_t *__restrict__ ksrc, const uint16_t *__restrict__ vsrc,
+                    f32x16 (&s_cur)[NT], f32x16 (&s_next)[NT]) {
+        bf16x8 vf[MT][2];
+        bf16x8 pf[NT][2];
+        read_v(vsrc, vf);
+        if (has1) scores(kf, s_next);
+        if (COLS && has1 && n + 1 == n_total - 1 && tail < kChunk) mask_tail(s_next);
+        weights(s_cur, pf);
+        if (has2) read_k(ksrc, kf);
+        if (COLS) {
+            if (has1) issue_v_tok(tok_v, vdst);
+            if (has3) issue_k_tok(tok_k, kdst);
+            // A FULL step has chunks up to n+4 (the loop runs while n+4 <
+            // n_total); a tail step never needs chunk n+4.
+            if (full || n + 2 < n_total) load_tok(n + 2, tok_v);
+            if (full) load_tok(n + 4, tok_k);
+        } else {
+            if (has1) issue_v(key1, vdst);
+            if (has3) issue_k(key3, kdst);
+        }
+        pv(vf, pf);
+        if (has1) update_max(s_next);
+    };
     auto step = [&](int n, bool full, f32x16 (&s_cur)[NT], f32x16 (&s_next)[NT]) {
         const bool has1 = full || n + 1 < n_total;
         const bool has2 = full || n + 2 < n_total;
@@ -464,26 +492,9 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         // memory, which is idle right after the sync.
         const int key1 = (!COLS && has1) ? chunk_key0(n + 1) : 0;
         const int key3 = (!COLS && has3) ? chunk_key0(n + 3) : 0;
-        bf16x8 vf[MT][2];
-        bf16x8 pf[NT][2];
-        read_v(n & 1, vf);
-        if (has1) scores(kf, s_next);
-        if (COLS && has1 && n + 1 == n_total - 1 && tail < kChunk) mask_tail(s_next);
-        weights(s_cur, pf);
-        if (has2) read_k((n + 2) % 3, kf);
-        if (COLS) {
-            if (has1) issue_v_tok(tok_v, (n + 1) & 1);
-            if (has3) issue_k_tok(tok_k, n % 3);
-            // A FULL step has chunks up to n+4 (the loop runs while n+4 <
-            // n_total); a tail step never needs chunk n+4.
-            if (full || n + 2 < n_total) load_tok(n + 2, tok_v);
-            if (full) load_tok(n + 4, tok_k);
-        } else {
-            if (has1) issue_v(key1, (n + 1) & 1);
-            if (has3) issue_k(key3, n % 3);
-        }
-        pv(vf, pf);
-        if (has1) update_max(s_next);
+        body(n, full, has1, has2, has3, key1, key3, kring + (n % 3) * TILE,
+             vring + ((n + 1) & 1) * TILE, kring + ((n + 2) % 3) * TILE, vring + (n & 1) * TILE,
+             s_cur, s_next);
     };
 
     f32x16 sA[NT], sB[NT];
@@ -495,22 +506,22 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         load_tok(1, tok_v);
         load_tok(2, t2);
         load_tok(3, tok_k);
-        issue_k_tok(t0, 0);
-        issue_v_tok(t0, 0);
-        if (n_total > 1) issue_k_tok(tok_v, 1);
-        if (n_total > 2) issue_k_tok(t2, 2);
+        issue_k_tok(t0, kring);
+        issue_v_tok(t0, vring);
+        if (n_total > 1) issue_k_tok(tok_v, kring + TILE);
+        if (n_total > 2) issue_k_tok(t2, kring + 2 * TILE);
     } else {
         const int key0 = chunk_key0(0);
-        issue_k(key0, 0);
-        issue_v(key0, 0);
-        if (n_total > 1) issue_k(chunk_key0(1), 1);
-        if (n_total > 2) issue_k(chunk_key0(2), 2);
+        issue_k(key0, kring);
+        issue_v(key0, vring);
+        if (n_total > 1) issue_k(chunk_key0(1), kring + TILE);
+        if (n_total > 2) issue_k(chunk_key0(2), kring + 2 * TILE);
     }
     sync();
-    read_k(0, kf);
+    read_k(kring, kf);
     scores(kf, sA);
     if (COLS && n_total == 1 && tail < kChunk) mask_tail(sA);
-    if (n_total > 1) read_k(1, kf);
+    if (n_total > 1) read_k(kring + TILE, kf);
     update_max(sA);
 
     int n = 0;
