@@ -200,6 +200,29 @@ def test_sparsity_zero_equals_dense(shape):
     assert torch.equal(o_s, o_d)
 
 
+def test_zero_budget_keeps_nothing():
+    """s just below 1 leaves K = 0 (the guard of R13 takes x below zero): no
+    digit pass runs, every row is empty, the plan's records have empty lists
+    and the sparse launch writes zeros over the NaN-filled output."""
+    H, Hkv, L, d, blk = 4, 2, 8 * 64, 64, 64
+    s = 1.0 - 1e-10
+    q, k, v = _qkv((H, Hkv, L, d, blk, 1.0), 808)
+    dims = B.dims_of(q, k, blk)
+    nb = L // blk
+    assert B.keep_count(dims, s) == 0 == O.keep_count(H * nb * nb, s)
+    buf = B.MaskBuffers(dims, s, device=DEV)
+    B.build_mask(dims, s, q, k, buf.ws, buf.row_ptr, buf.col_idx)
+    o = torch.full_like(q, float("nan"))
+    B.sparse_attn(dims, q, k, v, buf.col_idx, buf.ws, o, nnz=0)
+    torch.cuda.synchronize()
+    rp = buf.row_ptr.cpu().numpy()
+    assert not rp.any()
+    work_ref, n_ref = O.plan(rp, H, nb, blk)
+    assert np.array_equal(buf.work().cpu().numpy(), work_ref) and n_ref == 0
+    _check_records(buf.work_rec().cpu().numpy(), work_ref, rp, np.zeros(1, np.int32))
+    assert torch.equal(o, torch.zeros_like(o))
+
+
 def test_dropped_block_is_detected():
     """Mutation: remove one kept block from the longest row of the mask given
     to the GPU; the comparison with the oracle on the full mask must fail."""
