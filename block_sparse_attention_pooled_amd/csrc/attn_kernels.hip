@@ -59,6 +59,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define SD_LDS __attribute__((address_space(3)))
@@ -81,10 +82,6 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
 // write-back.
 __device__ __forceinline__ void store_nt(uint16_t *p, uint4 v) {
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
-}
-
-__device__ __forceinline__ uint16_t bf16_rne(float x) {
-    return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
 // 16 bytes per lane from a buffer straight into LDS (64 lanes -> 1 KiB
@@ -560,13 +557,14 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 const int i = 4 * i4;
-                const uint32_t lo = (uint32_t)bf16_rne(oacc[mt][nt][i] * inv_l) |
-                                    ((uint32_t)bf16_rne(oacc[mt][nt][i + 1] * inv_l) << 16);
-                const uint32_t hi = (uint32_t)bf16_rne(oacc[mt][nt][i + 2] * inv_l) |
-                                    ((uint32_t)bf16_rne(oacc[mt][nt][i + 3] * inv_l) << 16);
+                // Four dims at once: two packed round-to-nearest-even converts.
+                const bf16x4 v4 = {(__bf16)(oacc[mt][nt][i] * inv_l),
+                                   (__bf16)(oacc[mt][nt][i + 1] * inv_l),
+                                   (__bf16)(oacc[mt][nt][i + 2] * inv_l),
+                                   (__bf16)(oacc[mt][nt][i + 3] * inv_l)};
                 const int seg = 4 * mt + i4;    // dims 8*seg .. +8; this lane's half is 4*hh
-                *reinterpret_cast<uint2 *>(ot + r * D + 8 * (seg ^ (r & (SEGS - 1))) + 4 * hh) =
-                    make_uint2(lo, hi);
+                *reinterpret_cast<bf16x4 *>(ot + r * D + 8 * (seg ^ (r & (SEGS - 1))) + 4 * hh) =
+                    v4;
             }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
