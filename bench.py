@@ -58,6 +58,9 @@ def parse_args():
     p.add_argument("--columns", action="store_true",
                    help="the column-sparse variant (PulseCol): per head the ceil((1-s)L) key "
                         "columns of largest pooled-query mass, refreshed at the same anchors")
+    p.add_argument("--gqa-group", action="store_true",
+                   help="GQA variant with group-shared K/V tiles against the per-head kernel, "
+                        "at the workload's anchor for each of its sparsities")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (for counter calibration)")
     return p.parse_args()
@@ -299,6 +302,60 @@ def mask_quality(args, w, sparsity, dev, T):
     print(json.dumps(result), flush=True)
 
 
+def gqa_group(args, w, dev):
+    """Per-head sparse kernel against the group-shared variant on the anchor
+    step's mask: kernel times, bit identity, K/V tiles streamed per kept pair."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_pooled_amd import binding as B
+    from block_sparse_attention_pooled_amd.inputs import Trajectory
+    q, k, v = Trajectory(w, dev).next()
+    dims = B.make_dims(w.H, w.Hkv, w.L, w.d, w.B)
+    G = w.H // w.Hkv
+    sps = [args.sparsity] if args.sparsity is not None else list(w.sparsities)
+    out = []
+
+    def med(fn, reps=30):
+        for _ in range(5):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(); fn(); b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+
+    for s in sps:
+        buf = B.MaskBuffers(dims, s, device=dev)
+        B.build_mask(dims, s, q, k, buf.ws, buf.row_ptr, buf.col_idx)
+        o1, o2 = torch.empty_like(q), torch.empty_like(q)
+        t_head = med(lambda: B.sparse_attn(dims, q, k, v, buf.col_idx, buf.ws, o1, nnz=buf.K))
+        t_group = med(lambda: B.sparse_attn_group(dims, q, k, v, buf.row_ptr, buf.col_idx, o2,
+                                                  nnz=buf.K))
+        rp = buf.row_ptr.cpu().numpy()
+        ci = buf.col_idx[:buf.K].cpu().numpy()
+        keep = np.zeros((w.H, w.nb, w.nb), bool)
+        rows = np.repeat(np.arange(w.H * w.nb), np.diff(rp))
+        keep.reshape(-1, w.nb)[rows, ci] = True
+        union = 0
+        for g in range(w.Hkv):
+            for h0 in range(g * G, (g + 1) * G, 2):
+                union += int(keep[h0:min(h0 + 2, (g + 1) * G)].any(axis=0).sum())
+        flops = 4.0 * w.B ** 2 * w.d * buf.K
+        out.append({"sparsity": s, "kept_blocks": buf.K,
+                    "per_head_kernel_ms": round(t_head, 4), "group_kernel_ms": round(t_group, 4),
+                    "per_head_tflops": round(flops / (t_head * 1e-3) / 1e12, 1),
+                    "group_tflops": round(flops / (t_group * 1e-3) / 1e12, 1),
+                    "identical_output": bool(torch.equal(o1, o2)),
+                    "kv_tiles_per_kept_pair": round(union / buf.K, 4)})
+    print(json.dumps({
+        "metric": "GQA group-shared K/V tiles: kernel time against the per-head sparse kernel",
+        "unit": "ms", "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+        "config": {"workload": w.name, "H": w.H, "Hkv": w.Hkv, "L": w.L, "d": w.d,
+                   "block": w.B, "heads_per_workgroup": 2},
+        "results": out}), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -317,6 +374,9 @@ def main():
     T = args.traj_steps or w.steps
     if args.mask_quality:
         mask_quality(args, w, sparsity, dev, T)
+        return
+    if args.gqa_group:
+        gqa_group(args, w, dev)
         return
     if args.columns and args.per_head_budget:
         print("bench.py: --columns already keeps the same number of columns per head",

@@ -67,6 +67,7 @@ def load():
         "stepdllm_plan": (i32, [D, _vp, _vp, i64, _vp, sz, _vp]),
         "stepdllm_sparse_attn": (i32, [D, _vp, _vp, _vp, _vp, i64, _vp, sz, _vp, _vp]),
         "stepdllm_dense_attn": (i32, [D, _vp, _vp, _vp, _vp, _vp]),
+        "stepdllm_sparse_attn_group": (i32, [D, _vp, _vp, _vp, _vp, _vp, i64, _vp, _vp]),
         "stepdllm_block_mass": (i32, [D, _vp, _vp, _vp, _vp]),
         "stepdllm_mask_recall": (i32, [D, _vp, _vp, _vp, i64, _vp, _vp]),
         "stepdllm_keep_count_columns": (i64, [D, dbl]),
@@ -92,7 +93,8 @@ def load():
 EXPORTS = ["stepdllm_keep_count", "stepdllm_workspace_bytes", "stepdllm_workspace_layout",
            "stepdllm_build_mask", "stepdllm_select_mask", "stepdllm_keep_count_per_head",
            "stepdllm_build_mask_per_head", "stepdllm_select_mask_per_head", "stepdllm_plan",
-           "stepdllm_sparse_attn", "stepdllm_dense_attn", "stepdllm_block_mass",
+           "stepdllm_sparse_attn", "stepdllm_sparse_attn_group", "stepdllm_dense_attn",
+           "stepdllm_block_mass",
            "stepdllm_mask_recall", "stepdllm_keep_count_columns", "stepdllm_build_col_mask",
            "stepdllm_select_col_mask", "stepdllm_col_attn", "stepdllm_col_recall",
            "stepdllm_driver_create",
@@ -198,6 +200,17 @@ def sparse_attn(dims, q, k, v, col_idx, ws, o, nnz=None, stream=None):
         _ptr(col_idx, torch.int32, "col_idx"), nnz,
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _ptr(o, bf, "o"), _stream(stream)),
         "stepdllm_sparse_attn")
+
+
+def sparse_attn_group(dims, q, k, v, row_ptr, col_idx, o, nnz=None, stream=None):
+    """GQA variant with group-shared K/V tiles (no plan, no workspace); nnz
+    defaults to col_idx.numel()."""
+    bf = torch.bfloat16
+    nnz = col_idx.numel() if nnz is None else int(nnz)
+    _check(load().stepdllm_sparse_attn_group(
+        ctypes.byref(dims), _ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
+        _ptr(row_ptr, torch.int32, "row_ptr"), _ptr(col_idx, torch.int32, "col_idx"), nnz,
+        _ptr(o, bf, "o"), _stream(stream)), "stepdllm_sparse_attn_group")
 
 
 def dense_attn(dims, q, k, v, o, stream=None):

@@ -270,6 +270,19 @@ int stepdllm_sparse_attn(const stepdllm_dims *dims, const uint16_t *q, const uin
                                              static_cast<hipStream_t>(stream)));
 }
 
+int stepdllm_sparse_attn_group(const stepdllm_dims *dims, const uint16_t *q, const uint16_t *k,
+                               const uint16_t *v, const int32_t *row_ptr,
+                               const int32_t *col_idx, int64_t nnz, uint16_t *o, void *stream) {
+    Dims D;
+    int st = check_dims(dims, &D);
+    if (st) return st;
+    if (!q || !k || !v || !row_ptr || !col_idx || !o) return STEPDLLM_EINVAL;
+    if (nnz < 0 || nnz > D.n_scores()) return STEPDLLM_EINVAL;
+    if (D.B != 64) return STEPDLLM_EUNSUPPORTED;
+    return hip_status(sd::launch_group_attn(D, q, k, v, row_ptr, col_idx, nnz, o,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int stepdllm_dense_attn(const stepdllm_dims *dims, const uint16_t *q, const uint16_t *k,
                         const uint16_t *v, uint16_t *o, void *stream) {
     Dims D;

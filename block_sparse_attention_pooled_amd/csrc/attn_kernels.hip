@@ -50,6 +50,13 @@
 // per-lane offsets come from the list.  The list entries a step needs are
 // loaded one step ahead; a short last chunk has its missing keys' scores set
 // to -inf, so they get weight 0.
+//
+// Group mode (grouped-query attention, heads h / (H/Hkv) sharing a key head):
+// a workgroup takes two query heads of one KV group for one query block and
+// streams the union of their kept-block lists through one K/V ring, so a tile
+// both keep is read once.  Each wave computes only the chunks its head keeps
+// (reads, scores, weights and products are skipped otherwise; the barriers
+// stay common), so each head's output is that of the sparse mode bit for bit.
 #include "common.h"
 
 namespace sd {
@@ -72,6 +79,8 @@ constexpr int kQW = 32;             // query rows per wave
 constexpr int kModeSparse = 0;      // the kept blocks of the row (CSR lists, work order)
 constexpr int kModeDense = 1;       // every key block
 constexpr int kModeCols = 2;        // the head's kept key columns (col_idx = [H, n_idx])
+constexpr int kModeGroup = 3;       // two heads of one KV group over the union of their lists
+constexpr int kGroupHeads = 2;      // query heads per workgroup in group mode
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
@@ -103,13 +112,18 @@ __device__ __forceinline__ int swz_v(int row) {
 }
 
 template <int D, int BLK, int QW, int MODE>
-__global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
+__global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads : 1),
+                             QW == 32 ? 2 : 1) void k_attn(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const int32_t *__restrict__ col_idx,
-    const int4 *__restrict__ recs, uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx, int64_t cap,
+    const uint16_t *__restrict__ v, const int32_t *__restrict__ row_ptr,
+    const int32_t *__restrict__ col_idx, const int4 *__restrict__ recs,
+    uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx, int64_t cap,
     float scale_log2) {
     constexpr int NT = QW / 32;                 // 32-query tiles per wave
-    constexpr int WQ = BLK / QW;                // query slices (= waves) per block
+    constexpr int WQ = BLK / QW;                // query slices (waves) per query block
+    constexpr bool GROUP = MODE == kModeGroup;
+    constexpr int HS = GROUP ? kGroupHeads : 1; // query heads per workgroup
+    constexpr int NW = WQ * HS;                 // waves per workgroup
     constexpr int KS = D / 16;                  // k steps of the score product
     constexpr int MT = D / 32;                  // 32-row tiles of O^T
     constexpr int CPB = BLK / kChunk;           // chunks per key block
@@ -119,23 +133,49 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     constexpr int LOADS = kChunk / ROWS_PER_LOAD;   // wave loads per tile
     constexpr bool SPARSE = MODE == kModeSparse;
     constexpr bool COLS = MODE == kModeCols;
-    // A three-stage K ring and a two-stage V ring, shared by the WQ waves of
+    // A three-stage K ring and a two-stage V ring, shared by the NW waves of
     // the workgroup.
     __shared__ __attribute__((aligned(16))) uint16_t rings[5 * TILE];
+    // Group mode: the union of the heads' lists, one entry per key block:
+    // block id | (bit s set when head slot s keeps it) << 16.
+    __shared__ int32_t uni[GROUP ? kMaxBlocks : 1];
+    __shared__ int32_t uflag[GROUP ? kMaxBlocks : 1];
+    __shared__ int32_t uwave[GROUP ? NW : 1];
     uint16_t *const kring = rings;
     uint16_t *const vring = rings + 3 * TILE;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-    const int wq = wave;
+    const int wq = wave % WQ;                   // query slice of this wave
+    const int hs = wave / WQ;                   // head slot (group mode)
     const int col = lane & 31, hh = lane >> 5;
 
     // Row of this workgroup and, in sparse mode, its list bounds and first
     // two block ids from the work record.
     int row;
     int rec_begin = 0, rec_end = 0, rec_ids = 0;
-    if (!SPARSE) {
+    bool head_ok = true;          // group mode: this wave's head slot holds a head
+    int grp_row0 = 0;             // group mode: row of head slot 0
+    if (GROUP) {
+        // Workgroup b: KV group g, head pair p (heads g*G + 2p, + 1), query
+        // block i; the pairs of a group sit on one XCD when they can.
+        const int pairs = (G + kGroupHeads - 1) / kGroupHeads;
+        const int units = H / G * pairs;
+        const int b = blockIdx.x;
+        int gp, i;
+        if ((units & 7) == 0) {
+            gp = (b & 7) + 8 * ((b >> 3) / nb);
+            i = (b >> 3) % nb;
+        } else {
+            gp = b / nb;
+            i = b % nb;
+        }
+        const int g_ = gp / pairs, slot0 = (gp % pairs) * kGroupHeads;
+        head_ok = slot0 + hs < G;
+        grp_row0 = (g_ * G + slot0) * nb + i;
+        row = head_ok ? grp_row0 + hs * nb : grp_row0;
+    } else if (!SPARSE) {
         const int b = blockIdx.x;
         if ((H & 7) == 0) {   // keep each head's rows on one XCD (round-robin dispatch)
             const int x = b & 7, kk = b >> 3;
@@ -165,16 +205,60 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         e_begin = max(rec_begin, 0);
         e_end = min(rec_end, n_idx);
     }
+    int n_union = 0;
+    if (GROUP) {
+        // Union of the head slots' lists (positions past n_idx are not read,
+        // ids clamped into [0, nb)), then compacted in ascending block order.
+        for (int j = tid; j < nb; j += NW * 64) uflag[j] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int sl = 0; sl < HS; ++sl) {
+            const int gr = grp_row0 + sl * nb;
+            const bool ok = (grp_row0 / nb) % G + sl < G && gr < H * nb;
+            const int lo = ok ? max(row_ptr[gr], 0) : 0;
+            const int hi = ok ? min(row_ptr[gr + 1], n_idx) : 0;
+            for (int e = lo + tid; e < hi; e += NW * 64)
+                atomicOr(&uflag[min(max(col_idx[e], 0), nb - 1)], 1 << sl);
+        }
+        __syncthreads();
+        const int per = (nb + NW * 64 - 1) / (NW * 64);
+        const int j0 = min(tid * per, nb), j1 = min(j0 + per, nb);
+        int cnt = 0;
+        for (int j = j0; j < j1; ++j) cnt += uflag[j] != 0;
+        int inc = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(inc, off);
+            if (lane >= off) inc += y;
+        }
+        if (lane == 63) uwave[wave] = inc;
+        __syncthreads();
+        int pos = inc - cnt;
+        for (int w = 0; w < wave; ++w) pos += uwave[w];
+        for (int w = 0; w < NW; ++w) n_union += uwave[w];
+        for (int j = j0; j < j1; ++j)
+            if (uflag[j]) uni[pos++] = j | (uflag[j] << 16);
+        __syncthreads();
+    }
     // The row's chunks: every 32-key chunk of every kept block e, in order
-    // (column mode: 32 consecutive entries of the head's column list).
-    const int n_total = COLS ? (n_idx + kChunk - 1) / kChunk
-                             : (e_end > e_begin ? (e_end - e_begin) * CPB : 0);
+    // (column mode: 32 consecutive entries of the head's column list; group
+    // mode: every chunk of the union, each wave computing only its head's).
+    const int n_total = COLS  ? (n_idx + kChunk - 1) / kChunk
+                        : GROUP ? n_union * CPB
+                                : (e_end > e_begin ? (e_end - e_begin) * CPB : 0);
     if (n_total <= 0) {     // no kept key: the row attends to nothing
         const uint4 z = make_uint4(0, 0, 0, 0);
-        for (int x = lane; x < QW * D / 8; x += 64)
-            store_nt(o + qbase + (int64_t)x * 8, z);
+        if (head_ok)
+            for (int x = lane; x < QW * D / 8; x += 64)
+                store_nt(o + qbase + (int64_t)x * 8, z);
         return;
     }
+    // Group mode: does this wave's head keep union entry e (chunks CPB*e ..)?
+    auto member = [&](int n) -> bool {
+        if (!GROUP) return true;
+        const int ent = __builtin_amdgcn_readfirstlane(uni[n / CPB]);
+        return head_ok && ((ent >> (16 + hs)) & 1);
+    };
 
     // Q^T operand fragments: lane holds query col (32*nt + col), dims 16*s + 8*hh .. +8.
     bf16x8 qf[NT][KS];
@@ -212,7 +296,9 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     auto chunk_key0 = [&](int n) -> int {
         const int e_rel = n / CPB;
         int j;
-        if (!SPARSE) {
+        if (GROUP) {
+            j = __builtin_amdgcn_readfirstlane(uni[e_rel]) & 0xFFFF;
+        } else if (!SPARSE) {
             j = e_begin + e_rel;
         } else if (e_rel < 2) {   // the record's ids: no wait on the list load
             j = (rec_ids >> (16 * e_rel)) & 0xFFFF;
@@ -240,13 +326,14 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(v + kvbase), 0, L * D * 2, 0x00020000);
     const int r_in = lane / NSEG, sp = lane % NSEG;
-    // The WQ waves of the workgroup split each tile's LOADS wave loads:
-    // this wave issues loads t = tt*WQ + wq.
-    constexpr int MY_LOADS = LOADS / WQ;
+    // The NW waves of the workgroup split each tile's LOADS wave loads:
+    // this wave issues loads t = tt*NW + wave.
+    static_assert(LOADS % NW == 0, "a tile's loads split evenly over the waves");
+    constexpr int MY_LOADS = LOADS / NW;
     uint32_t k_voff[MY_LOADS];
 #pragma unroll
     for (int tt = 0; tt < MY_LOADS; ++tt) {
-        const int r = (tt * WQ + wq) * ROWS_PER_LOAD + r_in;
+        const int r = (tt * NW + wave) * ROWS_PER_LOAD + r_in;
         k_voff[tt] = (uint32_t)(r_in * D * 2 + 16 * (sp ^ swz_k<D>(r)));
     }
     const uint32_t v_voff = (uint32_t)(r_in * D * 2 + 16 * (sp ^ swz_v<D>(r_in)));
@@ -254,7 +341,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         const uint32_t off = (uint32_t)key0 * (D * 2);
 #pragma unroll
         for (int tt = 0; tt < MY_LOADS; ++tt) {
-            const int t = tt * WQ + wq;
+            const int t = tt * NW + wave;
             load_lds16(k_rsrc, dst + t * 512, k_voff[tt], off + t * ROWS_PER_LOAD * D * 2);
         }
     };
@@ -262,7 +349,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         const uint32_t off = (uint32_t)key0 * (D * 2);
 #pragma unroll
         for (int tt = 0; tt < MY_LOADS; ++tt) {
-            const int t = tt * WQ + wq;
+            const int t = tt * NW + wave;
             load_lds16(v_rsrc, dst + t * 512, v_voff, off + t * ROWS_PER_LOAD * D * 2);
         }
     };
@@ -272,19 +359,19 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(col_idx + (COLS ? (int64_t)h * n_idx : 0)), 0, COLS ? n_idx * 4 : 0,
         0x00020000);
-    const uint32_t tok_voff = (uint32_t)((wq * ROWS_PER_LOAD + r_in) * 4);
+    const uint32_t tok_voff = (uint32_t)((wave * ROWS_PER_LOAD + r_in) * 4);
     auto load_tok = [&](int c, int (&tok)[MY_LOADS]) {
 #pragma unroll
         for (int tt = 0; tt < MY_LOADS; ++tt)
             tok[tt] = (int)__builtin_amdgcn_raw_buffer_load_b32(
-                c_rsrc, tok_voff + tt * WQ * ROWS_PER_LOAD * 4, c * kChunk * 4, 0);
+                c_rsrc, tok_voff + tt * NW * ROWS_PER_LOAD * 4, c * kChunk * 4, 0);
     };
     // Gathered rows: the token's row in the key head, at the segment the
     // contiguous loads would use.  Tokens outside the head read zeros.
     auto issue_k_tok = [&](const int (&tok)[MY_LOADS], uint16_t *dst) {
 #pragma unroll
         for (int tt = 0; tt < MY_LOADS; ++tt) {
-            const int t = tt * WQ + wq;
+            const int t = tt * NW + wave;
             load_lds16(k_rsrc, dst + t * 512,
                        (uint32_t)tok[tt] * (D * 2) + (k_voff[tt] - r_in * D * 2), 0);
         }
@@ -292,7 +379,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     auto issue_v_tok = [&](const int (&tok)[MY_LOADS], uint16_t *dst) {
 #pragma unroll
         for (int tt = 0; tt < MY_LOADS; ++tt) {
-            const int t = tt * WQ + wq;
+            const int t = tt * NW + wave;
             load_lds16(v_rsrc, dst + t * 512,
                        (uint32_t)tok[tt] * (D * 2) + (v_voff - r_in * D * 2), 0);
         }
@@ -429,7 +516,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     auto sync = [&] {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (WQ > 1) __syncthreads();
+        if (NW > 1) __syncthreads();
     };
 
     // Software pipeline over the row's chunks; K(c) sits in K stage c%3, V(c)
@@ -455,17 +542,19 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     // each LDS read wait for every buffer->LDS load in flight nor has to keep
     // the loads after the reads, and the step needs fewer registers (no
     // instance spills).
-    auto body = [&](int n, bool full, bool has1, bool has2, bool has3, int key1, int key3,
-                    uint16_t *__restrict__ kdst, uint16_t *__restrict__ vdst,
+    // m0, m1, m2: this wave computes chunks n, n+1, n+2 (always, except for
+    // the chunks of the union that its head does not keep in group mode).
+    auto body = [&](int n, bool full, bool has1, bool has2, bool has3, bool m0, bool m1, bool m2,
+                    int key1, int key3, uint16_t *__restrict__ kdst, uint16_t *__restrict__ vdst,
                     const uint16_t *__restrict__ ksrc, const uint16_t *__restrict__ vsrc,
                     f32x16 (&s_cur)[NT], f32x16 (&s_next)[NT]) {
         bf16x8 vf[MT][2];
         bf16x8 pf[NT][2];
-        read_v(vsrc, vf);
-        if (has1) scores(kf, s_next);
+        if (m0) read_v(vsrc, vf);
+        if (has1 && m1) scores(kf, s_next);
         if (COLS && has1 && n + 1 == n_total - 1 && tail < kChunk) mask_tail(s_next);
-        weights(s_cur, pf);
-        if (has2) read_k(ksrc, kf);
+        if (m0) weights(s_cur, pf);
+        if (has2 && m2) read_k(ksrc, kf);
         if (COLS) {
             if (has1) issue_v_tok(tok_v, vdst);
             if (has3) issue_k_tok(tok_k, kdst);
@@ -477,8 +566,8 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
             if (has1) issue_v(key1, vdst);
             if (has3) issue_k(key3, kdst);
         }
-        pv(vf, pf);
-        if (has1) update_max(s_next);
+        if (m0) pv(vf, pf);
+        if (has1 && m1) update_max(s_next);
     };
     auto step = [&](int n, bool full, f32x16 (&s_cur)[NT], f32x16 (&s_next)[NT]) {
         const bool has1 = full || n + 1 < n_total;
@@ -489,7 +578,8 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         // memory, which is idle right after the sync.
         const int key1 = (!COLS && has1) ? chunk_key0(n + 1) : 0;
         const int key3 = (!COLS && has3) ? chunk_key0(n + 3) : 0;
-        body(n, full, has1, has2, has3, key1, key3, kring + (n % 3) * TILE,
+        const bool m0 = member(n), m1 = has1 && member(n + 1), m2 = has2 && member(n + 2);
+        body(n, full, has1, has2, has3, m0, m1, m2, key1, key3, kring + (n % 3) * TILE,
              vring + ((n + 1) & 1) * TILE, kring + ((n + 2) % 3) * TILE, vring + (n & 1) * TILE,
              s_cur, s_next);
     };
@@ -515,11 +605,12 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
         if (n_total > 2) issue_k(chunk_key0(2), kring + 2 * TILE);
     }
     sync();
-    read_k(kring, kf);
-    scores(kf, sA);
+    const bool p0 = member(0), p1 = n_total > 1 && member(1);
+    if (p0) read_k(kring, kf);
+    if (p0) scores(kf, sA);
     if (COLS && n_total == 1 && tail < kChunk) mask_tail(sA);
-    if (n_total > 1) read_k(kring + TILE, kf);
-    update_max(sA);
+    if (p1) read_k(kring + TILE, kf);
+    if (p0) update_max(sA);
 
     int n = 0;
     for (; n + 4 < n_total; n += 2) {
@@ -546,11 +637,12 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
     sync();
     constexpr int SEGS = D / 8;                 // 16-byte segments per row
     constexpr int RPI = 64 / SEGS;              // rows per store instruction
-    static_assert(WQ * QW * D <= 5 * TILE, "the staged tiles fit in the rings");
-    uint16_t *ot = rings + wq * QW * D;
+    static_assert(NW * QW * D <= 5 * TILE, "the staged tiles fit in the rings");
+    uint16_t *ot = rings + wave * QW * D;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const float inv_l = 1.0f / l_run[nt];
+        // Group mode: a head that keeps no block of the union writes zeros.
+        const float inv_l = (GROUP && !(l_run[nt] > 0.0f)) ? 0.0f : 1.0f / l_run[nt];
         const int r = 32 * nt + col;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -568,6 +660,7 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
             }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (!head_ok) return;
     uint16_t *orow = o + qbase;
 #pragma unroll
     for (int t = 0; t < QW / RPI; ++t) {
@@ -580,14 +673,19 @@ __global__ __launch_bounds__(BLK / QW * 64, QW == 32 ? 2 : 1) void k_attn(
 
 template <int D, int BLK, int QW, int MODE>
 hipError_t launch_attn_t(const Dims &Dm, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                         const int32_t *col_idx, const int4 *recs, int n_idx, uint16_t *o,
-                         hipStream_t s) {
+                         const int32_t *row_ptr, const int32_t *col_idx, const int4 *recs,
+                         int n_idx, uint16_t *o, hipStream_t s) {
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int64_t cap = Dm.die_cap();
-    const unsigned grid = (unsigned)(MODE != kModeSparse ? Dm.rows() : kDies * cap);
-    hipLaunchKernelGGL((k_attn<D, BLK, QW, MODE>), dim3(grid), dim3(BLK / QW * 64),
-                       0, s, q, k, v, col_idx, recs, o, Dm.L, Dm.nb, Dm.G, Dm.H,
-                       n_idx, cap, scale_log2);
+    const int64_t group_units =
+        (int64_t)(Dm.H / Dm.G) * ((Dm.G + kGroupHeads - 1) / kGroupHeads) * Dm.nb;
+    const unsigned grid = (unsigned)(MODE == kModeSparse  ? kDies * cap
+                                     : MODE == kModeGroup ? group_units
+                                                          : Dm.rows());
+    const unsigned threads = BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads : 1);
+    hipLaunchKernelGGL((k_attn<D, BLK, QW, MODE>), dim3(grid), dim3(threads), 0, s, q, k, v,
+                       row_ptr, col_idx, recs, o, Dm.L, Dm.nb, Dm.G, Dm.H, n_idx, cap,
+                       scale_log2);
     return hipGetLastError();
 }
 
@@ -596,12 +694,14 @@ hipError_t launch_attn(const Dims &D, const uint16_t *q, const uint16_t *k, cons
                        const int32_t *col_idx, const int4 *recs, int n_idx, uint16_t *o,
                        hipStream_t s) {
     if (D.d == 128 && D.B == 64)
-        return launch_attn_t<128, 64, kQW, MODE>(D, q, k, v, col_idx, recs, n_idx, o, s);
+        return launch_attn_t<128, 64, kQW, MODE>(D, q, k, v, nullptr, col_idx, recs, n_idx, o,
+                                                 s);
     if (D.d == 128 && D.B == 128)
-        return launch_attn_t<128, 128, kQW, MODE>(D, q, k, v, col_idx, recs, n_idx, o, s);
+        return launch_attn_t<128, 128, kQW, MODE>(D, q, k, v, nullptr, col_idx, recs, n_idx, o,
+                                                  s);
     if (D.d == 64 && D.B == 64)
-        return launch_attn_t<64, 64, kQW, MODE>(D, q, k, v, col_idx, recs, n_idx, o, s);
-    return launch_attn_t<64, 128, kQW, MODE>(D, q, k, v, col_idx, recs, n_idx, o, s);
+        return launch_attn_t<64, 64, kQW, MODE>(D, q, k, v, nullptr, col_idx, recs, n_idx, o, s);
+    return launch_attn_t<64, 128, kQW, MODE>(D, q, k, v, nullptr, col_idx, recs, n_idx, o, s);
 }
 
 }  // namespace
@@ -621,6 +721,17 @@ hipError_t launch_col_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                            const uint16_t *v, const int32_t *cols, int64_t k_c, uint16_t *o,
                            hipStream_t s) {
     return launch_attn<kModeCols>(D, q, k, v, cols, nullptr, (int)k_c, o, s);
+}
+
+hipError_t launch_group_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
+                             const uint16_t *v, const int32_t *row_ptr, const int32_t *col_idx,
+                             int64_t nnz, uint16_t *o, hipStream_t s) {
+    if (D.B != 64) return hipErrorInvalidValue;   // the entry point rejects it first
+    if (D.d == 128)
+        return launch_attn_t<128, 64, kQW, kModeGroup>(D, q, k, v, row_ptr, col_idx, nullptr,
+                                                       (int)nnz, o, s);
+    return launch_attn_t<64, 64, kQW, kModeGroup>(D, q, k, v, row_ptr, col_idx, nullptr,
+                                                  (int)nnz, o, s);
 }
 
 }  // namespace sd

@@ -135,6 +135,12 @@ hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *
                               int64_t n_idx, uint16_t *o, hipStream_t s);
 hipError_t launch_dense_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                              const uint16_t *v, uint16_t *o, hipStream_t s);
+// GQA variant: one workgroup per (KV group, pair of its query heads, query
+// block) streams the union of the pair's lists through one K/V ring; each
+// head's output equals launch_sparse_attn's.  Block size 64 only.
+hipError_t launch_group_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
+                             const uint16_t *v, const int32_t *row_ptr, const int32_t *col_idx,
+                             int64_t nnz, uint16_t *o, hipStream_t s);
 // Every query of head h over the key tokens cols[h*k_c .. h*k_c + k_c).
 hipError_t launch_col_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                            const uint16_t *v, const int32_t *cols, int64_t k_c, uint16_t *o,

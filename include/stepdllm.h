@@ -214,6 +214,23 @@ int stepdllm_sparse_attn(const stepdllm_dims *dims, const uint16_t *q,
                          const void *ws, size_t ws_bytes,
                          uint16_t *o, void *stream);
 
+/* GQA variant of stepdllm_sparse_attn with group-shared K/V tiles: the heads
+ * of a key head's group (h / (H/Hkv), the contiguous grouping of the
+ * Step-dLLM layers' grouped-query attention) read the same K/V, so one
+ * workgroup takes a pair of the group's query heads for one query block and
+ * streams the union of their two kept-block lists through one K/V tile ring;
+ * each head computes only on its own blocks, in the same order as
+ * stepdllm_sparse_attn, so each head's output is identical to it.  A tile
+ * kept by both heads is read once.  Needs no plan and no workspace: the lists
+ * come straight from row_ptr [H*nb + 1] / col_idx [nnz] (list positions
+ * outside [0, nnz) are not read, block ids outside [0, nb) are clamped).
+ * Block size 64 only (EUNSUPPORTED otherwise).  A head with an empty list
+ * outputs zeros. */
+int stepdllm_sparse_attn_group(const stepdllm_dims *dims, const uint16_t *q,
+                               const uint16_t *k, const uint16_t *v,
+                               const int32_t *row_ptr, const int32_t *col_idx,
+                               int64_t nnz, uint16_t *o, void *stream);
+
 /* Dense bidirectional attention, every block kept: the same-GPU baseline that
  * stands for "dense FlashAttention" in the Step-dLLM and SparseD abstracts. */
 int stepdllm_dense_attn(const stepdllm_dims *dims, const uint16_t *q,

@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = B.load()
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(B.EXPORTS) == names
@@ -119,6 +119,9 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, None, FAKE, 16, FAKE, ws_need, FAKE, None) == B.EINVAL
     assert lib.stepdllm_sparse_attn(r(d), FAKE, FAKE, FAKE, None, 16, FAKE, ws_need, FAKE, None) == B.EINVAL
     assert lib.stepdllm_dense_attn(r(d), FAKE, FAKE, FAKE, None, None) == B.EINVAL
+    assert lib.stepdllm_sparse_attn_group(r(d), FAKE, FAKE, FAKE, None, FAKE, 16, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_sparse_attn_group(r(d), FAKE, FAKE, FAKE, FAKE, FAKE, 33, FAKE, None) == B.EINVAL
+    assert lib.stepdllm_sparse_attn_group(r(dims(2, 2, 256, 64, 128)), FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None) == B.EUNSUPPORTED
     assert lib.stepdllm_select_mask(r(d), 0.5, None, FAKE, ws_need, FAKE, FAKE, None) == B.EINVAL
     assert lib.stepdllm_plan(r(d), None, FAKE, 16, FAKE, ws_need, None) == B.EINVAL
     assert lib.stepdllm_plan(r(d), FAKE, None, 16, FAKE, ws_need, None) == B.EINVAL
