@@ -498,7 +498,10 @@ def main():
             roofline["frac_of_sustained_random"] = round(attn_tflops / rate["random"]["tflops"], 4)
 
     result = {
-        "metric": METRIC_COLS if args.columns else METRIC,
+        "metric": (METRIC_COLS if args.columns else METRIC) if w.name == "stepdllm_8k" else
+                  (f"{'column' if args.columns else 'block'}-sparse attn ms/step + effective "
+                   f"TFLOP/s, {w.name} (L={w.L} H={w.H} Hkv={w.Hkv} d={w.d} B={w.B}, "
+                   f"s={sparsity})"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
