@@ -302,6 +302,24 @@ def mask_quality(args, w, sparsity, dev, T):
     print(json.dumps(result), flush=True)
 
 
+def temperature_trend(w, per_head, args):
+    """Per-head kept fraction of the last mask against the head's temperature
+    t_h (workloads that draw temperatures, block masks): the pairs sorted by
+    t_h and their Spearman rank correlation."""
+    if args.columns or not w.temperatures:
+        return {}
+    import numpy as np
+    from block_sparse_attention_pooled_amd.inputs import head_temperatures
+    t = head_temperatures(w.H, w.seed).numpy().astype(np.float64)
+    f = np.asarray(per_head, np.float64) / (w.nb * w.nb)
+    rt, rf = np.argsort(np.argsort(t)), np.argsort(np.argsort(f, kind="stable"), kind="stable")
+    rho = float(np.corrcoef(rt, rf)[0, 1]) if f.std() > 0 else None
+    order = np.argsort(t)
+    return {"kept_fraction_by_temperature": [[round(float(t[h]), 3), round(float(f[h]), 4)]
+                                             for h in order],
+            "kept_vs_temperature_rank_corr": round(rho, 4) if rho is not None else None}
+
+
 def gqa_group(args, w, dev):
     """Per-head sparse kernel against the group-shared variant on the anchor
     step's mask: kernel times, bit identity, K/V tiles streamed per kept pair."""
@@ -524,6 +542,7 @@ def main():
         "roofline": roofline,
         "kept_per_head": {"min": min(per_head), "max": max(per_head),
                           "cv": round(ph_cv, 4)},
+        **temperature_trend(w, per_head, args),
         "empty_rows": (None if args.columns else
                        int((drv.row_ptr[1:] == drv.row_ptr[:-1]).sum().item())),
         "anchor_step_ms": round(anchor_ms, 5) if anchor_ms else None,
