@@ -13,9 +13,9 @@ and evaluation data are not available:
   extents", Step-dLLM abstract).
 * Attention sinks: keys 0-3 of every key head scaled by 4.
 * Denoising-step drift: after every step Q, K, V += 0.02 * N(0, 1), a fresh draw
-  per element ("attention patterns are only locally consistent across steps",
-  Step-dLLM abstract), with an abrupt full redraw of Q and K at chosen steps
-  ("shift abruptly at certain transitions").
+  per element (the Step-dLLM abstract: attention patterns stay similar only
+  over nearby steps), with a full redraw of Q and K at chosen steps (the same
+  abstract: patterns can also change suddenly at some points).
 * Block structure (the structured 8K variant only, for the mask-quality
   measurement): each key head g draws a unit direction e[g, j] per key block j;
   every key token of block j gets + a * e[g, j], and every query token of block

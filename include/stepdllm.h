@@ -232,7 +232,7 @@ int stepdllm_sparse_attn_group(const stepdllm_dims *dims, const uint16_t *q,
                                int64_t nnz, uint16_t *o, void *stream);
 
 /* Dense bidirectional attention, every block kept: the same-GPU baseline that
- * stands for "dense FlashAttention" in the Step-dLLM and SparseD abstracts. */
+ * stands for the dense FlashAttention of the Step-dLLM and SparseD abstracts. */
 int stepdllm_dense_attn(const stepdllm_dims *dims, const uint16_t *q,
                         const uint16_t *k, const uint16_t *v, uint16_t *o,
                         void *stream);
