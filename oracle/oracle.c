@@ -60,8 +60,8 @@ void oracle_pool(const float *x, int heads, int L, int d, int B, float *xb)
 
 /* ------------------------------------------------------ score + softmax --- */
 /* S[h,i,j] = (Qb[h,i,:] . Kb[g(h),j,:]) * (1/sqrt(d)), then a softmax over j
- * for each (h, i): the "normalised pooled scores" that the global budget
- * ranks.  Dot product in fp32, ascending c; softmax max-subtracted, sum in
+ * for each (h, i): the pooled scores, normalised per row, that the global
+ * budget ranks.  Dot product in fp32, ascending c; softmax max-subtracted, sum in
  * ascending j. */
 void oracle_scores(const float *qb, const float *kb, int H, int Hkv, int nb,
                    int d, float *P)
