@@ -377,8 +377,9 @@ def gqa_group(args, w, dev):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path would shard by query head, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported (a "
+              "multi-GPU run would shard the layer by query head, one all-reduce of the "
+              "select histogram per digit pass)", file=sys.stderr)
         sys.exit(2)
 
     import torch
