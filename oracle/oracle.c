@@ -232,8 +232,10 @@ int64_t oracle_build_mask_per_head(const float *q, const float *k, int H, int Hk
  *    each goes to the die with the least weight so far among those that
  *    hold fewer than cap_h = min(H, ceil(H/8) + 2) heads (ties: lowest die);
  *    the slack over ceil(H/8) lets the greedy balance skewed heads;
- *  - die x's list is its heads in that order, each head's rows by list
- *    length descending (ties by row id);
+ *  - die x's list is first the rows of its heads that keep a block (heads in
+ *    that order, each head's rows by list length descending, ties by row id),
+ *    then the rows that keep none (heads in the same order, rows ascending):
+ *    empty rows only write zeros, so they go where the launch runs down;
  *  - list x fills work[x*cap .. x*cap + cap), cap = cap_h*nb, and unused
  *    positions hold -1.
  * Returns the number of rows with at least one kept block. */
@@ -294,16 +296,27 @@ int32_t oracle_plan(const int32_t *row_ptr, int H, int nb, int B, int32_t *work)
     for (int64_t p = 0; p < ORACLE_DIES * cap; ++p)
         work[p] = -1;
     g_row_ptr = row_ptr;
+    int32_t *tmp = (int32_t *)malloc(sizeof(int32_t) * (size_t)nb);
     for (int x = 0; x < ORACLE_DIES; ++x) {
         int32_t *out = work + x * cap;
+        int64_t pos = 0;
         for (int c = 0; c < count[x]; ++c) {
             int h = die_heads[x * cap_heads + c];
             for (int i = 0; i < nb; ++i)
-                out[i] = h * nb + i;
-            qsort(out, (size_t)nb, sizeof(int32_t), by_len_desc_row_asc);
-            out += nb;
+                tmp[i] = h * nb + i;
+            qsort(tmp, (size_t)nb, sizeof(int32_t), by_len_desc_row_asc);
+            for (int i = 0; i < nb; ++i)
+                if (row_ptr[tmp[i] + 1] > row_ptr[tmp[i]])
+                    out[pos++] = tmp[i];
+        }
+        for (int c = 0; c < count[x]; ++c) {
+            int h = die_heads[x * cap_heads + c];
+            for (int i = 0; i < nb; ++i)
+                if (row_ptr[h * nb + i + 1] <= row_ptr[h * nb + i])
+                    out[pos++] = h * nb + i;
         }
     }
+    free(tmp);
     free(weight);
     free(heads);
     free(die_heads);

@@ -195,7 +195,8 @@ def _die_lists(lens, H, nb, B):
     """The die lists of the work-order spec written out in Python: heads by
     weight (B/32)*kept + 4*nonempty rows (descending, then id) to the
     least-loaded die with room for min(H, ceil(H/8) + 2) heads; each die lists
-    its heads in that order, rows by length desc, ties by row id."""
+    the non-empty rows of its heads in that order (rows by length desc, ties by
+    row id), then the empty rows of its heads in that order (ascending)."""
     cap_h = min(H, -(-H // 8) + 2)
     weight = [(B // 32) * int(sum(lens[h * nb:(h + 1) * nb]))
               + 4 * int(sum(1 for r in range(h * nb, (h + 1) * nb) if lens[r] > 0))
@@ -206,9 +207,13 @@ def _die_lists(lens, H, nb, B):
         x = min((x for x in range(8) if len(dies[x]) < cap_h), key=lambda x: (load[x], x))
         dies[x].append(h)
         load[x] += weight[h]
-    return [[r for h in dies[x] for r in sorted(range(h * nb, (h + 1) * nb),
-                                                 key=lambda r: (-lens[r], r))]
-            for x in range(8)]
+    out = []
+    for x in range(8):
+        full = [r for h in dies[x] for r in sorted(range(h * nb, (h + 1) * nb),
+                                                   key=lambda r: (-lens[r], r)) if lens[r] > 0]
+        empty = [r for h in dies[x] for r in range(h * nb, (h + 1) * nb) if lens[r] <= 0]
+        out.append(full + empty)
+    return out
 
 
 def pin_plan(lib):
@@ -244,6 +249,8 @@ def pin_plan(lib):
     # block (2 + 4 = 6).  Order: head 1, heads 2..7, head 0, head 8; heads
     # 1..7 take dies 0..6, head 0 die 7 (load 10) and head 8 the least-loaded
     # die, die 7.  (By kept blocks alone, head 8 would join head 0 on die 6.)
+    # Die 7 lists the two heads' non-empty rows, 0 and 32, before their empty
+    # rows 1, 2, 3 and 33, 34, 35.
     lens = np.zeros(9 * 4, np.int64)
     lens[0] = 3
     lens[4:7] = 1
@@ -256,12 +263,13 @@ def pin_plan(lib):
     assert list(work[:16]) == [4, 5, 6, 7] + [-1] * 12
     for x in range(1, 7):
         assert list(work[16 * x:16 * (x + 1)]) == [4 * (x + 1) + c for c in range(4)] + [-1] * 12, x
-    assert list(work[112:]) == [0, 1, 2, 3, 32, 33, 34, 35] + [-1] * 8
+    assert list(work[112:]) == [0, 32, 1, 2, 3, 33, 34, 35] + [-1] * 8
     # Head cap slack: 12 heads of kept 30, 1, 1, ..., 1 with 8 dies (weights
     # 2*30 + 4*2 = 68 and 2 + 4 = 6): each die may hold min(12, 2 + 2) = 4
     # heads.  Head 0 -> die 0; heads 1..7 -> dies 1..7; heads 8..11 go to the
     # lightest dies, 1..4, never to die 0.  Within a die, heads in assignment
-    # order.
+    # order, non-empty rows first: die x in 1..4 lists 2x, 2(x+7), then the
+    # empty rows 2x+1, 2(x+7)+1.
     lens = np.zeros(12 * 2, np.int64)
     lens[0], lens[1] = 20, 10
     for h in range(1, 12):
@@ -272,7 +280,7 @@ def pin_plan(lib):
     assert len(work) == 8 * cap and n == 13
     assert list(work[:cap]) == [0, 1] + [-1] * 6
     for x in range(1, 5):
-        assert list(work[x * cap:(x + 1) * cap]) == [2 * x, 2 * x + 1, 2 * (x + 7),
+        assert list(work[x * cap:(x + 1) * cap]) == [2 * x, 2 * (x + 7), 2 * x + 1,
                                                      2 * (x + 7) + 1] + [-1] * 4, x
     for x in range(5, 8):
         assert list(work[x * cap:(x + 1) * cap]) == [2 * x, 2 * x + 1] + [-1] * 6, x

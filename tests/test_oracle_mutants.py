@@ -42,6 +42,10 @@ MUTANTS = [
     ("plan_heads_ascending",
      "if (g_head_weight[a] > g_head_weight[b]) return -1;\n    if (g_head_weight[a] < g_head_weight[b]) return 1;",
      "if (g_head_weight[a] > g_head_weight[b]) return 1;\n    if (g_head_weight[a] < g_head_weight[b]) return -1;", 0),
+    ("plan_empty_rows_reversed", "                    out[pos++] = h * nb + i;",
+     "                    out[pos++] = h * nb + (nb - 1 - i);", 0),
+    ("plan_empty_rows_dropped", "if (row_ptr[h * nb + i + 1] <= row_ptr[h * nb + i])",
+     "if (row_ptr[h * nb + i + 1] < row_ptr[h * nb + i])", 0),
     ("plan_weight_kept_only", "weight[h] = (B / 32) * kept + 4 * rows;", "weight[h] = kept;", 0),
     ("plan_weight_no_row_cost", "weight[h] = (B / 32) * kept + 4 * rows;", "weight[h] = (B / 32) * kept;", 0),
     ("plan_weight_steps_ignore_block", "weight[h] = (B / 32) * kept + 4 * rows;", "weight[h] = 2 * kept + 4 * rows;", 0),
