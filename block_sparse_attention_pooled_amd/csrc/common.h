@@ -70,7 +70,7 @@ inline WsLayout ws_layout(const Dims &D) {
     w.col_stats = take(D.rows() * 8);              // per pooled query: max, 1 / normaliser
     w.col_part = take(D.rows() * D.col_splits() * 8);   // per key split: max, normaliser
     w.col_q16 = take((int64_t)D.H * ((D.nb + 31) / 32) * 32 * D.d * 2);   // bf16 pooled Q
-    w.plan_head_base = take((int64_t)D.H * 4);     // each head's first work position
+    w.plan_head_base = take((int64_t)D.H * 8);     // each head's first non-empty / empty position
     w.work_rec = take(kDies * D.die_cap() * 16);   // int4 record per work position
     // per compaction workgroup: above-cut and at-cut counts of its rows
     w.row_agg = take(2 * ((D.rows() + kCompactRows - 1) / kCompactRows) * 4);

@@ -665,9 +665,11 @@ __global__ __launch_bounds__(1024) void k_col_compact(const float *__restrict__ 
 //  * heads are ranked by weight (descending, ties by head id) and, in that
 //    order, each goes to the die with the least weight so far among those
 //    holding fewer than min(H, ceil(H / kDies) + 2) heads (ties: lowest die);
-//  * die x's list is its heads in assignment order, each head's rows by list
-//    length descending (ties by row id), at work[x*cap ..], cap = (heads a die
-//    may hold) * nb; unused positions hold -1;
+//  * die x's list, at work[x*cap ..], cap = (heads a die may hold) * nb, is
+//    first the non-empty rows of its heads (heads in assignment order, each
+//    head's rows by list length descending, ties by row id), then their empty
+//    rows (same head order, rows ascending): empty rows only write zeros and
+//    run in the launch's ramp-down; unused positions hold -1;
 //  * beside it, work_rec holds one record per position for the attention
 //    launch: row, list begin, list end (clamped into [0, nnz]) and the row's
 //    first two block ids (16 bits each, clamped into [0, nb)), so that a
@@ -676,11 +678,12 @@ __global__ __launch_bounds__(1024) void k_col_compact(const float *__restrict__ 
 // Two launches.  k_plan_assign, one workgroup: the heads' weights straight
 // from row_ptr, their ranks, the die assignment by one wave with one die per
 // lane (the least-loaded open die found by a three-step 8-lane argmin), each
-// head's first position, the padding and the meta words.  k_plan_rows, one
-// wave per head: the head's row records, its rows by list length descending,
-// ties by row id, with a stable counting sort (length histogram, descending
-// bucket starts, ranks among equal lengths from wave ballots), written
-// straight to the head's positions.
+// head's first position among its die's non-empty rows and among its die's
+// empty rows, the padding and the meta words.  k_plan_rows, one wave per
+// head: the head's row records, its rows by list length descending, ties by
+// row id, with a stable counting sort (length histogram, descending bucket
+// starts, ranks among equal lengths from wave ballots), written straight to
+// the head's positions.
 
 // One step of the die argmin: take the (load, die) pair of the lane that
 // dpp_ctrl names when it is smaller.
@@ -707,6 +710,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__r
     __shared__ int64_t weight[kMaxHeads];
     __shared__ int32_t ne[kMaxHeads], kept[kMaxHeads];
     __shared__ int32_t order[kMaxHeads];
+    __shared__ int32_t die_of[kMaxHeads], slot_of[kMaxHeads];
+    __shared__ int32_t die_list[kDies * kMaxHeads];   // die x's heads in slot order
     __shared__ int32_t die_heads[kDies];
     __shared__ int32_t nonempty;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -764,7 +769,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__r
                 argmin_step<0x141>(load, die);   // row_half_mirror: lane i <-> 7 - i
                 const int best = __builtin_amdgcn_readlane(die, 0);
                 if (lane == best) {
-                    head_base[h] = best * cap + my_count * nb;
+                    die_of[h] = best;
+                    slot_of[h] = my_count;
+                    die_list[best * cap_h + my_count] = h;
                     ++my_count;
                     my_load += wh;
                 }
@@ -773,6 +780,22 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__r
         if (lane < kDies) die_heads[lane] = my_count;
     }
     __syncthreads();
+    // Each head's two bases: its die's non-empty rows come first (heads in
+    // slot order), then the die's empty rows (same order).
+    for (int h = tid; h < H; h += kPlanThreads) {
+        const int x = die_of[h], sl = slot_of[h];
+        int ne_before = 0, ne_die = 0, em_before = 0;
+        for (int c = 0; c < die_heads[x]; ++c) {
+            const int n_o = ne[die_list[x * cap_h + c]];
+            ne_die += n_o;
+            if (c < sl) {
+                ne_before += n_o;
+                em_before += nb - n_o;
+            }
+        }
+        head_base[2 * h] = x * cap + ne_before;
+        head_base[2 * h + 1] = x * cap + ne_die + em_before;
+    }
     // Padding: the positions past each die's heads.
     for (int q = tid; q < kDies * cap; q += kPlanThreads) {
         const int x = q / cap;
@@ -800,7 +823,7 @@ __global__ __launch_bounds__(64) void k_plan_rows(const int32_t *__restrict__ ro
     const int lane = threadIdx.x, h = blockIdx.x;
     const uint64_t lt = lanemask_lt();
     const int64_t r0 = (int64_t)h * nb;
-    const int64_t base = head_base[h];
+    const int64_t ne_base = head_base[2 * h], em_base = head_base[2 * h + 1];
     // Stage row_ptr[r0 .. r0 + nb] (loads issued together), then the lengths.
     // A wave's LDS requests complete in order.
     for (int c = 0; c <= nb; c += 512) {
@@ -835,10 +858,13 @@ __global__ __launch_bounds__(64) void k_plan_rows(const int32_t *__restrict__ ro
             rec[i] = make_int4((int)r0 + i, lo[t], hi[t], a | (b << 16));
         }
     }
+    int my_ne = 0;
     for (int i = lane; i < nb; i += 64) {
         const int64_t len = (int64_t)nx[i + 1] - nx[i];
         ln[i] = (int16_t)min(max(len, (int64_t)0), (int64_t)nb);
+        my_ne += len > 0;
     }
+    const int ne_cnt = wave_sum(my_ne);   // the sorted order puts these first
     for (int l = lane; l <= nb; l += 64) nx[l] = 0;
     for (int i = lane; i < nb; i += 64) atomicAdd(&nx[ln[i]], 1);
     // Bucket starts, longest lists first: nx[l] = rows with length > l.
@@ -869,8 +895,9 @@ __global__ __launch_bounds__(64) void k_plan_rows(const int32_t *__restrict__ ro
         const int rank = __popcll(same & lt);
         const int pos = valid ? nx[len] + rank : 0;
         if (valid && pos < nb) {
-            work[base + pos] = (int32_t)(r0 + i);
-            work_rec[base + pos] = rec[i];
+            const int64_t at = pos < ne_cnt ? ne_base + pos : em_base + (pos - ne_cnt);
+            work[at] = (int32_t)(r0 + i);
+            work_rec[at] = rec[i];
         }
         if (valid && rank == 0) nx[len] += __popcll(same);
     }
