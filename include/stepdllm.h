@@ -179,12 +179,14 @@ int stepdllm_select_mask_per_head(const stepdllm_dims *dims, double sparsity,
  * keep a block (its 32-key steps plus a fixed start-up and write-out per row);
  * heads are ranked by weight (descending, ties by id) and each goes to the
  * least-loaded die that holds fewer than min(H, ceil(H/8) + 2) heads (ties:
- * lowest die); a die's list is its heads in that
- * order, each head's rows by list length descending (ties by row id), at
- * positions [x*cap, x*cap + cap) of the work order.  Workgroup b of the
- * sparse launch takes position b / 8 of die b % 8's list, so each die starts
- * its longest rows first and the hardware hands the next row to whichever
- * workgroup slot frees first.  Beside the order, each position gets a record
+ * lowest die); a die's list is first the rows of its heads that keep a
+ * block (heads in that order, each head's rows by list length descending,
+ * ties by row id), then the rows that keep none (same head order, rows
+ * ascending), at positions [x*cap, x*cap + cap) of the work order.  Workgroup
+ * b of the sparse launch takes position b / 8 of die b % 8's list, so each die
+ * starts its longest rows first, the hardware hands the next row to whichever
+ * workgroup slot frees first, and the zero rows fill the slots that free up
+ * at the end.  Beside the order, each position gets a record
  * (work_rec in the layout) of the row's list bounds and first two block ids,
  * so the plan describes this mask's contents, not only its row lengths: plan
  * again after any change to row_ptr or col_idx.  Memory safety on malformed
