@@ -61,6 +61,9 @@ def parse_args():
     p.add_argument("--gqa-group", action="store_true",
                    help="GQA variant with group-shared K/V tiles against the per-head kernel, "
                         "at the workload's anchor for each of its sparsities")
+    p.add_argument("--cpu-all", action="store_true",
+                   help="time the CPU oracle on every configuration (host only, no GPU): one "
+                        "mask build, one sparse and one dense step, row-sampled past a budget")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (for counter calibration)")
     return p.parse_args()
@@ -320,6 +323,73 @@ def temperature_trend(w, per_head, args):
             "kept_vs_temperature_rank_corr": round(rho, 4) if rho is not None else None}
 
 
+CPU_ALL_WORKLOADS = ("tiny", "llada_2k", "stepdllm_8k", "dream_gqa_8k", "long_64k")
+
+
+def cpu_all(args, names=CPU_ALL_WORKLOADS):
+    """The oracle as it stands on the host cores, per configuration: one full
+    mask build on the step-0 Q/K, then sparse and dense attention over seeded
+    random rows until a time budget each, extrapolated to a whole step by kept
+    pairs (sparse) or rows (dense) when the budget ends first."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import oracle as O
+    from block_sparse_attention_pooled_amd.inputs import WORKLOADS, Trajectory, to_host_f32
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    budget = args.cpu_budget_s
+    out = []
+
+    def timed_rows(fn, order, weight, total_weight):
+        done, acc, t0 = 0, 0, time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            while done < order.size and time.perf_counter() - t0 < budget:
+                chunk = order[done:done + 2 * threads]
+                list(ex.map(fn, chunk))
+                done += chunk.size
+                acc += int(weight[chunk].sum())
+        t = time.perf_counter() - t0
+        full = done == order.size
+        return (t if full else t * total_weight / max(acc, 1)), full, done
+
+    for name in names:
+        w = WORKLOADS[name]
+        s = w.sparsities[-1]
+        q, k, v = (to_host_f32(x) for x in Trajectory(w).next())
+        t0 = time.perf_counter()
+        ref = O.build_mask(q, k, w.B, s)
+        t_mask = time.perf_counter() - t0
+        rp, ci, K = ref["row_ptr"], ref["col_idx"], ref["K"]
+        lens = np.diff(rp)
+        rng = np.random.default_rng(w.seed)
+        nonempty = rng.permutation(np.nonzero(lens)[0])
+        buf = np.zeros(q.shape, np.float64)
+        t_sp, sp_full, sp_rows = timed_rows(
+            lambda r: O.sparse_attn(q, k, v, w.B, rp, ci, rows=[int(r)], out=buf),
+            nonempty, lens, K)
+        rows = w.H * w.nb
+        t_de, de_full, de_rows = timed_rows(
+            lambda r: O.dense_attn(q, k, v, w.B, rows=[int(r)], out=buf),
+            rng.permutation(rows), np.ones(rows, np.int64), rows)
+        sp_flops = 4.0 * w.B ** 2 * w.d * K
+        de_flops = 4.0 * w.H * w.L * w.L * w.d
+        out.append({"workload": name, "H": w.H, "Hkv": w.Hkv, "L": w.L, "d": w.d, "B": w.B,
+                    "sparsity": s, "mask_build_s": round(t_mask, 3),
+                    "sparse_step_s": round(t_sp, 3), "sparse_step": (
+                        "full" if sp_full else f"extrapolated from {sp_rows} rows"),
+                    "sparse_tflops": round(sp_flops / t_sp / 1e12, 5),
+                    "dense_step_s": round(t_de, 3), "dense_step": (
+                        "full" if de_full else f"extrapolated from {de_rows} rows"),
+                    "dense_tflops": round(de_flops / t_de / 1e12, 5)})
+        print(f"cpu-all: {name} done", file=sys.stderr, flush=True)
+        del q, k, v, buf, ref
+    print(json.dumps({"metric": "CPU oracle time per configuration (fp64, host cores)",
+                      "unit": "s", "higher_is_better": False, "kind": "oracle",
+                      "cores": threads, "budget_s_per_part": budget, "results": out}),
+          flush=True)
+
+
 def gqa_group(args, w, dev):
     """Per-head sparse kernel against the group-shared variant on the anchor
     step's mask: kernel times, bit identity, K/V tiles streamed per kept pair."""
@@ -381,6 +451,10 @@ def main():
               "multi-GPU run would shard the layer by query head, one all-reduce of the "
               "select histogram per digit pass)", file=sys.stderr)
         sys.exit(2)
+
+    if args.cpu_all:
+        cpu_all(args)
+        return
 
     import torch
     from block_sparse_attention_pooled_amd import binding as B

@@ -53,3 +53,13 @@ def test_cpu_baseline_on_the_tiny_workload():
     r = bench.cpu_baseline(inputs0, w, w.sparsities[0], flops, budget_s=5.0)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
     assert r["value"] > 0 and r["cores"] >= 1
+
+
+def test_cpu_all_on_the_tiny_workload(capsys):
+    bench.cpu_all(types.SimpleNamespace(cpu_budget_s=5.0), names=("tiny",))
+    line = [x for x in capsys.readouterr().out.splitlines() if x.startswith("{")][-1]
+    r = json.loads(line)
+    assert r["kind"] == "oracle" and len(r["results"]) == 1
+    t = r["results"][0]
+    assert t["workload"] == "tiny" and t["sparse_step"] == "full" and t["dense_step"] == "full"
+    assert t["mask_build_s"] >= 0 and t["sparse_tflops"] > 0 and t["dense_tflops"] > 0
