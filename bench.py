@@ -538,6 +538,22 @@ def main():
     ph_mean = sum(per_head) / len(per_head)
     ph_cv = (sum((x - ph_mean) ** 2 for x in per_head) / len(per_head)) ** 0.5 / ph_mean
     value = flops_step / (ms_per_step * 1e-3) / 1e12
+    # Whole-step roofline: each timed step at its bound (kept flops at the bf16
+    # peak or its Q/K/V/O bytes at HBM speed, whichever is longer; a dense step
+    # likewise), plus each anchor's mask build at HBM speed (Q and K read once,
+    # pooled means written, about four passes over the score matrix). Block
+    # masks only: a column step moves the kept K/V rows and its anchor scores
+    # every key, which this byte count does not describe.
+    attn_bytes = (2 * w.H + 2 * w.Hkv) * w.L * w.d * 2
+    mask_bytes = ((w.H + w.Hkv) * w.L * w.d * 2 + (w.H + w.Hkv) * w.nb * w.d * 4
+                  + 4 * w.H * w.nb * w.nb * 4)
+    ideal_s = 0.0
+    for kd in kinds:
+        f = 4.0 * w.H * w.L * w.L * w.d if kd == 0 else flops_step
+        ideal_s += max(f / (PEAK_BF16_TFLOPS * 1e12), attn_bytes / (PEAK_HBM_GBS * 1e9))
+        if kd == 1:
+            ideal_s += mask_bytes / (PEAK_HBM_GBS * 1e9)
+    ideal_ms_step = ideal_s * 1e3 / K_steps
 
     # Same-GPU dense baseline on the step-0 inputs.
     q0, k0, v0 = inputs[0]
@@ -629,6 +645,9 @@ def main():
         "dense_kernel_frac": round(dense_flops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "speedup_vs_dense_kernel": round(dense_ms / attn_ms, 3) if attn_ms else None,
         "speedup_vs_dense_per_step": round(dense_ms / ms_per_step, 3),
+        "step_roofline": (None if args.columns else
+                          {"ideal_ms_per_step": round(ideal_ms_step, 5),
+                           "frac": round(ideal_ms_step / ms_per_step, 4)}),
     }
     if not args.no_cpu_baseline and args.columns:
         result["cpu_baseline"] = cpu_baseline_cols(inputs[0], w, sparsity, flops_step,
