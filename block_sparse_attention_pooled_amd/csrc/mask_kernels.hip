@@ -154,8 +154,13 @@ __global__ __launch_bounds__(kScoreThreads) void k_scores(const float *__restric
     // The global select that follows reads a fresh state: block 0 sets it.
     if (init_sel && blockIdx.x == 0) select_init(init_hist, init_sel, init_K, tid, kScoreThreads);
     const int tiles = (nb + kScoreRows - 1) / kScoreRows;
-    const int h = blockIdx.x / tiles;
-    const int i0 = (blockIdx.x % tiles) * kScoreRows;
+    // Workgroups go round-robin to the 8 dies, each with its own L2: renumber
+    // so that consecutive tiles (one head's rows, sharing its key means) run
+    // on one die, and each die fetches a head's key means once.
+    int bid = blockIdx.x;
+    if (gridDim.x % 8 == 0) bid = (bid % 8) * (gridDim.x / 8) + bid / 8;
+    const int h = bid / tiles;
+    const int i0 = (bid % tiles) * kScoreRows;
     const int g = h / G;
     constexpr int Q4 = (kScoreRows * D / 4 + kScoreThreads - 1) / kScoreThreads;
     constexpr int K4 = kScoreCols * D / 4 / kScoreThreads;
