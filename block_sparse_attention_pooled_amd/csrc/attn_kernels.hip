@@ -82,6 +82,28 @@ constexpr int kModeCols = 2;        // the head's kept key columns (col_idx = [H
 constexpr int kModeGroup = 3;       // two heads of one KV group over the union of their lists
 constexpr int kGroupHeads = 2;      // query heads per workgroup in group mode
 
+// Issue order of one full pipeline step (d = 128: 16 MFMAs, 24 LDS reads, 8
+// buffer->LDS loads, about 60 VALU): while the score chain runs, each MFMA is
+// followed by two fragment reads, five softmax VALU ops and one ring load;
+// while the O product runs, by one read and three VALU ops.  Against the
+// compiler's own order, 1.0-1.5% faster on 8K sparse launches and 1.4% dense,
+// same instructions and results.
+__device__ __forceinline__ void step_issue_order() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // vector memory read
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+}
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
 }
@@ -133,6 +155,8 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
     constexpr int LOADS = kChunk / ROWS_PER_LOAD;   // wave loads per tile
     constexpr bool SPARSE = MODE == kModeSparse;
     constexpr bool COLS = MODE == kModeCols;
+    // The fixed issue order is tuned for (and applied to) these instances.
+    constexpr bool ORDERED = D == 128 && BLK == 64 && (SPARSE || MODE == kModeDense);
     // A three-stage K ring and a two-stage V ring, shared by the NW waves of
     // the workgroup.
     __shared__ __attribute__((aligned(16))) uint16_t rings[5 * TILE];
@@ -447,7 +471,9 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
     // checks its 16 keys of the column (the other 16 are in lane ^ 32) against
     // the running max; the max only moves here, from the max over all 32 keys,
     // so both halves of a column always hold the same value.
-    auto update_max = [&](const f32x16 (&sacc)[NT]) {
+    // in_step: called at the end of a pipeline step (its straight-line code
+    // ends at the rescale branch, where the step's issue order is set).
+    auto update_max = [&](const f32x16 (&sacc)[NT], bool in_step) {
         float mx[NT];
         bool raise = false;
 #pragma unroll
@@ -461,6 +487,7 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
             mx[nt] = m * scale_log2;
             raise = raise || (mx[nt] > m_run[nt] + 8.0f);
         }
+        if (ORDERED && in_step) step_issue_order();
         if (__any(raise)) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -567,7 +594,7 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
             if (has3) issue_k(key3, kdst);
         }
         if (m0) pv(vf, pf);
-        if (has1 && m1) update_max(s_next);
+        if (has1 && m1) update_max(s_next, true);
     };
     auto step = [&](int n, bool full, f32x16 (&s_cur)[NT], f32x16 (&s_next)[NT]) {
         const bool has1 = full || n + 1 < n_total;
@@ -610,7 +637,7 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
     if (p0) scores(kf, sA);
     if (COLS && n_total == 1 && tail < kChunk) mask_tail(sA);
     if (p1) read_k(kring + TILE, kf);
-    if (p0) update_max(sA);
+    if (p0) update_max(sA, false);
 
     int n = 0;
     for (; n + 4 < n_total; n += 2) {
