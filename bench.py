@@ -36,6 +36,20 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_stepdllm_8k_traffic.j
 TRAFFIC_FILE_COLS = os.path.join(ROOT, "profiles", "col_attn_stepdllm_8k_traffic.json")
 
 
+
+def physical_cores():
+    """Distinct (socket, core) pairs among the CPUs this process may run on,
+    from sysfs; None where the topology files are missing."""
+    pairs = set()
+    for c in os.sched_getaffinity(0):
+        base = f"/sys/devices/system/cpu/cpu{c}/topology/"
+        try:
+            with open(base + "physical_package_id") as f1, open(base + "core_id") as f2:
+                pairs.add((f1.read().strip(), f2.read().strip()))
+        except OSError:
+            return None
+    return len(pairs) or None
+
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -137,7 +151,7 @@ def cpu_baseline(inputs0, w, sparsity, flops_per_step, budget_s, per_head=False)
     return {
         "value": round(flops_per_step / t_step / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": threads, "physical_cores_available": physical_cores(),
         "kind": "oracle",
         "sample": (f"one full mask build on the step-0 Q/K ({t_mask:.2f} s, amortised over "
                    f"{period} steps) + fp64 sparse attention on {done_rows} of {nonempty.size} "
@@ -180,7 +194,7 @@ def cpu_baseline_cols(inputs0, w, sparsity, flops_per_step, budget_s):
     return {
         "value": round(flops_per_step / t_step / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": threads, "physical_cores_available": physical_cores(),
         "kind": "oracle",
         "sample": (f"one full column mask build on the step-0 Q/K ({t_mask:.2f} s, amortised "
                    f"over {period} steps) + fp64 column attention on {done} of {rows_all} "
@@ -386,7 +400,7 @@ def cpu_all(args, names=CPU_ALL_WORKLOADS):
         del q, k, v, buf, ref
     print(json.dumps({"metric": "CPU oracle time per configuration (fp64, host cores)",
                       "unit": "s", "higher_is_better": False, "kind": "oracle",
-                      "cores": threads, "budget_s_per_part": budget, "results": out}),
+                      "cores": threads, "physical_cores_available": physical_cores(), "budget_s_per_part": budget, "results": out}),
           flush=True)
 
 
