@@ -86,8 +86,9 @@ constexpr int kGroupHeads = 2;      // query heads per workgroup in group mode
 // buffer->LDS loads, about 60 VALU): while the score chain runs, each MFMA is
 // followed by two fragment reads, five softmax VALU ops and one ring load;
 // while the O product runs, by one read and three VALU ops.  Against the
-// compiler's own order, 1.0-1.5% faster on 8K sparse launches and 1.4% dense,
-// same instructions and results.
+// compiler's own order, 0.3-1.7% faster on 8K launches (64-token blocks) and
+// 1.2-1.9% at 64K (128-token blocks), sparse and dense, same results.  (The
+// column instance is slower with it: it stays with the compiler's order.)
 __device__ __forceinline__ void step_issue_order() {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
     constexpr bool SPARSE = MODE == kModeSparse;
     constexpr bool COLS = MODE == kModeCols;
     // The fixed issue order is tuned for (and applied to) these instances.
-    constexpr bool ORDERED = D == 128 && BLK == 64 && (SPARSE || MODE == kModeDense);
+    constexpr bool ORDERED = D == 128 && (SPARSE || MODE == kModeDense);
     // A three-stage K ring and a two-stage V ring, shared by the NW waves of
     // the workgroup.
     __shared__ __attribute__((aligned(16))) uint16_t rings[5 * TILE];
