@@ -95,22 +95,27 @@ def test_llada_2k():
 
 @pytest.mark.timeout(900)
 def test_stepdllm_8k_anchors_and_resample():
+    """The whole 256-step trajectory: the mask at all 8 anchors (the Q/K
+    redraws at 64 and 160 included), outputs at the first step, the last
+    step before the first refresh, both redraws and the last step."""
     w = WORKLOADS["stepdllm_8k"]
-    _run(w, w.sparsities[0], 64, mask_steps={0, 32, 64}, out_steps={0, 31, 64}, heads=(0, 17))
+    _run(w, w.sparsities[0], 255, mask_steps=set(range(0, 256, 32)),
+         out_steps={0, 31, 64, 160, 255}, heads=(0, 17))
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("sparsity", WORKLOADS["dream_gqa_8k"].sparsities)
 def test_dream_gqa_8k(sparsity):
+    """64 steps per sparsity: the mask at its 4 anchors, outputs at the first
+    and last steps."""
     w = WORKLOADS["dream_gqa_8k"]
-    last = 16 if sparsity == 0.9 else 0
-    _run(w, sparsity, last, mask_steps={0, 16}, out_steps={0, last}, heads=(0, 6, 7))
+    _run(w, sparsity, 63, mask_steps={0, 16, 32, 48}, out_steps={0, 63}, heads=(0, 6, 7))
 
 
 @pytest.mark.timeout(900)
 def test_long_64k_dense_then_sparse():
     w = WORKLOADS["long_64k"]
-    _run(w, w.sparsities[0], 27, mask_steps={26}, out_steps={0, 26, 27}, heads=())
+    _run(w, w.sparsities[0], 127, mask_steps={26}, out_steps={0, 26, 27, 127}, heads=())
 
 
 @pytest.mark.timeout(900)
