@@ -53,6 +53,8 @@ def test_cpu_baseline_on_the_tiny_workload():
     r = bench.cpu_baseline(inputs0, w, w.sparsities[0], flops, budget_s=5.0)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
     assert r["value"] > 0 and r["cores"] >= 1
+    phys = r["physical_cores_available"]
+    assert phys is None or 1 <= phys <= len(os.sched_getaffinity(0))
 
 
 def test_cpu_all_on_the_tiny_workload(capsys):
