@@ -9,6 +9,7 @@ pin against deliberately broken copies of the oracle to show that the pins
 can fail.
 """
 import math
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -24,6 +25,23 @@ def _bf16_round(x):
     u = x.view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
     return u.astype(np.uint32).view(np.float32)
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden_lists(name):
+    """A hand-derived fixture under tests/golden/: '# ...' lines are its
+    citation and derivation, every other line is 'key: id id ...'."""
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, ids = line.partition(":")
+            out[int(key)] = [int(x) for x in ids.split()]
+    return out
 
 
 def _rand(shape, rng, scale=1.0):
@@ -417,6 +435,10 @@ def pin_worked_w1(lib):
     for r in range(8):
         keep.reshape(8, 4)[r, m["col_idx"][m["row_ptr"][r]:m["row_ptr"][r + 1]]] = 1
     assert np.array_equal(keep, keep_want)
+    want = golden_lists("w1_global_mask.txt")
+    assert sorted(want) == list(range(8))
+    for r, cols in want.items():
+        assert list(m["col_idx"][m["row_ptr"][r]:m["row_ptr"][r + 1]]) == cols, r
     o = O.sparse_attn(q, k, v, B, m["row_ptr"], m["col_idx"], lib=lib)
     for i in range(4):
         want = v[0, i * B:(i + 1) * B].astype(np.float64).mean(axis=0)
@@ -435,8 +457,8 @@ def pin_worked_w1_per_head(lib):
     B = 64
     m = O.build_mask(q, k, B, 0.5, lib, per_head=True)
     assert m["K"] == 16
-    want = {0: [0, 1, 2, 3], 1: [0, 1], 2: [2], 3: [3], 4: [0, 1, 2, 3], 5: [0, 1, 2, 3],
-            6: [], 7: []}
+    want = golden_lists("w1_per_head_mask.txt")
+    assert sorted(want) == list(range(8))
     rp, ci = m["row_ptr"], m["col_idx"]
     for r, cols in want.items():
         assert list(ci[rp[r]:rp[r + 1]]) == cols, (r, list(ci[rp[r]:rp[r + 1]]))
@@ -644,7 +666,8 @@ def pin_col_select(lib):
             assert np.array_equal(got[h], np.sort(order[:k_c])), (k_c, h)
     # W3: k_c = 2 keeps keys 5 and 70; k_c = 3 adds the lowest-index tie, 0.
     q, k, _ = worked_example_w3()
-    for s, want in ((1 - 2 / 128, [5, 70]), (1 - 3 / 128, [0, 5, 70]), (0.0, list(range(128)))):
+    gold = golden_lists("w3_columns.txt")
+    for s, want in ((1 - 2 / 128, gold[2]), (1 - 3 / 128, gold[3]), (0.0, list(range(128)))):
         c, cols, k_c = O.build_col_mask(q, k, 64, s, lib)
         assert k_c == len(want) and list(cols[0]) == want, (s, list(cols[0]))
 
