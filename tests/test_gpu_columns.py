@@ -148,6 +148,31 @@ def _random_cols(H, L, k_c, rng, shuffle=False):
     return np.ascontiguousarray(cols, dtype=np.int32)
 
 
+@pytest.mark.timeout(600)
+def test_column_variant_at_the_largest_block_count():
+    """L = 65536 in 64-token blocks (nb = 1024, the most the library takes),
+    with GQA: the column masses, the kept columns (the oracle's except within
+    rounding of a cut) and column attention on sampled rows, against the
+    oracle (its fp32 masses, which hold the fp64 definition to ~1e-6)."""
+    H, Hkv, L, d, blk, s = 2, 1, 65536, 128, 64, 0.9
+    q, k, v = random_qkv(H, Hkv, L, d, 919, device=DEV, q_scale=2.0, sinks=True)
+    qf, kf, vf = PT.oracle_inputs(q, k, v)
+    m = GpuCols(q, k, blk, s)
+    c_ref, cols_ref, k_c = O.build_col_mask(qf, kf, blk, s)
+    assert m.k_c == k_c == 6554
+    _check_mass(m.scores(), c_ref.astype(np.float64))
+    cols = m.cols()
+    _check_cols_form(cols, k_c, L)
+    assert np.array_equal(cols, O.col_select(m.scores(), k_c))
+    assert len(_compare_cols(cols, cols_ref, c_ref, k_c)) <= 2
+    o = torch.empty_like(q)
+    B.col_attn(m.dims, q, k, v, m.cols_t(), o)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(9).choice(H * (L // blk), 48, replace=False))
+    want = O.col_attn(qf, kf, vf, blk, cols, rows=rows.astype(np.int32))
+    PT.check_outputs(o, want, PT.token_mask_for_rows(rows, H, L // blk, blk))
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=SHAPE_IDS)
 def test_column_attention_matches_oracle(shape):
     """Ragged column counts (one partial chunk, exact chunks, under one chunk),

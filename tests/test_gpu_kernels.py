@@ -200,6 +200,38 @@ def test_sparsity_zero_equals_dense(shape):
     assert torch.equal(o_s, o_d)
 
 
+@pytest.mark.timeout(600)
+def test_largest_block_count():
+    """nb = 1024, the most the library takes (L = 65536 in 64-token blocks),
+    with GQA: the mask build (each score workgroup holds 16 rows of 1024
+    scores in LDS), the plan records and the sparse attention on sampled rows
+    against the oracle."""
+    H, Hkv, L, d, blk, s = 2, 1, 65536, 128, 64, 0.9
+    q, k, v = random_qkv(H, Hkv, L, d, 909, device=DEV, q_scale=2.0, sinks=True)
+    qf, kf, vf = PT.oracle_inputs(q, k, v)
+    ref = O.build_mask(qf, kf, blk, s)
+    m = PT.GpuMask(q, k, blk, s)
+    assert m.nb == 1024 and m.K == ref["K"]
+    rp, ci = m.csr()
+    PT.check_csr_form(rp, ci, m.K, m.nb)
+    keep = m.keep()
+    PT.compare_masks(keep, PT.keep_from_csr(ref["row_ptr"], ref["col_idx"], H, m.nb),
+                     ref["P"], m.K)
+    assert np.array_equal(O.select(m.P(), m.K), keep)
+    lay = B.workspace_layout(m.dims)
+    work_ref, _ = O.plan(rp, H, m.nb, blk)
+    work = m.buf.ws[lay.work:lay.work + 4 * work_ref.size].view(torch.int32).cpu().numpy()
+    assert np.array_equal(work, work_ref)
+    o = torch.full_like(q, float("nan"))
+    B.sparse_attn(m.dims, q, k, v, m.buf.col_idx, m.buf.ws, o, nnz=m.K)
+    torch.cuda.synchronize()
+    rows = PT.sample_rows(rp, H, m.nb, heads=(), seed=9)
+    out = np.zeros(qf.shape, np.float64)
+    PT.oracle_rows_parallel(O.sparse_attn, rows, q=qf, k=kf, v=vf, B=blk, row_ptr=rp,
+                            col_idx=ci, out=out)
+    PT.check_outputs(o, out, PT.token_mask_for_rows(rows, H, m.nb, blk))
+
+
 def test_zero_budget_keeps_nothing():
     """s just below 1 leaves K = 0 (the guard of R13 takes x below zero): no
     digit pass runs, every row is empty, the plan's records have empty lists
