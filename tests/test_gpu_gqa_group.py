@@ -47,6 +47,24 @@ def test_group_equals_per_head_on_built_masks(shape, s):
     assert torch.equal(o, o_ref)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("s", [0.5, 0.9])
+def test_group_equals_per_head_at_the_largest_block_count(s):
+    """nb = 1024 (L = 65536), the most the library takes: at s = 0.5 a head
+    pair's union of lists fills most of the 1024 entries the workgroup holds
+    in LDS; the output equals the per-head kernel's bit for bit."""
+    H, Hkv, L, d = 4, 2, 65536, 128
+    q, k, v = random_qkv(H, Hkv, L, d, 1313, device=DEV, q_scale=2.0)
+    dims = B.dims_of(q, k, 64)
+    m = PT.GpuMask(q, k, 64, s, scores_copy=False)
+    rp = m.buf.row_ptr.cpu().numpy()
+    assert m.nb == 1024 and int(np.diff(rp).max()) > 64
+    o_ref = _per_head(dims, q, k, v, m.buf.row_ptr, m.buf.col_idx, m.K)
+    o = _group(dims, q, k, v, m.buf.row_ptr, m.buf.col_idx, m.K)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+
+
 def test_group_matches_oracle():
     H, Hkv, L, d = 14, 2, 37 * 64, 128
     q, k, v = random_qkv(H, Hkv, L, d, 1313, device=DEV, q_scale=2.0, sinks=True)
