@@ -518,10 +518,12 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(K_steps)]
     kinds = [drv.step_kind((args.warmup + i) % T) for i in range(K_steps)]
-    # HIP events on the launch stream bracket every anchor / dense step and
-    # every 8th reuse step: a pair of timing events between two kernels costs
-    # the stream about 6 us, which would otherwise be counted in every step.
-    timed = [kd != 2 or i % 8 == 0 for i, kd in enumerate(kinds)]
+    # HIP events on the launch stream: every anchor / dense step is bracketed
+    # on its own, and each run of consecutive reuse steps (one sparse launch
+    # each) as a whole, so the cost of a pair of events (about 6 us of stream
+    # time) is spread over the run instead of counted in a single launch.
+    opens = [kd != 2 or i == 0 or kinds[i - 1] != 2 for i, kd in enumerate(kinds)]
+    closes = [kd != 2 or i == K_steps - 1 or kinds[i + 1] != 2 for i, kd in enumerate(kinds)]
     # --runs R > 1 repeats the timed region R times (the same K steps) and
     # takes the median run's wall time; the events are those of the last run.
     walls = []
@@ -529,23 +531,32 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K_steps):
-            if timed[i]:
+            if opens[i]:
                 ev[i][0].record(stream)
             run_step(args.warmup + i)
-            if timed[i]:
+            if closes[i]:
                 ev[i][1].record(stream)
         torch.cuda.synchronize()
         walls.append(time.perf_counter() - t0)
     wall = sorted(walls)[len(walls) // 2]
-    step_ms = [a.elapsed_time(b) if tm else None for (a, b), tm in zip(ev, timed)]
     ms_per_step = wall * 1e3 / K_steps
+    spans = []                      # (kind, first step, last step, ms)
+    i = 0
+    while i < K_steps:
+        j = i
+        while not closes[j]:
+            j += 1
+        spans.append((kinds[i], i, j, ev[i][0].elapsed_time(ev[j][1])))
+        i = j + 1
 
     def mean(xs):
         return sum(xs) / len(xs) if xs else None
 
-    attn_ms = mean([m for m, kd in zip(step_ms, kinds) if kd == 2 and m is not None])
-    anchor_ms = mean([m for m, kd in zip(step_ms, kinds) if kd == 1])
-    dense_step_ms = mean([m for m, kd in zip(step_ms, kinds) if kd == 0])
+    reuse = [(j - i + 1, ms) for kd, i, j, ms in spans if kd == 2]
+    n_reuse_timed = sum(n for n, _ in reuse)
+    attn_ms = sum(ms for _, ms in reuse) / n_reuse_timed if n_reuse_timed else None
+    anchor_ms = mean([ms for kd, _, _, ms in spans if kd == 1])
+    dense_step_ms = mean([ms for kd, _, _, ms in spans if kd == 0])
     n_anchor = sum(1 for kd in kinds if kd == 1)
 
     Kkept = drv.K
@@ -616,7 +627,7 @@ def main():
         "traffic": trec["hbm_bytes_per_launch"] if trec else None,
         "algorithmic_flops_per_launch": flops_step,
         "kernel_ms": round(attn_ms, 5) if attn_ms else None,
-        "kernel_launches_timed": sum(1 for kd, tm in zip(kinds, timed) if kd == 2 and tm),
+        "kernel_launches_timed": n_reuse_timed,
     }
     # What the chip sustains under pure MFMA load (power-limited clock with
     # real-valued operands), measured after the timed region.
