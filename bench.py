@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import struct
 import sys
 import time
 
@@ -49,6 +50,18 @@ def physical_cores():
         except OSError:
             return None
     return len(pairs) or None
+
+def window_start(kind_at, warmup, T):
+    """First step index t >= warmup at which the timed window opens: the
+    trajectory's first step (t % T == 0) when the schedule starts with dense
+    steps, else an anchor step.  kind_at(t) is the driver's step kind
+    (0 dense, 1 anchor, 2 reuse)."""
+    first = kind_at(0)
+    for t in range(warmup, warmup + T):
+        if (first == 0 and t % T == 0) or (first == 1 and kind_at(t) == 1):
+            return t
+    return warmup
+
 
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -85,6 +98,45 @@ def parse_args():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (for counter calibration)")
     return p.parse_args()
+
+
+def mask_build_bandwidth(w, anchor_ms, attn_ms, columns):
+    """Mask build of a block mask against HBM speed: its algorithmic bytes
+    (Q and K read once, pooled means written, four fp32 passes over the
+    H * nb^2 score matrix) over the measured build time (anchor step minus a
+    reuse step)."""
+    if columns or not (anchor_ms and attn_ms) or anchor_ms <= attn_ms:
+        return {}
+    nbytes = ((w.H + w.Hkv) * w.L * w.d * 2 + (w.H + w.Hkv) * w.nb * w.d * 4
+              + 4 * w.H * w.nb * w.nb * 4)
+    gbs = nbytes / ((anchor_ms - attn_ms) * 1e-3) / 1e9
+    return {"mask_build_bytes": nbytes, "mask_build_gbs": round(gbs, 1),
+            "mask_build_frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def near_ties(drv, w, dims, rel=1e-5, show=8):
+    """Scores of the last anchor's pooled map within rel of the cut (the K-th
+    largest), from the GPU's own scores and select state in the workspace:
+    the count and the first few (flat index, score, kept)."""
+    import torch
+    from block_sparse_attention_pooled_amd import binding as B
+    lay = B.workspace_layout(dims)
+    n = w.H * w.nb * w.nb
+    P = drv.ws[lay.scores:lay.scores + 4 * n].view(torch.float32)
+    key = int(drv.ws[lay.select:lay.select + 4].view(torch.int32).item()) & 0xFFFFFFFF
+    bits = key ^ 0x80000000 if key & 0x80000000 else ~key & 0xFFFFFFFF
+    cut = struct.unpack("<f", struct.pack("<I", bits))[0]
+    if not cut > 0:
+        return {"near_ties": {"count": 0, "cut": cut, "listed": []}}
+    idx = torch.nonzero(torch.abs(P - cut) <= rel * cut).view(-1)
+    rp = drv.row_ptr.cpu()
+    ci = drv.col_idx[:drv.K].cpu()
+    listed = []
+    for f in idx[:show].tolist():
+        r, j = divmod(f, w.nb)
+        kept = bool((ci[int(rp[r]):int(rp[r + 1])] == j).any())
+        listed.append([f, float(P[f]), kept])
+    return {"near_ties": {"count": int(idx.numel()), "cut": cut, "rel": rel, "listed": listed}}
 
 
 def src_sha(path):
@@ -514,10 +566,15 @@ def main():
         run_step(t)
     torch.cuda.synchronize()
 
+    # The timed window opens on an anchor: the first trajectory position at or
+    # after the warm-up whose step builds a mask (dense steps first if the
+    # schedule has them, as in the long configuration), so a window of any
+    # length holds the mask builds the schedule makes in it.
+    start = window_start(lambda p: drv.step_kind(p % T), args.warmup, T)
     K_steps = args.steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(K_steps)]
-    kinds = [drv.step_kind((args.warmup + i) % T) for i in range(K_steps)]
+    kinds = [drv.step_kind((start + i) % T) for i in range(K_steps)]
     # HIP events on the launch stream: every anchor / dense step is bracketed
     # on its own, and each run of consecutive reuse steps (one sparse launch
     # each) as a whole, so the cost of a pair of events (about 6 us of stream
@@ -533,7 +590,7 @@ def main():
         for i in range(K_steps):
             if opens[i]:
                 ev[i][0].record(stream)
-            run_step(args.warmup + i)
+            run_step(start + i)
             if closes[i]:
                 ev[i][1].record(stream)
         torch.cuda.synchronize()
@@ -558,6 +615,12 @@ def main():
     anchor_ms = mean([ms for kd, _, _, ms in spans if kd == 1])
     dense_step_ms = mean([ms for kd, _, _, ms in spans if kd == 0])
     n_anchor = sum(1 for kd in kinds if kd == 1)
+    # One refresh interval of the schedule (an anchor then R - 1 reuse steps),
+    # from the measured anchor-step and reuse-step times: the per-step cost
+    # over the whole trajectory, whatever the window length.
+    R = w.refresh_every
+    interval_ms = ((anchor_ms + (R - 1) * attn_ms) / R
+                   if (R > 0 and anchor_ms and attn_ms) else None)
 
     Kkept = drv.K
     if args.columns:
@@ -625,6 +688,7 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
         "traffic": trec["hbm_bytes_per_launch"] if trec else None,
+        "l2_hit_rate": trec.get("l2_hit_rate") if trec else None,
         "algorithmic_flops_per_launch": flops_step,
         "kernel_ms": round(attn_ms, 5) if attn_ms else None,
         "kernel_launches_timed": n_reuse_timed,
@@ -670,9 +734,15 @@ def main():
         **temperature_trend(w, per_head, args),
         "empty_rows": (None if args.columns else
                        int((drv.row_ptr[1:] == drv.row_ptr[:-1]).sum().item())),
+        **({} if args.columns or args.per_head_budget else near_ties(drv, w, dims)),
+        "timed_window": {"first_step": start % T, "anchor_steps": n_anchor,
+                         "dense_steps": sum(1 for kd in kinds if kd == 0),
+                         "reuse_steps": sum(1 for kd in kinds if kd == 2)},
         "anchor_step_ms": round(anchor_ms, 5) if anchor_ms else None,
         "mask_build_ms": round(anchor_ms - attn_ms, 5) if (anchor_ms and attn_ms) else None,
+        **mask_build_bandwidth(w, anchor_ms, attn_ms, args.columns),
         "anchors_timed": n_anchor,
+        "ms_per_step_refresh_interval": round(interval_ms, 5) if interval_ms else None,
         "dense_step_ms": round(dense_step_ms, 5) if dense_step_ms else None,
         "dense_kernel_ms": round(dense_ms, 5),
         "dense_kernel_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 3),

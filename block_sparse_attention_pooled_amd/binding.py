@@ -11,10 +11,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# STEPDLLM_LIB selects another build of the same library (A/B comparisons).
-LIB_PATH = os.environ.get("STEPDLLM_LIB") or os.path.join(_PKG, "libstepdllm.so")
+LIB_PATH = os.path.join(_PKG, "libstepdllm.so")
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ESTATE = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ESTATE, ENOMEM = 0, -1, -2, -3, -4, -5, -6
 
 
 class Dims(ctypes.Structure):
@@ -374,6 +373,13 @@ class MaskBuffers:
 
     def work_meta(self):
         return self.view(self.layout.work_meta, 16, torch.int32)
+
+    def plan_check(self):
+        """The plan check word (work_meta[7]): 0 after a plan; bit 0 set by a
+        sparse launch on another col_idx, nnz or shape than planned, bit 1 by
+        one that found a row's first list entries changed.  Reads device
+        memory (synchronises the device)."""
+        return int(self.work_meta()[7].item())
 
     def work_rec(self):
         """[8 * cap, 4] int32: row, list begin, list end, first two block ids."""

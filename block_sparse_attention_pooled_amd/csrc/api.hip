@@ -7,6 +7,7 @@
 // Models", abstract (dense attention for the early steps, then one sparse
 // pattern reused for every later step).
 #include <math.h>
+#include <stdio.h>
 #include <stdlib.h>
 
 #include "../../include/stepdllm.h"
@@ -44,33 +45,43 @@ int check_dims(const stepdllm_dims *d, Dims *out) {
     return STEPDLLM_OK;
 }
 
-int64_t keep_count(const Dims &D, double s) {
-    const double n = (double)D.n_scores();
-    const double x = (1.0 - s) * n - 1e-9 * n;
-    if (x <= 0.0) return 0;
-    int64_t k = (int64_t)ceil(x);
-    return k > D.n_scores() ? D.n_scores() : k;
+// Budget of kept entries out of n for sparsity s: ceil((1 - s) * n), with s
+// read as the decimal number the caller wrote, i.e. the decimal with the
+// fewest significant digits that converts back to the same double (the
+// nearest of that length).  The ceiling is then exact: with s = m / 10^e,
+// (1 - s) * n = n - m * n / 10^e, so K = n - floor(m * n / 10^e) in 128-bit
+// integers (m < 10^17, n < 2^31).  s = 0 keeps all n, s = 1 keeps none.
+int64_t exact_budget(int64_t n, double s) {
+    if (!(s > 0.0)) return n;
+    if (s >= 1.0) return 0;
+    for (int p = 1; p <= 17; ++p) {
+        char buf[48];
+        snprintf(buf, sizeof buf, "%.*e", p - 1, s);   // d.ddd...e-XX, p digits
+        if (strtod(buf, nullptr) != s) continue;
+        unsigned long long digits = 0;
+        const char *c = buf;
+        for (; *c && *c != 'e'; ++c)
+            if (*c >= '0' && *c <= '9') digits = digits * 10 + (unsigned long long)(*c - '0');
+        const int e = (p - 1) - atoi(c + 1);   // s = digits / 10^e, e >= 1
+        if (e > 36) return n;                  // s * n < 1
+        unsigned __int128 pow10 = 1;
+        for (int i = 0; i < e; ++i) pow10 *= 10;
+        return n - (int64_t)(((unsigned __int128)digits * (unsigned __int128)n) / pow10);
+    }
+    return n;   // not reached: 17 significant digits always read back
 }
+
+int64_t keep_count(const Dims &D, double s) { return exact_budget(D.n_scores(), s); }
 
 // Uniform per-head budget: k_h of each head's nb * nb scores.
 int64_t keep_count_per_head(const Dims &D, double s) {
-    const double n = (double)D.nb * D.nb;
-    const double x = (1.0 - s) * n - 1e-9 * n;
-    if (x <= 0.0) return 0;
-    int64_t k = (int64_t)ceil(x);
-    return k > (int64_t)D.nb * D.nb ? (int64_t)D.nb * D.nb : k;
+    return exact_budget((int64_t)D.nb * D.nb, s);
 }
 
 // Column-sparse variant: k_c of each head's L key columns.
-int64_t keep_count_columns(const Dims &D, double s) {
-    const double n = (double)D.L;
-    const double x = (1.0 - s) * n - 1e-9 * n;
-    if (x <= 0.0) return 0;
-    int64_t k = (int64_t)ceil(x);
-    return k > D.L ? D.L : k;
-}
+int64_t keep_count_columns(const Dims &D, double s) { return exact_budget(D.L, s); }
 
-bool sparsity_ok(double s) { return s >= 0.0 && s < 1.0; }   // false for NaN
+bool sparsity_ok(double s) { return s >= 0.0 && s <= 1.0; }   // false for NaN
 
 int hip_status(hipError_t e) { return e == hipSuccess ? STEPDLLM_OK : STEPDLLM_EHIP; }
 
@@ -257,7 +268,7 @@ int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr, const int32
 
 int stepdllm_sparse_attn(const stepdllm_dims *dims, const uint16_t *q, const uint16_t *k,
                          const uint16_t *v, const int32_t *col_idx, int64_t nnz,
-                         const void *ws, size_t ws_bytes, uint16_t *o, void *stream) {
+                         void *ws, size_t ws_bytes, uint16_t *o, void *stream) {
     Dims D;
     int st = check_dims(dims, &D);
     if (st) return st;
@@ -265,8 +276,10 @@ int stepdllm_sparse_attn(const stepdllm_dims *dims, const uint16_t *q, const uin
     if (nnz < 0 || nnz > D.n_scores()) return STEPDLLM_EINVAL;
     WsLayout w = sd::ws_layout(D);
     if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
-    const int4 *recs = reinterpret_cast<const int4 *>(static_cast<const char *>(ws) + w.work_rec);
-    return hip_status(sd::launch_sparse_attn(D, q, k, v, col_idx, recs, nnz, o,
+    char *base = static_cast<char *>(ws);
+    const int4 *recs = reinterpret_cast<const int4 *>(base + w.work_rec);
+    int32_t *meta = reinterpret_cast<int32_t *>(base + w.work_meta);
+    return hip_status(sd::launch_sparse_attn(D, q, k, v, col_idx, recs, meta, nnz, o,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -366,7 +379,7 @@ int stepdllm_driver_create(stepdllm_driver **out, const stepdllm_dims *dims,
     if (!schedule->column_sparse && !row_ptr) return STEPDLLM_EINVAL;
     if ((int64_t)ws_bytes < sd::ws_layout(D).total) return STEPDLLM_EWORKSPACE;
     stepdllm_driver *drv = static_cast<stepdllm_driver *>(malloc(sizeof(stepdllm_driver)));
-    if (!drv) return STEPDLLM_EINVAL;
+    if (!drv) return STEPDLLM_ENOMEM;
     drv->D = D;
     drv->sched = *schedule;
     drv->ws = static_cast<char *>(ws);
@@ -428,6 +441,7 @@ const char *stepdllm_status_string(int status) {
     case STEPDLLM_EWORKSPACE: return "workspace too small";
     case STEPDLLM_EHIP: return "HIP launch error";
     case STEPDLLM_ESTATE: return "no mask built yet (reuse step before any anchor)";
+    case STEPDLLM_ENOMEM: return "host memory allocation failed";
     default: return "unknown status";
     }
 }

@@ -140,8 +140,8 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ row_ptr,
     const int32_t *__restrict__ col_idx, const int4 *__restrict__ recs,
-    uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx, int64_t cap,
-    float scale_log2) {
+    int32_t *__restrict__ meta, uint16_t *__restrict__ o, int L, int nb, int G, int H, int n_idx,
+    int64_t cap, float scale_log2) {
     constexpr int NT = QW / 32;                 // 32-query tiles per wave
     constexpr int WQ = BLK / QW;                // query slices (waves) per query block
     constexpr bool GROUP = MODE == kModeGroup;
@@ -214,11 +214,22 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
         // the first K/V loads need, so they leave one load after the start.
         const int b = blockIdx.x;
         const int4 rc = recs[(b % kDies) * cap + b / kDies];
+        // The plan's tag: the list array and length it was made from, and
+        // the shape.  A launch on another array, length or shape (a stale
+        // plan) writes zeros and flags bit 0 of the check word.
+        const int4 tag = *reinterpret_cast<const int4 *>(meta + kMetaListLo);
+        const int tag_nb = meta[kMetaNb];
         row = __builtin_amdgcn_readfirstlane(rc.x);
         if (row < 0 || row >= H * nb) return;   // padding (or a malformed order): nothing to do
         rec_begin = __builtin_amdgcn_readfirstlane(rc.y);
         rec_end = __builtin_amdgcn_readfirstlane(rc.z);
         rec_ids = __builtin_amdgcn_readfirstlane(rc.w);
+        const uint64_t list_addr = reinterpret_cast<uint64_t>(col_idx);
+        if (tag.x != (int)(uint32_t)list_addr || tag.y != (int)(uint32_t)(list_addr >> 32) ||
+            tag.z != n_idx || tag.w != H || tag_nb != nb) {
+            if (tid == 0) atomicOr(meta + kMetaCheck, kCheckStalePlan);
+            rec_end = rec_begin;   // no chunk: the row writes zeros
+        }
     }
     const int h = row / nb, blk = row % nb, g = h / G;
     const int q0 = blk * BLK + QW * wq;
@@ -655,6 +666,17 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) l_run[nt] += __shfl_xor(l_run[nt], 32);
 
+    // The row's first two list entries must still be the ones its record
+    // holds (col_idx rewritten after planning): otherwise the row writes
+    // zeros and flags bit 1 of the check word.
+    bool list_changed = false;
+    if (SPARSE) {
+        const int c0 = min(max(col_idx[e_begin], 0), nb - 1);
+        const int c1 = e_end - e_begin > 1 ? min(max(col_idx[e_begin + 1], 0), nb - 1) : 0;
+        list_changed = (c0 | (c1 << 16)) != rec_ids;
+        if (list_changed && tid == 0) atomicOr(meta + kMetaCheck, kCheckListChanged);
+    }
+
     // O = O^T / l, rounded to bf16, staged through LDS so that every store
     // writes whole rows.  Lane holds query col (32*nt + col) and 4 consecutive
     // dims per group of 4 accumulators; the wave's 32 x D tile goes into the
@@ -693,8 +715,8 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
 #pragma unroll
     for (int t = 0; t < QW / RPI; ++t) {
         const int r = t * RPI + lane / SEGS, sg = lane % SEGS;
-        const uint4 val =
-            *reinterpret_cast<const uint4 *>(ot + r * D + 8 * (sg ^ (r & (SEGS - 1))));
+        uint4 val = *reinterpret_cast<const uint4 *>(ot + r * D + 8 * (sg ^ (r & (SEGS - 1))));
+        if (list_changed) val = make_uint4(0, 0, 0, 0);
         store_nt(orow + (int64_t)r * D + 8 * sg, val);
     }
 }
@@ -702,7 +724,7 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
 template <int D, int BLK, int QW, int MODE>
 hipError_t launch_attn_t(const Dims &Dm, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const int32_t *row_ptr, const int32_t *col_idx, const int4 *recs,
-                         int n_idx, uint16_t *o, hipStream_t s) {
+                         int32_t *meta, int n_idx, uint16_t *o, hipStream_t s) {
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int64_t cap = Dm.die_cap();
     const int64_t group_units =
@@ -712,43 +734,45 @@ hipError_t launch_attn_t(const Dims &Dm, const uint16_t *q, const uint16_t *k, c
                                                           : Dm.rows());
     const unsigned threads = BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads : 1);
     hipLaunchKernelGGL((k_attn<D, BLK, QW, MODE>), dim3(grid), dim3(threads), 0, s, q, k, v,
-                       row_ptr, col_idx, recs, o, Dm.L, Dm.nb, Dm.G, Dm.H, n_idx, cap,
+                       row_ptr, col_idx, recs, meta, o, Dm.L, Dm.nb, Dm.G, Dm.H, n_idx, cap,
                        scale_log2);
     return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t launch_attn(const Dims &D, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                       const int32_t *col_idx, const int4 *recs, int n_idx, uint16_t *o,
-                       hipStream_t s) {
+                       const int32_t *col_idx, const int4 *recs, int32_t *meta, int n_idx,
+                       uint16_t *o, hipStream_t s) {
     if (D.d == 128 && D.B == 64)
-        return launch_attn_t<128, 64, kQW, MODE>(D, q, k, v, nullptr, col_idx, recs, n_idx, o,
-                                                 s);
+        return launch_attn_t<128, 64, kQW, MODE>(D, q, k, v, nullptr, col_idx, recs, meta, n_idx,
+                                                 o, s);
     if (D.d == 128 && D.B == 128)
-        return launch_attn_t<128, 128, kQW, MODE>(D, q, k, v, nullptr, col_idx, recs, n_idx, o,
-                                                  s);
+        return launch_attn_t<128, 128, kQW, MODE>(D, q, k, v, nullptr, col_idx, recs, meta, n_idx,
+                                                  o, s);
     if (D.d == 64 && D.B == 64)
-        return launch_attn_t<64, 64, kQW, MODE>(D, q, k, v, nullptr, col_idx, recs, n_idx, o, s);
-    return launch_attn_t<64, 128, kQW, MODE>(D, q, k, v, nullptr, col_idx, recs, n_idx, o, s);
+        return launch_attn_t<64, 64, kQW, MODE>(D, q, k, v, nullptr, col_idx, recs, meta, n_idx,
+                                                o, s);
+    return launch_attn_t<64, 128, kQW, MODE>(D, q, k, v, nullptr, col_idx, recs, meta, n_idx, o,
+                                             s);
 }
 
 }  // namespace
 
 hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                               const uint16_t *v, const int32_t *col_idx, const int4 *recs,
-                              int64_t n_idx, uint16_t *o, hipStream_t s) {
-    return launch_attn<kModeSparse>(D, q, k, v, col_idx, recs, (int)n_idx, o, s);
+                              int32_t *meta, int64_t n_idx, uint16_t *o, hipStream_t s) {
+    return launch_attn<kModeSparse>(D, q, k, v, col_idx, recs, meta, (int)n_idx, o, s);
 }
 
 hipError_t launch_dense_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                              const uint16_t *v, uint16_t *o, hipStream_t s) {
-    return launch_attn<kModeDense>(D, q, k, v, nullptr, nullptr, 0, o, s);
+    return launch_attn<kModeDense>(D, q, k, v, nullptr, nullptr, nullptr, 0, o, s);
 }
 
 hipError_t launch_col_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                            const uint16_t *v, const int32_t *cols, int64_t k_c, uint16_t *o,
                            hipStream_t s) {
-    return launch_attn<kModeCols>(D, q, k, v, cols, nullptr, (int)k_c, o, s);
+    return launch_attn<kModeCols>(D, q, k, v, cols, nullptr, nullptr, (int)k_c, o, s);
 }
 
 hipError_t launch_group_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
@@ -757,9 +781,9 @@ hipError_t launch_group_attn(const Dims &D, const uint16_t *q, const uint16_t *k
     if (D.B != 64) return hipErrorInvalidValue;   // the entry point rejects it first
     if (D.d == 128)
         return launch_attn_t<128, 64, kQW, kModeGroup>(D, q, k, v, row_ptr, col_idx, nullptr,
-                                                       (int)nnz, o, s);
+                                                       nullptr, (int)nnz, o, s);
     return launch_attn_t<64, 64, kQW, kModeGroup>(D, q, k, v, row_ptr, col_idx, nullptr,
-                                                  (int)nnz, o, s);
+                                                  nullptr, (int)nnz, o, s);
 }
 
 }  // namespace sd

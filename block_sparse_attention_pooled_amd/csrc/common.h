@@ -29,6 +29,20 @@ enum SelectWord {
                       // above the prefix, rank wanted inside it), 3 words each
 };
 
+// Words of the plan's metadata (work_meta in the workspace).
+enum MetaWord {
+    kMetaCap = 0,        // work-order positions per die
+    kMetaNonEmpty = 1,   // rows that keep a block
+    kMetaListLo = 2,     // tag: address of the col_idx array planned (low, high word),
+    kMetaListHi = 3,     //      its length nnz, the head count H and block count nb
+    kMetaNnz = 4,
+    kMetaHeads = 5,
+    kMetaNb = 6,
+    kMetaCheck = 7,      // cleared by each plan; sparse launches OR in the bits below
+};
+constexpr int kCheckStalePlan = 1;     // launch on another col_idx, nnz or shape than planned
+constexpr int kCheckListChanged = 2;   // a row's first list entries differ from its record
+
 // Shapes after validation, with derived sizes.
 struct Dims {
     int H, Hkv, L, d, B, nb, G;
@@ -130,9 +144,11 @@ hipError_t launch_mask_recall(const Dims &D, const float *mass, const int32_t *r
 
 // Attention launches (attn_kernels.hip).
 // Rows, list bounds and first block ids from the work records of the plan.
+// meta: the plan's metadata words; the launch checks the tag and ORs the
+// check bits into meta[kMetaCheck].
 hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                               const uint16_t *v, const int32_t *col_idx, const int4 *recs,
-                              int64_t n_idx, uint16_t *o, hipStream_t s);
+                              int32_t *meta, int64_t n_idx, uint16_t *o, hipStream_t s);
 hipError_t launch_dense_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                              const uint16_t *v, uint16_t *o, hipStream_t s);
 // GQA variant: one workgroup per (KV group, pair of its query heads, query

@@ -706,6 +706,7 @@ __device__ __forceinline__ void argmin_step(int64_t &load, int &die) {
 constexpr int kPlanThreads = 1024;
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__restrict__ row_ptr,
+                                                              const int32_t *list, int64_t nnz,
                                                               int H, int nb, int steps_per_block,
                                                               int32_t *__restrict__ head_base,
                                                               int32_t *__restrict__ work,
@@ -810,8 +811,15 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__r
         }
     }
     if (tid == 0) {
-        meta[0] = (int32_t)cap;
-        meta[1] = nonempty;
+        meta[kMetaCap] = (int32_t)cap;
+        meta[kMetaNonEmpty] = nonempty;
+        const uint64_t addr = reinterpret_cast<uint64_t>(list);
+        meta[kMetaListLo] = (int32_t)(uint32_t)addr;
+        meta[kMetaListHi] = (int32_t)(uint32_t)(addr >> 32);
+        meta[kMetaNnz] = (int32_t)nnz;
+        meta[kMetaHeads] = H;
+        meta[kMetaNb] = nb;
+        meta[kMetaCheck] = 0;
     }
 }
 
@@ -1013,8 +1021,8 @@ hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, const int32_t *col
     int4 *work_rec = reinterpret_cast<int4 *>(ws + w.work_rec);
     int32_t *meta = reinterpret_cast<int32_t *>(ws + w.work_meta);
     int32_t *head_base = reinterpret_cast<int32_t *>(ws + w.plan_head_base);
-    hipLaunchKernelGGL(k_plan_assign, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, D.H, D.nb,
-                       D.B / 32, head_base, work, work_rec, meta);
+    hipLaunchKernelGGL(k_plan_assign, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, col_idx, nnz,
+                       D.H, D.nb, D.B / 32, head_base, work, work_rec, meta);
     hipLaunchKernelGGL(k_plan_rows, dim3(D.H), dim3(64), 0, s, row_ptr, col_idx, nnz, D.nb,
                        head_base, work, work_rec);
     return hipGetLastError();

@@ -55,11 +55,12 @@ extern "C" {
 
 typedef enum {
     STEPDLLM_OK = 0,
-    STEPDLLM_EINVAL = -1,       /* bad argument: null pointer, bad size or ratio, sparsity not in [0,1) */
+    STEPDLLM_EINVAL = -1,       /* bad argument: null pointer, bad size or ratio, sparsity not in [0,1] */
     STEPDLLM_EUNSUPPORTED = -2, /* valid shape the kernels do not implement (head_dim, block, nb) */
     STEPDLLM_EWORKSPACE = -3,   /* workspace smaller than stepdllm_workspace_bytes() */
     STEPDLLM_EHIP = -4,         /* the HIP runtime rejected a launch */
-    STEPDLLM_ESTATE = -5        /* driver: a reuse step came before any mask was built */
+    STEPDLLM_ESTATE = -5,       /* driver: a reuse step came before any mask was built */
+    STEPDLLM_ENOMEM = -6        /* driver: the host allocation of the driver object failed */
 } stepdllm_status;
 
 typedef struct {
@@ -78,7 +79,7 @@ typedef struct {
 typedef struct {
     int32_t dense_steps;
     int32_t refresh_every;
-    double sparsity;    /* s in [0, 1): fraction of the H*nb*nb blocks dropped */
+    double sparsity;    /* s in [0, 1]: fraction of the H*nb*nb blocks dropped */
     int32_t per_head_budget;  /* 0: head-adaptive global budget (Step-dLLM);
                                  1: the uniform per-head budget it is compared
                                  with (see stepdllm_build_mask_per_head) */
@@ -101,7 +102,15 @@ typedef struct {
     int64_t work;       /* int32 [8 * cap]: attention work order, cap =
                            min(H, ceil(H/8) + 2) * nb positions per die;
                            -1 = padding                                           */
-    int64_t work_meta;  /* int32 [16]: [0] cap, [1] number of non-empty rows      */
+    int64_t work_meta;  /* int32 [16]: [0] cap, [1] number of non-empty rows,
+                           [2], [3] address (low, high word) of the col_idx
+                           array the plan was made from, [4] its nnz, [5] H,
+                           [6] nb; [7] the plan check word: set to 0 by every
+                           plan, then each stepdllm_sparse_attn ORs in 1 if
+                           its col_idx, nnz, H or nb differ from [2]-[6] (every
+                           row then outputs zeros) and 2 if some row's first
+                           two list entries in col_idx differ from the ones
+                           its plan record holds (that row outputs zeros)     */
     int64_t head_select;/* uint32 [H, 8]: per-head select state under the uniform
                            budget: [h*8 + 0] cut key, [+1] count above the cut,
                            [+2] ties kept at the cut, [+3] k_h; the column mask
@@ -118,9 +127,14 @@ typedef struct {
     int64_t total;      /* == stepdllm_workspace_bytes()                          */
 } stepdllm_ws_layout;
 
-/* Number of kept blocks K = ceil((1 - s) * H * nb^2) (a guard of 1e-9 * N is
- * subtracted first so an exact integer is not rounded up by representation
- * error).  Host only.  Returns K >= 0, or a negative stepdllm_status. */
+/* Number of kept blocks under the head-adaptive global budget (Step-dLLM
+ * abstract: one sparsity budget shared by all heads of the layer, so heads
+ * compete for it): K = ceil((1 - s) * H * nb^2), counted over query heads.
+ * s is read as the decimal number the caller wrote (the shortest decimal that
+ * converts back to the same double, e.g. 0.3 for the double nearest 0.3), and
+ * the ceiling is evaluated exactly on it, so K never depends on binary
+ * representation error.  s in [0, 1]: s = 0 keeps every block, s = 1 none.
+ * Host only.  Returns K >= 0, or a negative stepdllm_status. */
 int64_t stepdllm_keep_count(const stepdllm_dims *dims, double sparsity);
 
 /* Workspace size in bytes for these dims, or a negative stepdllm_status. */
@@ -154,8 +168,9 @@ int stepdllm_select_mask(const stepdllm_dims *dims, double sparsity,
 
 /* The uniform per-head budget, the baseline that the Step-dLLM abstract sets
  * its head-adaptive budget against: every head keeps the same number
- * k_h = ceil((1 - s) * nb^2) of its own nb^2 pooled scores (a guard of
- * 1e-9 * nb^2 is subtracted first), largest first, ties by lowest index.
+ * k_h = ceil((1 - s) * nb^2) of its own nb^2 pooled scores (evaluated
+ * exactly on the decimal s, as in stepdllm_keep_count), largest first, ties
+ * by lowest index.
  * Host only.  Returns H * k_h (the length of col_idx), or a negative status. */
 int64_t stepdllm_keep_count_per_head(const stepdllm_dims *dims, double sparsity);
 
@@ -173,9 +188,11 @@ int stepdllm_select_mask_per_head(const stepdllm_dims *dims, double sparsity,
                                   int32_t *row_ptr, int32_t *col_idx, void *stream);
 
 /* Work order for a caller-built mask (row_ptr as above; col_idx holds nnz
- * list entries).  The GPU's 8 dies
- * (XCDs) each have their own L2 and take workgroups round robin, so all rows
- * of a head go to one die.  A head weighs (B/32) * kept blocks + 4 * rows that
+ * list entries).  The pages give no work order (the Step-dLLM abstract only
+ * names an IO-aware fused kernel); this is the library's own scheduling
+ * reading, with no effect on any output.  The GPU's 8 dies (XCDs) each have
+ * their own L2 and take workgroups round robin, so all rows of a head go to
+ * one die.  A head weighs (B/32) * kept blocks + 4 * rows that
  * keep a block (its 32-key steps plus a fixed start-up and write-out per row);
  * heads are ranked by weight (descending, ties by id) and each goes to the
  * least-loaded die that holds fewer than min(H, ceil(H/8) + 2) heads (ties:
@@ -189,8 +206,11 @@ int stepdllm_select_mask_per_head(const stepdllm_dims *dims, double sparsity,
  * at the end.  Beside the order, each position gets a record
  * (work_rec in the layout) of the row's list bounds and first two block ids,
  * so the plan describes this mask's contents, not only its row lengths: plan
- * again after any change to row_ptr or col_idx.  Memory safety on malformed
- * masks: list positions outside [0, nnz) are not read. */
+ * again after any change to row_ptr or col_idx.  The plan also tags the
+ * workspace with col_idx's address, nnz, H and nb and clears the check word
+ * (work_meta in the layout), which stepdllm_sparse_attn uses to detect a
+ * stale plan.  Memory safety on malformed masks: list positions outside
+ * [0, nnz) are not read. */
 int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr,
                   const int32_t *col_idx, int64_t nnz,
                   void *ws, size_t ws_bytes, void *stream);
@@ -205,15 +225,23 @@ int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr,
  * records and the rest of the list from col_idx, which must be the array the
  * plan was made from, unchanged since.
  * nnz is the length of col_idx (row_ptr[H*nb] for a well-formed mask, K for a
- * built one).  Memory safety on malformed masks: list positions at or past nnz
- * are not read, and block ids outside [0, nb) are clamped into range (the
- * output of such a row is then unspecified).
+ * built one).  Stale plans are detected, not trusted: if col_idx, nnz or the
+ * shape differ from the plan's tag, every row outputs zeros and bit 0 of the
+ * check word (work_meta[7] in the workspace layout) is set; if a row's first
+ * two list entries differ from its plan record (col_idx rewritten in place
+ * after planning), that row outputs zeros and bit 1 is set.  The word is
+ * cleared by every plan and read by the caller (device memory, after the
+ * launch has completed); a rewrite that keeps every row's length and first
+ * two entries is not detected.  Memory safety on malformed masks: list
+ * positions at or past nnz are not read, and block ids outside [0, nb) are
+ * clamped into range (the output of such a row is then unspecified).
+ * ws is written (the check word) as well as read.
  * q [H,L,d], k/v [Hkv,L,d], o [H,L,d] bf16; bf16 MFMA with fp32 accumulation
  * and softmax; o rounded to nearest-even bf16. */
 int stepdllm_sparse_attn(const stepdllm_dims *dims, const uint16_t *q,
                          const uint16_t *k, const uint16_t *v,
                          const int32_t *col_idx, int64_t nnz,
-                         const void *ws, size_t ws_bytes,
+                         void *ws, size_t ws_bytes,
                          uint16_t *o, void *stream);
 
 /* GQA variant of stepdllm_sparse_attn with group-shared K/V tiles: the heads
@@ -246,8 +274,9 @@ int stepdllm_dense_attn(const stepdllm_dims *dims, const uint16_t *q,
  *   c[h,u] = (1/nb) sum_i softmax_u(qb[h,i] . k_u / sqrt(d))
  * over all L key tokens u of key head h / (H/Hkv), qb[h,i] the mean of query
  * block i rounded to bf16; each head keeps the same number
- * k_c = ceil((1 - s) * L) of its columns (a guard of 1e-9 * L is subtracted
- * first), largest mass first, ties by lowest column, and every query of the
+ * k_c = ceil((1 - s) * L) of its columns (evaluated exactly on the decimal s,
+ * as in stepdllm_keep_count), largest mass first, ties by lowest column, and
+ * every query of the
  * head attends to exactly those key tokens.
  * Host only.  Returns k_c, or a negative status. */
 int64_t stepdllm_keep_count_columns(const stepdllm_dims *dims, double sparsity);

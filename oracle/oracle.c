@@ -37,6 +37,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -100,16 +101,39 @@ void oracle_scores(const float *qb, const float *kb, int H, int Hkv, int nb,
 
 /* ------------------------------------------------------------ keep count --- */
 /* K = ceil((1 - s) * N) with N = H * nb^2 (the head-adaptive global budget of
- * [SD] counts all query heads together).  A guard of 1e-9*N is subtracted
- * before the ceiling so that a product that is mathematically an integer is
- * not pushed up by binary representation error. */
+ * [SD] counts all query heads together), s taken as the decimal number the
+ * caller wrote: the decimal with the fewest significant digits that reads
+ * back as the same double (the nearest one of that length).  With
+ * s = m / 10^E the budget is the ceiling of the fraction (10^E - m) * N / 10^E,
+ * exact in 128-bit integers for N < 2^31. */
 int64_t oracle_keep_count(int64_t n, double s)
 {
-    double x = (1.0 - s) * (double)n - 1e-9 * (double)n;
-    if (x <= 0.0)
+    if (s == 0.0)
+        return n;
+    if (s == 1.0)
         return 0;
-    int64_t k = (int64_t)ceil(x);
-    return k > n ? n : k;
+    long long m = 0;
+    int E = 0;
+    for (int p = 1; p <= 17; ++p) {
+        /* the nearest decimal with p significant digits, as digits * 10^-E */
+        char b[64];
+        snprintf(b, sizeof b, "%.*e", p - 1, s);
+        if (strtod(b, NULL) != s)
+            continue;
+        char *c = b;
+        for (; *c != 'e'; ++c)
+            if (*c != '.')
+                m = 10 * m + (*c - '0');
+        E = (p - 1) - (int)strtol(c + 1, NULL, 10);
+        break;
+    }
+    if (E > 27)     /* s < 1e-10, so 0 < s * N < 1 and (1 - s) * N is in (N-1, N) */
+        return n;
+    unsigned __int128 ten_e = 1;
+    for (int i = 0; i < E; ++i)
+        ten_e *= 10;
+    unsigned __int128 num = (ten_e - (unsigned __int128)m) * (unsigned __int128)n;
+    return (int64_t)((num + ten_e - 1) / ten_e);
 }
 
 /* ---------------------------------------------------------------- select --- */

@@ -76,18 +76,43 @@ def brute_attention(q, k, v, token_mask):
 
 # ------------------------------------------------------------------ budget --
 def pin_keep_count(lib):
-    """K = ceil((1-s)*N) in exact rational arithmetic, for every workload size."""
+    """K = ceil((1-s)*N) in exact rational arithmetic on the decimal s the
+    caller wrote (Python's repr: the shortest decimal that reads back as the
+    same double), for every workload size and for cases where binary
+    representation error or a relative guard would change the answer."""
     cases = [(32, "0.5"), (32768, "0.9"), (524288, "0.9"), (458752, "0.7"), (458752, "0.8"),
              (458752, "0.9"), (458752, "0.95"), (8388608, "0.95"), (64, "0.75"), (96, "0"),
-             (100, "0.99"), (7, "0.5"), (1, "0.5")]
+             (100, "0.99"), (7, "0.5"), (1, "0.5"), (2 ** 25, "0.956"), (10, "0.3"),
+             (10, "0.1"), (10 ** 6, "0.999999"), (8000, "0.999"), (2 ** 30, "0.123457"),
+             (2 ** 20, "1e-07"), (32, "0.999999999999"), (5, "1"), (2 ** 30, "1e-300")]
     for n, s in cases:
+        assert repr(float(s)) == s or float(s) in (0.0, 1.0), s
         want = math.ceil((1 - Fraction(s)) * n)
         got = O.keep_count(n, float(s), lib)
         assert got == want, (n, s, got, want)
-    # Values the workloads rely on, written out.
+    # Random decimals of 1 to 9 digits, and powers of two with their upper
+    # neighbours (at a power of two the double's rounding interval is
+    # lopsided, so repr may pick a decimal that is not the nearest one of its
+    # length; s * N is then dyadic and the two decimals give the same K).
+    rng = np.random.default_rng(7)
+    for u in rng.random(400):
+        s = float(f"{u:.{1 + int(u * 1000) % 9}g}")
+        n = int(rng.integers(1, 2 ** 31))
+        assert O.keep_count(n, s, lib) == math.ceil((1 - Fraction(repr(s))) * n), (n, s)
+    for k in range(1, 60):
+        for s in (2.0 ** -k, np.nextafter(2.0 ** -k, 1.0)):
+            s = float(s)
+            n = 2 ** 30 + 12345
+            assert O.keep_count(n, s, lib) == math.ceil((1 - Fraction(repr(s))) * n), (n, s)
+    # Values written out by hand.
     assert O.keep_count(524288, 0.9, lib) == 52429
     assert O.keep_count(8388608, 0.95, lib) == 419431
     assert O.keep_count(32, 0.5, lib) == 16
+    assert O.keep_count(2 ** 25, 0.956, lib) == 1476396     # (0.044 * 2^25 = 1476395.008)
+    assert O.keep_count(10, 0.3, lib) == 7                  # the double is below 0.3
+    assert O.keep_count(10 ** 6, 0.999999, lib) == 1        # 1 - s carries 1e-11 relative error
+    assert O.keep_count(32, 1.0, lib) == 0
+    assert O.keep_count(32, 0.0, lib) == 32
 
 
 # -------------------------------------------------------------------- pool --

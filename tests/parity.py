@@ -14,6 +14,26 @@ ROW_REL_L2 = 2e-2
 NEAR_TIE_REL = 1e-5
 
 
+def score_rel_bound(nb):
+    """Largest relative difference between the GPU's and the oracle's
+    row-softmaxed pooled scores P that fp32 rounding allows.  Both sides form
+    the logits identically (fp32 block sums in ascending order, products and
+    sums in ascending dimension order without fused multiply-adds, then the
+    scale), take the same row maximum and subtract it exactly, so the logits
+    agree bit for bit.  Then, with u = 2^-24:
+      * exp: the device library's expf and glibc's are each within 1 ulp
+        (at most 2u relative), so a numerator differs by at most 4u, and so
+        does the exact sum of a row's terms;
+      * row sums: the oracle adds the nb terms in order (error at most
+        (nb - 1) u relative, all terms positive), the GPU adds ceil(nb/32)
+        terms per lane and then 5 butterfly levels (at most
+        (ceil(nb/32) + 4) u);
+      * each side's division rounds once (u each).
+    First-order total, with 1% for the second-order terms."""
+    u = 2.0 ** -24
+    return 1.01 * u * (4 + 4 + (nb - 1) + (-(-nb // 32) + 4) + 2)
+
+
 def keep_from_csr(row_ptr, col_idx, H, nb):
     row_ptr = np.asarray(row_ptr)
     col_idx = np.asarray(col_idx)

@@ -65,3 +65,40 @@ def test_cpu_all_on_the_tiny_workload(capsys):
     t = r["results"][0]
     assert t["workload"] == "tiny" and t["sparse_step"] == "full" and t["dense_step"] == "full"
     assert t["mask_build_s"] >= 0 and t["sparse_tflops"] > 0 and t["dense_tflops"] > 0
+
+
+def _kind(dense, every):
+    """The driver's step kind (0 dense, 1 anchor, 2 reuse) for a schedule."""
+    def kind(t):
+        if t < dense:
+            return 0
+        since = t - dense
+        return 1 if since == 0 or (every > 0 and since % every == 0) else 2
+    return kind
+
+
+def test_timed_window_opens_on_an_anchor():
+    T = 256
+    k = _kind(0, 32)
+    # The driver's short command (--warmup 5 --steps 20) times an anchor first.
+    assert bench.window_start(lambda t: k(t % T), 5, T) == 32
+    assert bench.window_start(lambda t: k(t % T), 512, T) == 512
+    assert bench.window_start(lambda t: k(t % T), 0, T) == 0
+    # The GQA schedule refreshes every 16 of 64 steps.
+    k16 = _kind(0, 16)
+    assert bench.window_start(lambda t: k16(t % 64), 17, 64) == 32
+    # Dense steps first (the long configuration): the window opens on step 0
+    # of the next pass, so it holds the dense steps and then the anchor.
+    kd = _kind(26, 0)
+    assert bench.window_start(lambda t: kd(t % 128), 5, 128) == 128
+    assert bench.window_start(lambda t: kd(t % 128), 0, 128) == 0
+
+
+def test_mask_build_bandwidth():
+    w = WORKLOADS["stepdllm_8k"]
+    r = bench.mask_build_bandwidth(w, 0.236, 0.136, False)
+    want = (64 * 8192 * 128 * 2 + 64 * 128 * 128 * 4 + 4 * 32 * 128 * 128 * 4)
+    assert r["mask_build_bytes"] == want
+    assert abs(r["mask_build_gbs"] - want / 0.1e-3 / 1e9) < 0.1
+    assert bench.mask_build_bandwidth(w, None, 0.136, False) == {}
+    assert bench.mask_build_bandwidth(w, 0.236, 0.136, True) == {}

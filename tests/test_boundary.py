@@ -6,6 +6,7 @@ import os
 import re
 from fractions import Fraction
 
+import numpy as np
 import pytest
 
 from block_sparse_attention_pooled_amd import binding as B
@@ -58,11 +59,39 @@ def test_keep_count_edges():
     assert B.keep_count(d, 0.0) == 32
     assert B.keep_count(d, 0.5) == 16
     assert B.keep_count(d, 0.999999) == 1
-    assert B.keep_count(d, 1 - 1e-12) == 0       # (1-s)*N below the guard
-    for bad in (-0.1, 1.0, 1.5, float("nan")):
+    assert B.keep_count(d, 1 - 1e-12) == 1       # (1-s)*N = 3.2e-11 > 0
+    assert B.keep_count(d, 1.0) == 0             # s = 1 drops every block
+    for bad in (-0.1, 1.5, float("nan")):
         with pytest.raises(B.StepDLLMError) as e:
             B.keep_count(d, bad)
         assert e.value.status == B.EINVAL
+
+
+@pytest.mark.parametrize("shape,s,want", [
+    ((32, 32, 65536, 128, 64), 0.956, 1476396),   # N = 2^25: 0.044 N = 1476395.008
+    ((100, 100, 6400, 128, 64), 0.999999, 1),     # N = 10^6: (1 - s) N is exactly 1
+    ((10, 10, 64, 64, 64), 0.3, 7),               # N = 10: the double is below 0.3
+    ((10, 10, 64, 64, 64), 0.1, 9),               # ... and above 0.1
+    ((125, 125, 512, 64, 64), 0.999, 8),          # N = 8000
+])
+def test_keep_count_exact_on_the_decimal(shape, s, want, olib):
+    """The library's budget is the exact ceiling on the decimal s, equal to
+    the oracle's and to Python's rational arithmetic on repr(s)."""
+    import oracle as O
+    H, Hkv, L, d, blk = shape
+    n = H * (L // blk) ** 2
+    assert math.ceil((1 - Fraction(repr(s))) * n) == want
+    assert B.keep_count(dims(*shape), s) == want == O.keep_count(n, s, olib)
+
+
+def test_keep_count_random_decimals(olib):
+    import oracle as O
+    rng = np.random.default_rng(11)
+    d = dims(32, 32, 65536, 128, 64)             # N = 2^25
+    for u in rng.random(300):
+        s = float(f"{u:.{1 + int(u * 1000) % 9}g}")
+        want = math.ceil((1 - Fraction(repr(s))) * 2 ** 25)
+        assert B.keep_count(d, s) == want == O.keep_count(2 ** 25, s, olib), s
 
 
 @pytest.mark.parametrize("args,status", [
@@ -129,18 +158,20 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.stepdllm_plan(r(d), FAKE, FAKE, -1, FAKE, ws_need, None) == B.EINVAL
     assert lib.stepdllm_build_mask_per_head(r(d), 0.5, None, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL
     assert lib.stepdllm_select_mask_per_head(r(d), 0.5, FAKE, FAKE, ws_need - 1, FAKE, FAKE, None) == B.EWORKSPACE
-    assert lib.stepdllm_keep_count_per_head(r(d), 1.0) == B.EINVAL
+    assert lib.stepdllm_keep_count_per_head(r(d), 1.0001) == B.EINVAL
+    assert lib.stepdllm_keep_count_per_head(r(d), 1.0) == 0
     assert lib.stepdllm_block_mass(r(d), FAKE, None, FAKE, None) == B.EINVAL
     assert lib.stepdllm_block_mass(r(dims(2, 2, 256, 80, 64)), FAKE, FAKE, FAKE, None) == B.EUNSUPPORTED
     assert lib.stepdllm_mask_recall(r(d), FAKE, FAKE, FAKE, 33, FAKE, None) == B.EINVAL
     assert lib.stepdllm_mask_recall(r(d), FAKE, None, FAKE, 16, FAKE, None) == B.EINVAL
     # column-sparse entry points
-    assert lib.stepdllm_keep_count_columns(r(d), 1.0) == B.EINVAL
+    assert lib.stepdllm_keep_count_columns(r(d), 1.0001) == B.EINVAL
+    assert lib.stepdllm_keep_count_columns(r(d), 1.0) == 0
     assert lib.stepdllm_keep_count_columns(r(d), 0.0) == 256
     assert lib.stepdllm_build_col_mask(r(d), 0.5, FAKE, None, FAKE, ws_need, FAKE, None, None) == B.EINVAL
     assert lib.stepdllm_build_col_mask(r(d), 0.5, FAKE, FAKE, FAKE, ws_need, None, None, None) == B.EINVAL
     assert lib.stepdllm_build_col_mask(r(d), 0.5, FAKE, FAKE, FAKE, ws_need - 1, FAKE, None, None) == B.EWORKSPACE
-    assert lib.stepdllm_build_col_mask(r(d), 1.0, FAKE, FAKE, FAKE, ws_need, FAKE, None, None) == B.EINVAL
+    assert lib.stepdllm_build_col_mask(r(d), 1.5, FAKE, FAKE, FAKE, ws_need, FAKE, None, None) == B.EINVAL
     assert lib.stepdllm_select_col_mask(r(d), 0.5, None, FAKE, ws_need, FAKE, None) == B.EINVAL
     assert lib.stepdllm_select_col_mask(r(d), 0.5, FAKE, FAKE, 8, FAKE, None) == B.EWORKSPACE
     assert lib.stepdllm_col_attn(r(d), FAKE, FAKE, FAKE, FAKE, 257, FAKE, None) == B.EINVAL
@@ -152,7 +183,7 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.stepdllm_col_recall(r(d), FAKE, FAKE, FAKE, 257, FAKE, None) == B.EINVAL
     assert lib.stepdllm_col_recall(r(d), FAKE, FAKE, FAKE, 4, None, None) == B.EINVAL
     # sparsity out of range
-    for s in (-0.5, 1.0, float("nan")):
+    for s in (-0.5, 1.0000001, float("nan")):
         assert lib.stepdllm_build_mask(r(d), s, FAKE, FAKE, FAKE, ws_need, FAKE, FAKE, None, None) == B.EINVAL
     # workspace too small
     assert lib.stepdllm_build_mask(r(d), 0.5, FAKE, FAKE, FAKE, ws_need - 1, FAKE, FAKE, None, None) == B.EWORKSPACE
@@ -205,7 +236,7 @@ def test_driver_rejects_reuse_before_anchor_and_bad_schedules():
         lib.stepdllm_driver_destroy(h)
     assert _driver(d, -1, 4, 0.5)[0] == B.EINVAL
     assert _driver(d, 0, -4, 0.5)[0] == B.EINVAL
-    assert _driver(d, 0, 4, 1.0)[0] == B.EINVAL
+    assert _driver(d, 0, 4, 1.5)[0] == B.EINVAL
     assert _driver(d, 0, 4, 0.5, ws_bytes=16)[0] == B.EWORKSPACE
     assert _driver(d, 0, 4, 0.5, per_head=2)[0] == B.EINVAL
     st, h = _driver(d, 0, 4, 0.5, per_head=1)

@@ -128,7 +128,7 @@ def test_column_select_on_injected_ties(H, L, blk):
     ws = torch.empty(B.workspace_bytes(dims), dtype=torch.uint8, device=DEV)
     sc = torch.from_numpy(vals.reshape(-1)).to(DEV)
     for want_k in (0, 1, 31, 32, 33, L // 3, L - 1, L):
-        s = 1.0 - want_k / L if want_k > 0 else 1.0 - 1e-12
+        s = (L - want_k) / L
         k_c = B.keep_count_columns(dims, s)
         assert k_c == want_k
         buf = torch.full((max(H * k_c, 1),), -7, dtype=torch.int32, device=DEV)

@@ -44,7 +44,8 @@ def test_pool_bit_exact_and_scores_close(shape):
     P = m.P()
     assert np.array_equal(P, m.buf.scores().cpu().numpy().reshape(P.shape))
     rel = np.max(np.abs(P.astype(np.float64) - P_ref) / P_ref)
-    assert rel < 4e-6, rel
+    print(f"max relative score difference {rel:.3g} (bound {PT.score_rel_bound(m.nb):.3g})")
+    assert rel <= PT.score_rel_bound(m.nb), rel
 
 
 @pytest.mark.parametrize("s", [0.0, 0.5, 0.9, 0.97])
@@ -233,11 +234,11 @@ def test_largest_block_count():
 
 
 def test_zero_budget_keeps_nothing():
-    """s just below 1 leaves K = 0 (the guard of R13 takes x below zero): no
-    digit pass runs, every row is empty, the plan's records have empty lists
-    and the sparse launch writes zeros over the NaN-filled output."""
+    """s = 1 leaves K = 0: no digit pass runs, every row is empty, the plan's
+    records have empty lists and the sparse launch writes zeros over the
+    NaN-filled output."""
     H, Hkv, L, d, blk = 4, 2, 8 * 64, 64, 64
-    s = 1.0 - 1e-10
+    s = 1.0
     q, k, v = _qkv((H, Hkv, L, d, blk, 1.0), 808)
     dims = B.dims_of(q, k, blk)
     nb = L // blk
@@ -253,6 +254,55 @@ def test_zero_budget_keeps_nothing():
     assert np.array_equal(buf.work().cpu().numpy(), work_ref) and n_ref == 0
     _check_records(buf.work_rec().cpu().numpy(), work_ref, rp, np.zeros(1, np.int32))
     assert torch.equal(o, torch.zeros_like(o))
+
+
+def test_stale_plan_is_flagged():
+    """A sparse launch checks the plan's tag.  On another col_idx array (same
+    contents), another nnz, every row outputs zeros and bit 0 of the check
+    word is set; with one row's first list entry rewritten in place after
+    planning, that row outputs zeros, bit 1 is set and every other row is
+    unchanged; a new plan clears the word and restores the output."""
+    H, Hkv, L, d, blk = 4, 2, 8 * 64, 128, 64
+    q, k, v = _qkv((H, Hkv, L, d, blk, 2.0), 515)
+    m = PT.GpuMask(q, k, blk, 0.7)
+    nb = L // blk
+    ref = torch.empty_like(q)
+    B.sparse_attn(m.dims, q, k, v, m.buf.col_idx, m.buf.ws, ref, nnz=m.K)
+    torch.cuda.synchronize()
+    assert m.buf.plan_check() == 0
+    other = m.buf.col_idx.clone()
+    o = torch.full_like(q, float("nan"))
+    B.sparse_attn(m.dims, q, k, v, other, m.buf.ws, o, nnz=m.K)
+    torch.cuda.synchronize()
+    assert m.buf.plan_check() == 1
+    assert torch.equal(o, torch.zeros_like(o))
+    B.plan(m.dims, m.buf.row_ptr, other, m.buf.ws, nnz=m.K)
+    o.fill_(float("nan"))
+    B.sparse_attn(m.dims, q, k, v, other, m.buf.ws, o, nnz=m.K)
+    torch.cuda.synchronize()
+    assert m.buf.plan_check() == 0 and torch.equal(o, ref)
+    o.fill_(float("nan"))
+    B.sparse_attn(m.dims, q, k, v, other, m.buf.ws, o, nnz=m.K - 1)
+    torch.cuda.synchronize()
+    assert m.buf.plan_check() == 1 and torch.equal(o, torch.zeros_like(o))
+    B.plan(m.dims, m.buf.row_ptr, other, m.buf.ws, nnz=m.K)
+    rp, ci = m.csr()
+    lens = np.diff(rp)
+    r = int(np.argmax(lens))
+    assert lens[r] >= 2 and lens[r] < nb
+    ci2 = ci.copy()
+    ci2[rp[r]] = int(np.setdiff1d(np.arange(nb), ci[rp[r]:rp[r + 1]])[0])
+    other.copy_(torch.from_numpy(ci2))
+    o.fill_(float("nan"))
+    B.sparse_attn(m.dims, q, k, v, other, m.buf.ws, o, nnz=m.K)
+    torch.cuda.synchronize()
+    assert m.buf.plan_check() == 2
+    h, i = divmod(r, nb)
+    rows = o.view(H, nb, blk, d)
+    assert torch.equal(rows[h, i], torch.zeros_like(rows[h, i]))
+    keep = torch.ones(H, nb, dtype=torch.bool)
+    keep[h, i] = False
+    assert torch.equal(rows[keep], ref.view(H, nb, blk, d)[keep])
 
 
 def test_dropped_block_is_detected():
@@ -301,10 +351,11 @@ def test_worked_example_w1_on_gpu():
 
 
 def test_constant_values_and_zero_queries():
-    """V = c gives O = c on non-empty rows (to one bf16 ulp: the weights enter
-    the value product rounded to bf16, unit roundoff 2^-8, while the softmax
-    normaliser sums them in fp32); Q = 0 gives the mean of V over the kept
-    blocks."""
+    """V = c gives O = c exactly on non-empty rows: the normaliser sums the
+    same bf16-rounded weights that enter the value product, so O^T and l
+    differ only by fp32 rounding (far below half a bf16 ulp of c = -1.5),
+    and the bf16 output rounds back to c; Q = 0 gives the mean of V over the
+    kept blocks."""
     H, Hkv, L, d, blk = 4, 2, 8 * 64, 128, 64
     q, k, v = random_qkv(H, Hkv, L, d, 808, device=DEV, q_scale=2.0)
     vc = torch.full_like(v, -1.5)
@@ -314,7 +365,7 @@ def test_constant_values_and_zero_queries():
     torch.cuda.synchronize()
     nonempty = np.diff(m.csr()[0]) > 0
     on = o.cpu().to(torch.float32).numpy().reshape(H * (L // blk), blk, d)
-    assert np.all(np.abs(on[nonempty] + 1.5) <= 1.5 * 2.0 ** -7) and np.all(on[~nonempty] == 0)
+    assert np.all(on[nonempty] == -1.5) and np.all(on[~nonempty] == 0)
     z = torch.zeros_like(q)
     B.sparse_attn(m.dims, z, k, v, m.buf.col_idx, m.buf.ws, o)
     torch.cuda.synchronize()

@@ -24,7 +24,9 @@ MUTANTS = [
     ("softmax_unnormalised", "prow[j] = prow[j] / sum;", "prow[j] = prow[j];", 0),
     ("score_transposed_kb", "const float *b = kb + ((int64_t)g * nb + j) * d;",
      "const float *b = kb + ((int64_t)g * nb + j);", 0),
-    ("keep_count_floor", "int64_t k = (int64_t)ceil(x);", "int64_t k = (int64_t)floor(x);", 0),
+    ("keep_count_floor", "return (int64_t)((num + ten_e - 1) / ten_e);",
+     "return (int64_t)(num / ten_e);", 0),
+    ("keep_count_binary_s", "if (strtod(b, NULL) != s)", "if (p < 17)", 0),
     ("select_ascending", "if (va > vb) return -1;", "if (va < vb) return -1;", 0),
     ("select_ties_highest_index", "return (a < b) ? -1 : (a > b);",
      "return (a > b) ? -1 : (a < b);", 0),
