@@ -77,6 +77,8 @@ def load():
         "stepdllm_driver_create": (i32, [ctypes.POINTER(_vp), D, ctypes.POINTER(Schedule), _vp,
                                          sz, _vp, _vp]),
         "stepdllm_driver_step_kind": (i32, [_vp, ctypes.c_int32]),
+        "stepdllm_step_noalloc": (i32, [D, ctypes.POINTER(Schedule), ctypes.c_int32, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _vp]),
         "stepdllm_step": (i32, [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]),
         "stepdllm_driver_destroy": (i32, [_vp]),
         "stepdllm_status_string": (ctypes.c_char_p, [i32]),
@@ -98,6 +100,7 @@ EXPORTS = ["stepdllm_keep_count", "stepdllm_workspace_bytes", "stepdllm_workspac
            "stepdllm_select_col_mask", "stepdllm_col_attn", "stepdllm_col_recall",
            "stepdllm_driver_create",
            "stepdllm_driver_step_kind", "stepdllm_step", "stepdllm_driver_destroy",
+           "stepdllm_step_noalloc",
            "stepdllm_status_string"]
 
 
@@ -279,6 +282,20 @@ def col_recall(dims, q, k, cols, recall, k_c=None, stream=None):
         ctypes.byref(dims), _ptr(q, bf, "q"), _ptr(k, bf, "k"),
         _ptr(cols, torch.int32, "cols") if cols.numel() else None, k_c,
         _ptr(recall, torch.float32, "recall"), _stream(stream)), "stepdllm_col_recall")
+
+
+def step_noalloc(dims, dense_steps, refresh_every, sparsity, step, q, k, v, row_ptr, col_idx,
+                 o, per_head_budget=False, column_sparse=False, stream=None):
+    """One denoising step with the library's static workspace (no driver, no
+    workspace argument); returns the status code (0 = ok) instead of raising,
+    so callers can see a rejected shape."""
+    bf = torch.bfloat16
+    sched = Schedule(int(dense_steps), int(refresh_every), float(sparsity),
+                     int(bool(per_head_budget)), int(bool(column_sparse)))
+    return int(load().stepdllm_step_noalloc(
+        ctypes.byref(dims), ctypes.byref(sched), int(step), _ptr(q, bf, "q"), _ptr(k, bf, "k"),
+        _ptr(v, bf, "v"), _ptr(row_ptr, torch.int32, "row_ptr"),
+        _ptr(col_idx, torch.int32, "col_idx"), _ptr(o, bf, "o"), _stream(stream)))
 
 
 class Driver:

@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["mask_kernels.hip", "attn_kernels.hip", "quality_kernels.hip", "col_kernels.hip",
-           "api.hip"]
+           "api.hip", "noalloc.hip"]
 LIB = os.path.join(PKG, "libstepdllm.so")
 # A standalone measurement aid (sustained MFMA rate and shader clock), not
 # linked into the library.

@@ -363,6 +363,32 @@ int stepdllm_step(stepdllm_driver *drv, int32_t step, const uint16_t *q,
                   void *stream);
 int stepdllm_driver_destroy(stepdllm_driver *drv);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * denoising step as stepdllm_step with a driver made from (dims, schedule,
+ * row_ptr, col_idx) -- dense / anchor (mask build into row_ptr, col_idx, then
+ * sparse attention) / reuse (sparse attention on the stored mask) -- but with
+ * no driver object and no workspace argument: the workspace is a static
+ * device array inside the library of STEPDLLM_NOALLOC_SCRATCH_BYTES (80 MiB,
+ * enough for every shape up to L = 65536, H = 32, 128-token blocks), one copy
+ * per GPU, looked up on the first call on each device and held until the
+ * process ends.  Shapes whose workspace (stepdllm_workspace_bytes) is larger
+ * are rejected with STEPDLLM_EWORKSPACE.  The call allocates nothing: no
+ * hipMalloc, hipFree or host allocation.  The stream must belong to the
+ * current device.  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents: a reuse step runs on the plan the last anchor
+ * call on this GPU left there (if that anchor was for another col_idx or
+ * shape, the stale-plan check of stepdllm_sparse_attn makes the output
+ * zeros); calls that overlap on one GPU (other streams, other threads) race
+ * on the array and must be serialised by the caller.  The output of each
+ * step is identical to stepdllm_step's.  Nothing in the array needs to start
+ * at zero: every launch writes what it later reads. */
+#define STEPDLLM_NOALLOC_SCRATCH_BYTES (80ll << 20)
+int stepdllm_step_noalloc(const stepdllm_dims *dims, const stepdllm_schedule *schedule,
+                          int32_t step, const uint16_t *q, const uint16_t *k,
+                          const uint16_t *v, int32_t *row_ptr, int32_t *col_idx,
+                          uint16_t *o, void *stream);
+
 /* Static description of a status code. */
 const char *stepdllm_status_string(int status);
 

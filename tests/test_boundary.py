@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = B.load()
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(B.EXPORTS) == names
@@ -267,3 +267,29 @@ def test_library_has_no_undefined_kernel_stubs():
     out = subprocess.run(["nm", "-D", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
     undefined = [l for l in out.splitlines() if " U " in l and "__device_stub__" in l]
     assert not undefined, undefined
+
+
+def test_step_noalloc_validates_before_touching_the_gpu():
+    """The allocation-free step rejects bad arguments and shapes whose
+    workspace exceeds its static array before any HIP call."""
+    lib = B.load()
+    r = ctypes.byref
+    d = dims(2, 2, 256, 64, 64)
+    sched = B.Schedule(0, 4, 0.5, 0, 0)
+    f = lib.stepdllm_step_noalloc
+    assert f(r(d), None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.EINVAL
+    assert f(r(d), r(sched), -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.EINVAL
+    assert f(r(d), r(sched), 0, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == B.EINVAL
+    assert f(r(d), r(sched), 0, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == B.EINVAL
+    assert f(r(d), r(B.Schedule(0, 4, 1.5, 0, 0)), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+             None) == B.EINVAL
+    assert f(r(d), r(B.Schedule(0, 4, 0.5, 1, 1)), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+             None) == B.EINVAL
+    assert f(r(dims(2, 2, 256, 80, 64)), r(sched), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+             None) == B.EUNSUPPORTED
+    big = dims(64, 64, 65536, 128, 128)
+    assert B.workspace_bytes(big) > 80 << 20
+    assert f(r(big), r(sched), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.EWORKSPACE
+    # Every workload of the benchmark fits the static array.
+    for w in WORKLOADS.values():
+        assert B.workspace_bytes(dims(w.H, w.Hkv, w.L, w.d, w.B)) <= 80 << 20, w.name
