@@ -113,9 +113,11 @@ int build_mask(const stepdllm_dims *dims, double sparsity, bool per_head, const 
     float *qb = reinterpret_cast<float *>(base + w.qb);
     float *kb = reinterpret_cast<float *>(base + w.kb);
     float *p = reinterpret_cast<float *>(base + w.p);
-    if ((st = hip_status(sd::launch_pool(D, q, k, qb, kb, s)))) return st;
+    // Global budget: the pool launch prepares the select state and the score
+    // launch counts the first digit of the select.
     const int64_t sel_init_K = per_head ? -1 : keep_count(D, sparsity);
-    if ((st = hip_status(sd::launch_scores(D, qb, kb, p, scores_out, base, w, sel_init_K, s))))
+    if ((st = hip_status(sd::launch_pool(D, q, k, qb, kb, base, w, sel_init_K, s)))) return st;
+    if ((st = hip_status(sd::launch_scores(D, qb, kb, p, scores_out, base, w, !per_head, s))))
         return st;
     return select_and_plan(D, sparsity, per_head, p, base, w, row_ptr, col_idx, !per_head, s);
 }

@@ -103,12 +103,15 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
 }
 
 // Mask-building launches (mask_kernels.hip).
-hipError_t launch_pool(const Dims &D, const uint16_t *q, const uint16_t *k, float *qb, float *kb,
-                       hipStream_t s);
 // With sel_init_K >= 0 the launch also prepares the global select state in ws
-// for a budget of sel_init_K (then launch_select may skip its own init).
+// for a budget of sel_init_K (zero histograms).
+hipError_t launch_pool(const Dims &D, const uint16_t *q, const uint16_t *k, float *qb, float *kb,
+                       char *ws, const WsLayout &w, int64_t sel_init_K, hipStream_t s);
+// With first_digit set the launch also counts the scores into the first digit
+// histogram of the global select (prepared by launch_pool); launch_select then
+// runs with state_ready and starts at the second digit.
 hipError_t launch_scores(const Dims &D, const float *qb, const float *kb, float *p, float *copy,
-                         char *ws, const WsLayout &w, int64_t sel_init_K, hipStream_t s);
+                         char *ws, const WsLayout &w, bool first_digit, hipStream_t s);
 hipError_t launch_select(const Dims &D, int64_t K, const float *p, char *ws, const WsLayout &w,
                          int32_t *row_ptr, int32_t *col_idx, bool state_ready, hipStream_t s);
 // Uniform per-head budget: head h keeps its k_h largest scores.

@@ -54,55 +54,72 @@ __device__ int64_t block_exclusive_scan_1024(int64_t x, int64_t *total) {
 }
 
 // ------------------------------------------------------------------- pool --
-// One thread owns 4 consecutive columns of one (head, block) and adds the B
-// rows in ascending token order in fp32, then scales by 1/B (a power of two,
-// exact).  A wave covers 4 (d=64) or 2 (d=128) blocks with 128/256-byte
-// contiguous segments per load, and a thread keeps a whole 64-row batch of
-// loads in flight.
+// A workgroup pools kPoolPairs consecutive (head, block) pairs of Q (or K),
+// which are one contiguous piece of the tensor: its 256 threads first copy
+// the piece into LDS with 16-byte buffer->LDS loads (1 KiB per wave
+// instruction, all of a wave's loads in flight), then thread t adds the B
+// rows of two columns of one block in ascending token order in fp32 (the
+// order of the definition) and scales by 1/B (a power of two, exact).
+// With init_sel set, block 0 also prepares the global select state for a
+// budget of init_K (zero histograms), which the score launch then fills.
+__device__ void select_init(uint32_t *__restrict__ hist, uint32_t *__restrict__ sel, int64_t K,
+                            int tid, int nthreads);
+
 template <int D>
+constexpr int pool_pairs() { return 256 / (D / 2); }   // (head, block) pairs per workgroup
+
+template <int D, int BLK>
 __global__ __launch_bounds__(256) void k_pool(const uint16_t *__restrict__ q,
                                               const uint16_t *__restrict__ k,
                                               float *__restrict__ qb, float *__restrict__ kb,
-                                              int L, int B, int64_t nq_items, int64_t nk_items) {
-    constexpr int CG = D / 4;   // 4-column groups per row
-    int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x;
+                                              int64_t q_pairs, int64_t k_pairs,
+                                              uint32_t *__restrict__ init_hist,
+                                              uint32_t *__restrict__ init_sel, int64_t init_K) {
+    constexpr int PAIRS = pool_pairs<D>();
+    constexpr int PIECE = PAIRS * BLK * D * 2;   // bytes: 64 KiB (B = 64) or 128 KiB (B = 128)
+    constexpr int LOADS = PIECE / 1024;          // 1 KiB wave loads per piece
+    __shared__ __attribute__((aligned(16))) uint16_t piece[PIECE / 2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (init_sel && blockIdx.x == 0) select_init(init_hist, init_sel, init_K, tid, 256);
+    // Group g of PAIRS consecutive (head, block) pairs; the last group of a
+    // tensor may hold fewer (its loads past the tensor read zeros).
+    const int64_t q_groups = (q_pairs + PAIRS - 1) / PAIRS;
+    const int64_t k_groups = (k_pairs + PAIRS - 1) / PAIRS;
+    int64_t g = blockIdx.x;
     const uint16_t *src = q;
     float *dst = qb;
-    if (it >= nq_items) {
-        it -= nq_items;
-        if (it >= nk_items) return;
+    int64_t pairs = q_pairs;
+    if (g >= q_groups) {
+        g -= q_groups;
+        if (g >= k_groups) return;
         src = k;
         dst = kb;
+        pairs = k_pairs;
     }
-    const int cg = (int)(it % CG);
-    const int64_t hb = it / CG;              // head * nb + block
-    const int nb = L / B;
-    const int64_t head = hb / nb;
-    const int blk = (int)(hb % nb);
-    const uint2 *p = reinterpret_cast<const uint2 *>(src + (head * L + (int64_t)blk * B) * D) + cg;
-    float acc[4];
+    const int here = (int)min((int64_t)PAIRS, pairs - g * PAIRS);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(src + g * (PIECE / 2)), 0, here * (PIECE / PAIRS), 0x00020000);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = 0.0f;
-    // Batches of 64 rows: all of a batch's loads are in flight before the
-    // first add; the adds still run in ascending token order.
-    constexpr int kBatch = 64;   // B is 64 or 128
-    for (int t0 = 0; t0 < B; t0 += kBatch) {
-        uint2 u[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) u[j] = p[(int64_t)(t0 + j) * CG];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const uint32_t w[2] = {u[j].x, u[j].y};
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                acc[2 * c] = acc[2 * c] + bf16_bits_to_float(w[c] & 0xFFFFu);
-                acc[2 * c + 1] = acc[2 * c + 1] + bf16_bits_to_float(w[c] >> 16);
-            }
-        }
+    for (int t = wave; t < LOADS; t += 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void *)(piece + t * 512), 16, lane * 16,
+            t * 1024, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int pr = tid / (D / 2), c = tid % (D / 2);   // pair, column pair
+    const uint32_t *rows = reinterpret_cast<const uint32_t *>(piece) + pr * BLK * (D / 2) + c;
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll 16
+    for (int t = 0; t < BLK; ++t) {
+        const uint32_t w = rows[t * (D / 2)];
+        a0 = a0 + bf16_bits_to_float(w & 0xFFFFu);
+        a1 = a1 + bf16_bits_to_float(w >> 16);
     }
-    const float inv_b = 1.0f / (float)B;
-    *reinterpret_cast<float4 *>(dst + hb * D + cg * 4) =
-        make_float4(acc[0] * inv_b, acc[1] * inv_b, acc[2] * inv_b, acc[3] * inv_b);
+    const float inv_b = 1.0f / (float)BLK;
+    if (pr < here)
+        *reinterpret_cast<float2 *>(dst + (g * PAIRS + pr) * D + 2 * c) =
+            make_float2(a0 * inv_b, a1 * inv_b);
 }
 
 // Select state before the first digit pass: all three histograms zero, the
@@ -131,8 +148,9 @@ __device__ void select_init(uint32_t *__restrict__ hist, uint32_t *__restrict__ 
 // separately rounded multiply and add.  The scaled scores of the 16 rows wait
 // in LDS (up to kMaxBlocks per row: 105 KB in all, within gfx950's 160 KB per
 // workgroup); then each row is softmaxed by its 32 lanes and written once.
-// With init_sel set, block 0 also prepares the select state of a global
-// budget of init_K (the job of k_select_init).
+// With hist0 set, the workgroup also counts its scores into the histogram of
+// the first digit of the global select (bits 31..21 of the order keys; the
+// pool launch zeroed it), so the select starts at its second digit.
 constexpr int kScoreRows = 16;
 constexpr int kScoreCols = 64;
 constexpr int kScoreThreads = kScoreRows * 32;
@@ -143,16 +161,15 @@ __global__ __launch_bounds__(kScoreThreads) void k_scores(const float *__restric
                                                           float *__restrict__ p,
                                                           float *__restrict__ copy, int nb, int G,
                                                           float sigma,
-                                                          uint32_t *__restrict__ init_hist,
-                                                          uint32_t *__restrict__ init_sel,
-                                                          int64_t init_K) {
+                                                          uint32_t *__restrict__ hist0) {
 #pragma clang fp contract(off)
     __shared__ float sq[kScoreRows][D];
     __shared__ float sk[kScoreCols][D + 1];
     __shared__ float srow[kScoreRows][kMaxBlocks];
+    __shared__ uint32_t hh[kRadixBins];
     const int tid = threadIdx.x;
-    // The global select that follows reads a fresh state: block 0 sets it.
-    if (init_sel && blockIdx.x == 0) select_init(init_hist, init_sel, init_K, tid, kScoreThreads);
+    if (hist0)
+        for (int b = tid; b < kRadixBins; b += kScoreThreads) hh[b] = 0;
     const int tiles = (nb + kScoreRows - 1) / kScoreRows;
     // Workgroups go round-robin to the 8 dies, each with its own L2: renumber
     // so that consecutive tiles (one head's rows, sharing its key means) run
@@ -211,25 +228,49 @@ __global__ __launch_bounds__(kScoreThreads) void k_scores(const float *__restric
         if (j + 32 < nb) srow[r][j + 32] = d1 * sigma;
     }
     __syncthreads();
-    if (i0 + r >= nb) return;
-    float m = -INFINITY;
-    for (int j = jj; j < nb; j += 32) m = fmaxf(m, srow[r][j]);
+    const bool row_ok = i0 + r < nb;
+    if (row_ok) {
+        float m = -INFINITY;
+        for (int j = jj; j < nb; j += 32) m = fmaxf(m, srow[r][j]);
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
-    float sum = 0.0f;
-    for (int j = jj; j < nb; j += 32) {
-        float e = expf(srow[r][j] - m);
-        srow[r][j] = e;
-        sum = sum + e;
-    }
+        for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+        float sum = 0.0f;
+        for (int j = jj; j < nb; j += 32) {
+            float e = expf(srow[r][j] - m);
+            srow[r][j] = e;
+            sum = sum + e;
+        }
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) sum = sum + __shfl_xor(sum, o, 32);
-    const int64_t base = ((int64_t)h * nb + i0 + r) * nb;
-    for (int j = jj; j < nb; j += 32) {
-        float v = srow[r][j] / sum;
-        p[base + j] = v;
-        if (copy) copy[base + j] = v;
+        for (int o = 16; o > 0; o >>= 1) sum = sum + __shfl_xor(sum, o, 32);
+        const int64_t base = ((int64_t)h * nb + i0 + r) * nb;
+        for (int j = jj; j < nb; j += 32) {
+            float v = srow[r][j] / sum;
+            srow[r][j] = v;
+            p[base + j] = v;
+            if (copy) copy[base + j] = v;
+        }
     }
+    if (!hist0) return;
+    // First-digit histogram of this tile's scores: a wave's lanes that share a
+    // bin (the scores of a row crowd into a few) add with one atomic.
+    const int lane = tid & 63;
+    for (int j0 = 0; j0 < nb; j0 += 32) {
+        const int j = j0 + jj;
+        const bool valid = row_ok && j < nb;
+        const uint32_t bin = valid ? order_key(srow[r][j]) >> 21 : 0u;
+        uint64_t todo = __ballot(valid);
+        for (int round = 0; round < 2 && todo; ++round) {
+            const int leader = __builtin_ctzll(todo);
+            const uint32_t lb = __builtin_amdgcn_readlane(bin, leader);
+            const uint64_t same = __ballot(valid && bin == lb) & todo;
+            if (lane == leader) atomicAdd(&hh[lb], (uint32_t)__popcll(same));
+            todo &= ~same;
+        }
+        if ((todo >> lane) & 1) atomicAdd(&hh[bin], 1u);
+    }
+    __syncthreads();
+    for (int b = tid; b < kRadixBins; b += kScoreThreads)
+        if (hh[b]) atomicAdd(&hist0[b], hh[b]);
 }
 
 // ------------------------------------------------------------ radix select --
@@ -363,20 +404,6 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_pass(const float *__res
         if (h[b]) atomicAdd(&hp[b], h[b]);
 }
 
-// The last step, one block: the state after digit pass 2 fixes the cut (the
-// K-th largest key), the count strictly above it and the ties to keep.
-__global__ __launch_bounds__(kRadixThreads) void k_radix_final(const uint32_t *__restrict__ hist,
-                                                               uint32_t *__restrict__ sel) {
-    const RadixState st = radix_step(hist + 2 * kRadixBins, 2, load_state(sel, 2));
-    if (threadIdx.x == 0) {
-        sel[SEL_PREFIX] = st.prefix;
-        sel[SEL_ABOVE] = st.above;
-        sel[SEL_REMAIN] = st.remain;
-        sel[SEL_CUT] = st.prefix;
-        sel[SEL_TIES] = st.remain;
-    }
-}
-
 // --------------------------------------------------------------- compaction --
 // Per row (one wave; 16 rows per workgroup): how many scores are above the
 // cut and how many equal it.  Rows come in groups of group_rows that share one
@@ -384,18 +411,36 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_final(const uint32_t *_
 // per-head one), kHeadSelWords apart.  With agg set, workgroup b also writes
 // its rows' sums of both counts to agg[2b], agg[2b + 1].
 
+// With final_hist set (global budget, K > 0), every workgroup first takes the
+// select's last digit step from the histogram of the last pass (cheaper than a
+// launch of its own); workgroup 0 records the cut, the count above it and the
+// ties to keep in the state words.
 __global__ __launch_bounds__(1024) void k_row_count(const float *__restrict__ p, int nb,
                                                     int64_t rows, int64_t group_rows,
-                                                    const uint32_t *__restrict__ sel,
+                                                    uint32_t *__restrict__ sel,
+                                                    const uint32_t *__restrict__ final_hist,
                                                     int32_t *__restrict__ gt,
                                                     int32_t *__restrict__ eq,
                                                     int32_t *__restrict__ agg) {
     __shared__ int32_t sg[kCompactRows], se[kCompactRows];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * kCompactRows + wave;
+    uint32_t final_cut = 0;
+    if (final_hist) {
+        const RadixState st = radix_step(final_hist, 2, load_state(sel, 2));
+        final_cut = st.prefix;
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            sel[SEL_PREFIX] = st.prefix;
+            sel[SEL_ABOVE] = st.above;
+            sel[SEL_REMAIN] = st.remain;
+            sel[SEL_CUT] = st.prefix;
+            sel[SEL_TIES] = st.remain;
+        }
+    }
     int cg = 0, ce = 0;
     if (r < rows) {
-        const uint32_t cut = sel[(r / group_rows) * kHeadSelWords + SEL_CUT];
+        const uint32_t cut =
+            final_hist ? final_cut : sel[(r / group_rows) * kHeadSelWords + SEL_CUT];
         for (int j = lane; j < nb; j += 64) {
             uint32_t key = order_key(p[r * nb + j]);
             cg += key > cut;
@@ -680,73 +725,91 @@ __global__ __launch_bounds__(1024) void k_col_compact(const float *__restrict__ 
 //    first two block ids (16 bits each, clamped into [0, nb)), so that a
 //    workgroup's first K/V loads need one load, not a chain of three; padding
 //    records have row -1.
-// Two launches.  k_plan_assign, one workgroup: the heads' weights straight
-// from row_ptr, their ranks, the die assignment by one wave with one die per
-// lane (the least-loaded open die found by a three-step 8-lane argmin), each
-// head's first position among its die's non-empty rows and among its die's
-// empty rows, the padding and the meta words.  k_plan_rows, one wave per
-// head: the head's row records, its rows by list length descending, ties by
+// Two launches.  k_plan_assign, one workgroup: the heads' weights from one
+// pass over row_ptr (rows summed per lane, then per wave and head, into LDS
+// counters), their ranks, the die assignment by one wave (one lane per die,
+// the least-loaded open die by a cross-lane minimum), each head's first
+// position among its die's non-empty rows and among its die's empty rows, the
+// padding and the meta words (including the tag of the list the plan
+// describes).  k_plan_rows, one wave per head: the head's row records, its rows by list length descending, ties by
 // row id, with a stable counting sort (length histogram, descending bucket
 // starts, ranks among equal lengths from wave ballots), written straight to
 // the head's positions.
-
-// One step of the die argmin: take the (load, die) pair of the lane that
-// dpp_ctrl names when it is smaller.
-template <int CTRL>
-__device__ __forceinline__ void argmin_step(int64_t &load, int &die) {
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)load, CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(load >> 32), CTRL, 0xF, 0xF, false);
-    const int64_t l2 = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-    const int d2 = __builtin_amdgcn_update_dpp(0, die, CTRL, 0xF, 0xF, false);
-    const bool take = l2 < load || (l2 == load && d2 < die);
-    load = take ? l2 : load;
-    die = take ? d2 : die;
-}
 
 constexpr int kPlanThreads = 1024;
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__restrict__ row_ptr,
                                                               const int32_t *list, int64_t nnz,
                                                               int H, int nb, int steps_per_block,
+                                                              bool narrow,
                                                               int32_t *__restrict__ head_base,
                                                               int32_t *__restrict__ work,
                                                               int4 *__restrict__ work_rec,
                                                               int32_t *__restrict__ meta) {
-    static_assert(kDies == 8, "the die argmin covers 8 lanes");
+    static_assert(kDies == 8, "the die loop covers 8 dies");
     __shared__ int64_t weight[kMaxHeads];
-    __shared__ int32_t ne[kMaxHeads], kept[kMaxHeads];
+    __shared__ int32_t ne[kMaxHeads];
     __shared__ int32_t order[kMaxHeads];
     __shared__ int32_t die_of[kMaxHeads], slot_of[kMaxHeads];
     __shared__ int32_t die_list[kDies * kMaxHeads];   // die x's heads in slot order
     __shared__ int32_t die_heads[kDies];
-    __shared__ int32_t nonempty;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int kWaves = kPlanThreads / 64;
     const int cap_h = min(H, (H + kDies - 1) / kDies + 2);
     const int cap = cap_h * nb;   // below 2^31: 8 * cap <= 8 * H * nb
-    for (int h = tid; h < H; h += kPlanThreads) ne[h] = kept[h] = 0;
-    if (tid == 0) nonempty = 0;
-    __syncthreads();
     // Per head: rows that keep a block and blocks kept.  Thread t reads the
-    // bounds of rows 4u .. 4u + 3, u = t, t + 1024, ..., in one batch.
+    // bounds of rows 4u .. 4u + 3, u = t, t + 1024, ..., all in one batch per
+    // round; a wave's rows that fall in one head add with one LDS atomic.
+    __shared__ int32_t kept[kMaxHeads];
+    for (int h = tid; h < H; h += kPlanThreads) ne[h] = kept[h] = 0;
+    __syncthreads();
     const int rows = H * nb;
-    for (int r = 4 * tid; r < rows; r += 4 * kPlanThreads) {
+    for (int r0 = 0; r0 < rows; r0 += 4 * kPlanThreads) {
+        const int r = r0 + 4 * tid;
         int v[5];
 #pragma unroll
         for (int k = 0; k < 5; ++k) v[k] = row_ptr[min(r + k, rows)];
+        // Rows of the thread's first row's head are summed here; rows of later
+        // heads (only where a head boundary falls inside the four) add one by
+        // one below.
+        const int h_lo = min(r, rows - 1) / nb;
+        int ne_lo = 0, kept_lo = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int len = v[k + 1] - v[k];
             if (r + k < rows && len > 0) {
-                atomicAdd(&ne[(r + k) / nb], 1);
-                atomicAdd(&kept[(r + k) / nb], len);
+                if ((r + k) / nb == h_lo) {
+                    ++ne_lo;
+                    kept_lo += len;
+                } else {
+                    atomicAdd(&ne[(r + k) / nb], 1);
+                    atomicAdd(&kept[(r + k) / nb], len);
+                }
             }
+        }
+        // Lanes of the wave with the same head add with one atomic.
+        uint64_t todo = __ballot(r < rows);
+        while (todo) {
+            const int leader = __builtin_ctzll(todo);
+            const int hl = __builtin_amdgcn_readlane(h_lo, leader);
+            const uint64_t same = __ballot(r < rows && h_lo == hl) & todo;
+            int a = (same >> lane) & 1 ? ne_lo : 0, b = (same >> lane) & 1 ? kept_lo : 0;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                a += __shfl_xor(a, o);
+                b += __shfl_xor(b, o);
+            }
+            if (lane == leader) {
+                atomicAdd(&ne[hl], a);
+                atomicAdd(&kept[hl], b);
+            }
+            todo &= ~same;
         }
     }
     __syncthreads();
-    for (int h = tid; h < H; h += kPlanThreads) {
+    for (int h = tid; h < H; h += kPlanThreads)
         weight[h] = (int64_t)steps_per_block * kept[h] + 4 * (int64_t)ne[h];
-        atomicAdd(&nonempty, ne[h]);
-    }
     __syncthreads();
     for (int h = tid; h < H; h += kPlanThreads) {
         int rank = 0;
@@ -755,35 +818,91 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__r
         order[rank] = h;
     }
     __syncthreads();
-    if (wave == 0) {
-        // Lane x < 8 holds die x: its weight so far and its head count.
-        int64_t my_load = 0;
-        int my_count = 0;
+    if (wave == 0 && narrow) {
+        // Heads by rank, each to the least-loaded die with room (ties: lowest
+        // die).  Every load is below 2^28 (known from nnz on the host), so
+        // lane x < 8 holds die x's key load * 8 + x (~0 once the die is
+        // full) and the least key over lanes 0..7 (three DPP minima) names
+        // the die.  Lane a keeps the die and slot of the a-th head of each 64.
+        uint32_t dload = 0;
+        int dcnt = 0;
+        for (int a0 = 0; a0 < H; a0 += 64) {
+            const int my_h = a0 + lane < H ? order[a0 + lane] : 0;
+            const uint32_t my_w = (uint32_t)weight[my_h];
+            int my_die = 0, my_slot = 0;
+            const int n = min(64, H - a0);
+            for (int a = 0; a < n; ++a) {
+                const uint32_t wh = (uint32_t)__builtin_amdgcn_readlane((int)my_w, a);
+                int key = lane < kDies && dcnt < cap_h ? (int)((dload << 3) | (uint32_t)lane) : -1;
+                key = (int)min((uint32_t)key, (uint32_t)__builtin_amdgcn_update_dpp(
+                                                  -1, key, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+                key = (int)min((uint32_t)key, (uint32_t)__builtin_amdgcn_update_dpp(
+                                                  -1, key, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+                key = (int)min((uint32_t)key, (uint32_t)__builtin_amdgcn_update_dpp(
+                                                  -1, key, 0x141, 0xF, 0xF, false));  // 7 - lane
+                const int best = __builtin_amdgcn_readfirstlane(key) & 7;
+                const int slot = __builtin_amdgcn_readlane(dcnt, best);
+                dload += lane == best ? wh : 0u;
+                dcnt += lane == best ? 1 : 0;
+                my_die = lane == a ? best : my_die;
+                my_slot = lane == a ? slot : my_slot;
+            }
+            if (lane < n) {
+                die_of[my_h] = my_die;
+                slot_of[my_h] = my_slot;
+                die_list[my_die * cap_h + my_slot] = my_h;
+            }
+        }
+        if (lane < kDies) die_heads[lane] = dcnt;
+    } else if (wave == 0) {
+        // The same greedy with 64-bit loads in scalar registers; lane a of
+        // the wave keeps the die and slot of the a-th head of each 64.
+        int64_t load[kDies];
+        int cnt[kDies];
+#pragma unroll
+        for (int x = 0; x < kDies; ++x) {
+            load[x] = 0;
+            cnt[x] = 0;
+        }
         for (int a0 = 0; a0 < H; a0 += 64) {
             const int my_h = a0 + lane < H ? order[a0 + lane] : 0;
             const int64_t my_w = weight[my_h];
+            int my_die = 0, my_slot = 0;
             const int n = min(64, H - a0);
             for (int a = 0; a < n; ++a) {
-                const int h = __builtin_amdgcn_readlane(my_h, a);
                 const int64_t wh = (int64_t)(
                     ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(my_w >> 32), a) << 32) |
                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_w, a));
-                int64_t load = (lane < kDies && my_count < cap_h) ? my_load : INT64_MAX;
-                int die = lane;
-                argmin_step<0xB1>(load, die);    // quad_perm [1,0,3,2]
-                argmin_step<0x4E>(load, die);    // quad_perm [2,3,0,1]
-                argmin_step<0x141>(load, die);   // row_half_mirror: lane i <-> 7 - i
-                const int best = __builtin_amdgcn_readlane(die, 0);
-                if (lane == best) {
-                    die_of[h] = best;
-                    slot_of[h] = my_count;
-                    die_list[best * cap_h + my_count] = h;
-                    ++my_count;
-                    my_load += wh;
+                int best = 0;
+                int64_t best_load = INT64_MAX;
+#pragma unroll
+                for (int x = 0; x < kDies; ++x) {
+                    const bool take = cnt[x] < cap_h && load[x] < best_load;
+                    best_load = take ? load[x] : best_load;
+                    best = take ? x : best;
                 }
+                int slot = 0;
+#pragma unroll
+                for (int x = 0; x < kDies; ++x) {
+                    load[x] += x == best ? wh : 0;
+                    slot = x == best ? cnt[x] : slot;
+                    cnt[x] += x == best ? 1 : 0;
+                }
+                my_die = lane == a ? best : my_die;
+                my_slot = lane == a ? slot : my_slot;
+            }
+            if (lane < n) {
+                die_of[my_h] = my_die;
+                slot_of[my_h] = my_slot;
+                die_list[my_die * cap_h + my_slot] = my_h;
             }
         }
-        if (lane < kDies) die_heads[lane] = my_count;
+        if (lane < kDies) {
+            int c = 0;
+#pragma unroll
+            for (int x = 0; x < kDies; ++x) c = x == lane ? cnt[x] : c;
+            die_heads[lane] = c;
+        }
     }
     __syncthreads();
     // Each head's two bases: its die's non-empty rows come first (heads in
@@ -811,6 +930,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__r
         }
     }
     if (tid == 0) {
+        int nonempty = 0;
+        for (int h = 0; h < H; ++h) nonempty += ne[h];
         meta[kMetaCap] = (int32_t)cap;
         meta[kMetaNonEmpty] = nonempty;
         const uint64_t addr = reinterpret_cast<uint64_t>(list);
@@ -919,29 +1040,39 @@ __global__ __launch_bounds__(64) void k_plan_rows(const int32_t *__restrict__ ro
 }  // namespace
 
 // ------------------------------------------------------------------ launches --
-hipError_t launch_pool(const Dims &D, const uint16_t *q, const uint16_t *k, float *qb, float *kb,
-                       hipStream_t s) {
-    const int64_t cg = D.d / 4;
-    const int64_t nq = (int64_t)D.H * D.nb * cg, nk = (int64_t)D.Hkv * D.nb * cg;
-    const int64_t grid = (nq + nk + 255) / 256;
-    if (D.d == 128)
-        hipLaunchKernelGGL(k_pool<128>, dim3((unsigned)grid), dim3(256), 0, s, q, k, qb, kb, D.L,
-                           D.B, nq, nk);
+namespace {
+template <int D>
+void pool_launch(const Dims &Dm, const uint16_t *q, const uint16_t *k, float *qb, float *kb,
+                 int64_t q_pairs, int64_t k_pairs, uint32_t *hist, uint32_t *sel, int64_t K,
+                 hipStream_t s) {
+    constexpr int PAIRS = pool_pairs<D>();
+    const unsigned grid = (unsigned)((q_pairs + PAIRS - 1) / PAIRS + (k_pairs + PAIRS - 1) / PAIRS);
+    if (Dm.B == 64)
+        hipLaunchKernelGGL((k_pool<D, 64>), dim3(grid), dim3(256), 0, s, q, k, qb, kb, q_pairs,
+                           k_pairs, hist, sel, K);
     else
-        hipLaunchKernelGGL(k_pool<64>, dim3((unsigned)grid), dim3(256), 0, s, q, k, qb, kb, D.L,
-                           D.B, nq, nk);
+        hipLaunchKernelGGL((k_pool<D, 128>), dim3(grid), dim3(256), 0, s, q, k, qb, kb, q_pairs,
+                           k_pairs, hist, sel, K);
+}
+}  // namespace
+
+hipError_t launch_pool(const Dims &D, const uint16_t *q, const uint16_t *k, float *qb, float *kb,
+                       char *ws, const WsLayout &w, int64_t sel_init_K, hipStream_t s) {
+    uint32_t *hist = sel_init_K >= 0 ? reinterpret_cast<uint32_t *>(ws + w.hist) : nullptr;
+    uint32_t *sel = sel_init_K >= 0 ? reinterpret_cast<uint32_t *>(ws + w.sel) : nullptr;
+    const int64_t kv_pairs = (int64_t)D.Hkv * D.nb;
+    if (D.d == 128)
+        pool_launch<128>(D, q, k, qb, kb, D.rows(), kv_pairs, hist, sel, sel_init_K, s);
+    else
+        pool_launch<64>(D, q, k, qb, kb, D.rows(), kv_pairs, hist, sel, sel_init_K, s);
     return hipGetLastError();
 }
 
 hipError_t launch_pool_q(const Dims &D, const uint16_t *q, float *qb, hipStream_t s) {
-    const int64_t nq = (int64_t)D.H * D.nb * (D.d / 4);
-    const int64_t grid = (nq + 255) / 256;
     if (D.d == 128)
-        hipLaunchKernelGGL(k_pool<128>, dim3((unsigned)grid), dim3(256), 0, s, q, nullptr, qb,
-                           nullptr, D.L, D.B, nq, (int64_t)0);
+        pool_launch<128>(D, q, nullptr, qb, nullptr, D.rows(), 0, nullptr, nullptr, 0, s);
     else
-        hipLaunchKernelGGL(k_pool<64>, dim3((unsigned)grid), dim3(256), 0, s, q, nullptr, qb,
-                           nullptr, D.L, D.B, nq, (int64_t)0);
+        pool_launch<64>(D, q, nullptr, qb, nullptr, D.rows(), 0, nullptr, nullptr, 0, s);
     return hipGetLastError();
 }
 
@@ -955,18 +1086,17 @@ hipError_t launch_col_select(const Dims &D, int64_t k_c, const float *c, char *w
 }
 
 hipError_t launch_scores(const Dims &D, const float *qb, const float *kb, float *p, float *copy,
-                         char *ws, const WsLayout &w, int64_t sel_init_K, hipStream_t s) {
-    uint32_t *hist = sel_init_K >= 0 ? reinterpret_cast<uint32_t *>(ws + w.hist) : nullptr;
-    uint32_t *sel = sel_init_K >= 0 ? reinterpret_cast<uint32_t *>(ws + w.sel) : nullptr;
+                         char *ws, const WsLayout &w, bool first_digit, hipStream_t s) {
+    uint32_t *hist0 = first_digit ? reinterpret_cast<uint32_t *>(ws + w.hist) : nullptr;
     const int tiles = (D.nb + kScoreRows - 1) / kScoreRows;
     const float sigma = (float)(1.0 / sqrt((double)D.d));
     dim3 grid((unsigned)(D.H * tiles));
     if (D.d == 128)
         hipLaunchKernelGGL(k_scores<128>, grid, dim3(kScoreThreads), 0, s, qb, kb, p, copy, D.nb,
-                           D.G, sigma, hist, sel, sel_init_K);
+                           D.G, sigma, hist0);
     else
         hipLaunchKernelGGL(k_scores<64>, grid, dim3(kScoreThreads), 0, s, qb, kb, p, copy, D.nb,
-                           D.G, sigma, hist, sel, sel_init_K);
+                           D.G, sigma, hist0);
     return hipGetLastError();
 }
 
@@ -977,19 +1107,21 @@ hipError_t launch_select(const Dims &D, int64_t K, const float *p, char *ws, con
     int32_t *gt = reinterpret_cast<int32_t *>(ws + w.gt);
     int32_t *eq = reinterpret_cast<int32_t *>(ws + w.eq);
     const int64_t n = D.n_scores(), rows = D.rows();
+    // With state_ready the state is set and the first digit's histogram is
+    // already counted (pool and score launches of the mask build).
     if (!state_ready) hipLaunchKernelGGL(k_select_init, dim3(1), dim3(1024), 0, s, hist, sel, K);
     if (K > 0) {
         int64_t g = (n / 4 + kRadixThreads - 1) / kRadixThreads;
         g = g < 1 ? 1 : (g > 256 ? 256 : g);
-        for (int pass = 0; pass < 3; ++pass)
+        for (int pass = state_ready ? 1 : 0; pass < 3; ++pass)
             hipLaunchKernelGGL(k_radix_pass, dim3((unsigned)g), dim3(kRadixThreads), 0, s, p, n,
                                sel, hist, pass);
-        hipLaunchKernelGGL(k_radix_final, dim3(1), dim3(kRadixThreads), 0, s, hist, sel);
     }
+    // The last digit step (the cut) is taken by the count launch.
     int32_t *agg = reinterpret_cast<int32_t *>(ws + w.row_agg);
     const unsigned row_grid = (unsigned)((rows + kCompactRows - 1) / kCompactRows);
-    hipLaunchKernelGGL(k_row_count, dim3(row_grid), dim3(1024), 0, s, p, D.nb, rows, rows, sel, gt,
-                       eq, agg);
+    hipLaunchKernelGGL(k_row_count, dim3(row_grid), dim3(1024), 0, s, p, D.nb, rows, rows, sel,
+                       K > 0 ? hist + 2 * kRadixBins : nullptr, gt, eq, agg);
     hipLaunchKernelGGL(k_row_emit, dim3(row_grid), dim3(1024), 0, s, p, D.nb, rows, K, sel, gt, eq,
                        agg, row_ptr, col_idx);
     return hipGetLastError();
@@ -1007,7 +1139,8 @@ hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, ch
     hipLaunchKernelGGL(k_head_select, dim3(D.H), dim3(1024), 0, s, p, (int64_t)D.nb * D.nb, k_h,
                        hsel);
     hipLaunchKernelGGL(k_row_count, dim3((unsigned)((rows + kCompactRows - 1) / kCompactRows)),
-                       dim3(1024), 0, s, p, D.nb, rows, (int64_t)D.nb, hsel, gt, eq, nullptr);
+                       dim3(1024), 0, s, p, D.nb, rows, (int64_t)D.nb, hsel, nullptr, gt, eq,
+                       nullptr);
     hipLaunchKernelGGL(k_head_ties, dim3(D.H), dim3(1024), 0, s, gt, eq, D.nb, hsel, tie_base);
     hipLaunchKernelGGL(k_kept_scan, dim3(1), dim3(1024), 0, s, gt, rows, row_ptr);
     hipLaunchKernelGGL(k_row_scatter, dim3(row_grid), dim3(256), 0, s, p, D.nb, rows,
@@ -1021,8 +1154,12 @@ hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, const int32_t *col
     int4 *work_rec = reinterpret_cast<int4 *>(ws + w.work_rec);
     int32_t *meta = reinterpret_cast<int32_t *>(ws + w.work_meta);
     int32_t *head_base = reinterpret_cast<int32_t *>(ws + w.plan_head_base);
+    // Every die load fits in 28 bits when the weight of the whole mask does
+    // (for a well-formed mask the list lengths add up to nnz; a malformed one
+    // only gets another valid assignment of heads to dies).
+    const bool narrow = (int64_t)(D.B / 32) * nnz + 4 * D.rows() < ((int64_t)1 << 28);
     hipLaunchKernelGGL(k_plan_assign, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, col_idx, nnz,
-                       D.H, D.nb, D.B / 32, head_base, work, work_rec, meta);
+                       D.H, D.nb, D.B / 32, narrow, head_base, work, work_rec, meta);
     hipLaunchKernelGGL(k_plan_rows, dim3(D.H), dim3(64), 0, s, row_ptr, col_idx, nnz, D.nb,
                        head_base, work, work_rec);
     return hipGetLastError();
