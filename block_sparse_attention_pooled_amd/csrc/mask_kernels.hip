@@ -142,18 +142,22 @@ __device__ void select_init(uint32_t *__restrict__ hist, uint32_t *__restrict__ 
 
 // ---------------------------------------------------------- score + softmax --
 // A workgroup of 512 threads owns 16 query-block rows of one head.  Key-block
-// means stream through LDS 64 rows at a time (read once per 16 rows), each
-// thread's loads in flight together.  Thread (r, jj) forms two dot products
-// at once, row r against tile columns jj and jj + 32, each in ascending c with
-// separately rounded multiply and add.  The scaled scores of the 16 rows wait
-// in LDS (up to kMaxBlocks per row: 105 KB in all, within gfx950's 160 KB per
-// workgroup); then each row is softmaxed by its 32 lanes and written once.
-// With hist0 set, the workgroup also counts its scores into the histogram of
-// the first digit of the global select (bits 31..21 of the order keys; the
-// pool launch zeroed it), so the select starts at its second digit.
+// means stream through LDS 128 rows at a time (read once per 16 rows; the
+// next 128 are loaded into registers while the current ones are used).  Wave
+// w forms the products of rows 2w and 2w + 1, lane c of it those of columns c
+// and c + 64 of the tile: each operand is one 16-byte LDS read per four
+// elements (rows padded by four floats so that the lanes' reads hit distinct
+// banks), and each dot product is summed in ascending element order with
+// separately rounded multiply and add, then scaled.  Each wave softmaxes its
+// own two rows (lane l takes columns l + 64 t, then a butterfly over the
+// wave): rows of at most 128 blocks straight from registers, wider rows from
+// LDS (up to kMaxBlocks per row), in the same order.  With hist0 set, the
+// workgroup also counts its scores into the histogram of the first digit of
+// the global select (bits 31..21 of the order keys; the pool launch zeroed
+// it), so the select starts at its second digit.
 constexpr int kScoreRows = 16;
-constexpr int kScoreCols = 64;
-constexpr int kScoreThreads = kScoreRows * 32;
+constexpr int kScoreCols = 128;
+constexpr int kScoreThreads = 512;
 
 template <int D>
 __global__ __launch_bounds__(kScoreThreads) void k_scores(const float *__restrict__ qb,
@@ -163,13 +167,12 @@ __global__ __launch_bounds__(kScoreThreads) void k_scores(const float *__restric
                                                           float sigma,
                                                           uint32_t *__restrict__ hist0) {
 #pragma clang fp contract(off)
-    __shared__ float sq[kScoreRows][D];
-    __shared__ float sk[kScoreCols][D + 1];
+    constexpr int SP = D + 4;   // padded LDS row (floats)
+    static_assert(kScoreCols * SP >= kRadixBins, "the first-digit histogram reuses the key tile");
+    __shared__ __attribute__((aligned(16))) float sq[kScoreRows * SP];
+    __shared__ __attribute__((aligned(16))) float sk[kScoreCols * SP];
     __shared__ float srow[kScoreRows][kMaxBlocks];
-    __shared__ uint32_t hh[kRadixBins];
     const int tid = threadIdx.x;
-    if (hist0)
-        for (int b = tid; b < kRadixBins; b += kScoreThreads) hh[b] = 0;
     const int tiles = (nb + kScoreRows - 1) / kScoreRows;
     // Workgroups go round-robin to the 8 dies, each with its own L2: renumber
     // so that consecutive tiles (one head's rows, sharing its key means) run
@@ -179,94 +182,155 @@ __global__ __launch_bounds__(kScoreThreads) void k_scores(const float *__restric
     const int h = bid / tiles;
     const int i0 = (bid % tiles) * kScoreRows;
     const int g = h / G;
-    constexpr int Q4 = (kScoreRows * D / 4 + kScoreThreads - 1) / kScoreThreads;
-    constexpr int K4 = kScoreCols * D / 4 / kScoreThreads;
-    {
-        float4 v[Q4];
+    constexpr int C4 = D / 4;   // float4 per row
+    constexpr int Q4 = (kScoreRows * C4 + kScoreThreads - 1) / kScoreThreads;
+    constexpr int K4 = kScoreCols * C4 / kScoreThreads;
 #pragma unroll
-        for (int t = 0; t < Q4; ++t) {
-            const int x = tid + kScoreThreads * t, r = x / (D / 4), c4 = x % (D / 4);
-            v[t] = (r < kScoreRows && i0 + r < nb)
-                       ? reinterpret_cast<const float4 *>(qb + ((int64_t)h * nb + i0 + r) * D)[c4]
-                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        }
-#pragma unroll
-        for (int t = 0; t < Q4; ++t) {
-            const int x = tid + kScoreThreads * t, r = x / (D / 4), c4 = x % (D / 4);
-            if (r < kScoreRows) *reinterpret_cast<float4 *>(&sq[r][4 * c4]) = v[t];
-        }
+    for (int t = 0; t < Q4; ++t) {
+        const int x = tid + kScoreThreads * t, r = x / C4, c4 = x % C4;
+        if (r < kScoreRows)
+            *reinterpret_cast<float4 *>(&sq[r * SP + 4 * c4]) =
+                i0 + r < nb
+                    ? reinterpret_cast<const float4 *>(qb + ((int64_t)h * nb + i0 + r) * D)[c4]
+                    : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    const int r = tid / 32, jj = tid % 32;
+    float4 kv[K4];
+    auto load_keys = [&](int j0) {
+#pragma unroll
+        for (int t = 0; t < K4; ++t) {
+            const int x = tid + kScoreThreads * t, rr = x / C4, c4 = x % C4;
+            kv[t] = j0 + rr < nb ? reinterpret_cast<const float4 *>(
+                                       kb + ((int64_t)g * nb + j0 + rr) * D)[c4]
+                                 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    };
+    load_keys(0);
+    const int w2 = 2 * (tid >> 6), cl = tid & 63;
+    const float *q0 = sq + w2 * SP, *q1 = q0 + SP;
+    const float *k0 = sk + cl * SP, *k1 = sk + (cl + 64) * SP;
+    float s00 = 0.0f, s01 = 0.0f, s10 = 0.0f, s11 = 0.0f;
     for (int j0 = 0; j0 < nb; j0 += kScoreCols) {
-        float4 v[K4];
+        __syncthreads();   // the previous tile's reads are done
 #pragma unroll
         for (int t = 0; t < K4; ++t) {
-            const int x = tid + kScoreThreads * t, rr = x / (D / 4), c4 = x % (D / 4);
-            v[t] = (j0 + rr < nb) ? reinterpret_cast<const float4 *>(
-                                        kb + ((int64_t)g * nb + j0 + rr) * D)[c4]
-                                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            const int x = tid + kScoreThreads * t, rr = x / C4, c4 = x % C4;
+            *reinterpret_cast<float4 *>(&sk[rr * SP + 4 * c4]) = kv[t];
         }
         __syncthreads();
-#pragma unroll
-        for (int t = 0; t < K4; ++t) {
-            const int x = tid + kScoreThreads * t, rr = x / (D / 4), c4 = x % (D / 4);
-            sk[rr][4 * c4] = v[t].x;
-            sk[rr][4 * c4 + 1] = v[t].y;
-            sk[rr][4 * c4 + 2] = v[t].z;
-            sk[rr][4 * c4 + 3] = v[t].w;
+        if (j0 + kScoreCols < nb) load_keys(j0 + kScoreCols);
+        s00 = s01 = s10 = s11 = 0.0f;
+#pragma unroll 8
+        for (int c = 0; c < D; c += 4) {
+            const float4 x0 = *reinterpret_cast<const float4 *>(q0 + c);
+            const float4 x1 = *reinterpret_cast<const float4 *>(q1 + c);
+            const float4 y0 = *reinterpret_cast<const float4 *>(k0 + c);
+            const float4 y1 = *reinterpret_cast<const float4 *>(k1 + c);
+            s00 = s00 + x0.x * y0.x; s01 = s01 + x0.x * y1.x;
+            s10 = s10 + x1.x * y0.x; s11 = s11 + x1.x * y1.x;
+            s00 = s00 + x0.y * y0.y; s01 = s01 + x0.y * y1.y;
+            s10 = s10 + x1.y * y0.y; s11 = s11 + x1.y * y1.y;
+            s00 = s00 + x0.z * y0.z; s01 = s01 + x0.z * y1.z;
+            s10 = s10 + x1.z * y0.z; s11 = s11 + x1.z * y1.z;
+            s00 = s00 + x0.w * y0.w; s01 = s01 + x0.w * y1.w;
+            s10 = s10 + x1.w * y0.w; s11 = s11 + x1.w * y1.w;
         }
-        __syncthreads();
-        float d0 = 0.0f, d1 = 0.0f;
-        for (int c = 0; c < D; ++c) {
-            const float a = sq[r][c];
-            float p0 = a * sk[jj][c], p1 = a * sk[jj + 32][c];
-            d0 = d0 + p0;
-            d1 = d1 + p1;
+        s00 = s00 * sigma;
+        s01 = s01 * sigma;
+        s10 = s10 * sigma;
+        s11 = s11 * sigma;
+        if (nb > kScoreCols) {   // wider rows wait in LDS
+            const int j = j0 + cl;
+            if (j < nb) {
+                srow[w2][j] = s00;
+                srow[w2 + 1][j] = s10;
+            }
+            if (j + 64 < nb) {
+                srow[w2][j + 64] = s01;
+                srow[w2 + 1][j + 64] = s11;
+            }
         }
-        const int j = j0 + jj;
-        if (j < nb) srow[r][j] = d0 * sigma;
-        if (j + 32 < nb) srow[r][j + 32] = d1 * sigma;
     }
+    uint32_t *hh = reinterpret_cast<uint32_t *>(sk);   // free once the products are done
     __syncthreads();
-    const bool row_ok = i0 + r < nb;
-    if (row_ok) {
-        float m = -INFINITY;
-        for (int j = jj; j < nb; j += 32) m = fmaxf(m, srow[r][j]);
+    if (hist0)
+        for (int b = tid; b < kRadixBins; b += kScoreThreads) hh[b] = 0;
+    // Softmax of rows w2 and w2 + 1 by the wave that formed them: lane l
+    // takes columns l + 64 t (t ascending), then a 6-level butterfly over the
+    // wave.  Rows of at most 128 blocks are still in registers (lane l holds
+    // columns l and l + 64); wider rows are read back from LDS in the same
+    // order, so both give the same sums.
+    const int64_t base0 = ((int64_t)h * nb + i0 + w2) * nb;
+    const bool ok0 = i0 + w2 < nb, ok1 = i0 + w2 + 1 < nb;
+    auto wave_max = [](float x) {
 #pragma unroll
-        for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
-        float sum = 0.0f;
-        for (int j = jj; j < nb; j += 32) {
-            float e = expf(srow[r][j] - m);
-            srow[r][j] = e;
-            sum = sum + e;
-        }
+        for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+        return x;
+    };
+    auto wave_fsum = [](float x) {
 #pragma unroll
-        for (int o = 16; o > 0; o >>= 1) sum = sum + __shfl_xor(sum, o, 32);
-        const int64_t base = ((int64_t)h * nb + i0 + r) * nb;
-        for (int j = jj; j < nb; j += 32) {
-            float v = srow[r][j] / sum;
-            srow[r][j] = v;
-            p[base + j] = v;
-            if (copy) copy[base + j] = v;
+        for (int o = 32; o > 0; o >>= 1) x = x + __shfl_xor(x, o);
+        return x;
+    };
+    if (nb <= kScoreCols) {
+        const bool v0 = cl < nb, v1 = cl + 64 < nb;
+        const float m0 = wave_max(fmaxf(v0 ? s00 : -INFINITY, v1 ? s01 : -INFINITY));
+        const float m1 = wave_max(fmaxf(v0 ? s10 : -INFINITY, v1 ? s11 : -INFINITY));
+        const float e00 = v0 ? expf(s00 - m0) : 0.0f, e01 = v1 ? expf(s01 - m0) : 0.0f;
+        const float e10 = v0 ? expf(s10 - m1) : 0.0f, e11 = v1 ? expf(s11 - m1) : 0.0f;
+        const float z0 = wave_fsum(e00 + e01), z1 = wave_fsum(e10 + e11);
+        const float p00 = e00 / z0, p01 = e01 / z0, p10 = e10 / z1, p11 = e11 / z1;
+        if (ok0) {
+            if (v0) p[base0 + cl] = p00;
+            if (v1) p[base0 + cl + 64] = p01;
+            if (copy && v0) copy[base0 + cl] = p00;
+            if (copy && v1) copy[base0 + cl + 64] = p01;
         }
-    }
-    if (!hist0) return;
-    // First-digit histogram of this tile's scores: a wave's lanes that share a
-    // bin (the scores of a row crowd into a few) add with one atomic.
-    const int lane = tid & 63;
-    for (int j0 = 0; j0 < nb; j0 += 32) {
-        const int j = j0 + jj;
-        const bool valid = row_ok && j < nb;
-        const uint32_t bin = valid ? order_key(srow[r][j]) >> 21 : 0u;
-        uint64_t todo = __ballot(valid);
-        for (int round = 0; round < 2 && todo; ++round) {
-            const int leader = __builtin_ctzll(todo);
-            const uint32_t lb = __builtin_amdgcn_readlane(bin, leader);
-            const uint64_t same = __ballot(valid && bin == lb) & todo;
-            if (lane == leader) atomicAdd(&hh[lb], (uint32_t)__popcll(same));
-            todo &= ~same;
+        if (ok1) {
+            if (v0) p[base0 + nb + cl] = p10;
+            if (v1) p[base0 + nb + cl + 64] = p11;
+            if (copy && v0) copy[base0 + nb + cl] = p10;
+            if (copy && v1) copy[base0 + nb + cl + 64] = p11;
         }
-        if ((todo >> lane) & 1) atomicAdd(&hh[bin], 1u);
+        if (!hist0) return;
+        __syncthreads();   // the histogram is zeroed
+        // First-digit histogram (bits 31..21 of the order keys).
+        if (ok0 && v0) atomicAdd(&hh[order_key(p00) >> 21], 1u);
+        if (ok0 && v1) atomicAdd(&hh[order_key(p01) >> 21], 1u);
+        if (ok1 && v0) atomicAdd(&hh[order_key(p10) >> 21], 1u);
+        if (ok1 && v1) atomicAdd(&hh[order_key(p11) >> 21], 1u);
+    } else {
+        float m0 = -INFINITY, m1 = -INFINITY;
+        for (int j = cl; j < nb; j += 64) {
+            m0 = fmaxf(m0, srow[w2][j]);
+            m1 = fmaxf(m1, srow[w2 + 1][j]);
+        }
+        m0 = wave_max(m0);
+        m1 = wave_max(m1);
+        float z0 = 0.0f, z1 = 0.0f;
+        for (int j = cl; j < nb; j += 64) {
+            const float e0 = expf(srow[w2][j] - m0), e1 = expf(srow[w2 + 1][j] - m1);
+            srow[w2][j] = e0;
+            srow[w2 + 1][j] = e1;
+            z0 = z0 + e0;
+            z1 = z1 + e1;
+        }
+        z0 = wave_fsum(z0);
+        z1 = wave_fsum(z1);
+        if (hist0) __syncthreads();   // the histogram is zeroed
+        for (int j = cl; j < nb; j += 64) {
+            const float a0 = srow[w2][j] / z0, a1 = srow[w2 + 1][j] / z1;
+            if (ok0) {
+                p[base0 + j] = a0;
+                if (copy) copy[base0 + j] = a0;
+                if (hist0) atomicAdd(&hh[order_key(a0) >> 21], 1u);
+            }
+            if (ok1) {
+                p[base0 + nb + j] = a1;
+                if (copy) copy[base0 + nb + j] = a1;
+                if (hist0) atomicAdd(&hh[order_key(a1) >> 21], 1u);
+            }
+        }
+        if (!hist0) return;
     }
     __syncthreads();
     for (int b = tid; b < kRadixBins; b += kScoreThreads)

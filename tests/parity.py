@@ -25,13 +25,13 @@ def score_rel_bound(nb):
         (at most 2u relative), so a numerator differs by at most 4u, and so
         does the exact sum of a row's terms;
       * row sums: the oracle adds the nb terms in order (error at most
-        (nb - 1) u relative, all terms positive), the GPU adds ceil(nb/32)
-        terms per lane and then 5 butterfly levels (at most
-        (ceil(nb/32) + 4) u);
+        (nb - 1) u relative, all terms positive), the GPU adds ceil(nb/64)
+        terms per lane and then 6 butterfly levels over the wave (at most
+        (ceil(nb/64) + 5) u);
       * each side's division rounds once (u each).
     First-order total, with 1% for the second-order terms."""
     u = 2.0 ** -24
-    return 1.01 * u * (4 + 4 + (nb - 1) + (-(-nb // 32) + 4) + 2)
+    return 1.01 * u * (4 + 4 + (nb - 1) + (-(-nb // 64) + 5) + 2)
 
 
 def keep_from_csr(row_ptr, col_idx, H, nb):
