@@ -92,11 +92,13 @@ int select_and_plan(const Dims &D, double sparsity, bool per_head, const float *
                     hipStream_t s) {
     const int64_t k_h = per_head ? keep_count_per_head(D, sparsity) : 0;
     const int64_t K = per_head ? k_h * D.H : keep_count(D, sparsity);
+    // The global budget's list launch also writes the plan's row records and
+    // head counts.
     int st = hip_status(
         per_head ? sd::launch_select_per_head(D, k_h, p, ws, w, row_ptr, col_idx, s)
-                 : sd::launch_select(D, K, p, ws, w, row_ptr, col_idx, state_ready, s));
+                 : sd::launch_select(D, K, p, ws, w, row_ptr, col_idx, state_ready, true, s));
     if (st) return st;
-    return hip_status(sd::launch_plan(D, row_ptr, col_idx, K, ws, w, s));
+    return hip_status(sd::launch_plan(D, row_ptr, col_idx, K, ws, w, !per_head, s));
 }
 
 int build_mask(const stepdllm_dims *dims, double sparsity, bool per_head, const uint16_t *q,
@@ -264,7 +266,7 @@ int stepdllm_plan(const stepdllm_dims *dims, const int32_t *row_ptr, const int32
     if (nnz < 0 || nnz > D.n_scores()) return STEPDLLM_EINVAL;
     WsLayout w = sd::ws_layout(D);
     if ((int64_t)ws_bytes < w.total) return STEPDLLM_EWORKSPACE;
-    return hip_status(sd::launch_plan(D, row_ptr, col_idx, nnz, static_cast<char *>(ws), w,
+    return hip_status(sd::launch_plan(D, row_ptr, col_idx, nnz, static_cast<char *>(ws), w, false,
                                       static_cast<hipStream_t>(stream)));
 }
 

@@ -60,7 +60,7 @@ struct Dims {
 // Workspace carve-up (byte offsets, 256-byte aligned).
 struct WsLayout {
     int64_t qb, kb, p, hist, sel, gt, eq, tie_base, work, work_meta, hsel, col_scores, col_stats,
-        col_part, col_q16, plan_head_base, work_rec, row_agg, total;
+        col_part, col_q16, plan_head_base, work_rec, row_agg, row_rec, head_counts, total;
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -88,6 +88,8 @@ inline WsLayout ws_layout(const Dims &D) {
     w.work_rec = take(kDies * D.die_cap() * 16);   // int4 record per work position
     // per compaction workgroup: above-cut and at-cut counts of its rows
     w.row_agg = take(2 * ((D.rows() + kCompactRows - 1) / kCompactRows) * 4);
+    w.row_rec = take(D.rows() * 16);               // each row's plan record, from the list launch
+    w.head_counts = take((int64_t)D.H * 8);        // each head's kept blocks, non-empty rows
     w.total = off;
     return w;
 }
@@ -112,8 +114,12 @@ hipError_t launch_pool(const Dims &D, const uint16_t *q, const uint16_t *k, floa
 // runs with state_ready and starts at the second digit.
 hipError_t launch_scores(const Dims &D, const float *qb, const float *kb, float *p, float *copy,
                          char *ws, const WsLayout &w, bool first_digit, hipStream_t s);
+// With plan_inputs set, the list launch also writes what launch_plan with
+// prepared set reads: each row's plan record (w.row_rec) and each head's kept
+// blocks and non-empty rows (w.head_counts).
 hipError_t launch_select(const Dims &D, int64_t K, const float *p, char *ws, const WsLayout &w,
-                         int32_t *row_ptr, int32_t *col_idx, bool state_ready, hipStream_t s);
+                         int32_t *row_ptr, int32_t *col_idx, bool state_ready, bool plan_inputs,
+                         hipStream_t s);
 // Uniform per-head budget: head h keeps its k_h largest scores.
 hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, char *ws,
                                   const WsLayout &w, int32_t *row_ptr, int32_t *col_idx,
@@ -121,8 +127,10 @@ hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, ch
 // Work order of the mask row_ptr / col_idx (nnz list entries): the row ids
 // into w.work and one record per position into w.work_rec (row, list begin,
 // list end, first two block ids in 16 bits each; row -1 for padding).
+// prepared: the row records and head counts come from the list launch
+// (launch_select with plan_inputs), not from row_ptr and col_idx.
 hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, const int32_t *col_idx,
-                       int64_t nnz, char *ws, const WsLayout &w, hipStream_t s);
+                       int64_t nnz, char *ws, const WsLayout &w, bool prepared, hipStream_t s);
 
 // Column-sparse variant.  Block means of Q only (mask_kernels.hip).
 hipError_t launch_pool_q(const Dims &D, const uint16_t *q, float *qb, hipStream_t s);

@@ -475,6 +475,8 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_pass(const float *__res
 // per-head one), kHeadSelWords apart.  With agg set, workgroup b also writes
 // its rows' sums of both counts to agg[2b], agg[2b + 1].
 
+// With zero_words set, workgroup 0 also clears n_zero words (the head counts
+// that k_row_emit adds to).
 // With final_hist set (global budget, K > 0), every workgroup first takes the
 // select's last digit step from the histogram of the last pass (cheaper than a
 // launch of its own); workgroup 0 records the cut, the count above it and the
@@ -485,9 +487,12 @@ __global__ __launch_bounds__(1024) void k_row_count(const float *__restrict__ p,
                                                     const uint32_t *__restrict__ final_hist,
                                                     int32_t *__restrict__ gt,
                                                     int32_t *__restrict__ eq,
-                                                    int32_t *__restrict__ agg) {
+                                                    int32_t *__restrict__ agg,
+                                                    int32_t *__restrict__ zero_words, int n_zero) {
     __shared__ int32_t sg[kCompactRows], se[kCompactRows];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (zero_words && blockIdx.x == 0)
+        for (int t = threadIdx.x; t < n_zero; t += 1024) zero_words[t] = 0;
     const int64_t r = (int64_t)blockIdx.x * kCompactRows + wave;
     uint32_t final_cut = 0;
     if (final_hist) {
@@ -540,7 +545,10 @@ __global__ __launch_bounds__(1024) void k_row_count(const float *__restrict__ p,
 // min(ties, ties met): the list start of workgroup b's first row is (above-cut
 // count of the rows before) + min(ties, cut ties before), both from the
 // per-workgroup sums of k_row_count.  Inside the workgroup the rows add up in
-// LDS.  K bounds col_idx.
+// LDS.  K bounds col_idx.  With rec_out set, each row's plan record goes to
+// rec_out[row] (row, list begin, list end, first two kept ids in 16 bits each,
+// as k_plan_rows forms it) and each head's kept blocks and non-empty rows are
+// added to head_counts[h], head_counts[H + h] (cleared by k_row_count).
 __global__ __launch_bounds__(1024) void k_row_emit(const float *__restrict__ p, int nb,
                                                    int64_t rows, int64_t K,
                                                    const uint32_t *__restrict__ sel,
@@ -548,8 +556,11 @@ __global__ __launch_bounds__(1024) void k_row_emit(const float *__restrict__ p, 
                                                    const int32_t *__restrict__ eq,
                                                    const int32_t *__restrict__ agg,
                                                    int32_t *__restrict__ row_ptr,
-                                                   int32_t *__restrict__ col_idx) {
+                                                   int32_t *__restrict__ col_idx,
+                                                   int4 *__restrict__ rec_out,
+                                                   int32_t *__restrict__ head_counts, int H) {
     __shared__ int64_t row_eq[kCompactRows], row_kept[kCompactRows];
+    __shared__ int32_t s_hk[kCompactRows], s_hn[kCompactRows];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t r = (int64_t)blockIdx.x * kCompactRows + wave;
     int64_t g_loc = 0, e_loc = 0;
@@ -570,28 +581,60 @@ __global__ __launch_bounds__(1024) void k_row_emit(const float *__restrict__ p, 
     int64_t take = ties - tie;
     take = take < 0 ? 0 : (take > my_eq ? my_eq : take);
     if (lane == 0) row_kept[wave] = my_gt + take;
+    if (tid < kCompactRows) s_hk[tid] = s_hn[tid] = 0;
     __syncthreads();
-    if (r >= rows) return;
-    int64_t out = g_before + (ties < e_before ? ties : e_before);
-    for (int w = 0; w < wave; ++w) out += row_kept[w];
-    if (lane == 0) {
-        row_ptr[r] = (int32_t)out;
-        if (r == rows - 1) row_ptr[rows] = (int32_t)(out + my_gt + take);
+    // The rows of this workgroup start at head h_first.
+    const int64_t h_first = (int64_t)blockIdx.x * kCompactRows / nb;
+    if (r < rows) {
+        int64_t out = g_before + (ties < e_before ? ties : e_before);
+        for (int w = 0; w < wave; ++w) out += row_kept[w];
+        const int64_t start = out, kept = my_gt + take;
+        if (lane == 0) {
+            row_ptr[r] = (int32_t)out;
+            if (r == rows - 1) row_ptr[rows] = (int32_t)(out + kept);
+        }
+        const uint64_t lt = lanemask_lt();
+        int id0 = 0, id1 = 0, seen = 0;
+        for (int j0 = 0; j0 < nb; j0 += 64) {
+            const int j = j0 + lane;
+            const bool valid = j < nb;
+            const uint32_t key = valid ? order_key(p[r * nb + j]) : 0u;
+            const bool is_eq = valid && key == cut;
+            const uint64_t eqm = __ballot(is_eq);
+            const int64_t my_tie = tie + __popcll(eqm & lt);
+            const bool keep = valid && (key > cut || (is_eq && my_tie < ties));
+            const uint64_t km = __ballot(keep);
+            const int64_t slot = out + __popcll(km & lt);
+            if (keep && slot < K) col_idx[slot] = j;   // K bounds the list; never exceeded
+            if (rec_out && seen < 2 && km) {   // the first two ids, for the record
+                const uint64_t km1 = km & (km - 1);
+                if (seen == 0) {
+                    id0 = j0 + __builtin_ctzll(km);
+                    if (km1) id1 = j0 + __builtin_ctzll(km1);
+                } else {
+                    id1 = j0 + __builtin_ctzll(km);
+                }
+                seen += km1 ? 2 : 1;
+            }
+            out += __popcll(km);
+            tie += __popcll(eqm);
+        }
+        // The row's plan record, as k_plan_rows forms it from the lists, and
+        // its share of its head's counts.
+        if (rec_out && lane == 0) {
+            const int lo = (int)max(start, (int64_t)0), hi = (int)min(start + kept, K);
+            const int a = min(max(id0, 0), nb - 1), b = min(max(id1, 0), nb - 1);
+            rec_out[r] = make_int4((int)r, lo, hi, a | (b << 16));
+            const int hl = (int)(r / nb - h_first);
+            atomicAdd(&s_hk[hl], (int32_t)kept);
+            atomicAdd(&s_hn[hl], kept > 0 ? 1 : 0);
+        }
     }
-    const uint64_t lt = lanemask_lt();
-    for (int j0 = 0; j0 < nb; j0 += 64) {
-        const int j = j0 + lane;
-        const bool valid = j < nb;
-        const uint32_t key = valid ? order_key(p[r * nb + j]) : 0u;
-        const bool is_eq = valid && key == cut;
-        const uint64_t eqm = __ballot(is_eq);
-        const int64_t my_tie = tie + __popcll(eqm & lt);
-        const bool keep = valid && (key > cut || (is_eq && my_tie < ties));
-        const uint64_t km = __ballot(keep);
-        const int64_t slot = out + __popcll(km & lt);
-        if (keep && slot < K) col_idx[slot] = j;   // K bounds the list; never exceeded
-        out += __popcll(km);
-        tie += __popcll(eqm);
+    if (!rec_out) return;
+    __syncthreads();
+    if (tid < kCompactRows && h_first + tid < H && (s_hk[tid] || s_hn[tid])) {
+        atomicAdd(&head_counts[h_first + tid], s_hk[tid]);
+        atomicAdd(&head_counts[H + h_first + tid], s_hn[tid]);
     }
 }
 
@@ -802,79 +845,25 @@ __global__ __launch_bounds__(1024) void k_col_compact(const float *__restrict__ 
 
 constexpr int kPlanThreads = 1024;
 
-__global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__restrict__ row_ptr,
-                                                              const int32_t *list, int64_t nnz,
-                                                              int H, int nb, int steps_per_block,
-                                                              bool narrow,
-                                                              int32_t *__restrict__ head_base,
-                                                              int32_t *__restrict__ work,
-                                                              int4 *__restrict__ work_rec,
-                                                              int32_t *__restrict__ meta) {
+// The die part of the plan, by one 1024-thread workgroup, from each head's
+// weight and count of non-empty rows (in LDS): the heads' ranks, the die
+// assignment, each head's first position among its die's non-empty rows and
+// among its die's empty rows (into head_base and the returned LDS copy), the
+// padding and the meta words.
+__device__ const int32_t *plan_dies(int H, int nb, bool narrow, const int32_t *list, int64_t nnz,
+                                    const int64_t *weight, const int32_t *ne,
+                                    int32_t *__restrict__ head_base, int32_t *__restrict__ work,
+                                    int4 *__restrict__ work_rec, int32_t *__restrict__ meta) {
     static_assert(kDies == 8, "the die loop covers 8 dies");
-    __shared__ int64_t weight[kMaxHeads];
-    __shared__ int32_t ne[kMaxHeads];
     __shared__ int32_t order[kMaxHeads];
     __shared__ int32_t die_of[kMaxHeads], slot_of[kMaxHeads];
     __shared__ int32_t die_list[kDies * kMaxHeads];   // die x's heads in slot order
     __shared__ int32_t die_heads[kDies];
+    __shared__ int32_t bases[2 * kMaxHeads];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    constexpr int kWaves = kPlanThreads / 64;
     const int cap_h = min(H, (H + kDies - 1) / kDies + 2);
     const int cap = cap_h * nb;   // below 2^31: 8 * cap <= 8 * H * nb
-    // Per head: rows that keep a block and blocks kept.  Thread t reads the
-    // bounds of rows 4u .. 4u + 3, u = t, t + 1024, ..., all in one batch per
-    // round; a wave's rows that fall in one head add with one LDS atomic.
-    __shared__ int32_t kept[kMaxHeads];
-    for (int h = tid; h < H; h += kPlanThreads) ne[h] = kept[h] = 0;
-    __syncthreads();
-    const int rows = H * nb;
-    for (int r0 = 0; r0 < rows; r0 += 4 * kPlanThreads) {
-        const int r = r0 + 4 * tid;
-        int v[5];
-#pragma unroll
-        for (int k = 0; k < 5; ++k) v[k] = row_ptr[min(r + k, rows)];
-        // Rows of the thread's first row's head are summed here; rows of later
-        // heads (only where a head boundary falls inside the four) add one by
-        // one below.
-        const int h_lo = min(r, rows - 1) / nb;
-        int ne_lo = 0, kept_lo = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int len = v[k + 1] - v[k];
-            if (r + k < rows && len > 0) {
-                if ((r + k) / nb == h_lo) {
-                    ++ne_lo;
-                    kept_lo += len;
-                } else {
-                    atomicAdd(&ne[(r + k) / nb], 1);
-                    atomicAdd(&kept[(r + k) / nb], len);
-                }
-            }
-        }
-        // Lanes of the wave with the same head add with one atomic.
-        uint64_t todo = __ballot(r < rows);
-        while (todo) {
-            const int leader = __builtin_ctzll(todo);
-            const int hl = __builtin_amdgcn_readlane(h_lo, leader);
-            const uint64_t same = __ballot(r < rows && h_lo == hl) & todo;
-            int a = (same >> lane) & 1 ? ne_lo : 0, b = (same >> lane) & 1 ? kept_lo : 0;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                a += __shfl_xor(a, o);
-                b += __shfl_xor(b, o);
-            }
-            if (lane == leader) {
-                atomicAdd(&ne[hl], a);
-                atomicAdd(&kept[hl], b);
-            }
-            todo &= ~same;
-        }
-    }
-    __syncthreads();
-    for (int h = tid; h < H; h += kPlanThreads)
-        weight[h] = (int64_t)steps_per_block * kept[h] + 4 * (int64_t)ne[h];
-    __syncthreads();
     for (int h = tid; h < H; h += kPlanThreads) {
         int rank = 0;
         for (int o = 0; o < H; ++o)
@@ -982,8 +971,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__r
                 em_before += nb - n_o;
             }
         }
-        head_base[2 * h] = x * cap + ne_before;
-        head_base[2 * h + 1] = x * cap + ne_die + em_before;
+        bases[2 * h] = head_base[2 * h] = x * cap + ne_before;
+        bases[2 * h + 1] = head_base[2 * h + 1] = x * cap + ne_die + em_before;
     }
     // Padding: the positions past each die's heads.
     for (int q = tid; q < kDies * cap; q += kPlanThreads) {
@@ -1006,12 +995,92 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__r
         meta[kMetaNb] = nb;
         meta[kMetaCheck] = 0;
     }
+    __syncthreads();
+    return bases;
+}
+
+
+__global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__restrict__ row_ptr,
+                                                              const int32_t *list, int64_t nnz,
+                                                              int H, int nb, int steps_per_block,
+                                                              bool narrow,
+                                                              const int32_t *head_counts,
+                                                              int32_t *__restrict__ head_base,
+                                                              int32_t *__restrict__ work,
+                                                              int4 *__restrict__ work_rec,
+                                                              int32_t *__restrict__ meta) {
+    __shared__ int64_t weight[kMaxHeads];
+    __shared__ int32_t ne[kMaxHeads];
+    const int tid = threadIdx.x, lane = tid & 63;
+    if (head_counts) {   // counted by the list launch
+        for (int h = tid; h < H; h += kPlanThreads)
+            weight[h] = (int64_t)steps_per_block * head_counts[h] + 4 * (int64_t)head_counts[H + h];
+        for (int h = tid; h < H; h += kPlanThreads) ne[h] = head_counts[H + h];
+        __syncthreads();
+        plan_dies(H, nb, narrow, list, nnz, weight, ne, head_base, work, work_rec, meta);
+        return;
+    }
+    // Per head: rows that keep a block and blocks kept.  Thread t reads the
+    // bounds of rows 4u .. 4u + 3, u = t, t + 1024, ..., all in one batch per
+    // round; a wave's rows that fall in one head add with one LDS atomic.
+    __shared__ int32_t kept[kMaxHeads];
+    for (int h = tid; h < H; h += kPlanThreads) ne[h] = kept[h] = 0;
+    __syncthreads();
+    const int rows = H * nb;
+    for (int r0 = 0; r0 < rows; r0 += 4 * kPlanThreads) {
+        const int r = r0 + 4 * tid;
+        int v[5];
+#pragma unroll
+        for (int k = 0; k < 5; ++k) v[k] = row_ptr[min(r + k, rows)];
+        // Rows of the thread's first row's head are summed here; rows of later
+        // heads (only where a head boundary falls inside the four) add one by
+        // one below.
+        const int h_lo = min(r, rows - 1) / nb;
+        int ne_lo = 0, kept_lo = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int len = v[k + 1] - v[k];
+            if (r + k < rows && len > 0) {
+                if ((r + k) / nb == h_lo) {
+                    ++ne_lo;
+                    kept_lo += len;
+                } else {
+                    atomicAdd(&ne[(r + k) / nb], 1);
+                    atomicAdd(&kept[(r + k) / nb], len);
+                }
+            }
+        }
+        // Lanes of the wave with the same head add with one atomic.
+        uint64_t todo = __ballot(r < rows);
+        while (todo) {
+            const int leader = __builtin_ctzll(todo);
+            const int hl = __builtin_amdgcn_readlane(h_lo, leader);
+            const uint64_t same = __ballot(r < rows && h_lo == hl) & todo;
+            int a = (same >> lane) & 1 ? ne_lo : 0, b = (same >> lane) & 1 ? kept_lo : 0;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                a += __shfl_xor(a, o);
+                b += __shfl_xor(b, o);
+            }
+            if (lane == leader) {
+                atomicAdd(&ne[hl], a);
+                atomicAdd(&kept[hl], b);
+            }
+            todo &= ~same;
+        }
+    }
+    __syncthreads();
+    for (int h = tid; h < H; h += kPlanThreads)
+        weight[h] = (int64_t)steps_per_block * kept[h] + 4 * (int64_t)ne[h];
+    __syncthreads();
+    plan_dies(H, nb, narrow, list, nnz, weight, ne, head_base, work, work_rec, meta);
 }
 
 __global__ __launch_bounds__(64) void k_plan_rows(const int32_t *__restrict__ row_ptr,
                                                   const int32_t *__restrict__ col_idx,
                                                   int64_t nnz, int nb,
                                                   const int32_t *__restrict__ head_base,
+                                                  const int4 *__restrict__ rec_in,
                                                   int32_t *__restrict__ work,
                                                   int4 *__restrict__ work_rec) {
     constexpr int kRowsPerLane = kMaxBlocks / 64;
@@ -1022,45 +1091,55 @@ __global__ __launch_bounds__(64) void k_plan_rows(const int32_t *__restrict__ ro
     const uint64_t lt = lanemask_lt();
     const int64_t r0 = (int64_t)h * nb;
     const int64_t ne_base = head_base[2 * h], em_base = head_base[2 * h + 1];
-    // Stage row_ptr[r0 .. r0 + nb] (loads issued together), then the lengths.
-    // A wave's LDS requests complete in order.
-    for (int c = 0; c <= nb; c += 512) {
-        int v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = row_ptr[r0 + min(c + lane + 64 * j, nb)];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (c + lane + 64 * j <= nb) nx[c + lane + 64 * j] = v[j];
-    }
-    // Records: list bounds clamped into [0, nnz], the first two ids of the
-    // list (all loads of a lane issued together).
-    int lo[kRowsPerLane], hi[kRowsPerLane], id0[kRowsPerLane], id1[kRowsPerLane];
-#pragma unroll
-    for (int t = 0; t < kRowsPerLane; ++t) {
-        const int i = lane + 64 * t;
-        lo[t] = hi[t] = id0[t] = id1[t] = 0;
-        if (i < nb) {
-            lo[t] = max(nx[i], 0);
-            hi[t] = (int)min((int64_t)nx[i + 1], nnz);
-            if (hi[t] > lo[t]) {
-                id0[t] = col_idx[lo[t]];
-                if (hi[t] - lo[t] > 1) id1[t] = col_idx[lo[t] + 1];
+    int my_ne = 0;
+    if (rec_in) {   // records formed by the list launch
+        for (int i = lane; i < nb; i += 64) {
+            const int4 rc = rec_in[r0 + i];
+            rec[i] = rc;
+            const int len = rc.z - rc.y;
+            ln[i] = (int16_t)min(max(len, 0), nb);
+            my_ne += len > 0;
+        }
+    } else {
+        // Stage row_ptr[r0 .. r0 + nb] (loads issued together), then the lengths.
+        // A wave's LDS requests complete in order.
+        for (int c = 0; c <= nb; c += 512) {
+            int v[8];
+    #pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = row_ptr[r0 + min(c + lane + 64 * j, nb)];
+    #pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (c + lane + 64 * j <= nb) nx[c + lane + 64 * j] = v[j];
+        }
+        // Records: list bounds clamped into [0, nnz], the first two ids of the
+        // list (all loads of a lane issued together).
+        int lo[kRowsPerLane], hi[kRowsPerLane], id0[kRowsPerLane], id1[kRowsPerLane];
+    #pragma unroll
+        for (int t = 0; t < kRowsPerLane; ++t) {
+            const int i = lane + 64 * t;
+            lo[t] = hi[t] = id0[t] = id1[t] = 0;
+            if (i < nb) {
+                lo[t] = max(nx[i], 0);
+                hi[t] = (int)min((int64_t)nx[i + 1], nnz);
+                if (hi[t] > lo[t]) {
+                    id0[t] = col_idx[lo[t]];
+                    if (hi[t] - lo[t] > 1) id1[t] = col_idx[lo[t] + 1];
+                }
             }
         }
-    }
-#pragma unroll
-    for (int t = 0; t < kRowsPerLane; ++t) {
-        const int i = lane + 64 * t;
-        if (i < nb) {
-            const int a = min(max(id0[t], 0), nb - 1), b = min(max(id1[t], 0), nb - 1);
-            rec[i] = make_int4((int)r0 + i, lo[t], hi[t], a | (b << 16));
+    #pragma unroll
+        for (int t = 0; t < kRowsPerLane; ++t) {
+            const int i = lane + 64 * t;
+            if (i < nb) {
+                const int a = min(max(id0[t], 0), nb - 1), b = min(max(id1[t], 0), nb - 1);
+                rec[i] = make_int4((int)r0 + i, lo[t], hi[t], a | (b << 16));
+            }
         }
-    }
-    int my_ne = 0;
-    for (int i = lane; i < nb; i += 64) {
-        const int64_t len = (int64_t)nx[i + 1] - nx[i];
-        ln[i] = (int16_t)min(max(len, (int64_t)0), (int64_t)nb);
-        my_ne += len > 0;
+        for (int i = lane; i < nb; i += 64) {
+            const int64_t len = (int64_t)nx[i + 1] - nx[i];
+            ln[i] = (int16_t)min(max(len, (int64_t)0), (int64_t)nb);
+            my_ne += len > 0;
+        }
     }
     const int ne_cnt = wave_sum(my_ne);   // the sorted order puts these first
     for (int l = lane; l <= nb; l += 64) nx[l] = 0;
@@ -1105,6 +1184,13 @@ __global__ __launch_bounds__(64) void k_plan_rows(const int32_t *__restrict__ ro
 
 // ------------------------------------------------------------------ launches --
 namespace {
+// Every die load fits in 28 bits when the weight of the whole mask does (for
+// a well-formed mask the list lengths add up to nnz; a malformed one only
+// gets another valid assignment of heads to dies).
+bool plan_narrow(const Dims &D, int64_t nnz) {
+    return (int64_t)(D.B / 32) * nnz + 4 * D.rows() < ((int64_t)1 << 28);
+}
+
 template <int D>
 void pool_launch(const Dims &Dm, const uint16_t *q, const uint16_t *k, float *qb, float *kb,
                  int64_t q_pairs, int64_t k_pairs, uint32_t *hist, uint32_t *sel, int64_t K,
@@ -1165,7 +1251,8 @@ hipError_t launch_scores(const Dims &D, const float *qb, const float *kb, float 
 }
 
 hipError_t launch_select(const Dims &D, int64_t K, const float *p, char *ws, const WsLayout &w,
-                         int32_t *row_ptr, int32_t *col_idx, bool state_ready, hipStream_t s) {
+                         int32_t *row_ptr, int32_t *col_idx, bool state_ready, bool plan_inputs,
+                         hipStream_t s) {
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + w.hist);
     uint32_t *sel = reinterpret_cast<uint32_t *>(ws + w.sel);
     int32_t *gt = reinterpret_cast<int32_t *>(ws + w.gt);
@@ -1184,10 +1271,15 @@ hipError_t launch_select(const Dims &D, int64_t K, const float *p, char *ws, con
     // The last digit step (the cut) is taken by the count launch.
     int32_t *agg = reinterpret_cast<int32_t *>(ws + w.row_agg);
     const unsigned row_grid = (unsigned)((rows + kCompactRows - 1) / kCompactRows);
+    int32_t *head_counts =
+        plan_inputs ? reinterpret_cast<int32_t *>(ws + w.head_counts) : nullptr;
     hipLaunchKernelGGL(k_row_count, dim3(row_grid), dim3(1024), 0, s, p, D.nb, rows, rows, sel,
-                       K > 0 ? hist + 2 * kRadixBins : nullptr, gt, eq, agg);
+                       K > 0 ? hist + 2 * kRadixBins : nullptr, gt, eq, agg, head_counts,
+                       2 * D.H);
     hipLaunchKernelGGL(k_row_emit, dim3(row_grid), dim3(1024), 0, s, p, D.nb, rows, K, sel, gt, eq,
-                       agg, row_ptr, col_idx);
+                       agg, row_ptr, col_idx,
+                       plan_inputs ? reinterpret_cast<int4 *>(ws + w.row_rec) : nullptr,
+                       head_counts, D.H);
     return hipGetLastError();
 }
 
@@ -1204,7 +1296,7 @@ hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, ch
                        hsel);
     hipLaunchKernelGGL(k_row_count, dim3((unsigned)((rows + kCompactRows - 1) / kCompactRows)),
                        dim3(1024), 0, s, p, D.nb, rows, (int64_t)D.nb, hsel, nullptr, gt, eq,
-                       nullptr);
+                       nullptr, nullptr, 0);
     hipLaunchKernelGGL(k_head_ties, dim3(D.H), dim3(1024), 0, s, gt, eq, D.nb, hsel, tie_base);
     hipLaunchKernelGGL(k_kept_scan, dim3(1), dim3(1024), 0, s, gt, rows, row_ptr);
     hipLaunchKernelGGL(k_row_scatter, dim3(row_grid), dim3(256), 0, s, p, D.nb, rows,
@@ -1213,19 +1305,19 @@ hipError_t launch_select_per_head(const Dims &D, int64_t k_h, const float *p, ch
 }
 
 hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, const int32_t *col_idx,
-                       int64_t nnz, char *ws, const WsLayout &w, hipStream_t s) {
+                       int64_t nnz, char *ws, const WsLayout &w, bool prepared, hipStream_t s) {
     int32_t *work = reinterpret_cast<int32_t *>(ws + w.work);
     int4 *work_rec = reinterpret_cast<int4 *>(ws + w.work_rec);
     int32_t *meta = reinterpret_cast<int32_t *>(ws + w.work_meta);
     int32_t *head_base = reinterpret_cast<int32_t *>(ws + w.plan_head_base);
-    // Every die load fits in 28 bits when the weight of the whole mask does
-    // (for a well-formed mask the list lengths add up to nnz; a malformed one
-    // only gets another valid assignment of heads to dies).
-    const bool narrow = (int64_t)(D.B / 32) * nnz + 4 * D.rows() < ((int64_t)1 << 28);
+    const int32_t *head_counts =
+        prepared ? reinterpret_cast<const int32_t *>(ws + w.head_counts) : nullptr;
+    const int4 *rec_in = prepared ? reinterpret_cast<const int4 *>(ws + w.row_rec) : nullptr;
     hipLaunchKernelGGL(k_plan_assign, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, col_idx, nnz,
-                       D.H, D.nb, D.B / 32, narrow, head_base, work, work_rec, meta);
+                       D.H, D.nb, D.B / 32, plan_narrow(D, nnz), head_counts, head_base, work,
+                       work_rec, meta);
     hipLaunchKernelGGL(k_plan_rows, dim3(D.H), dim3(64), 0, s, row_ptr, col_idx, nnz, D.nb,
-                       head_base, work, work_rec);
+                       head_base, rec_in, work, work_rec);
     return hipGetLastError();
 }
 

@@ -113,6 +113,24 @@ def test_plan_matches_oracle(shape):
     _check_records(m.buf.work_rec().cpu().numpy(), work_ref, rp, ci)
 
 
+@pytest.mark.parametrize("s", [0.0, 0.5, 0.93, 1.0])
+@pytest.mark.parametrize("shape", SHAPES, ids=SHAPE_IDS)
+def test_mask_build_plan_equals_plan_launch(shape, s):
+    """The global-budget mask build writes the lists and the work order in
+    one launch (per-head part in every workgroup, dies in the last one); a
+    separate plan launch on the lists it wrote gives the same work order,
+    records and meta words, including K = 0 and every block kept."""
+    H, Hkv, L, d, blk, _ = shape
+    q, k, v = _qkv(shape, 505)
+    m = PT.GpuMask(q, k, blk, s)
+    fused = (m.buf.work().clone(), m.buf.work_rec().clone(), m.buf.work_meta()[:8].clone())
+    B.plan(m.dims, m.buf.row_ptr, m.buf.col_idx, m.buf.ws, nnz=m.K)
+    torch.cuda.synchronize()
+    assert torch.equal(fused[0], m.buf.work())
+    assert torch.equal(fused[1], m.buf.work_rec())
+    assert torch.equal(fused[2], m.buf.work_meta()[:8])
+
+
 @pytest.mark.parametrize("H,nb,blk", [(64, 320, 64), (28, 129, 128), (3, 1024, 64), (13, 7, 128)])
 def test_plan_many_rows_and_lengths(H, nb, blk):
     """Injected lists with every length 0..nb, ragged head counts per die."""
