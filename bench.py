@@ -170,6 +170,22 @@ def sustained_mfma_rate():
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
+def data_path_rates():
+    """Run the package's data-path probe (built beside the library): buffer->LDS
+    fill and LDS read rates per CU at the attention kernel's occupancy, one
+    step's reads, fills and matrix products without the softmax, and a
+    streaming HBM read.  None if the probe is not built."""
+    import subprocess
+    exe = os.path.join(ROOT, "block_sparse_attention_pooled_amd", "path_rates")
+    if not os.path.exists(exe):
+        return None
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        print(f"bench.py: path_rates failed: {r.stderr.strip()}", file=sys.stderr)
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def cpu_baseline(inputs0, w, sparsity, flops_per_step, budget_s, per_head=False):
     """The oracle as it stands, on the host cores: one full mask build on step-0
     Q/K plus sparse attention on a deterministic sample of rows, extrapolated
@@ -703,6 +719,30 @@ def main():
             "probe": "block_sparse_attention_pooled_amd/mfma_rate"}
         if attn_tflops:
             roofline["frac_of_sustained_random"] = round(attn_tflops / rate["random"]["tflops"], 4)
+    # The path the K/V tiles take into each CU.  A row fills every kept
+    # block's K and V tiles (4*B*d bytes) into LDS once for its B queries, so
+    # a launch fills flops/B bytes: at 64-token blocks as many fill cycles per
+    # CU as matrix cycles per SIMD.
+    paths = data_path_rates()
+    if paths:
+        cus = paths["cus"]
+        fill_bytes = flops_step / w.B
+        step_flops_per_cu = 8 * 16 * 2 * 32 * 32 * 16   # 8 waves x 16 MFMAs per iteration
+        roofline["data_path"] = {
+            "probe": "block_sparse_attention_pooled_amd/path_rates",
+            "fill_bytes_per_launch": fill_bytes,
+            "fill_achieved_tbs": round(fill_bytes / (attn_ms * 1e-3) / 1e12, 3) if attn_ms else None,
+            "fill_bytes_per_clk_per_cu": paths["fill"]["bytes_per_clk_per_cu"],
+            "fill_peak_tbs": round(paths["fill"]["bytes_per_clk_per_cu"] * cus *
+                                   paths["fill"]["ghz"] / 1e3, 3),
+            "fill_ghz": paths["fill"]["ghz"],
+            "lds_read_bytes_per_clk_per_cu": {"b128": paths["b128"]["bytes_per_clk_per_cu"],
+                                              "tr16_b64": paths["tr"]["bytes_per_clk_per_cu"]},
+            "step_without_softmax_tflops": round(step_flops_per_cu * cus /
+                                                 paths["step"]["ns_per_iter"] / 1e3, 1),
+            "step_without_softmax_ghz": paths["step"]["ghz"],
+            "hbm_stream_read_gbs": paths["stream_read_128mib"]["gbs_median"],
+        }
 
     result = {
         "metric": (METRIC_COLS if args.columns else METRIC) if w.name == "stepdllm_8k" else

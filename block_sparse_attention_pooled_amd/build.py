@@ -11,10 +11,12 @@ CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["mask_kernels.hip", "attn_kernels.hip", "quality_kernels.hip", "col_kernels.hip",
            "api.hip", "noalloc.hip"]
 LIB = os.path.join(PKG, "libstepdllm.so")
-# A standalone measurement aid (sustained MFMA rate and shader clock), not
-# linked into the library.
-PROBE_SRC = "mfma_rate.hip"
-PROBE = os.path.join(PKG, "mfma_rate")
+# Standalone measurement aids, not linked into the library: the sustained
+# MFMA rate and shader clock, and the data-path rates (buffer->LDS fills, LDS
+# reads, a step's traffic with its matrix products, streaming HBM reads).
+PROBES = {"mfma_rate.hip": os.path.join(PKG, "mfma_rate"),
+          "path_rates.hip": os.path.join(PKG, "path_rates")}
+PROBE = PROBES["mfma_rate.hip"]
 BUILD_DIR = os.path.join(PKG, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -49,13 +51,14 @@ def build(extra_flags=(), verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
-    cmd = [HIPCC, *FLAGS, *extra_flags, os.path.join(CSRC, PROBE_SRC), "-o", PROBE + ".tmp"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stderr}")
-    os.replace(PROBE + ".tmp", PROBE)
+    for src, exe in PROBES.items():
+        cmd = [HIPCC, *FLAGS, *extra_flags, os.path.join(CSRC, src), "-o", exe + ".tmp"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        os.replace(exe + ".tmp", exe)
     if verbose:
-        print("built", LIB, "and", PROBE)
+        print("built", LIB, "and", ", ".join(PROBES.values()))
     return LIB
 
 
