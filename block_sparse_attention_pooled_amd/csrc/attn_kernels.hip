@@ -644,6 +644,16 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
         if (n_total > 2) issue_k(chunk_key0(2), kring + 2 * TILE);
     }
     sync();
+    // The row's first two list entries must still be the ones its record
+    // holds (col_idx rewritten after planning): otherwise the row writes
+    // zeros and flags bit 1 of the check word.  Lanes 0 and 1 of the first
+    // id load hold them, landed at the sync above, so the check adds no load.
+    bool list_changed = false;
+    if (SPARSE) {
+        const int c0 = min(max(__builtin_amdgcn_readlane(ids, 0), 0), nb - 1);
+        const int c1 = e_end - e_begin > 1 ? min(max(__builtin_amdgcn_readlane(ids, 1), 0), nb - 1) : 0;
+        list_changed = (c0 | (c1 << 16)) != rec_ids;
+    }
     const bool p0 = member(0), p1 = n_total > 1 && member(1);
     if (p0) read_k(kring, kf);
     if (p0) scores(kf, sA);
@@ -666,16 +676,7 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) l_run[nt] += __shfl_xor(l_run[nt], 32);
 
-    // The row's first two list entries must still be the ones its record
-    // holds (col_idx rewritten after planning): otherwise the row writes
-    // zeros and flags bit 1 of the check word.
-    bool list_changed = false;
-    if (SPARSE) {
-        const int c0 = min(max(col_idx[e_begin], 0), nb - 1);
-        const int c1 = e_end - e_begin > 1 ? min(max(col_idx[e_begin + 1], 0), nb - 1) : 0;
-        list_changed = (c0 | (c1 << 16)) != rec_ids;
-        if (list_changed && tid == 0) atomicOr(meta + kMetaCheck, kCheckListChanged);
-    }
+    if (list_changed && tid == 0) atomicOr(meta + kMetaCheck, kCheckListChanged);
 
     // O = O^T / l, rounded to bf16, staged through LDS so that every store
     // writes whole rows.  Lane holds query col (32*nt + col) and 4 consecutive
