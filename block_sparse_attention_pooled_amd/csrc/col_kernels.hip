@@ -10,12 +10,15 @@
 // query block i rounded to bf16 (the matrix-core input).  c estimates the
 // share of head h's attention that lands on key u; each head's row sums to 1.
 //
-// Pass 1 (k_col_part): one workgroup per (head, 32 pooled queries, 1024-key
-// split), four waves of eight 32-key chunks each; scores transposed
+// Pass 1 (k_col_part): one workgroup per (head, four tiles of 32 pooled
+// queries, 1024-key split); wave w takes tile w of the four and walks the
+// split's 32-key chunks in ascending order.  The four waves load the same K
+// chunks at about the same time, so the die's caches serve three of the four
+// loads and a head's K leaves HBM once per four tiles.  Scores are transposed
 // (S^T = K . Qb^T, lane = pooled query) so each lane keeps its query's running
-// max and normaliser in registers; the waves' states are merged in wave order
-// and written per split.  The split-0 workgroup also writes the tile's bf16
-// query fragments in MFMA lane order.  k_col_merge folds the splits in order.
+// max and normaliser in registers; each wave writes its tile's state per
+// split.  Split-0 workgroups also write their tiles' bf16 query fragments in
+// MFMA lane order.  k_col_merge folds the splits in order.
 // Pass 2 (k_col_mass): one wave per 32 keys, scores untransposed (S = Qb .
 // K^T, lane = key), so each lane adds its key's probabilities over the 16
 // pooled queries it holds, walking the head's query tiles in order with the
@@ -32,9 +35,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kColChunk = 32;       // keys per score tile
-constexpr int kPartWaves = 4;       // waves of a pass-1 workgroup
-constexpr int kPartChunksPerWave = 8;
-constexpr int kPartChunks = kPartWaves * kPartChunksPerWave;   // 1024 keys per split
+constexpr int kPartWaves = 4;       // waves (tiles of 32 pooled queries) of a pass-1 workgroup
+constexpr int kPartChunks = 32;     // 32-key chunks per split: 1024 keys
 constexpr int kMassWaves = 4;       // 32-key chunks per pass-2 workgroup
 
 // Pooled-query fragment: 8 consecutive fp32 dims rounded to bf16 (RNE); a
@@ -73,14 +75,16 @@ __global__ __launch_bounds__(kPartWaves * 64) void k_col_part(
     const float *__restrict__ qb, const uint16_t *__restrict__ k, float2 *__restrict__ part,
     uint4 *__restrict__ q16, int L, int nb, int G, int splits, float scale_log2) {
     constexpr int KS = D / 16;
-    __shared__ float2 wstate[kPartWaves][32];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, hh = lane >> 5;
     const int tiles = (nb + 31) / 32;
+    const int groups = (tiles + kPartWaves - 1) / kPartWaves;
     const int split = blockIdx.x % splits;
-    const int ht = blockIdx.x / splits;
-    const int h = ht / tiles, tile = ht % tiles, g = h / G;
+    const int hg = blockIdx.x / splits;
+    const int h = hg / groups, tile = (hg % groups) * kPartWaves + wave, g = h / G;
+    if (tile >= tiles) return;   // the head's last group has fewer tiles
+    const int ht = h * tiles + tile;
     const int r = tile * 32 + col;
     const bool valid = r < nb;
 
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(kPartWaves * 64) void k_col_part(
 #pragma unroll
     for (int s = 0; s < KS; ++s)
         qf[s] = pooled_frag(qb + ((int64_t)h * nb + (valid ? r : 0)) * D + 16 * s + 8 * hh, valid);
-    if (split == 0 && wave == 0) {
+    if (split == 0) {
         uint4 *dst = q16 + (int64_t)ht * KS * 64 + lane;
 #pragma unroll
         for (int s = 0; s < KS; ++s) dst[s * 64] = __builtin_bit_cast(uint4, qf[s]);
@@ -123,30 +127,23 @@ __global__ __launch_bounds__(kPartWaves * 64) void k_col_part(
         l = l * __builtin_amdgcn_exp2f(m - m_new) + acc;
         m = m_new;
     };
-    // This wave's chunks of the split: c0 + wave + kPartWaves * j.
+    // The split's chunks in ascending order, the next one's K in flight.
     const int n_chunks = L / kColChunk;
     const int c_end = min(n_chunks, (split + 1) * kPartChunks);
     bf16x8 ka[KS], kb[KS];
-    int c = split * kPartChunks + wave;
+    int c = split * kPartChunks;
     if (c < c_end) load_k(c, ka);
-    for (; c < c_end; c += 2 * kPartWaves) {
-        const int c1 = c + kPartWaves;
+    for (; c < c_end; c += 2) {
+        const int c1 = c + 1;
         if (c1 < c_end) load_k(c1, kb);
         pass1(ka);
         if (c1 < c_end) {
-            if (c1 + kPartWaves < c_end) load_k(c1 + kPartWaves, ka);
+            if (c1 + 1 < c_end) load_k(c1 + 1, ka);
             pass1(kb);
         }
     }
     merge_state(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
-    if (lane < 32) wstate[wave][lane] = make_float2(m, l);
-    __syncthreads();
-    if (wave == 0 && lane < 32 && valid) {
-        float M = -INFINITY, S = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kPartWaves; ++w) merge_state(M, S, wstate[w][lane].x, wstate[w][lane].y);
-        part[((int64_t)h * nb + r) * splits + split] = make_float2(M, S);
-    }
+    if (lane < 32 && valid) part[((int64_t)h * nb + r) * splits + split] = make_float2(m, l);
 }
 
 // Per pooled query: fold the key splits in split order -> (max, 1 / normaliser).
@@ -237,7 +234,8 @@ hipError_t launch_col_scores_t(const Dims &Dm, const float *qb, const uint16_t *
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int tiles = (Dm.nb + 31) / 32;
     const int splits = (int)Dm.col_splits();
-    hipLaunchKernelGGL((k_col_part<D>), dim3((unsigned)(Dm.H * tiles * splits)),
+    const int tile_groups = (tiles + kPartWaves - 1) / kPartWaves;
+    hipLaunchKernelGGL((k_col_part<D>), dim3((unsigned)(Dm.H * tile_groups * splits)),
                        dim3(kPartWaves * 64), 0, s, qb, k, part, q16, Dm.L, Dm.nb, Dm.G, splits,
                        scale_log2);
     hipLaunchKernelGGL(k_col_merge, dim3((unsigned)((Dm.rows() + 255) / 256)), dim3(256), 0, s,
