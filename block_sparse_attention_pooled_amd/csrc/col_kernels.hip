@@ -11,14 +11,15 @@
 // share of head h's attention that lands on key u; each head's row sums to 1.
 //
 // Pass 1 (k_col_part): one workgroup per (head, four tiles of 32 pooled
-// queries, 1024-key split); wave w takes tile w of the four and walks the
-// split's 32-key chunks in ascending order.  The four waves load the same K
-// chunks at about the same time, so the die's caches serve three of the four
-// loads and a head's K leaves HBM once per four tiles.  Scores are transposed
-// (S^T = K . Qb^T, lane = pooled query) so each lane keeps its query's running
-// max and normaliser in registers; each wave writes its tile's state per
-// split.  Split-0 workgroups also write their tiles' bf16 query fragments in
-// MFMA lane order.  k_col_merge folds the splits in order.
+// queries, 1024-key split); four waves per tile, each walking one quarter of
+// the split's 32-key chunks in ascending order (16 waves per workgroup hide
+// the chunk loads' latency).  The four waves of a quarter share each chunk
+// through LDS (one coalesced buffer->LDS copy of its 32 rows), so a head's K
+// is read once per four tiles.  Scores are transposed (S^T = K . Qb^T, lane = pooled query) so each lane keeps its
+// query's running max and normaliser in registers; the quarters' states are
+// merged in quarter order and written per split.  Split-0 workgroups also write
+// their tiles' bf16 query fragments in MFMA lane order.  k_col_merge folds the
+// splits in order.
 // Pass 2 (k_col_mass): one wave per 32 keys, scores untransposed (S = Qb .
 // K^T, lane = key), so each lane adds its key's probabilities over the 16
 // pooled queries it holds, walking the head's query tiles in order with the
@@ -35,7 +36,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kColChunk = 32;       // keys per score tile
-constexpr int kPartWaves = 4;       // waves (tiles of 32 pooled queries) of a pass-1 workgroup
+constexpr int kPartTiles = 4;       // tiles of 32 pooled queries per pass-1 workgroup
+constexpr int kPartParts = 4;       // waves per tile, each over a quarter of the split
 constexpr int kPartChunks = 32;     // 32-key chunks per split: 1024 keys
 constexpr int kMassWaves = 4;       // 32-key chunks per pass-2 workgroup
 
@@ -61,6 +63,14 @@ __device__ __forceinline__ bf16x8 pooled_frag(const float *p, bool valid) {
     return r;
 }
 
+// 16 bytes per lane from a buffer straight into LDS (64 lanes -> 1 KiB
+// contiguous at `lds`).
+__device__ __forceinline__ void col_load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint16_t *lds,
+                                               uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds,
+                                             16, voff, soff, 0, 0);
+}
+
 // Merge (m2, l2) into (m, l): maxima in log2 units, l sums of 2^(s - m).
 __device__ __forceinline__ void merge_state(float &m, float &l, float m2, float l2) {
     if (l2 > 0.0f) {   // an empty state is (-inf, 0)
@@ -71,41 +81,85 @@ __device__ __forceinline__ void merge_state(float &m, float &l, float m2, float 
 }
 
 template <int D>
-__global__ __launch_bounds__(kPartWaves * 64) void k_col_part(
+__global__ __launch_bounds__(kPartTiles * kPartParts * 64) void k_col_part(
     const float *__restrict__ qb, const uint16_t *__restrict__ k, float2 *__restrict__ part,
     uint4 *__restrict__ q16, int L, int nb, int G, int splits, float scale_log2) {
     constexpr int KS = D / 16;
+    constexpr int NSEG = D / 8;                 // 16-byte segments per K row
+    constexpr int RPL = 64 / NSEG;              // rows per 1 KiB load
+    constexpr int LOADS = kColChunk / RPL;      // 1 KiB loads per chunk
+    constexpr int WL = LOADS / kPartTiles;      // of which each wave of a quarter issues WL
+    constexpr int CHUNK = kColChunk * D;        // bf16 elements of a chunk
+    static_assert(LOADS % kPartTiles == 0, "a chunk's loads split evenly over a quarter's waves");
+    __shared__ float2 wstate[kPartParts - 1][kPartTiles][32];   // quarters 1.. states
+    // Two chunk stages per quarter: the next chunk lands while this one is used.
+    __shared__ __attribute__((aligned(16))) uint16_t ring[kPartParts][2][CHUNK];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slot = wave % kPartTiles, part_i = wave / kPartTiles;
     const int col = lane & 31, hh = lane >> 5;
     const int tiles = (nb + 31) / 32;
-    const int groups = (tiles + kPartWaves - 1) / kPartWaves;
+    const int groups = (tiles + kPartTiles - 1) / kPartTiles;
     const int split = blockIdx.x % splits;
     const int hg = blockIdx.x / splits;
-    const int h = hg / groups, tile = (hg % groups) * kPartWaves + wave, g = h / G;
-    if (tile >= tiles) return;   // the head's last group has fewer tiles
-    const int ht = h * tiles + tile;
+    const int h = hg / groups, tile = (hg % groups) * kPartTiles + slot, g = h / G;
+    // The head's last group can have fewer tiles: those waves still load
+    // their share of each chunk but compute nothing.
+    const bool active = tile < tiles;
+    const int ht = h * tiles + (active ? tile : 0);
     const int r = tile * 32 + col;
-    const bool valid = r < nb;
+    const bool valid = active && r < nb;
 
+    // The tile's bf16 query fragments: quarter 0 forms them from the fp32
+    // pooled means and shares them through LDS with the other quarters.
+    __shared__ uint4 qshare[kPartTiles][KS][64];
     bf16x8 qf[KS];
+    if (part_i == 0) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-        qf[s] = pooled_frag(qb + ((int64_t)h * nb + (valid ? r : 0)) * D + 16 * s + 8 * hh, valid);
-    if (split == 0) {
-        uint4 *dst = q16 + (int64_t)ht * KS * 64 + lane;
+        for (int s = 0; s < KS; ++s) {
+            qf[s] = pooled_frag(qb + ((int64_t)h * nb + (valid ? r : 0)) * D + 16 * s + 8 * hh,
+                                valid);
+            qshare[slot][s][lane] = __builtin_bit_cast(uint4, qf[s]);
+        }
+        if (split == 0 && active) {
+            uint4 *dst = q16 + (int64_t)ht * KS * 64 + lane;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) dst[s * 64] = __builtin_bit_cast(uint4, qf[s]);
+            for (int s = 0; s < KS; ++s) dst[s * 64] = __builtin_bit_cast(uint4, qf[s]);
+        }
     }
+    __syncthreads();
+    if (part_i != 0) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, qshare[slot][s][lane]);
+    }
+    // A chunk is 32 consecutive key rows, contiguous in memory: load t of the
+    // chunk copies rows RPL*t .. +RPL (1 KiB) into the stage, segment x of row
+    // w stored at x ^ (w % NSEG), so the fragment reads below hit distinct
+    // banks.  Reads past the key head return zeros.
     const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(k + (int64_t)g * L * D), 0, L * D * 2, 0x00020000);
-    const uint32_t k_voff = (uint32_t)(col * D * 2 + 16 * hh);
-    auto load_k = [&](int c, bf16x8 (&kf)[KS]) {
+    const int r_in = lane / NSEG, sp = lane % NSEG;
+    uint32_t voff[WL];
+#pragma unroll
+    for (int tt = 0; tt < WL; ++tt) {
+        const int w = (slot * WL + tt) * RPL + r_in;
+        voff[tt] = (uint32_t)(r_in * D * 2 + 16 * (sp ^ (w % NSEG)));
+    }
+    auto issue = [&](int c, uint16_t *dst) {
+#pragma unroll
+        for (int tt = 0; tt < WL; ++tt) {
+            const int t = slot * WL + tt;
+            col_load_lds16(k_rsrc, dst + t * 512, voff[tt],
+                           (uint32_t)(c * kColChunk * D * 2 + t * RPL * D * 2));
+        }
+    };
+    // K as the A operand: lane row = key col, dims 16*s + 8*hh.
+    auto read = [&](const uint16_t *kt, bf16x8 (&kf)[KS]) {
 #pragma unroll
         for (int s = 0; s < KS; ++s)
             kf[s] = __builtin_bit_cast(
-                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, k_voff,
-                                                              c * kColChunk * D * 2 + 32 * s, 0));
+                bf16x8, *reinterpret_cast<const uint4 *>(kt + col * D +
+                                                        8 * ((2 * s + hh) ^ (col % NSEG))));
     };
     // Running max m and sum l of 2^(s*scale - m) over this lane's keys (the
     // other 16 keys of each chunk are in lane ^ 32), log2 units.
@@ -127,23 +181,34 @@ __global__ __launch_bounds__(kPartWaves * 64) void k_col_part(
         l = l * __builtin_amdgcn_exp2f(m - m_new) + acc;
         m = m_new;
     };
-    // The split's chunks in ascending order, the next one's K in flight.
+    // This quarter's chunks in ascending order.  Every wave runs all steps (the
+    // barriers are common); a step reads its chunk, then starts the next
+    // chunk's loads into the other stage (read one step earlier), then forms
+    // the scores.  s_waitcnt fields: vmcnt 3:0 and 15:14, expcnt 6:4, lgkmcnt
+    // 11:8; 0x0070 waits for every load and LDS access.
+    constexpr int kPartLen = kPartChunks / kPartParts;
     const int n_chunks = L / kColChunk;
-    const int c_end = min(n_chunks, (split + 1) * kPartChunks);
-    bf16x8 ka[KS], kb[KS];
-    int c = split * kPartChunks;
-    if (c < c_end) load_k(c, ka);
-    for (; c < c_end; c += 2) {
-        const int c1 = c + 1;
-        if (c1 < c_end) load_k(c1, kb);
-        pass1(ka);
-        if (c1 < c_end) {
-            if (c1 + 1 < c_end) load_k(c1 + 1, ka);
-            pass1(kb);
-        }
+    const int c0 = split * kPartChunks + part_i * kPartLen;
+    const int c_lim = min(n_chunks, c0 + kPartLen);
+    if (c0 < c_lim) issue(c0, ring[part_i][0]);
+    for (int j = 0; j < kPartLen; ++j) {
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __syncthreads();
+        const int cj = c0 + j;
+        bf16x8 kf[KS];
+        if (active && cj < c_lim) read(ring[part_i][j & 1], kf);
+        if (cj + 1 < c_lim) issue(cj + 1, ring[part_i][(j + 1) & 1]);
+        if (active && cj < c_lim) pass1(kf);
     }
     merge_state(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
-    if (lane < 32 && valid) part[((int64_t)h * nb + r) * splits + split] = make_float2(m, l);
+    if (part_i > 0 && lane < 32) wstate[part_i - 1][slot][lane] = make_float2(m, l);
+    __syncthreads();
+    if (part_i == 0 && lane < 32 && valid) {
+#pragma unroll
+        for (int q = 0; q < kPartParts - 1; ++q)
+            merge_state(m, l, wstate[q][slot][lane].x, wstate[q][slot][lane].y);
+        part[((int64_t)h * nb + r) * splits + split] = make_float2(m, l);
+    }
 }
 
 // Per pooled query: fold the key splits in split order -> (max, 1 / normaliser).
@@ -234,9 +299,9 @@ hipError_t launch_col_scores_t(const Dims &Dm, const float *qb, const uint16_t *
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int tiles = (Dm.nb + 31) / 32;
     const int splits = (int)Dm.col_splits();
-    const int tile_groups = (tiles + kPartWaves - 1) / kPartWaves;
+    const int tile_groups = (tiles + kPartTiles - 1) / kPartTiles;
     hipLaunchKernelGGL((k_col_part<D>), dim3((unsigned)(Dm.H * tile_groups * splits)),
-                       dim3(kPartWaves * 64), 0, s, qb, k, part, q16, Dm.L, Dm.nb, Dm.G, splits,
+                       dim3(kPartTiles * kPartParts * 64), 0, s, qb, k, part, q16, Dm.L, Dm.nb, Dm.G, splits,
                        scale_log2);
     hipLaunchKernelGGL(k_col_merge, dim3((unsigned)((Dm.rows() + 255) / 256)), dim3(256), 0, s,
                        part, stats, Dm.rows(), splits);
