@@ -767,6 +767,16 @@ hipError_t launch_sparse_attn(const Dims &D, const uint16_t *q, const uint16_t *
 
 hipError_t launch_dense_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                              const uint16_t *v, uint16_t *o, hipStream_t s) {
+    // Dense rows have no block lists, so 128 queries can share every K/V tile
+    // (half the tile loads per flop).  Each wave still holds the same 32
+    // queries and walks the same 32-key chunks in the same order, so the
+    // output is the same as with 64-query workgroups, bit for bit.
+    if (D.B == 64 && D.L % 128 == 0) {
+        Dims D2 = D;
+        D2.B = 128;
+        D2.nb = D.L / 128;
+        return launch_attn<kModeDense>(D2, q, k, v, nullptr, nullptr, nullptr, 0, o, s);
+    }
     return launch_attn<kModeDense>(D, q, k, v, nullptr, nullptr, nullptr, 0, o, s);
 }
 
