@@ -15,11 +15,11 @@
 // the split's 32-key chunks in ascending order (16 waves per workgroup hide
 // the chunk loads' latency).  The four waves of a quarter share each chunk
 // through LDS (one coalesced buffer->LDS copy of its 32 rows), so a head's K
-// is read once per four tiles.  Scores are transposed (S^T = K . Qb^T, lane = pooled query) so each lane keeps its
-// query's running max and normaliser in registers; the quarters' states are
-// merged in quarter order and written per split.  Split-0 workgroups also write
-// their tiles' bf16 query fragments in MFMA lane order.  k_col_merge folds the
-// splits in order.
+// is read once per four tiles.  Scores are transposed (S^T = K . Qb^T, lane =
+// pooled query) so each lane keeps its query's running max and normaliser in
+// registers; the quarters' states are merged in quarter order and written per
+// split.  Split-0 workgroups also write their tiles' bf16 query fragments in
+// MFMA lane order.  k_col_merge folds the splits in order.
 // Pass 2 (k_col_mass): one wave per 32 keys, scores untransposed (S = Qb .
 // K^T, lane = key), so each lane adds its key's probabilities over the 16
 // pooled queries it holds, walking the head's query tiles in order with the
@@ -177,7 +177,8 @@ __global__ __launch_bounds__(kPartTiles * kPartParts * 64) void k_col_part(
         const float m_new = fmaxf(m, cm * scale_log2);
         float acc = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc += __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -m_new));
+        for (int i = 0; i < 16; ++i)
+            acc += __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -m_new));
         l = l * __builtin_amdgcn_exp2f(m - m_new) + acc;
         m = m_new;
     };
@@ -301,8 +302,8 @@ hipError_t launch_col_scores_t(const Dims &Dm, const float *qb, const uint16_t *
     const int splits = (int)Dm.col_splits();
     const int tile_groups = (tiles + kPartTiles - 1) / kPartTiles;
     hipLaunchKernelGGL((k_col_part<D>), dim3((unsigned)(Dm.H * tile_groups * splits)),
-                       dim3(kPartTiles * kPartParts * 64), 0, s, qb, k, part, q16, Dm.L, Dm.nb, Dm.G, splits,
-                       scale_log2);
+                       dim3(kPartTiles * kPartParts * 64), 0, s, qb, k, part, q16, Dm.L, Dm.nb,
+                       Dm.G, splits, scale_log2);
     hipLaunchKernelGGL(k_col_merge, dim3((unsigned)((Dm.rows() + 255) / 256)), dim3(256), 0, s,
                        part, stats, Dm.rows(), splits);
     const int n_chunks = Dm.L / kColChunk;

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(128) void k_path(const uint16_t *__restrict__ src,
         sacc[i] = 0.0f;
         for (int m = 0; m < 4; ++m) oacc[m][i] = 0.0f;
     }
-    const bf16x8 qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(base + lane * 16));
+    const bf16x8 qf =
+        __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(base + lane * 16));
     const bf16x8 pf =
         __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(base + 1024 + lane * 16));
     const uint64_t t0 = __builtin_amdgcn_s_memtime();
@@ -78,7 +79,8 @@ __global__ __launch_bounds__(128) void k_path(const uint16_t *__restrict__ src,
         if (B128) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(base + half + j * 1024 + lane * 16);
+                const uint4 v =
+                    *reinterpret_cast<const uint4 *>(base + half + j * 1024 + lane * 16);
                 kf[j] = __builtin_bit_cast(bf16x8, v);
                 if (!MF) x ^= v.x ^ v.y ^ v.z ^ v.w;
             }
@@ -115,13 +117,15 @@ __global__ __launch_bounds__(128) void k_path(const uint16_t *__restrict__ src,
             }
             f32x16 s = sacc;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf, s, 0, 0, 0);
+            for (int j = 0; j < 8; ++j)
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf, s, 0, 0, 0);
             sacc = s;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
-                    oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 * ks + m], pf, oacc[m], 0, 0, 0);
+                    oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 * ks + m], pf,
+                                                                      oacc[m], 0, 0, 0);
         }
         if (MODE == kFill) {
             asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // one iteration in flight
@@ -209,15 +213,17 @@ bool stream_rate(int grid, double &gbs_median, double &gbs_best) {
     uint32_t *sink = nullptr;
     bool good = ok(hipMalloc(&sink, (size_t)grid * 256 * 4), "hipMalloc");
     for (auto &b : bufs)
-        good = good && ok(hipMalloc(&b, bytes), "hipMalloc") && ok(hipMemset(b, 1, bytes), "hipMemset");
+        good = good && ok(hipMalloc(&b, bytes), "hipMalloc") &&
+               ok(hipMemset(b, 1, bytes), "hipMemset");
     hipEvent_t e0, e1;
-    good = good && ok(hipEventCreate(&e0), "hipEventCreate") && ok(hipEventCreate(&e1), "hipEventCreate");
+    good = good && ok(hipEventCreate(&e0), "hipEventCreate") &&
+           ok(hipEventCreate(&e1), "hipEventCreate");
     std::vector<float> ts;
     for (int r = 0; good && r < 48; ++r) {
         good = ok(hipEventRecord(e0, 0), "hipEventRecord");
         hipLaunchKernelGGL(k_stream, dim3(grid), dim3(256), 0, 0, bufs[r % 8], n16, sink);
-        good = good && ok(hipGetLastError(), "launch") && ok(hipEventRecord(e1, 0), "hipEventRecord") &&
-               ok(hipEventSynchronize(e1), "stream");
+        good = good && ok(hipGetLastError(), "launch") &&
+               ok(hipEventRecord(e1, 0), "hipEventRecord") && ok(hipEventSynchronize(e1), "stream");
         float ms = 0.0f;
         good = good && ok(hipEventElapsedTime(&ms, e0, e1), "hipEventElapsedTime");
         if (r >= 8) ts.push_back(ms);   // the first pass over each buffer is a warm-up
@@ -226,7 +232,8 @@ bool stream_rate(int grid, double &gbs_median, double &gbs_best) {
         std::sort(ts.begin(), ts.end());
         gbs_median = bytes / (double)ts[ts.size() / 2] / 1e6;
         gbs_best = bytes / (double)ts[0] / 1e6;
-        good = ok(hipEventDestroy(e0), "hipEventDestroy") && ok(hipEventDestroy(e1), "hipEventDestroy");
+        good = ok(hipEventDestroy(e0), "hipEventDestroy") &&
+               ok(hipEventDestroy(e1), "hipEventDestroy");
     }
     for (auto b : bufs)
         if (b) good = ok(hipFree(b), "hipFree") && good;
@@ -239,13 +246,15 @@ bool stream_rate(int grid, double &gbs_median, double &gbs_best) {
 int main() {
     hipDeviceProp_t prop;
     int dev = 0;
-    if (!ok(hipGetDevice(&dev), "hipGetDevice") || !ok(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties"))
+    if (!ok(hipGetDevice(&dev), "hipGetDevice") ||
+        !ok(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties"))
         return 1;
     const int cus = prop.multiProcessorCount, wgs = cus * 4;   // all resident at once
     uint16_t *src = nullptr;
     float *sink = nullptr;
     uint64_t *t = nullptr;
-    if (!ok(hipMalloc(&src, kSrcBytes), "hipMalloc") || !ok(hipMemset(src, 0x3c, kSrcBytes), "hipMemset") ||
+    if (!ok(hipMalloc(&src, kSrcBytes), "hipMalloc") ||
+        !ok(hipMemset(src, 0x3c, kSrcBytes), "hipMemset") ||
         !ok(hipMalloc(&sink, sizeof(float) * 128 * wgs), "hipMalloc") ||
         !ok(hipMalloc(&t, sizeof(uint64_t) * 2 * wgs), "hipMalloc"))
         return 1;
@@ -263,14 +272,20 @@ int main() {
     const double fill_b = 8.0 * 8192, read_b = 8.0 * 8192;
     std::printf("{\"cus\": %d, \"waves_per_cu\": 8, \"iters\": %d", cus, iters);
     for (int m = 0; m < kModes; ++m) {
-        std::printf(", \"%s\": {\"ns_per_iter\": %.1f, \"ghz\": %.3f, \"cycles_per_iter\": %.0f", kNames[m],
+        std::printf(", \"%s\": {\"ns_per_iter\": %.1f, \"ghz\": %.3f, \"cycles_per_iter\": %.0f",
+                    kNames[m],
                     r[m].ns_per_iter, r[m].ghz, r[m].cycles_per_iter);
-        if (m == kFill) std::printf(", \"bytes_per_clk_per_cu\": %.1f", fill_b / r[m].cycles_per_iter);
+        if (m == kFill)
+            std::printf(", \"bytes_per_clk_per_cu\": %.1f", fill_b / r[m].cycles_per_iter);
         if (m == kB128 || m == kTr)
             std::printf(", \"bytes_per_clk_per_cu\": %.1f", read_b / r[m].cycles_per_iter);
         std::printf("}");
     }
-    std::printf(", \"stream_read_128mib\": {\"gbs_median\": %.0f, \"gbs_best\": %.0f, \"frac_of_8tbs\": %.3f}}\n",
+    std::printf(", \"stream_read_128mib\": {\"gbs_median\": %.0f, \"gbs_best\": %.0f, "
+                "\"frac_of_8tbs\": %.3f}}\n",
                 med, best, med / 8000.0);
-    return ok(hipFree(src), "hipFree") && ok(hipFree(sink), "hipFree") && ok(hipFree(t), "hipFree") ? 0 : 1;
+    return ok(hipFree(src), "hipFree") && ok(hipFree(sink), "hipFree") &&
+                   ok(hipFree(t), "hipFree")
+               ? 0
+               : 1;
 }
