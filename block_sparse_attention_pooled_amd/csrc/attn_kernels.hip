@@ -651,8 +651,7 @@ __global__ __launch_bounds__(BLK / QW * 64 * (MODE == kModeGroup ? kGroupHeads :
     bool list_changed = false;
     if (SPARSE) {
         const int c0 = min(max(__builtin_amdgcn_readlane(ids, 0), 0), nb - 1);
-        const int c1 =
-            e_end - e_begin > 1 ? min(max(__builtin_amdgcn_readlane(ids, 1), 0), nb - 1) : 0;
+        const int c1 = e_end - e_begin > 1 ? min(max(__builtin_amdgcn_readlane(ids, 1), 0), nb - 1) : 0;
         list_changed = (c0 | (c1 << 16)) != rec_ids;
     }
     const bool p0 = member(0), p1 = n_total > 1 && member(1);
