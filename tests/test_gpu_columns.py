@@ -21,6 +21,7 @@ SHAPES = [
     (3, 1, 5 * 128, 64, 128, 1.5),
     (7, 7, 3 * 128, 128, 128, 0.7),
     (8, 8, 41 * 64, 128, 64, 3.0),     # 41 pooled queries: a ragged 32-query tile
+    (2, 2, 160 * 64, 64, 64, 1.0),     # 5 tiles: a second group of four with one tile
 ]
 SHAPE_IDS = [f"H{s[0]}kv{s[1]}L{s[2]}d{s[3]}B{s[4]}" for s in SHAPES]
 

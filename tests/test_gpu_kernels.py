@@ -20,6 +20,7 @@ SHAPES = [
     (2, 2, 33 * 64, 128, 64, 3.0),
     (4, 4, 128, 128, 128, 1.0),
     (7, 7, 3 * 128, 128, 128, 0.7),
+    (6, 2, 6 * 64, 128, 64, 1.2),      # GQA, 64-token blocks, L a multiple of 128
 ]
 SHAPE_IDS = [f"H{s[0]}kv{s[1]}L{s[2]}d{s[3]}B{s[4]}" for s in SHAPES]
 
