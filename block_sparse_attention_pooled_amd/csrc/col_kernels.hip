@@ -23,8 +23,9 @@
 // Pass 2 (k_col_mass): one wave per 32 keys, scores untransposed (S = Qb .
 // K^T, lane = key), so each lane adds its key's probabilities over the 16
 // pooled queries it holds, walking the head's query tiles in order with the
-// next tile's fragments in flight.  Both passes use v_mfma_f32_32x32x16_bf16
-// with fp32 accumulation; every sum is in a fixed order, so the result is
+// next tile's fragments in flight; its K chunk reaches LDS through coalesced
+// buffer->LDS loads.  Both passes use v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation; every sum is in a fixed order, so the result is
 // deterministic.
 #include "common.h"
 
@@ -232,16 +233,35 @@ __global__ __launch_bounds__(kMassWaves * 64) void k_col_mass(
     const float2 *__restrict__ stats, float *__restrict__ c, int L, int nb, int G,
     float scale_log2) {
     constexpr int KS = D / 16;
+    constexpr int NSEG = D / 8;                 // 16-byte segments per K row
+    constexpr int RPL = 64 / NSEG;              // rows per 1 KiB load
+    constexpr int LOADS = kColChunk / RPL;      // 1 KiB loads per chunk
+    constexpr int CHUNK = kColChunk * D;        // bf16 elements of a chunk
     __shared__ float2 st[kMaxBlocks];   // per pooled query: max, 1 / normaliser
+    __shared__ __attribute__((aligned(16))) uint16_t kl[kMassWaves][CHUNK];   // each wave's chunk
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, hh = lane >> 5;
     const int n_chunks = L / kColChunk;
     const int groups = (n_chunks + kMassWaves - 1) / kMassWaves;
     const int h = blockIdx.x / groups, grp = blockIdx.x % groups, g = h / G;
-    for (int i = tid; i < nb; i += kMassWaves * 64) st[i] = stats[(int64_t)h * nb + i];
-    __syncthreads();
     const int chunk = grp * kMassWaves + wave;
+    // This wave's chunk (32 contiguous key rows) into its own stage with
+    // coalesced buffer->LDS loads, segment x of row w stored at x ^ (w %
+    // NSEG); reads past the key head return zeros.
+    const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(k + (int64_t)g * L * D), 0, L * D * 2, 0x00020000);
+    const int r_in = lane / NSEG, sp = lane % NSEG;
+    if (chunk < n_chunks) {
+#pragma unroll
+        for (int t = 0; t < LOADS; ++t)
+            col_load_lds16(k_rsrc, kl[wave] + t * 512,
+                           (uint32_t)(r_in * D * 2 + 16 * (sp ^ ((t * RPL + r_in) % NSEG))),
+                           (uint32_t)(chunk * kColChunk * D * 2 + t * RPL * D * 2));
+    }
+    for (int i = tid; i < nb; i += kMassWaves * 64) st[i] = stats[(int64_t)h * nb + i];
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt 0, lgkmcnt 0: the chunk and the stats
+    __syncthreads();
     if (chunk >= n_chunks) return;
     const int key = chunk * kColChunk + col;
 
@@ -250,8 +270,8 @@ __global__ __launch_bounds__(kMassWaves * 64) void k_col_mass(
 #pragma unroll
     for (int s = 0; s < KS; ++s)
         kf[s] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4 *>(k + ((int64_t)g * L + key) * D + 16 * s +
-                                                     8 * hh));
+            bf16x8, *reinterpret_cast<const uint4 *>(kl[wave] + col * D +
+                                                    8 * ((2 * s + hh) ^ (col % NSEG))));
     // Query fragments of tile t, as pass 1 left them (lane order).
     const int tiles = (nb + 31) / 32;
     const uint4 *qh = q16 + (int64_t)h * tiles * KS * 64 + lane;
