@@ -783,6 +783,15 @@ hipError_t launch_dense_attn(const Dims &D, const uint16_t *q, const uint16_t *k
 hipError_t launch_col_attn(const Dims &D, const uint16_t *q, const uint16_t *k,
                            const uint16_t *v, const int32_t *cols, int64_t k_c, uint16_t *o,
                            hipStream_t s) {
+    // Every query block of a head attends to the head's same key columns, so
+    // 128 queries share each gathered K/V tile, as in dense mode (same output
+    // bit for bit).
+    if (D.B == 64 && D.L % 128 == 0) {
+        Dims D2 = D;
+        D2.B = 128;
+        D2.nb = D.L / 128;
+        return launch_attn<kModeCols>(D2, q, k, v, cols, nullptr, nullptr, (int)k_c, o, s);
+    }
     return launch_attn<kModeCols>(D, q, k, v, cols, nullptr, nullptr, (int)k_c, o, s);
 }
 
