@@ -186,6 +186,31 @@ def data_path_rates():
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
+def data_path_block(paths, flops_step, q_rows, attn_ms):
+    """The bench line's view of the path the K/V tiles take into each CU,
+    from the data-path probe's output.  A workgroup of q_rows query rows fills
+    each kept key block's K and V tiles (4*q_rows*d bytes for 4*q_rows^2*d
+    flops) into LDS once, so a launch fills flops/q_rows bytes."""
+    cus = paths["cus"]
+    fill_bytes = flops_step / q_rows
+    step_flops_per_cu = 8 * 16 * 2 * 32 * 32 * 16   # 8 waves x 16 MFMAs per iteration
+    return {
+        "probe": "block_sparse_attention_pooled_amd/path_rates",
+        "fill_bytes_per_launch": fill_bytes,
+        "fill_achieved_tbs": round(fill_bytes / (attn_ms * 1e-3) / 1e12, 3) if attn_ms else None,
+        "fill_bytes_per_clk_per_cu": paths["fill"]["bytes_per_clk_per_cu"],
+        "fill_peak_tbs": round(paths["fill"]["bytes_per_clk_per_cu"] * cus *
+                               paths["fill"]["ghz"] / 1e3, 3),
+        "fill_ghz": paths["fill"]["ghz"],
+        "lds_read_bytes_per_clk_per_cu": {"b128": paths["b128"]["bytes_per_clk_per_cu"],
+                                          "tr16_b64": paths["tr"]["bytes_per_clk_per_cu"]},
+        "step_without_softmax_tflops": round(step_flops_per_cu * cus /
+                                             paths["step"]["ns_per_iter"] / 1e3, 1),
+        "step_without_softmax_ghz": paths["step"]["ghz"],
+        "hbm_stream_read_gbs": paths["stream_read_128mib"]["gbs_median"],
+    }
+
+
 def cpu_baseline(inputs0, w, sparsity, flops_per_step, budget_s, per_head=False):
     """The oracle as it stands, on the host cores: one full mask build on step-0
     Q/K plus sparse attention on a deterministic sample of rows, extrapolated
@@ -722,30 +747,11 @@ def main():
             "probe": "block_sparse_attention_pooled_amd/mfma_rate"}
         if attn_tflops:
             roofline["frac_of_sustained_random"] = round(attn_tflops / rate["random"]["tflops"], 4)
-    # The path the K/V tiles take into each CU.  A row fills every kept
-    # block's K and V tiles (4*B*d bytes) into LDS once for its B queries, so
-    # a launch fills flops/B bytes: at 64-token blocks as many fill cycles per
-    # CU as matrix cycles per SIMD.
+    # The path the K/V tiles take into each CU: at 64-token blocks as many
+    # fill cycles per CU as matrix cycles per SIMD.
     paths = data_path_rates()
     if paths:
-        cus = paths["cus"]
-        fill_bytes = flops_step / w.B
-        step_flops_per_cu = 8 * 16 * 2 * 32 * 32 * 16   # 8 waves x 16 MFMAs per iteration
-        roofline["data_path"] = {
-            "probe": "block_sparse_attention_pooled_amd/path_rates",
-            "fill_bytes_per_launch": fill_bytes,
-            "fill_achieved_tbs": round(fill_bytes / (attn_ms * 1e-3) / 1e12, 3) if attn_ms else None,
-            "fill_bytes_per_clk_per_cu": paths["fill"]["bytes_per_clk_per_cu"],
-            "fill_peak_tbs": round(paths["fill"]["bytes_per_clk_per_cu"] * cus *
-                                   paths["fill"]["ghz"] / 1e3, 3),
-            "fill_ghz": paths["fill"]["ghz"],
-            "lds_read_bytes_per_clk_per_cu": {"b128": paths["b128"]["bytes_per_clk_per_cu"],
-                                              "tr16_b64": paths["tr"]["bytes_per_clk_per_cu"]},
-            "step_without_softmax_tflops": round(step_flops_per_cu * cus /
-                                                 paths["step"]["ns_per_iter"] / 1e3, 1),
-            "step_without_softmax_ghz": paths["step"]["ghz"],
-            "hbm_stream_read_gbs": paths["stream_read_128mib"]["gbs_median"],
-        }
+        roofline["data_path"] = data_path_block(paths, flops_step, inst_b, attn_ms)
 
     result = {
         "metric": (METRIC_COLS if args.columns else METRIC) if w.name == "stepdllm_8k" else

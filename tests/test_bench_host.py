@@ -102,3 +102,33 @@ def test_mask_build_bandwidth():
     assert abs(r["mask_build_gbs"] - want / 0.1e-3 / 1e9) < 0.1
     assert bench.mask_build_bandwidth(w, None, 0.136, False) == {}
     assert bench.mask_build_bandwidth(w, 0.236, 0.136, True) == {}
+
+
+def test_data_path_block_units():
+    """The data-path view of the bench line from a fixed probe output: a
+    64-query workgroup fills 4*64*d bytes of K/V per kept block for
+    4*64^2*d flops (bytes = flops/64); per-clock rates times CUs and clock
+    give TB/s; 8 waves x 16 MFMAs of 32x32x16 per CU and iteration give the
+    step's TFLOP/s."""
+    paths = {"cus": 256,
+             "fill": {"ns_per_iter": 491.6, "ghz": 2.301, "cycles_per_iter": 1131,
+                      "bytes_per_clk_per_cu": 57.9},
+             "b128": {"ns_per_iter": 138.9, "ghz": 2.180, "cycles_per_iter": 303,
+                      "bytes_per_clk_per_cu": 216.5},
+             "tr": {"ns_per_iter": 145.0, "ghz": 2.225, "cycles_per_iter": 323,
+                    "bytes_per_clk_per_cu": 203.1},
+             "step": {"ns_per_iter": 812.7, "ghz": 1.868, "cycles_per_iter": 1518},
+             "mfma": {"ns_per_iter": 525.0, "ghz": 1.993, "cycles_per_iter": 1046},
+             "stream_read_128mib": {"gbs_median": 5678, "gbs_best": 6226, "frac_of_8tbs": 0.71}}
+    kept, d = 52429, 128
+    flops = 4.0 * 64 * 64 * d * kept
+    out = bench.data_path_block(paths, flops, 64, 0.14)
+    assert out["fill_bytes_per_launch"] == kept * 2 * 64 * d * 2      # K and V tiles, bf16
+    assert abs(out["fill_achieved_tbs"] - kept * 2 * 64 * d * 2 / 0.14e-3 / 1e12) < 1e-3
+    assert abs(out["fill_peak_tbs"] - 57.9 * 256 * 2.301e9 / 1e12) < 1e-3
+    assert abs(out["step_without_softmax_tflops"] - 8 * 16 * 32768 * 256 / 812.7e-9 / 1e12) < 0.1
+    assert out["hbm_stream_read_gbs"] == 5678
+    # 128-query workgroups (dense and column launches) fill half the bytes.
+    assert bench.data_path_block(paths, flops, 128, 0.14)["fill_bytes_per_launch"] == \
+        out["fill_bytes_per_launch"] / 2
+    assert bench.data_path_block(paths, flops, 64, None)["fill_achieved_tbs"] is None
