@@ -410,7 +410,8 @@ __device__ __forceinline__ RadixState load_state(const uint32_t *__restrict__ se
 // the lanes of a wave that fall in one bin are counted with one atomic, for
 // up to two bins per element slot (the pooled scores crowd into a few bins of
 // the first digit), the rest one by one; its nonzero bins are then added to
-// the pass's global histogram.
+// the pass's global histogram.  The workgroup's first batch of scores does
+// not depend on the prefix: its loads are issued before the digit step.
 constexpr int kRadixThreads = 1024;
 
 __global__ __launch_bounds__(kRadixThreads) void k_radix_pass(const float *__restrict__ p,
@@ -420,6 +421,12 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_pass(const float *__res
                                                               int pass) {
     __shared__ uint32_t h[kRadixBins];
     const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t stride = (int64_t)gridDim.x * kRadixThreads;
+    const int64_t n4 = n >> 2;
+    const float4 *p4 = reinterpret_cast<const float4 *>(p);
+    const int64_t first = (int64_t)blockIdx.x * kRadixThreads;
+    const bool in0 = first + tid < n4;
+    const float4 v0 = in0 ? p4[first + tid] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (int b = tid; b < kRadixBins; b += kRadixThreads) h[b] = 0;
     RadixState st = load_state(sel, 0);
     if (pass > 0) {
@@ -449,10 +456,13 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_pass(const float *__res
         }
         if ((todo >> lane) & 1) atomicAdd(&h[bin], 1u);
     };
-    const int64_t stride = (int64_t)gridDim.x * kRadixThreads;
-    const int64_t n4 = n >> 2;
-    const float4 *p4 = reinterpret_cast<const float4 *>(p);
-    for (int64_t base = (int64_t)blockIdx.x * kRadixThreads; base < n4; base += stride) {
+    if (first < n4) {
+        count(v0.x, in0);
+        count(v0.y, in0);
+        count(v0.z, in0);
+        count(v0.w, in0);
+    }
+    for (int64_t base = first + stride; base < n4; base += stride) {
         const int64_t x = base + tid;
         const bool in = x < n4;
         const float4 v = in ? p4[x] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -494,9 +504,14 @@ __global__ __launch_bounds__(1024) void k_row_count(const float *__restrict__ p,
                                                     int32_t *__restrict__ zero_words, int n_zero) {
     __shared__ int32_t sg[kCompactRows], se[kCompactRows];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * kCompactRows + wave;
+    // The row's first 128 scores, loaded before the digit step they do not
+    // depend on.
+    const float *pr = p + r * nb;
+    const float pre0 = r < rows && lane < nb ? pr[lane] : 0.0f;
+    const float pre1 = r < rows && lane + 64 < nb ? pr[lane + 64] : 0.0f;
     if (zero_words && blockIdx.x == 0)
         for (int t = threadIdx.x; t < n_zero; t += 1024) zero_words[t] = 0;
-    const int64_t r = (int64_t)blockIdx.x * kCompactRows + wave;
     uint32_t final_cut = 0;
     if (final_hist) {
         const RadixState st = radix_step(final_hist, 2, load_state(sel, 2));
@@ -514,7 +529,7 @@ __global__ __launch_bounds__(1024) void k_row_count(const float *__restrict__ p,
         const uint32_t cut =
             final_hist ? final_cut : sel[(r / group_rows) * kHeadSelWords + SEL_CUT];
         for (int j = lane; j < nb; j += 64) {
-            uint32_t key = order_key(p[r * nb + j]);
+            const uint32_t key = order_key(j < 64 ? pre0 : (j < 128 ? pre1 : pr[j]));
             cg += key > cut;
             ce += key == cut;
         }
@@ -566,6 +581,14 @@ __global__ __launch_bounds__(1024) void k_row_emit(const float *__restrict__ p, 
     __shared__ int32_t s_hk[kCompactRows], s_hn[kCompactRows];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t r = (int64_t)blockIdx.x * kCompactRows + wave;
+    // Loads that do not depend on the scans below, issued first: the cut,
+    // the row's counts and its first 128 scores.
+    const uint32_t cut = sel[SEL_CUT];
+    const int64_t ties = sel[SEL_TIES];
+    const int64_t my_gt = r < rows ? gt[r] : 0, my_eq = r < rows ? eq[r] : 0;
+    const float *pr = p + r * nb;
+    const float pre0 = r < rows && lane < nb ? pr[lane] : 0.0f;
+    const float pre1 = r < rows && lane + 64 < nb ? pr[lane + 64] : 0.0f;
     int64_t g_loc = 0, e_loc = 0;
     for (int64_t b = tid; b < blockIdx.x; b += 1024) {
         g_loc += agg[2 * b];
@@ -574,9 +597,6 @@ __global__ __launch_bounds__(1024) void k_row_emit(const float *__restrict__ p, 
     int64_t g_before, e_before;
     block_exclusive_scan_1024(g_loc, &g_before);
     block_exclusive_scan_1024(e_loc, &e_before);
-    const uint32_t cut = sel[SEL_CUT];
-    const int64_t ties = sel[SEL_TIES];
-    const int64_t my_gt = r < rows ? gt[r] : 0, my_eq = r < rows ? eq[r] : 0;
     if (lane == 0) row_eq[wave] = my_eq;
     __syncthreads();
     int64_t tie = e_before;
@@ -601,7 +621,8 @@ __global__ __launch_bounds__(1024) void k_row_emit(const float *__restrict__ p, 
         for (int j0 = 0; j0 < nb; j0 += 64) {
             const int j = j0 + lane;
             const bool valid = j < nb;
-            const uint32_t key = valid ? order_key(p[r * nb + j]) : 0u;
+            const uint32_t key =
+                valid ? order_key(j0 == 0 ? pre0 : (j0 == 64 ? pre1 : pr[j])) : 0u;
             const bool is_eq = valid && key == cut;
             const uint64_t eqm = __ballot(is_eq);
             const int64_t my_tie = tie + __popcll(eqm & lt);
@@ -835,39 +856,39 @@ __global__ __launch_bounds__(1024) void k_col_compact(const float *__restrict__ 
 //    first two block ids (16 bits each, clamped into [0, nb)), so that a
 //    workgroup's first K/V loads need one load, not a chain of three; padding
 //    records have row -1.
-// Two launches.  k_plan_assign, one workgroup: the heads' weights from one
-// pass over row_ptr (rows summed per lane, then per wave and head, into LDS
+// Prepared (lists from the mask build, which also counted each head's kept
+// blocks and non-empty rows) and H <= kPlanHeadsMax: one launch,
+// k_plan_heads, one workgroup per head.  Every workgroup redoes the die part
+// from the heads' counts (the same values in every workgroup: a few hundred
+// LDS operations for a few dozen heads), takes its own head's two base
+// positions, writes its share of the padding (workgroup 0 the meta words),
+// then places its head's rows.  Otherwise two launches.  k_plan_assign, one
+// workgroup: the heads' weights (from the mask build's counts, or from one
+// pass over row_ptr: rows summed per lane, then per wave and head, into LDS
 // counters), their ranks, the die assignment by one wave (one lane per die,
 // the least-loaded open die by a cross-lane minimum), each head's first
 // position among its die's non-empty rows and among its die's empty rows, the
 // padding and the meta words (including the tag of the list the plan
-// describes).  k_plan_rows, one wave per head: the head's row records, its rows by list length descending, ties by
-// row id, with a stable counting sort (length histogram, descending bucket
-// starts, ranks among equal lengths from wave ballots), written straight to
-// the head's positions.
+// describes).  k_plan_rows, one wave per head: the head's row records, its
+// rows by list length descending, ties by row id, with a stable counting sort
+// (length histogram, descending bucket starts, ranks among equal lengths from
+// wave ballots), written straight to the head's positions.
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanHeadsThreads = 256;
+constexpr int kPlanHeadsMax = 256;
 
-// The die part of the plan, by one 1024-thread workgroup, from each head's
-// weight and count of non-empty rows (in LDS): the heads' ranks, the die
-// assignment, each head's first position among its die's non-empty rows and
-// among its die's empty rows (into head_base and the returned LDS copy), the
-// padding and the meta words.
-__device__ const int32_t *plan_dies(int H, int nb, bool narrow, const int32_t *list, int64_t nnz,
-                                    const int64_t *weight, const int32_t *ne,
-                                    int32_t *__restrict__ head_base, int32_t *__restrict__ work,
-                                    int4 *__restrict__ work_rec, int32_t *__restrict__ meta) {
+// The heads' ranks by weight (descending, ties by head id) by every thread of
+// the block, then the die assignment by wave 0: die_of[h], slot_of[h],
+// die_list[x * cap_h + slot] (die x's heads in slot order), die_heads[x].
+// Ends with the block synchronised.
+__device__ void assign_dies(int H, bool narrow, int cap_h, const int64_t *weight, int32_t *order,
+                            int32_t *die_of, int32_t *slot_of, int32_t *die_list,
+                            int32_t *die_heads) {
     static_assert(kDies == 8, "the die loop covers 8 dies");
-    __shared__ int32_t order[kMaxHeads];
-    __shared__ int32_t die_of[kMaxHeads], slot_of[kMaxHeads];
-    __shared__ int32_t die_list[kDies * kMaxHeads];   // die x's heads in slot order
-    __shared__ int32_t die_heads[kDies];
-    __shared__ int32_t bases[2 * kMaxHeads];
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, nthreads = blockDim.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int cap_h = min(H, (H + kDies - 1) / kDies + 2);
-    const int cap = cap_h * nb;   // below 2^31: 8 * cap <= 8 * H * nb
-    for (int h = tid; h < H; h += kPlanThreads) {
+    for (int h = tid; h < H; h += nthreads) {
         int rank = 0;
         for (int o = 0; o < H; ++o)
             rank += (weight[o] > weight[h]) || (weight[o] == weight[h] && o < h);
@@ -961,47 +982,105 @@ __device__ const int32_t *plan_dies(int H, int nb, bool narrow, const int32_t *l
         }
     }
     __syncthreads();
-    // Each head's two bases: its die's non-empty rows come first (heads in
-    // slot order), then the die's empty rows (same order).
-    for (int h = tid; h < H; h += kPlanThreads) {
-        const int x = die_of[h], sl = slot_of[h];
-        int ne_before = 0, ne_die = 0, em_before = 0;
-        for (int c = 0; c < die_heads[x]; ++c) {
-            const int n_o = ne[die_list[x * cap_h + c]];
-            ne_die += n_o;
-            if (c < sl) {
-                ne_before += n_o;
-                em_before += nb - n_o;
-            }
+}
+
+// Head h's first position among its die's non-empty rows (x) and among its
+// die's empty rows (y): a die's non-empty rows come first (heads in slot
+// order), then its empty rows (same order).
+__device__ int2 head_bases(int h, int nb, int cap, int cap_h, const int32_t *ne,
+                           const int32_t *die_of, const int32_t *slot_of,
+                           const int32_t *die_list, const int32_t *die_heads) {
+    const int x = die_of[h], sl = slot_of[h];
+    int ne_before = 0, ne_die = 0, em_before = 0;
+    for (int c = 0; c < die_heads[x]; ++c) {
+        const int n_o = ne[die_list[x * cap_h + c]];
+        ne_die += n_o;
+        if (c < sl) {
+            ne_before += n_o;
+            em_before += nb - n_o;
         }
-        bases[2 * h] = head_base[2 * h] = x * cap + ne_before;
-        bases[2 * h + 1] = head_base[2 * h + 1] = x * cap + ne_die + em_before;
     }
-    // Padding: the positions past each die's heads.
-    for (int q = tid; q < kDies * cap; q += kPlanThreads) {
-        const int x = q / cap;
-        if (q - x * cap >= die_heads[x] * nb) {
+    return make_int2(x * cap + ne_before, x * cap + ne_die + em_before);
+}
+
+// Padding records (row -1) at the positions past each die's heads, for
+// positions first, first + stride, ...
+__device__ void plan_padding(int nb, int cap, const int32_t *die_heads, int64_t first,
+                             int64_t stride, int32_t *__restrict__ work,
+                             int4 *__restrict__ work_rec) {
+    for (int64_t q = first; q < (int64_t)kDies * cap; q += stride) {
+        const int x = (int)(q / cap);
+        if (q - (int64_t)x * cap >= (int64_t)die_heads[x] * nb) {
             work[q] = -1;
             work_rec[q] = make_int4(-1, 0, 0, 0);
         }
     }
-    if (tid == 0) {
-        int nonempty = 0;
-        for (int h = 0; h < H; ++h) nonempty += ne[h];
-        meta[kMetaCap] = (int32_t)cap;
-        meta[kMetaNonEmpty] = nonempty;
-        const uint64_t addr = reinterpret_cast<uint64_t>(list);
-        meta[kMetaListLo] = (int32_t)(uint32_t)addr;
-        meta[kMetaListHi] = (int32_t)(uint32_t)(addr >> 32);
-        meta[kMetaNnz] = (int32_t)nnz;
-        meta[kMetaHeads] = H;
-        meta[kMetaNb] = nb;
-        meta[kMetaCheck] = 0;
-    }
-    __syncthreads();
-    return bases;
 }
 
+// The meta words: positions per die, non-empty rows, and the tag of the list
+// the plan describes (address, length, heads, blocks per row), with the
+// stale-list check word cleared.
+__device__ void plan_meta(int H, int nb, int cap, const int32_t *ne, const int32_t *list,
+                          int64_t nnz, int32_t *__restrict__ meta) {
+    int nonempty = 0;
+    for (int h = 0; h < H; ++h) nonempty += ne[h];
+    meta[kMetaCap] = (int32_t)cap;
+    meta[kMetaNonEmpty] = nonempty;
+    const uint64_t addr = reinterpret_cast<uint64_t>(list);
+    meta[kMetaListLo] = (int32_t)(uint32_t)addr;
+    meta[kMetaListHi] = (int32_t)(uint32_t)(addr >> 32);
+    meta[kMetaNnz] = (int32_t)nnz;
+    meta[kMetaHeads] = H;
+    meta[kMetaNb] = nb;
+    meta[kMetaCheck] = 0;
+}
+
+// One wave: a head's rows (records rec[i] and clamped list lengths ln[i] of
+// rows r0 + i, i < nb, in LDS; ne_cnt of them non-empty) by list length
+// descending, ties by row id, to positions ne_base + rank (non-empty rows)
+// and em_base + rank - ne_cnt (empty rows).  nx is LDS for nb + 1 counters.
+__device__ void place_head_rows(int nb, int64_t r0, int ne_cnt, int64_t ne_base, int64_t em_base,
+                                int32_t *nx, const int16_t *ln, const int4 *rec,
+                                int32_t *__restrict__ work, int4 *__restrict__ work_rec) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t lt = lanemask_lt();
+    for (int l = lane; l <= nb; l += 64) nx[l] = 0;
+    for (int i = lane; i < nb; i += 64) atomicAdd(&nx[ln[i]], 1);
+    // Bucket starts, longest lists first: nx[l] = rows with length > l.
+    int carry = 0;
+    for (int c0 = nb; c0 >= 0; c0 -= 64) {
+        const int l = c0 - lane;
+        const int cnt = l >= 0 ? nx[l] : 0;
+        int inc = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o);
+            if (lane >= o) inc += y;
+        }
+        if (l >= 0) nx[l] = carry + inc - cnt;
+        carry += __shfl(inc, 63);
+    }
+    for (int i0 = 0; i0 < nb; i0 += 64) {
+        const int i = i0 + lane;
+        const bool valid = i < nb;
+        const int len = valid ? ln[i] : 0;
+        uint64_t same = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 11; ++bit) {
+            const bool mine = (len >> bit) & 1;
+            const uint64_t b = __ballot(valid && mine);
+            same &= mine ? b : ~b;
+        }
+        const int rank = __popcll(same & lt);
+        const int pos = valid ? nx[len] + rank : 0;
+        if (valid && pos < nb) {
+            const int64_t at = pos < ne_cnt ? ne_base + pos : em_base + (pos - ne_cnt);
+            work[at] = (int32_t)(r0 + i);
+            work_rec[at] = rec[i];
+        }
+        if (valid && rank == 0) nx[len] += __popcll(same);
+    }
+}
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__restrict__ row_ptr,
                                                               const int32_t *list, int64_t nnz,
@@ -1014,69 +1093,82 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_assign(const int32_t *__r
                                                               int32_t *__restrict__ meta) {
     __shared__ int64_t weight[kMaxHeads];
     __shared__ int32_t ne[kMaxHeads];
+    __shared__ int32_t order[kMaxHeads];
+    __shared__ int32_t die_of[kMaxHeads], slot_of[kMaxHeads];
+    __shared__ int32_t die_list[kDies * kMaxHeads];
+    __shared__ int32_t die_heads[kDies];
     const int tid = threadIdx.x, lane = tid & 63;
     if (head_counts) {   // counted by the list launch
-        for (int h = tid; h < H; h += kPlanThreads)
+        for (int h = tid; h < H; h += kPlanThreads) {
             weight[h] = (int64_t)steps_per_block * head_counts[h] + 4 * (int64_t)head_counts[H + h];
-        for (int h = tid; h < H; h += kPlanThreads) ne[h] = head_counts[H + h];
+            ne[h] = head_counts[H + h];
+        }
+    } else {
+        // Per head: rows that keep a block and blocks kept.  Thread t reads
+        // the bounds of rows 4u .. 4u + 3, u = t, t + 1024, ..., all in one
+        // batch per round; a wave's rows that fall in one head add with one
+        // LDS atomic.
+        __shared__ int32_t kept[kMaxHeads];
+        for (int h = tid; h < H; h += kPlanThreads) ne[h] = kept[h] = 0;
         __syncthreads();
-        plan_dies(H, nb, narrow, list, nnz, weight, ne, head_base, work, work_rec, meta);
-        return;
-    }
-    // Per head: rows that keep a block and blocks kept.  Thread t reads the
-    // bounds of rows 4u .. 4u + 3, u = t, t + 1024, ..., all in one batch per
-    // round; a wave's rows that fall in one head add with one LDS atomic.
-    __shared__ int32_t kept[kMaxHeads];
-    for (int h = tid; h < H; h += kPlanThreads) ne[h] = kept[h] = 0;
-    __syncthreads();
-    const int rows = H * nb;
-    for (int r0 = 0; r0 < rows; r0 += 4 * kPlanThreads) {
-        const int r = r0 + 4 * tid;
-        int v[5];
+        const int rows = H * nb;
+        for (int r0 = 0; r0 < rows; r0 += 4 * kPlanThreads) {
+            const int r = r0 + 4 * tid;
+            int v[5];
 #pragma unroll
-        for (int k = 0; k < 5; ++k) v[k] = row_ptr[min(r + k, rows)];
-        // Rows of the thread's first row's head are summed here; rows of later
-        // heads (only where a head boundary falls inside the four) add one by
-        // one below.
-        const int h_lo = min(r, rows - 1) / nb;
-        int ne_lo = 0, kept_lo = 0;
+            for (int k = 0; k < 5; ++k) v[k] = row_ptr[min(r + k, rows)];
+            // Rows of the thread's first row's head are summed here; rows of
+            // later heads (only where a head boundary falls inside the four)
+            // add one by one below.
+            const int h_lo = min(r, rows - 1) / nb;
+            int ne_lo = 0, kept_lo = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int len = v[k + 1] - v[k];
-            if (r + k < rows && len > 0) {
-                if ((r + k) / nb == h_lo) {
-                    ++ne_lo;
-                    kept_lo += len;
-                } else {
-                    atomicAdd(&ne[(r + k) / nb], 1);
-                    atomicAdd(&kept[(r + k) / nb], len);
+            for (int k = 0; k < 4; ++k) {
+                const int len = v[k + 1] - v[k];
+                if (r + k < rows && len > 0) {
+                    if ((r + k) / nb == h_lo) {
+                        ++ne_lo;
+                        kept_lo += len;
+                    } else {
+                        atomicAdd(&ne[(r + k) / nb], 1);
+                        atomicAdd(&kept[(r + k) / nb], len);
+                    }
                 }
             }
-        }
-        // Lanes of the wave with the same head add with one atomic.
-        uint64_t todo = __ballot(r < rows);
-        while (todo) {
-            const int leader = __builtin_ctzll(todo);
-            const int hl = __builtin_amdgcn_readlane(h_lo, leader);
-            const uint64_t same = __ballot(r < rows && h_lo == hl) & todo;
-            int a = (same >> lane) & 1 ? ne_lo : 0, b = (same >> lane) & 1 ? kept_lo : 0;
+            // Lanes of the wave with the same head add with one atomic.
+            uint64_t todo = __ballot(r < rows);
+            while (todo) {
+                const int leader = __builtin_ctzll(todo);
+                const int hl = __builtin_amdgcn_readlane(h_lo, leader);
+                const uint64_t same = __ballot(r < rows && h_lo == hl) & todo;
+                int a = (same >> lane) & 1 ? ne_lo : 0, b = (same >> lane) & 1 ? kept_lo : 0;
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                a += __shfl_xor(a, o);
-                b += __shfl_xor(b, o);
+                for (int o = 32; o > 0; o >>= 1) {
+                    a += __shfl_xor(a, o);
+                    b += __shfl_xor(b, o);
+                }
+                if (lane == leader) {
+                    atomicAdd(&ne[hl], a);
+                    atomicAdd(&kept[hl], b);
+                }
+                todo &= ~same;
             }
-            if (lane == leader) {
-                atomicAdd(&ne[hl], a);
-                atomicAdd(&kept[hl], b);
-            }
-            todo &= ~same;
         }
+        __syncthreads();
+        for (int h = tid; h < H; h += kPlanThreads)
+            weight[h] = (int64_t)steps_per_block * kept[h] + 4 * (int64_t)ne[h];
     }
     __syncthreads();
-    for (int h = tid; h < H; h += kPlanThreads)
-        weight[h] = (int64_t)steps_per_block * kept[h] + 4 * (int64_t)ne[h];
-    __syncthreads();
-    plan_dies(H, nb, narrow, list, nnz, weight, ne, head_base, work, work_rec, meta);
+    const int cap_h = min(H, (H + kDies - 1) / kDies + 2);
+    const int cap = cap_h * nb;   // below 2^31: 8 * cap <= 8 * H * nb
+    assign_dies(H, narrow, cap_h, weight, order, die_of, slot_of, die_list, die_heads);
+    for (int h = tid; h < H; h += kPlanThreads) {
+        const int2 b = head_bases(h, nb, cap, cap_h, ne, die_of, slot_of, die_list, die_heads);
+        head_base[2 * h] = b.x;
+        head_base[2 * h + 1] = b.y;
+    }
+    plan_padding(nb, cap, die_heads, tid, kPlanThreads, work, work_rec);
+    if (tid == 0) plan_meta(H, nb, cap, ne, list, nnz, meta);
 }
 
 __global__ __launch_bounds__(64) void k_plan_rows(const int32_t *__restrict__ row_ptr,
@@ -1091,9 +1183,7 @@ __global__ __launch_bounds__(64) void k_plan_rows(const int32_t *__restrict__ ro
     __shared__ int16_t ln[kMaxBlocks];
     __shared__ int4 rec[kMaxBlocks];
     const int lane = threadIdx.x, h = blockIdx.x;
-    const uint64_t lt = lanemask_lt();
     const int64_t r0 = (int64_t)h * nb;
-    const int64_t ne_base = head_base[2 * h], em_base = head_base[2 * h + 1];
     int my_ne = 0;
     if (rec_in) {   // records formed by the list launch
         for (int i = lane; i < nb; i += 64) {
@@ -1144,43 +1234,51 @@ __global__ __launch_bounds__(64) void k_plan_rows(const int32_t *__restrict__ ro
             my_ne += len > 0;
         }
     }
-    const int ne_cnt = wave_sum(my_ne);   // the sorted order puts these first
-    for (int l = lane; l <= nb; l += 64) nx[l] = 0;
-    for (int i = lane; i < nb; i += 64) atomicAdd(&nx[ln[i]], 1);
-    // Bucket starts, longest lists first: nx[l] = rows with length > l.
-    int carry = 0;
-    for (int c0 = nb; c0 >= 0; c0 -= 64) {
-        const int l = c0 - lane;
-        const int cnt = l >= 0 ? nx[l] : 0;
-        int inc = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(inc, o);
-            if (lane >= o) inc += y;
-        }
-        if (l >= 0) nx[l] = carry + inc - cnt;
-        carry += __shfl(inc, 63);
+    place_head_rows(nb, r0, wave_sum(my_ne), head_base[2 * h], head_base[2 * h + 1], nx, ln, rec,
+                    work, work_rec);
+}
+
+// The whole plan in one launch from the mask build's records and head counts
+// (H <= kPlanHeadsMax): workgroup h stages head h's records, redoes the die
+// part, writes its share of the padding (workgroup 0 also the meta words)
+// and places head h's rows, exactly as k_plan_assign then k_plan_rows do.
+__global__ __launch_bounds__(kPlanHeadsThreads) void k_plan_heads(
+    const int32_t *list, int64_t nnz, int H, int nb, int steps_per_block, bool narrow,
+    const int32_t *__restrict__ head_counts, const int4 *__restrict__ rec_in,
+    int32_t *__restrict__ work, int4 *__restrict__ work_rec, int32_t *__restrict__ meta) {
+    __shared__ int64_t weight[kPlanHeadsMax];
+    __shared__ int32_t ne[kPlanHeadsMax];
+    __shared__ int32_t order[kPlanHeadsMax];
+    __shared__ int32_t die_of[kPlanHeadsMax], slot_of[kPlanHeadsMax];
+    __shared__ int32_t die_list[kDies * kPlanHeadsMax];
+    __shared__ int32_t die_heads[kDies];
+    __shared__ int32_t nx[kMaxBlocks + 1];
+    __shared__ int16_t ln[kMaxBlocks];
+    __shared__ int4 rec[kMaxBlocks];
+    const int tid = threadIdx.x, h = blockIdx.x;
+    const int64_t r0 = (int64_t)h * nb;
+    // The head's records and every head's counts, loads issued together.
+    for (int i = tid; i < nb; i += kPlanHeadsThreads) {
+        const int4 rc = rec_in[r0 + i];
+        rec[i] = rc;
+        ln[i] = (int16_t)min(max(rc.z - rc.y, 0), nb);
     }
-    for (int i0 = 0; i0 < nb; i0 += 64) {
-        const int i = i0 + lane;
-        const bool valid = i < nb;
-        const int len = valid ? ln[i] : 0;
-        uint64_t same = __ballot(valid);
-#pragma unroll
-        for (int bit = 0; bit < 11; ++bit) {
-            const bool mine = (len >> bit) & 1;
-            const uint64_t b = __ballot(valid && mine);
-            same &= mine ? b : ~b;
-        }
-        const int rank = __popcll(same & lt);
-        const int pos = valid ? nx[len] + rank : 0;
-        if (valid && pos < nb) {
-            const int64_t at = pos < ne_cnt ? ne_base + pos : em_base + (pos - ne_cnt);
-            work[at] = (int32_t)(r0 + i);
-            work_rec[at] = rec[i];
-        }
-        if (valid && rank == 0) nx[len] += __popcll(same);
+    for (int x = tid; x < H; x += kPlanHeadsThreads) {
+        weight[x] = (int64_t)steps_per_block * head_counts[x] + 4 * (int64_t)head_counts[H + x];
+        ne[x] = head_counts[H + x];
     }
+    __syncthreads();
+    const int cap_h = min(H, (H + kDies - 1) / kDies + 2);
+    const int cap = cap_h * nb;
+    assign_dies(H, narrow, cap_h, weight, order, die_of, slot_of, die_list, die_heads);
+    plan_padding(nb, cap, die_heads, (int64_t)h * kPlanHeadsThreads + tid,
+                 (int64_t)gridDim.x * kPlanHeadsThreads, work, work_rec);
+    if (h == 0 && tid == 0) plan_meta(H, nb, cap, ne, list, nnz, meta);
+    if (tid >= 64) return;
+    int my_ne = 0;
+    for (int i = tid; i < nb; i += 64) my_ne += ln[i] > 0;
+    const int2 b = head_bases(h, nb, cap, cap_h, ne, die_of, slot_of, die_list, die_heads);
+    place_head_rows(nb, r0, wave_sum(my_ne), b.x, b.y, nx, ln, rec, work, work_rec);
 }
 
 }  // namespace
@@ -1316,6 +1414,12 @@ hipError_t launch_plan(const Dims &D, const int32_t *row_ptr, const int32_t *col
     const int32_t *head_counts =
         prepared ? reinterpret_cast<const int32_t *>(ws + w.head_counts) : nullptr;
     const int4 *rec_in = prepared ? reinterpret_cast<const int4 *>(ws + w.row_rec) : nullptr;
+    if (prepared && D.H <= kPlanHeadsMax) {
+        hipLaunchKernelGGL(k_plan_heads, dim3(D.H), dim3(kPlanHeadsThreads), 0, s, col_idx, nnz,
+                           D.H, D.nb, D.B / 32, plan_narrow(D, nnz), head_counts, rec_in, work,
+                           work_rec, meta);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_plan_assign, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, col_idx, nnz,
                        D.H, D.nb, D.B / 32, plan_narrow(D, nnz), head_counts, head_base, work,
                        work_rec, meta);

@@ -117,10 +117,11 @@ def test_plan_matches_oracle(shape):
 @pytest.mark.parametrize("s", [0.0, 0.5, 0.93, 1.0])
 @pytest.mark.parametrize("shape", SHAPES, ids=SHAPE_IDS)
 def test_mask_build_plan_equals_plan_launch(shape, s):
-    """The global-budget mask build writes the lists and the work order in
-    one launch (per-head part in every workgroup, dies in the last one); a
-    separate plan launch on the lists it wrote gives the same work order,
-    records and meta words, including K = 0 and every block kept."""
+    """The global-budget mask build plans from the records and head counts
+    its list launch wrote (one launch, every workgroup redoing the die part);
+    a separate plan launch on the lists it wrote (die part, then rows) gives
+    the same work order, records and meta words, including K = 0 and every
+    block kept."""
     H, Hkv, L, d, blk, _ = shape
     q, k, v = _qkv(shape, 505)
     m = PT.GpuMask(q, k, blk, s)
@@ -130,6 +131,28 @@ def test_mask_build_plan_equals_plan_launch(shape, s):
     assert torch.equal(fused[0], m.buf.work())
     assert torch.equal(fused[1], m.buf.work_rec())
     assert torch.equal(fused[2], m.buf.work_meta()[:8])
+
+
+@pytest.mark.parametrize("H", [255, 256, 257, 300])
+def test_mask_build_plan_many_heads(H):
+    """Around the one-launch plan's head limit (256; past it the mask build
+    plans in two launches): the oracle's work order and records, and the
+    same order from a separate plan launch."""
+    shape = (H, H, 3 * 64, 64, 64, 1.0)
+    q, k, v = _qkv(shape, 707)
+    m = PT.GpuMask(q, k, 64, 0.7)
+    rp, ci = m.csr()
+    work_ref, n_ref = O.plan(rp, H, 3, 64)
+    work = m.buf.work().cpu().numpy()
+    assert np.array_equal(work, work_ref)
+    assert int(m.buf.work_meta().cpu().numpy()[1]) == n_ref
+    _check_records(m.buf.work_rec().cpu().numpy(), work_ref, rp, ci)
+    fused = (m.buf.work_rec().clone(), m.buf.work_meta()[:8].clone())
+    B.plan(m.dims, m.buf.row_ptr, m.buf.col_idx, m.buf.ws, nnz=m.K)
+    torch.cuda.synchronize()
+    assert np.array_equal(m.buf.work().cpu().numpy(), work)
+    assert torch.equal(fused[0], m.buf.work_rec())
+    assert torch.equal(fused[1], m.buf.work_meta()[:8])
 
 
 @pytest.mark.parametrize("H,nb,blk", [(64, 320, 64), (28, 129, 128), (3, 1024, 64), (13, 7, 128)])
