@@ -699,14 +699,19 @@ __global__ __launch_bounds__(256) void k_row_scatter(const float *__restrict__ p
 // One workgroup per head: the k_h-th largest order key of the head's nb*nb
 // scores by the same three digit passes, with the histogram in LDS.  State
 // words at hsel[h * kHeadSelWords]: cut key, count above it, ties to keep, k_h.
-__global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ p, int64_t per,
-                                                      int64_t k_h,
-                                                      uint32_t *__restrict__ hsel) {
+// The select of one head by its 1024-thread workgroup (ph: the head's per
+// scores), its state words written to out; returns the cut and the ties to
+// keep to every thread.
+struct CutTies {
+    uint32_t cut;
+    int64_t ties;
+};
+
+__device__ CutTies head_select(const float *__restrict__ ph, int64_t per, int64_t k_h,
+                               uint32_t *__restrict__ out) {
     __shared__ uint32_t hist[kRadixBins];
     __shared__ uint32_t win[2];
-    const int h = blockIdx.x, tid = threadIdx.x;
-    const float *ph = p + (int64_t)h * per;
-    uint32_t *out = hsel + (int64_t)h * kHeadSelWords;
+    const int tid = threadIdx.x;
     if (k_h <= 0) {   // nothing kept: no score is above the cut, no tie is kept
         if (tid == 0) {
             out[SEL_CUT] = 0xFFFFFFFFu;
@@ -714,7 +719,7 @@ __global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ 
             out[SEL_TIES] = 0;
             out[SEL_K] = 0;
         }
-        return;
+        return CutTies{0xFFFFFFFFu, 0};
     }
     uint32_t prefix = 0;
     int64_t remain = k_h;   // rank wanted inside the prefix bucket, counted from the top
@@ -755,6 +760,14 @@ __global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ 
         out[SEL_TIES] = (uint32_t)remain;
         out[SEL_K] = (uint32_t)k_h;
     }
+    return CutTies{prefix, remain};
+}
+
+__global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ p, int64_t per,
+                                                      int64_t k_h,
+                                                      uint32_t *__restrict__ hsel) {
+    const int h = blockIdx.x;
+    head_select(p + (int64_t)h * per, per, k_h, hsel + (int64_t)h * kHeadSelWords);
 }
 
 // One workgroup per head: cut ties before each row within the head (flat
@@ -797,18 +810,21 @@ __global__ __launch_bounds__(1024) void k_kept_scan(const int32_t *__restrict__ 
 
 // ------------------------------------------------------------ column lists --
 // Column-sparse variant ("PulseCol" abstract: column-sparse attention): head
-// h keeps the k_c largest of its L column masses, the per-head select state
-// (cut key, ties kept at the cut) coming from k_head_select.  One workgroup
-// per head; thread t owns a contiguous run of columns.  Ties at the cut are
-// kept in ascending column order, so the kept set is the top-k_c under
-// (value descending, index ascending) and the list comes out ascending.
-__global__ __launch_bounds__(1024) void k_col_compact(const float *__restrict__ c, int L,
-                                                      const uint32_t *__restrict__ hsel,
-                                                      int64_t k_c, int32_t *__restrict__ cols) {
+// h keeps the k_c largest of its L column masses.  One workgroup per head
+// takes the head's select (as k_head_select, state words to hsel) and then
+// writes its list: thread t owns a contiguous run of columns.  Ties at the
+// cut are kept in ascending column order, so the kept set is the top-k_c
+// under (value descending, index ascending) and the list comes out
+// ascending.
+__global__ __launch_bounds__(1024) void k_col_select(const float *__restrict__ c, int L,
+                                                     uint32_t *__restrict__ hsel, int64_t k_c,
+                                                     int32_t *__restrict__ cols) {
     const int h = blockIdx.x, tid = threadIdx.x;
     const float *ch = c + (int64_t)h * L;
-    const uint32_t cut = hsel[(int64_t)h * kHeadSelWords + SEL_CUT];
-    const int64_t ties = hsel[(int64_t)h * kHeadSelWords + SEL_TIES];
+    const CutTies ct = head_select(ch, L, k_c, hsel + (int64_t)h * kHeadSelWords);
+    if (k_c <= 0) return;   // an empty list
+    const uint32_t cut = ct.cut;
+    const int64_t ties = ct.ties;
     const int per = (L + 1023) / 1024;
     const int lo = min(L, tid * per), hi = min(L, lo + per);
     int64_t n_eq = 0;
@@ -1330,9 +1346,7 @@ hipError_t launch_pool_q(const Dims &D, const uint16_t *q, float *qb, hipStream_
 hipError_t launch_col_select(const Dims &D, int64_t k_c, const float *c, char *ws,
                              const WsLayout &w, int32_t *cols, hipStream_t s) {
     uint32_t *hsel = reinterpret_cast<uint32_t *>(ws + w.hsel);
-    hipLaunchKernelGGL(k_head_select, dim3(D.H), dim3(1024), 0, s, c, (int64_t)D.L, k_c, hsel);
-    if (k_c > 0)
-        hipLaunchKernelGGL(k_col_compact, dim3(D.H), dim3(1024), 0, s, c, D.L, hsel, k_c, cols);
+    hipLaunchKernelGGL(k_col_select, dim3(D.H), dim3(1024), 0, s, c, D.L, hsel, k_c, cols);
     return hipGetLastError();
 }
 
