@@ -23,6 +23,12 @@ and evaluation data are not available:
   block and 4 random ones), with a = structure * (4 * sqrt(d))^(1/2), so a
   target pair scores about +4 * structure^2 before the head temperature.  The
   targets and directions are redrawn with Q and K.
+* Shared query heads (the shared-GQA 8K variant only): the query heads of one
+  KV group are one draw shared by the group plus a small draw of their own,
+  q_h = sqrt(shared) * base_g + sqrt(1 - shared) * own_h, and the heads of a
+  group take one temperature (the group's), so a group's heads keep nearly
+  the same blocks: the case sharing K/V tiles across a group's heads is for.
+  Redrawn with Q and K.
 * Column structure (the column-structured 8K variant only): each key head g
   draws one unit direction e[g] and L/64 heavy key tokens at random positions
   (not block-aligned); each heavy key gets + a * e[g] and every query token of
@@ -56,6 +62,7 @@ class Workload:
     seed: int = 0
     structure: float = 0.0  # block-affinity strength (0 = i.i.d. inputs)
     columns: float = 0.0    # heavy-column strength (0 = none)
+    shared: float = 0.0     # variance a KV group's query heads share (0 = independent heads)
 
     @property
     def nb(self):
@@ -91,6 +98,10 @@ WORKLOADS = {
                              sparsities=(0.7, 0.8, 0.9, 0.95), steps=64, dense_steps=0,
                              refresh_every=16, temperatures=True, sinks=False, drift=0.02,
                              seed=1004),
+    "dream_gqa_8k_shared": Workload("dream_gqa_8k_shared", H=28, Hkv=4, L=8192, d=128, B=64,
+                                    sparsities=(0.7, 0.8, 0.9, 0.95), steps=64, dense_steps=0,
+                                    refresh_every=16, temperatures=True, sinks=False,
+                                    drift=0.02, seed=1008, shared=0.99),
     "long_64k": Workload("long_64k", H=32, Hkv=32, L=65536, d=128, B=128, sparsities=(0.95,),
                          steps=128, dense_steps=26, refresh_every=0, temperatures=False,
                          sinks=True, drift=0.0, seed=1005),
@@ -114,8 +125,13 @@ class Trajectory:
     def __init__(self, w: Workload, device="cpu"):
         self.w = w
         self.device = torch.device(device)
-        self.temps = (head_temperatures(w.H, w.seed) if w.temperatures
-                      else torch.ones(w.H, dtype=torch.float32)).to(self.device)
+        if w.temperatures and w.shared:   # one temperature per KV group
+            temps = head_temperatures(w.Hkv, w.seed).repeat_interleave(w.H // w.Hkv)
+        elif w.temperatures:
+            temps = head_temperatures(w.H, w.seed)
+        else:
+            temps = torch.ones(w.H, dtype=torch.float32)
+        self.temps = temps.to(self.device)
         self.gen = torch.Generator(device=self.device).manual_seed(w.seed)
         self.step = 0
         self.q, self.k = self._draw_qk()
@@ -130,6 +146,10 @@ class Trajectory:
         k = self._randn(w.Hkv, w.L, w.d)
         if w.sinks:
             k[:, 0:4, :] *= 4.0
+        if w.shared:
+            base = self._randn(w.Hkv, w.L, w.d)
+            g = torch.arange(w.H, device=self.device) // (w.H // w.Hkv)
+            q = math.sqrt(w.shared) * base[g] + math.sqrt(1.0 - w.shared) * q
         if w.structure:
             a = w.structure * math.sqrt(4.0 * math.sqrt(w.d))
             e = self._randn(w.Hkv, w.nb, w.d)

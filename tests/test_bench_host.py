@@ -132,3 +132,22 @@ def test_data_path_block_units():
     assert bench.data_path_block(paths, flops, 128, 0.14)["fill_bytes_per_launch"] == \
         out["fill_bytes_per_launch"] / 2
     assert bench.data_path_block(paths, flops, 64, None)["fill_achieved_tbs"] is None
+
+
+def test_shared_gqa_inputs():
+    """dream_gqa_8k_shared: a KV group's query heads are one shared draw plus
+    a small own draw (correlation sqrt(0.99)^2 = 0.99 before rounding) with one
+    temperature per group; heads of different groups are independent."""
+    import torch
+    w = WORKLOADS["dream_gqa_8k_shared"]
+    tr = Trajectory(w)
+    G = w.H // w.Hkv
+    assert torch.equal(tr.temps.view(w.Hkv, G), tr.temps.view(w.Hkv, G)[:, :1].expand(w.Hkv, G))
+    assert len(set(tr.temps.view(w.Hkv, G)[:, 0].tolist())) == w.Hkv
+    q = tr.next()[0].float()[:, :1024].reshape(w.H, -1)
+    q = q / q.norm(dim=1, keepdim=True)
+    c = q @ q.T
+    g = torch.arange(w.H) // G
+    same = (g.view(-1, 1) == g.view(1, -1)) & ~torch.eye(w.H, dtype=torch.bool)
+    assert c[same].min() > 0.98
+    assert c[g.view(-1, 1) != g.view(1, -1)].abs().max() < 0.02
