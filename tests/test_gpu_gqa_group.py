@@ -137,10 +137,14 @@ def test_group_rejects_block_128():
     assert e.value.status == B.EUNSUPPORTED
 
 
-@pytest.mark.parametrize("s", [0.7, 0.9])
-def test_group_equals_per_head_at_full_size(s):
-    """The Dream-shaped GQA layer (H=28, Hkv=4, L=8192, d=128) at its anchor."""
-    w = WORKLOADS["dream_gqa_8k"]
+@pytest.mark.parametrize("name,s", [("dream_gqa_8k", 0.7), ("dream_gqa_8k", 0.9),
+                                    ("dream_gqa_8k_shared", 0.7), ("dream_gqa_8k_shared", 0.95)])
+def test_group_equals_per_head_at_full_size(name, s):
+    """The Dream-shaped GQA layer (H=28, Hkv=4, L=8192, d=128) at its anchor,
+    with independent heads and with a KV group's heads keeping nearly the same
+    blocks (long shared runs in every pair's union); on the shared inputs the
+    group output is also checked against the oracle on sampled rows."""
+    w = WORKLOADS[name]
     q, k, v = Trajectory(w, DEV).next()
     dims = B.make_dims(w.H, w.Hkv, w.L, w.d, w.B)
     buf = B.MaskBuffers(dims, s, device=DEV)
@@ -150,3 +154,13 @@ def test_group_equals_per_head_at_full_size(s):
     o = _group(dims, q, k, v, buf.row_ptr, buf.col_idx, buf.K)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref)
+    if w.shared:
+        rp = buf.row_ptr.cpu().numpy()
+        ci = buf.col_idx[:buf.K].cpu().numpy()
+        rows = PT.sample_rows(rp, w.H, w.nb, heads=(0, 1), n_longest=32, n_random=32)
+        qf, kf, vf = PT.oracle_inputs(q, k, v)
+        out = np.zeros(qf.shape, np.float64)
+        PT.oracle_rows_parallel(O.sparse_attn, rows, q=qf, k=kf, v=vf, B=w.B, row_ptr=rp,
+                                col_idx=ci, out=out)
+        stats = PT.check_outputs(o, out, PT.token_mask_for_rows(rows, w.H, w.nb, w.B))
+        print(f"{name} s={s} group: {len(rows)} rows {stats}", flush=True)
