@@ -1,5 +1,7 @@
 """Per-kernel parity of the HIP library against the oracle, through the C ABI,
 at sizes the oracle finishes in seconds (several tiles plus ragged tails)."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -450,3 +452,38 @@ def test_tiny_workload_end_to_end():
     B.dense_attn(drv.dims, q, k, v, o_d)
     torch.cuda.synchronize()
     PT.check_outputs(o_d, O.dense_attn(qf, kf, vf, w.B))
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0], ids=["rising", "falling"])
+@pytest.mark.parametrize("d,blk", [(128, 64), (64, 128)])
+def test_scores_moving_past_the_rescale_margin(d, blk, sign):
+    """Every key shares one direction with every query and its score moves by
+    about 0.45 natural units per key, about 21 log2 units per 32-key chunk.
+    That is past the lazy rescale's margin of 8, so with rising scores the
+    running max moves at every chunk of every row and O and the normaliser
+    are rescaled each time, by factors down to about 2^-21 per chunk.  With
+    falling scores the first chunk holds the max and every later weight
+    underflows.  Sparse and dense, against the oracle.  The sparse mask is the
+    library's at s = 0.5.  Most pooled scores underflow to exact zeros, so the
+    ties at zero fill the budget in flat order: the first rows keep every
+    block, and the others keep their few nonzero blocks."""
+    H, Hkv, L = 2, 2, 1024
+    g = torch.Generator().manual_seed(1212)
+    e = torch.ones(d, dtype=torch.float64) / math.sqrt(d)
+    a = sign * 0.45 * math.sqrt(d) / 4.0 * torch.arange(L, dtype=torch.float64)
+    q = 4.0 * e.expand(H, L, d) + 0.05 * torch.randn(H, L, d, generator=g, dtype=torch.float64)
+    k = a.view(1, L, 1) * e.view(1, 1, d) + 0.05 * torch.randn(Hkv, L, d, generator=g,
+                                                                dtype=torch.float64)
+    v = torch.randn(Hkv, L, d, generator=g, dtype=torch.float64)
+    q, k, v = (x.to(torch.bfloat16).to(DEV) for x in (q, k, v))
+    qf, kf, vf = PT.oracle_inputs(q, k, v)
+    m = PT.GpuMask(q, k, blk, 0.5)
+    o = torch.full_like(q, float("nan"))
+    B.sparse_attn(m.dims, q, k, v, m.buf.col_idx, m.buf.ws, o)
+    torch.cuda.synchronize()
+    rp, ci = m.csr()
+    PT.check_outputs(o, O.sparse_attn(qf, kf, vf, blk, rp, ci))
+    od = torch.full_like(q, float("nan"))
+    B.dense_attn(m.dims, q, k, v, od)
+    torch.cuda.synchronize()
+    PT.check_outputs(od, O.dense_attn(qf, kf, vf, blk))
