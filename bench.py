@@ -708,6 +708,23 @@ def main():
     dense_ms = mean([a.elapsed_time(b) for a, b in dev_ev])
     dense_flops = 4.0 * w.H * w.L * w.L * w.d
 
+    # The sparse kernel on the last anchor's mask, with one step's inputs
+    # repeated (the 256 MB last-level cache then holds them), timed as one run
+    # of 32 launches: against kernel_ms, where every step reads fresh inputs
+    # from HBM, the share of a launch that waits on HBM.
+    resident_ms = None
+    if attn_ms and not args.columns:
+        qL, kL, vL = inputs[(start + K_steps - 1) % T]
+        for _ in range(3):
+            B.sparse_attn(dims, qL, kL, vL, drv.col_idx, drv.ws, o, nnz=drv.K, stream=stream)
+        ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ra.record(stream)
+        for _ in range(32):
+            B.sparse_attn(dims, qL, kL, vL, drv.col_idx, drv.ws, o, nnz=drv.K, stream=stream)
+        rb.record(stream)
+        torch.cuda.synchronize()
+        resident_ms = ra.elapsed_time(rb) / 32
+
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -737,6 +754,9 @@ def main():
         "kernel_ms": round(attn_ms, 5) if attn_ms else None,
         "kernel_launches_timed": n_reuse_timed,
     }
+    if resident_ms:
+        roofline["kernel_ms_resident_inputs"] = round(resident_ms, 5)
+        roofline["fresh_input_cost"] = round(attn_ms / resident_ms - 1.0, 4)
     # What the chip sustains under pure MFMA load (power-limited clock with
     # real-valued operands), measured after the timed region.
     rate = sustained_mfma_rate()
