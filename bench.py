@@ -67,8 +67,8 @@ def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=256)
-    # Two passes over the trajectory before timing: the first pass of a process
-    # over its inputs runs 2-3% slower than every later one.
+    # Two passes over the trajectory before timing: the first few hundred steps
+    # of a process run 2-3% slower than later ones, whichever inputs they read.
     p.add_argument("--warmup", type=int, default=512)
     p.add_argument("--runs", type=int, default=1,
                    help="time the K steps this many times and report the median run")
